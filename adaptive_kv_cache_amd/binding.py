@@ -1,0 +1,280 @@
+"""ctypes binding of libconfkv.so (the C ABI in include/confkv.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity (so no kernel is launched on operands of the wrong size) and their
+data pointers are handed to the library together with torch's current stream.
+Every step of the decode path runs in the library's HIP kernels; there is no
+fallback.  Loading fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_char_p, c_float, c_int, c_int32, c_size_t, c_void_p
+
+import torch
+
+from .workloads import Workload
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libconfkv.so")
+
+CONF_F16, CONF_BF16 = 1, 2
+DTYPE16 = {"f16": (CONF_F16, torch.float16), "bf16": (CONF_BF16, torch.bfloat16)}
+ST_WINDOW_FULL, ST_INT8_FULL = 1, 2
+
+EXPORTED = ("conf_cache_layout", "conf_workspace_bytes", "conf_cache_reset", "conf_cache_ingest",
+            "conf_confidence", "conf_decode_attn", "conf_rank_evict", "conf_compact_demote",
+            "conf_step", "conf_cache_export", "conf_last_error", "conf_status_string")
+
+
+class ConfParams(ctypes.Structure):
+    _fields_ = [(n, c_int32) for n in ("n_layers", "batch", "n_q_heads", "n_kv_heads", "head_dim",
+                                        "vocab", "dtype16", "window", "protect", "n_high", "n_low",
+                                        "cap8", "pyramid")] + \
+               [(n, c_float) for n in ("tau", "w_H", "w_m", "w_p", "ema_decay", "s_ema", "s_rec")]
+
+
+_CACHE_FIELDS = ("k8", "v8", "k16", "v16", "k_amax", "v_amax", "pos8", "ema8", "pos16", "ema16",
+                 "n8", "n16", "t", "status")
+
+
+class ConfCache(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in _CACHE_FIELDS]
+
+
+class ConfCacheBytes(ctypes.Structure):
+    _fields_ = [(n, c_size_t) for n in _CACHE_FIELDS] + [("cap16", c_int32)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libconfkv.so once; raise if it is missing (no fallback exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m adaptive_kv_cache_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, C = POINTER(ConfParams), POINTER(ConfCache)
+    vp = c_void_p
+    sig = {
+        "conf_cache_layout": [P, POINTER(ConfCacheBytes)],
+        "conf_workspace_bytes": [P, POINTER(c_size_t)],
+        "conf_cache_reset": [P, C, vp],
+        "conf_cache_ingest": [P, C, c_int32, vp, vp, c_int32, vp, vp],
+        "conf_confidence": [P, vp, vp, vp, vp, vp],
+        "conf_decode_attn": [P, C, c_int32, vp, vp, vp, vp, vp, vp],
+        "conf_rank_evict": [P, C, c_int32, vp, vp, vp, vp],
+        "conf_compact_demote": [P, C, c_int32, vp, vp, vp],
+        "conf_step": [P, C, vp, vp, vp, vp, vp, vp, vp, vp, vp],
+        "conf_cache_export": [P, C, c_int32, c_int32, vp, vp, vp, vp, vp],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = c_int
+    lib.conf_last_error.argtypes = []
+    lib.conf_last_error.restype = c_char_p
+    lib.conf_status_string.argtypes = [c_int]
+    lib.conf_status_string.restype = c_char_p
+    _lib = lib
+    return lib
+
+
+class ConfKVError(RuntimeError):
+    pass
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        lib = load()
+        msg = lib.conf_status_string(rc).decode()
+        extra = lib.conf_last_error().decode() if rc == -4 else ""
+        raise ConfKVError(f"{what} failed: {msg} ({rc}) {extra}".strip())
+
+
+def params_from_workload(wl: Workload, cap8: int | None = None, **over) -> ConfParams:
+    d = dict(n_layers=wl.n_layers, batch=wl.batch, n_q_heads=wl.n_q_heads,
+             n_kv_heads=wl.n_kv_heads, head_dim=wl.head_dim, vocab=wl.vocab,
+             dtype16=DTYPE16[wl.dtype16][0], window=wl.window, protect=wl.protect,
+             n_high=wl.n_high, n_low=wl.n_low, cap8=wl.cap8 if cap8 is None else cap8,
+             pyramid=int(wl.pyramid), tau=wl.tau, w_H=wl.w_H, w_m=wl.w_m, w_p=wl.w_p,
+             ema_decay=wl.ema_decay, s_ema=wl.s_ema, s_rec=wl.s_rec)
+    d.update(over)
+    return ConfParams(**d)
+
+
+def _ptr(t: torch.Tensor) -> int:
+    return t.data_ptr()
+
+
+class Engine:
+    """Device state of one cache plus its workspace; every method is one C-ABI call.
+
+    All tensors live on `device`; calls are enqueued on torch's current stream.
+    """
+
+    def __init__(self, wl: Workload, device="cuda", cap8: int | None = None, **over):
+        self.lib = load()
+        self.wl = wl
+        self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
+        self.p = params_from_workload(wl, cap8, **over)
+        self.dtype16 = DTYPE16[wl.dtype16][1]
+        sizes = ConfCacheBytes()
+        _check(self.lib.conf_cache_layout(ctypes.byref(self.p), ctypes.byref(sizes)), "layout")
+        self.cap8 = self.p.cap8
+        self.cap16 = sizes.cap16
+        ws = c_size_t()
+        _check(self.lib.conf_workspace_bytes(ctypes.byref(self.p), ctypes.byref(ws)), "workspace")
+        L, B, Hkv, D = wl.n_layers, wl.batch, wl.n_kv_heads, wl.head_dim
+        dev = self.device
+        U = L * B * Hkv
+        self.t_k8 = torch.zeros(U * self.cap8 * D, dtype=torch.int8, device=dev)
+        self.t_v8 = torch.zeros_like(self.t_k8)
+        self.t_k16 = torch.zeros(U * self.cap16 * D, dtype=torch.int16, device=dev)
+        self.t_v16 = torch.zeros_like(self.t_k16)
+        self.t_k_amax = torch.zeros(L, B, Hkv, D, dtype=torch.float32, device=dev)
+        self.t_v_amax = torch.zeros_like(self.t_k_amax)
+        self.t_pos8 = torch.zeros(L, B, self.cap8, dtype=torch.int32, device=dev)
+        self.t_ema8 = torch.zeros(L, B, self.cap8, dtype=torch.float32, device=dev)
+        self.t_pos16 = torch.zeros(L, B, self.cap16, dtype=torch.int32, device=dev)
+        self.t_ema16 = torch.zeros(L, B, self.cap16, dtype=torch.float32, device=dev)
+        self.t_n8 = torch.zeros(L, B, dtype=torch.int32, device=dev)
+        self.t_n16 = torch.zeros_like(self.t_n8)
+        self.t_t = torch.zeros_like(self.t_n8)
+        self.t_status = torch.zeros(1, dtype=torch.int32, device=dev)
+        for f in _CACHE_FIELDS:
+            assert getattr(self, "t_" + f).numel() * getattr(self, "t_" + f).element_size() \
+                == getattr(sizes, f), f
+        self.cache = ConfCache(*[_ptr(getattr(self, "t_" + f)) for f in _CACHE_FIELDS])
+        self.ws = torch.zeros(max(ws.value, 256), dtype=torch.uint8, device=dev)
+        self.reset()
+
+    # -- helpers ------------------------------------------------------------
+    def _stream(self):
+        return c_void_p(torch.cuda.current_stream(self.device).cuda_stream)
+
+    def _expect(self, t: torch.Tensor, shape, dtype, name):
+        if t.device != self.device or t.dtype != dtype or tuple(t.shape) != tuple(shape) \
+                or not t.is_contiguous():
+            raise ValueError(f"{name}: want {dtype} {tuple(shape)} contiguous on {self.device}, "
+                             f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+    def _layer_shape(self, layer, *tail):
+        return tail if layer >= 0 else (self.wl.n_layers, *tail)
+
+    # -- C-ABI calls ---------------------------------------------------------
+    def reset(self):
+        _check(self.lib.conf_cache_reset(ctypes.byref(self.p), ctypes.byref(self.cache),
+                                         self._stream()), "conf_cache_reset")
+
+    def ingest(self, layer: int, k_pre: torch.Tensor, v_pre: torch.Tensor):
+        wl = self.wl
+        L0 = k_pre.shape[-2]
+        shp = self._layer_shape(layer, wl.batch, wl.n_kv_heads, L0, wl.head_dim)
+        self._expect(k_pre, shp, self.dtype16, "k_pre")
+        self._expect(v_pre, shp, self.dtype16, "v_pre")
+        _check(self.lib.conf_cache_ingest(ctypes.byref(self.p), ctypes.byref(self.cache), layer,
+                                          _ptr(k_pre), _ptr(v_pre), L0, _ptr(self.ws),
+                                          self._stream()), "conf_cache_ingest")
+
+    def confidence(self, logits: torch.Tensor, c=None, budget=None):
+        wl = self.wl
+        self._expect(logits, (wl.batch, wl.vocab), torch.float32, "logits")
+        c = torch.empty(wl.batch, dtype=torch.float32, device=self.device) if c is None else c
+        budget = torch.empty(wl.batch, wl.n_layers, dtype=torch.int32, device=self.device) \
+            if budget is None else budget
+        self._expect(c, (wl.batch,), torch.float32, "c")
+        self._expect(budget, (wl.batch, wl.n_layers), torch.int32, "budget")
+        _check(self.lib.conf_confidence(ctypes.byref(self.p), _ptr(logits), _ptr(c), _ptr(budget),
+                                        _ptr(self.ws), self._stream()), "conf_confidence")
+        return c, budget
+
+    def decode_attn(self, layer: int, q, k_new, v_new, out=None):
+        wl = self.wl
+        self._expect(q, self._layer_shape(layer, wl.batch, wl.n_q_heads, wl.head_dim),
+                     self.dtype16, "q")
+        kv = self._layer_shape(layer, wl.batch, wl.n_kv_heads, wl.head_dim)
+        self._expect(k_new, kv, self.dtype16, "k_new")
+        self._expect(v_new, kv, self.dtype16, "v_new")
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=self.device)
+        self._expect(out, q.shape, torch.float32, "out")
+        _check(self.lib.conf_decode_attn(ctypes.byref(self.p), ctypes.byref(self.cache), layer,
+                                         _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out),
+                                         _ptr(self.ws), self._stream()), "conf_decode_attn")
+        return out
+
+    def rank_evict(self, layer: int, budget, keep=None):
+        wl = self.wl
+        self._expect(budget, (wl.batch, wl.n_layers), torch.int32, "budget")
+        if keep is None:
+            keep = torch.zeros(wl.n_layers, wl.batch, self.cap8 + self.cap16, dtype=torch.uint8,
+                               device=self.device)
+        self._expect(keep, (wl.n_layers, wl.batch, self.cap8 + self.cap16), torch.uint8, "keep")
+        _check(self.lib.conf_rank_evict(ctypes.byref(self.p), ctypes.byref(self.cache), layer,
+                                        _ptr(budget), _ptr(keep), _ptr(self.ws), self._stream()),
+               "conf_rank_evict")
+        return keep
+
+    def compact_demote(self, layer: int, keep):
+        wl = self.wl
+        self._expect(keep, (wl.n_layers, wl.batch, self.cap8 + self.cap16), torch.uint8, "keep")
+        _check(self.lib.conf_compact_demote(ctypes.byref(self.p), ctypes.byref(self.cache), layer,
+                                            _ptr(keep), _ptr(self.ws), self._stream()),
+               "conf_compact_demote")
+
+    def step(self, logits, q, k_new, v_new, out=None, c=None, budget=None):
+        wl = self.wl
+        self._expect(logits, (wl.batch, wl.vocab), torch.float32, "logits")
+        self._expect(q, (wl.n_layers, wl.batch, wl.n_q_heads, wl.head_dim), self.dtype16, "q")
+        kv = (wl.n_layers, wl.batch, wl.n_kv_heads, wl.head_dim)
+        self._expect(k_new, kv, self.dtype16, "k_new")
+        self._expect(v_new, kv, self.dtype16, "v_new")
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=self.device)
+        if c is None:
+            c = torch.empty(wl.batch, dtype=torch.float32, device=self.device)
+        if budget is None:
+            budget = torch.empty(wl.batch, wl.n_layers, dtype=torch.int32, device=self.device)
+        self._expect(out, q.shape, torch.float32, "out")
+        self._expect(c, (wl.batch,), torch.float32, "c")
+        self._expect(budget, (wl.batch, wl.n_layers), torch.int32, "budget")
+        _check(self.lib.conf_step(ctypes.byref(self.p), ctypes.byref(self.cache), _ptr(logits),
+                                  _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(c),
+                                  _ptr(budget), _ptr(self.ws), self._stream()), "conf_step")
+        return out, c, budget
+
+    def export(self, layer: int, seq: int) -> dict:
+        """One (layer, sequence) as host numpy arrays, slot order, occupied slots only."""
+        wl = self.wl
+        H, D = wl.n_kv_heads, wl.head_dim
+        k8 = torch.empty(self.cap8, H, D, dtype=torch.int8, device=self.device)
+        v8 = torch.empty_like(k8)
+        k16 = torch.empty(self.cap16, H, D, dtype=torch.int16, device=self.device)
+        v16 = torch.empty_like(k16)
+        _check(self.lib.conf_cache_export(ctypes.byref(self.p), ctypes.byref(self.cache), layer,
+                                          seq, _ptr(k8), _ptr(v8), _ptr(k16), _ptr(v16),
+                                          self._stream()), "conf_cache_export")
+        torch.cuda.synchronize(self.device)
+        n8 = int(self.t_n8[layer, seq])
+        n16 = int(self.t_n16[layer, seq])
+        return dict(
+            n8=n8, n16=n16, t=int(self.t_t[layer, seq]),
+            k8=k8[:n8].cpu().numpy(), v8=v8[:n8].cpu().numpy(),
+            k16=k16[:n16].cpu().numpy().view("uint16"), v16=v16[:n16].cpu().numpy().view("uint16"),
+            pos8=self.t_pos8[layer, seq, :n8].cpu().numpy(),
+            ema8=self.t_ema8[layer, seq, :n8].cpu().numpy(),
+            pos16=self.t_pos16[layer, seq, :n16].cpu().numpy(),
+            ema16=self.t_ema16[layer, seq, :n16].cpu().numpy(),
+            k_amax=self.t_k_amax[layer, seq].cpu().numpy(),
+            v_amax=self.t_v_amax[layer, seq].cpu().numpy(),
+        )
+
+    def status(self) -> int:
+        return int(self.t_status[0])

@@ -1,0 +1,298 @@
+// Host side of the C ABI declared in include/confkv.h: argument validation,
+// workspace layout and kernel launches.  No call allocates device memory or
+// synchronises the device.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "common.hpp"
+
+namespace confkv {
+// kernel launchers (one translation unit per step)
+int conf_vchunks(int V);
+void launch_confidence(const Dims&, const float*, float*, float*, int32_t*, hipStream_t);
+void launch_reset(const Dims&, const conf_cache&, hipStream_t);
+void launch_append(const Dims&, const conf_cache&, int, int, const void*, const void*, hipStream_t);
+void launch_attn(const Dims&, const conf_cache&, int, int, const void*, float*, float*, hipStream_t);
+void launch_ema(const Dims&, const conf_cache&, int, int, const float*, hipStream_t);
+void launch_ingest(const Dims&, const conf_cache&, int, int, int, const void*, const void*,
+                   hipStream_t);
+void launch_select(const Dims&, const conf_cache&, int, int, const int32_t*, uint8_t*, hipStream_t);
+void launch_compact(const Dims&, const conf_cache&, int, int, const uint8_t*, int32_t*, int32_t*,
+                    int32_t*, uint8_t*, hipStream_t);
+void launch_export(const Dims&, const conf_cache&, int, int8_t*, int8_t*, void*, void*, hipStream_t);
+}  // namespace confkv
+
+using namespace confkv;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail_hip(hipError_t e, const char* where) {
+  snprintf(g_err, sizeof g_err, "%s: %s", where, hipGetErrorString(e));
+  return CONF_E_HIP;
+}
+
+int check_launch(const char* where) {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? CONF_OK : fail_hip(e, where);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int make_dims(const conf_params* p, Dims* d) {
+  if (!p || !d) return CONF_E_INVALID;
+  if (p->n_layers <= 0 || p->batch <= 0 || p->n_q_heads <= 0 || p->n_kv_heads <= 0 ||
+      p->vocab < 2)
+    return CONF_E_INVALID;
+  if (p->n_q_heads % p->n_kv_heads) return CONF_E_INVALID;
+  if (p->head_dim != 64 && p->head_dim != 128) return CONF_E_UNSUPPORTED;
+  if (p->dtype16 != CONF_F16 && p->dtype16 != CONF_BF16) return CONF_E_UNSUPPORTED;
+  const int G = p->n_q_heads / p->n_kv_heads;
+  if (G > kMaxGroup) return CONF_E_UNSUPPORTED;
+  if (p->window < 1 || p->protect < 1 || p->protect > p->window) return CONF_E_INVALID;
+  if (p->n_high < 1 || p->n_low < p->n_high) return CONF_E_INVALID;
+  const int min_budget = layer_budget(p->n_high, p->n_layers - 1, p->n_layers, p->pyramid);
+  if (p->protect > min_budget) return CONF_E_INVALID;
+  if (p->cap8 < 64 || p->cap8 % 64) return CONF_E_INVALID;
+  if (p->cap8 <= p->n_low) return CONF_E_CAPACITY;
+  if (!(p->ema_decay >= 0.f && p->ema_decay <= 1.f)) return CONF_E_INVALID;
+  if (!(p->s_ema >= 0.f && p->s_rec >= 0.f)) return CONF_E_INVALID;
+  if (p->pyramid != 0 && p->pyramid != 1) return CONF_E_INVALID;
+  d->L = p->n_layers;
+  d->B = p->batch;
+  d->Hq = p->n_q_heads;
+  d->Hkv = p->n_kv_heads;
+  d->G = G;
+  d->D = p->head_dim;
+  d->V = p->vocab;
+  d->W = p->window;
+  d->P = p->protect;
+  d->n_high = p->n_high;
+  d->n_low = p->n_low;
+  d->cap8 = p->cap8;
+  d->cap16 = (p->window + 1 + kTile - 1) / kTile * kTile;
+  d->capt = d->cap8 + d->cap16;
+  d->bf16 = p->dtype16 == CONF_BF16;
+  d->pyramid = p->pyramid;
+  d->tau = p->tau;
+  d->w_H = p->w_H;
+  d->w_m = p->w_m;
+  d->w_p = p->w_p;
+  d->decay = p->ema_decay;
+  d->one_minus_decay = 1.0f - p->ema_decay;
+  d->s_ema = p->s_ema;
+  d->s_rec = p->s_rec;
+  return CONF_OK;
+}
+
+WsMap make_ws(const Dims& d) {
+  WsMap w{};
+  size_t off = 0;
+  const size_t LB = (size_t)d.L * d.B;
+  w.n_vchunks = conf_vchunks(d.V);
+  w.conf_part = off;
+  off = align256(off + (size_t)d.B * w.n_vchunks * 8 * sizeof(float));
+  w.massp = off;
+  off = align256(off + LB * d.Hkv * d.capt * sizeof(float));
+  w.lse = off;
+  off = align256(off + LB * d.Hq * sizeof(float));
+  w.keep = off;
+  off = align256(off + LB * d.capt);
+  w.plan = off;
+  off = align256(off + LB * 16 * sizeof(int32_t));
+  w.mv8 = off;
+  off = align256(off + LB * d.cap8 * sizeof(int32_t));
+  w.mv16 = off;
+  off = align256(off + LB * d.cap16 * sizeof(int32_t));
+  w.wkeep = off;
+  off = align256(off + LB * d.cap16);
+  w.total = off;
+  return w;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return (T*)((char*)ws + off);
+}
+
+bool cache_ok(const conf_cache* c) {
+  return c && c->k8 && c->v8 && c->k16 && c->v16 && c->k_amax && c->v_amax && c->pos8 &&
+         c->ema8 && c->pos16 && c->ema16 && c->n8 && c->n16 && c->t && c->status;
+}
+
+// layer selector -> (first layer, layer count)
+bool layer_range(const Dims& d, int32_t layer, int* l0, int* nl) {
+  if (layer == -1) {
+    *l0 = 0;
+    *nl = d.L;
+    return true;
+  }
+  if (layer < 0 || layer >= d.L) return false;
+  *l0 = layer;
+  *nl = 1;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int conf_cache_layout(const conf_params* p, conf_cache_bytes_t* o) {
+  Dims d;
+  int rc = make_dims(p, &d);
+  if (rc) return rc;
+  if (!o) return CONF_E_INVALID;
+  const size_t U = (size_t)d.L * d.B * d.Hkv, LB = (size_t)d.L * d.B;
+  o->k8 = U * d.cap8 * d.D;
+  o->v8 = o->k8;
+  o->k16 = U * d.cap16 * d.D * 2;
+  o->v16 = o->k16;
+  o->k_amax = U * d.D * sizeof(float);
+  o->v_amax = o->k_amax;
+  o->pos8 = LB * d.cap8 * sizeof(int32_t);
+  o->ema8 = LB * d.cap8 * sizeof(float);
+  o->pos16 = LB * d.cap16 * sizeof(int32_t);
+  o->ema16 = LB * d.cap16 * sizeof(float);
+  o->n8 = LB * sizeof(int32_t);
+  o->n16 = o->n8;
+  o->t = o->n8;
+  o->status = sizeof(int32_t);
+  o->cap16 = d.cap16;
+  return CONF_OK;
+}
+
+int conf_workspace_bytes(const conf_params* p, size_t* bytes) {
+  Dims d;
+  int rc = make_dims(p, &d);
+  if (rc) return rc;
+  if (!bytes) return CONF_E_INVALID;
+  *bytes = make_ws(d).total;
+  return CONF_OK;
+}
+
+int conf_cache_reset(const conf_params* p, conf_cache* c, conf_stream_t stream) {
+  Dims d;
+  int rc = make_dims(p, &d);
+  if (rc) return rc;
+  if (!cache_ok(c)) return CONF_E_INVALID;
+  launch_reset(d, *c, (hipStream_t)stream);
+  return check_launch("conf_cache_reset");
+}
+
+int conf_cache_ingest(const conf_params* p, conf_cache* c, int32_t layer, const void* k_pre,
+                      const void* v_pre, int32_t prefill_len, void* ws, conf_stream_t stream) {
+  Dims d;
+  int rc = make_dims(p, &d);
+  if (rc) return rc;
+  int l0, nl;
+  if (!cache_ok(c) || !k_pre || !v_pre || prefill_len < 0 || !layer_range(d, layer, &l0, &nl))
+    return CONF_E_INVALID;
+  (void)ws;
+  if (prefill_len - d.W > d.cap8) return CONF_E_CAPACITY;
+  if (prefill_len == 0) return CONF_OK;
+  launch_ingest(d, *c, l0, nl, prefill_len, k_pre, v_pre, (hipStream_t)stream);
+  return check_launch("conf_cache_ingest");
+}
+
+int conf_confidence(const conf_params* p, const float* logits, float* c, int32_t* budget, void* ws,
+                    conf_stream_t stream) {
+  Dims d;
+  int rc = make_dims(p, &d);
+  if (rc) return rc;
+  if (!logits || !c || !budget || !ws) return CONF_E_INVALID;
+  const WsMap w = make_ws(d);
+  launch_confidence(d, logits, at<float>(ws, w.conf_part), c, budget, (hipStream_t)stream);
+  return check_launch("conf_confidence");
+}
+
+int conf_decode_attn(const conf_params* p, conf_cache* c, int32_t layer, const void* q,
+                     const void* k_new, const void* v_new, float* out, void* ws,
+                     conf_stream_t stream) {
+  Dims d;
+  int rc = make_dims(p, &d);
+  if (rc) return rc;
+  int l0, nl;
+  if (!cache_ok(c) || !q || !k_new || !v_new || !out || !ws || !layer_range(d, layer, &l0, &nl))
+    return CONF_E_INVALID;
+  const WsMap w = make_ws(d);
+  hipStream_t st = (hipStream_t)stream;
+  launch_append(d, *c, l0, nl, k_new, v_new, st);
+  launch_attn(d, *c, l0, nl, q, out, at<float>(ws, w.massp), st);
+  launch_ema(d, *c, l0, nl, at<float>(ws, w.massp), st);
+  return check_launch("conf_decode_attn");
+}
+
+int conf_rank_evict(const conf_params* p, conf_cache* c, int32_t layer, const int32_t* budget,
+                    uint8_t* keep, void* ws, conf_stream_t stream) {
+  Dims d;
+  int rc = make_dims(p, &d);
+  if (rc) return rc;
+  int l0, nl;
+  if (!cache_ok(c) || !budget || !keep || !layer_range(d, layer, &l0, &nl)) return CONF_E_INVALID;
+  (void)ws;
+  launch_select(d, *c, l0, nl, budget, keep, (hipStream_t)stream);
+  return check_launch("conf_rank_evict");
+}
+
+int conf_compact_demote(const conf_params* p, conf_cache* c, int32_t layer, const uint8_t* keep,
+                        void* ws, conf_stream_t stream) {
+  Dims d;
+  int rc = make_dims(p, &d);
+  if (rc) return rc;
+  int l0, nl;
+  if (!cache_ok(c) || !keep || !ws || !layer_range(d, layer, &l0, &nl)) return CONF_E_INVALID;
+  const WsMap w = make_ws(d);
+  launch_compact(d, *c, l0, nl, keep, at<int32_t>(ws, w.plan), at<int32_t>(ws, w.mv8),
+                 at<int32_t>(ws, w.mv16), at<uint8_t>(ws, w.wkeep), (hipStream_t)stream);
+  return check_launch("conf_compact_demote");
+}
+
+int conf_step(const conf_params* p, conf_cache* c, const float* logits, const void* q,
+              const void* k_new, const void* v_new, float* out, float* conf, int32_t* budget,
+              void* ws, conf_stream_t stream) {
+  Dims d;
+  int rc = make_dims(p, &d);
+  if (rc) return rc;
+  if (!cache_ok(c) || !logits || !q || !k_new || !v_new || !out || !conf || !budget || !ws)
+    return CONF_E_INVALID;
+  const WsMap w = make_ws(d);
+  hipStream_t st = (hipStream_t)stream;
+  launch_append(d, *c, 0, d.L, k_new, v_new, st);
+  launch_attn(d, *c, 0, d.L, q, out, at<float>(ws, w.massp), st);
+  launch_ema(d, *c, 0, d.L, at<float>(ws, w.massp), st);
+  launch_confidence(d, logits, at<float>(ws, w.conf_part), conf, budget, st);
+  uint8_t* keep = at<uint8_t>(ws, w.keep);
+  launch_select(d, *c, 0, d.L, budget, keep, st);
+  launch_compact(d, *c, 0, d.L, keep, at<int32_t>(ws, w.plan), at<int32_t>(ws, w.mv8),
+                 at<int32_t>(ws, w.mv16), at<uint8_t>(ws, w.wkeep), st);
+  return check_launch("conf_step");
+}
+
+int conf_cache_export(const conf_params* p, const conf_cache* c, int32_t layer, int32_t seq,
+                      int8_t* k8, int8_t* v8, void* k16, void* v16, conf_stream_t stream) {
+  Dims d;
+  int rc = make_dims(p, &d);
+  if (rc) return rc;
+  if (!cache_ok(c) || !k8 || !v8 || !k16 || !v16 || layer < 0 || layer >= d.L || seq < 0 ||
+      seq >= d.B)
+    return CONF_E_INVALID;
+  launch_export(d, *c, layer * d.B + seq, k8, v8, k16, v16, (hipStream_t)stream);
+  return check_launch("conf_cache_export");
+}
+
+const char* conf_last_error(void) { return g_err; }
+
+const char* conf_status_string(int status) {
+  switch (status) {
+    case CONF_OK: return "ok";
+    case CONF_E_INVALID: return "invalid argument";
+    case CONF_E_UNSUPPORTED: return "unsupported shape or dtype";
+    case CONF_E_CAPACITY: return "capacity too small";
+    case CONF_E_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Internal definitions shared by the HIP kernels and the host entry points of
+// the CONF-KV decode-step library.  Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "confkv.h"
+
+namespace confkv {
+
+constexpr int kTile = 64;        // tokens per value tile
+constexpr int kMaxGroup = 16;    // query heads per KV head handled by one unit
+
+// Shapes derived once on the host and passed by value to every kernel.
+struct Dims {
+  int L, B, Hq, Hkv, G, D, V;
+  int W, P, n_high, n_low, cap8, cap16, capt;  // capt = cap8 + cap16
+  int bf16;                                    // 1: bfloat16, 0: IEEE half
+  int pyramid;
+  float tau, w_H, w_m, w_p, decay, one_minus_decay, s_ema, s_rec;
+};
+
+// Byte offsets of the workspace regions (all 256-byte aligned).
+struct WsMap {
+  size_t conf_part;   // float [B][n_vchunks][8]
+  size_t massp;       // float [L][B][Hkv][capt]  per-KV-head attention mass
+  size_t lse;         // float [L][B][Hq]         log-sum-exp per query head
+  size_t keep;        // uint8 [L][B][capt]       keep flags of conf_step
+  size_t plan;        // int32 [L][B][16]         compaction plan
+  size_t mv8;         // int32 [L][B][cap8]       (src, dst) pairs, INT8 region
+  size_t mv16;        // int32 [L][B][cap16]      (src, dst) pairs, window
+  size_t wkeep;       // uint8 [L][B][cap16]      window keep flags minus the demotee
+  size_t total;
+  int n_vchunks;      // vocab chunks per sequence in the confidence reduction
+};
+
+// Slot -> column inside a 64-token value tile.  With s = 32u + 16a + 4g + b
+// the column is 16g + 8u + 4a + b: a 16-lane group of a wavefront then holds the
+// 16 tokens it contracts over in one contiguous 16-element run.
+__host__ __device__ inline int tile_col(int s) {
+  const int b = s & 3, g = (s >> 2) & 3, a = (s >> 4) & 1, u = (s >> 5) & 1;
+  return (g << 4) | (u << 3) | (a << 2) | b;
+}
+
+// Element offset of (slot, channel) in a tiled value region of one unit.
+__host__ __device__ inline size_t vtile_off(int slot, int c, int D) {
+  return (size_t)(slot >> 6) * (size_t)(D * kTile) + (size_t)c * kTile + tile_col(slot & 63);
+}
+
+__device__ inline float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+__device__ inline float f16_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+__device__ inline float h16_to_f32(uint16_t h, int bf16) {
+  return bf16 ? bf16_to_f32(h) : f16_to_f32(h);
+}
+
+// Pyramid (CONF-KV-L) layer budget, integer floor; identical to the host form.
+__host__ __device__ inline int layer_budget(int N, int l, int L, int pyramid) {
+  if (!pyramid || L <= 1) return N;
+  const long long Dn = 2LL * (L - 1);
+  return (int)(((long long)N * (Dn - l)) / Dn);
+}
+
+// Symmetric INT8 code, round half to even, clamp to [-127, 127]; s == 0 -> 0.
+__device__ inline int8_t quant_code(float x, float s) {
+#pragma clang fp contract(off)
+  if (!(s > 0.0f)) return 0;
+  float r = __builtin_rintf(x / s);
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return (int8_t)(int)r;
+}
+
+}  // namespace confkv

@@ -1,0 +1,218 @@
+/*
+ * confkv.h - C ABI of the MI355X (gfx950) CONF-KV decode-step library.
+ *
+ * CONF-KV keeps a budgeted, dense, mixed-precision KV cache and changes the
+ * budget at every decode step from the model's confidence in its next token.
+ * Citations name sections of the CONF-KV explainer pages (gist.science
+ * technical summary of "CONF-KV: Confidence-Aware KV Cache Eviction with
+ * Mixed-Precision Storage for Long-Horizon LLM"; the Dutch, Italian and Korean
+ * renderings agree):
+ *   [confidence]  Methodology, confidence estimation
+ *   [budget]      Methodology, adaptive budget selection
+ *   [ranking]     Methodology, token ranking and eviction
+ *   [storage]     Methodology, system integration, mixed-precision storage
+ *   [pyramid]     Methodology, system integration, pyramidal budgets (CONF-KV-L)
+ *   [impl]        Methodology, system integration, implementation
+ *   [online]      Key contributions, system design (block-wise online softmax)
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument is a DEVICE pointer owned by the caller, except
+ *     the `const conf_params*` / `conf_cache*` structs themselves, which are
+ *     host memory read during the call only.  The library allocates no device
+ *     memory and keeps no mutable global state; scratch lives in the caller's
+ *     workspace `ws` of conf_workspace_bytes() bytes (256-byte aligned).
+ *   - A call validates its arguments on the host, enqueues kernels on `stream`
+ *     (a hipStream_t; NULL is the null stream) and returns without waiting for
+ *     the device.  Results are valid once the stream has been synchronised.
+ *   - Return value: CONF_OK (0) or a negative CONF_E_* code; nothing is
+ *     enqueued when validation fails.  No C++ exception crosses the ABI.
+ *   - `layer` = -1 processes every layer in one launch per kernel; then per-
+ *     layer tensors carry a leading [L] dimension.  `layer` = l >= 0 processes
+ *     layer l only; then q/k_new/v_new/out/k_pre/v_pre have no [L] dimension.
+ *     `budget` and `keep` always cover every layer.
+ *   - Calls on the same cache must not overlap (use one stream per cache).
+ *   - Data-dependent sizes (tokens per layer and sequence) stay on the device;
+ *     no call reads them back, so a step can be captured in a HIP graph.
+ */
+#ifndef CONFKV_H
+#define CONFKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* conf_stream_t; /* hipStream_t */
+
+enum {
+  CONF_OK = 0,
+  CONF_E_INVALID = -1,     /* null pointer, inconsistent sizes, P > W, P > budget, ... */
+  CONF_E_UNSUPPORTED = -2, /* head_dim not 64/128, group > 16, unknown dtype */
+  CONF_E_CAPACITY = -3,    /* cap8 too small for the budgets or the prefill */
+  CONF_E_HIP = -4          /* a HIP launch failed; see conf_last_error() */
+};
+
+enum { CONF_F16 = 1, CONF_BF16 = 2 };
+
+/* Device status word bits (conf_cache.status), set by kernels, never cleared
+ * except by conf_cache_reset(). */
+enum {
+  CONF_ST_WINDOW_FULL = 1, /* append found the 16-bit window full: token dropped */
+  CONF_ST_INT8_FULL = 2    /* a demotion found the INT8 region full: token dropped */
+};
+
+typedef struct conf_params {
+  int32_t n_layers, batch, n_q_heads, n_kv_heads, head_dim, vocab;
+  int32_t dtype16;          /* CONF_F16 | CONF_BF16: q, k_new, v_new, k_pre, v_pre, window */
+  int32_t window;           /* W: positions (t-W, t] stay 16-bit [storage] */
+  int32_t protect;          /* P: positions (t-P, t] are never evicted [ranking]; P <= W */
+  int32_t n_high, n_low;    /* budgets for c >= tau and c < tau [budget]; P <= n_high <= n_low */
+  int32_t cap8;             /* INT8 slots per (layer, sequence): multiple of 64, > n_low */
+  int32_t pyramid;          /* 1: N_l = floor(N (2(L-1)-l) / (2(L-1))) [pyramid]; 0: N_l = N */
+  float tau;                /* confidence threshold [budget] */
+  float w_H, w_m, w_p;      /* confidence weights; the pages use 0.4, 0.3, 0.3 [confidence] */
+  float ema_decay;          /* e <- decay*e + (1-decay)*mass [ranking] */
+  float s_ema, s_rec;       /* score = s_ema*(e/e_max) + s_rec*(pos/t) [ranking] */
+} conf_params;
+
+/*
+ * The dense mixed-precision cache [storage][impl].  All arrays are caller-
+ * allocated device memory of the sizes conf_cache_layout() reports.  With
+ * cap16 = W+1 rounded up to 64 and U = L*B*Hkv units:
+ *   k8     int8  [L][B][Hkv][cap8][d]             INT8 key codes, token-major rows
+ *   v8     int8  [L][B][Hkv][cap8/64][d][64]      INT8 value codes, 64-token tiles,
+ *                                                 channel-major inside a tile
+ *   k16    16-bit[L][B][Hkv][cap16][d]            window keys, token-major rows
+ *   v16    16-bit[L][B][Hkv][cap16/64][d][64]     window values, tiled like v8
+ *   k_amax, v_amax fp32 [L][B][Hkv][d]            running absmax; scale = amax/127
+ *   pos8, ema8     [L][B][cap8]  int32 / fp32     position and EMA of INT8 slots
+ *   pos16, ema16   [L][B][cap16] int32 / fp32     position and EMA of window slots
+ *   n8, n16        int32 [L][B]                   occupied slots (dense prefix)
+ *   t              int32 [L][B]                   newest position (-1 = empty)
+ *   status         int32 [1]                      CONF_ST_* bits
+ * Inside a 64-token tile, slot s sits at column tile_col(s % 64), where for
+ * j = 32u + 16a + 4g + b (u, a in {0,1}; g, b in 0..3) tile_col(j) = 16g + 8u + 4a + b.
+ * (This order lets a wavefront feed the matrix cores straight from memory.)
+ * Slot order inside a region is arbitrary: compaction fills holes, so a token's
+ * identity is its stored position.
+ */
+typedef struct conf_cache {
+  int8_t* k8;
+  int8_t* v8;
+  void* k16;
+  void* v16;
+  float* k_amax;
+  float* v_amax;
+  int32_t* pos8;
+  float* ema8;
+  int32_t* pos16;
+  float* ema16;
+  int32_t* n8;
+  int32_t* n16;
+  int32_t* t;
+  int32_t* status;
+} conf_cache;
+
+typedef struct conf_cache_bytes_t {
+  size_t k8, v8, k16, v16, k_amax, v_amax, pos8, ema8, pos16, ema16, n8, n16, t, status;
+  int32_t cap16;
+} conf_cache_bytes_t;
+
+/* Byte size of every cache array for `p`.  Returns CONF_E_* if p is invalid. */
+int conf_cache_layout(const conf_params* p, conf_cache_bytes_t* out);
+
+/* Workspace bytes every call below may use for `p`. */
+int conf_workspace_bytes(const conf_params* p, size_t* bytes);
+
+/* Empty every (layer, sequence): n8 = n16 = 0, t = -1, absmax = 0, status = 0.
+ * Fills with kernels (no memset nodes), so it may be graph-captured. */
+int conf_cache_reset(const conf_params* p, conf_cache* c, conf_stream_t stream);
+
+/*
+ * Load a prefilled context of `prefill_len` tokens, positions 0..prefill_len-1.
+ * k_pre, v_pre: 16-bit [L][B][Hkv][prefill_len][d] (layer = -1) or
+ * [B][Hkv][prefill_len][d] (layer = l).  Positions < prefill_len - W become
+ * INT8 with absmax over exactly those tokens; the rest fill the window; every
+ * EMA is 0 and t = prefill_len - 1 [storage].  The layer must be empty.
+ * CONF_E_CAPACITY if prefill_len - W > cap8.
+ */
+int conf_cache_ingest(const conf_params* p, conf_cache* c, int32_t layer, const void* k_pre,
+                      const void* v_pre, int32_t prefill_len, void* ws, conf_stream_t stream);
+
+/*
+ * (a) Confidence and budget [confidence][budget][pyramid].
+ * logits: fp32 [B][vocab], row-contiguous.  Per sequence:
+ *   p = softmax(z), H^ = -sum p ln p / ln V, m = z(1) - z(2) (top two logits,
+ *   duplicates counted), p1 = max p, c = w_H (1-H^) + w_m / (1+e^-m) + w_p p1.
+ * c: fp32 [B] (NaN when any logit is non-finite).  budget: int32 [B][L],
+ * budget[b][l] = layer budget of (c >= tau ? n_high : n_low).
+ */
+int conf_confidence(const conf_params* p, const float* logits, float* c, int32_t* budget,
+                    void* ws, conf_stream_t stream);
+
+/*
+ * (b)+(c) Append, decode attention and EMA update [online][impl][ranking].
+ * Appends this step's key/value (k_new, v_new: 16-bit [L][B][Hkv][d]) at
+ * position t+1 in the window, then for every query head h (q: 16-bit
+ * [L][B][Hq][d]) computes o_h = sum_j softmax_j(q_h . k_j / sqrt(d)) v_j over all
+ * cached tokens of KV head h / (Hq/Hkv), INT8 tokens dequantised as code*amax/127
+ * inside the block reads.  out: fp32 [L][B][Hq][d].  Then every token's EMA
+ * becomes decay*e + (1-decay)*mass_j, mass_j = mean over the Hq heads of its
+ * softmax probability; the new token starts from e = 0.
+ */
+int conf_decode_attn(const conf_params* p, conf_cache* c, int32_t layer, const void* q,
+                     const void* k_new, const void* v_new, float* out, void* ws,
+                     conf_stream_t stream);
+
+/*
+ * (d) Rank and select [ranking].  budget: int32 [B][L] (conf_confidence).
+ * keep: uint8 [L][B][cap8 + cap16]; entry i < cap8 flags INT8 slot i, entry
+ * cap8 + w flags window slot w; only occupied slots are written.  If a
+ * (layer, sequence) holds n <= N tokens every slot is kept (no-op).  Otherwise
+ * keep the positions (t-P, t] and the N - |protected| best other tokens in the
+ * order (score desc, position desc), score = s_ema*(e/e_max) + s_rec*(pos/t),
+ * evaluated in fp32 one rounding per operation (e/e_max = 0 if e_max = 0;
+ * pos/t = 1 if t = 0).
+ */
+int conf_rank_evict(const conf_params* p, conf_cache* c, int32_t layer, const int32_t* budget,
+                    uint8_t* keep, void* ws, conf_stream_t stream);
+
+/*
+ * (e) Compact and demote [impl][storage].  Drops the tokens whose keep flag is
+ * 0 by moving survivors from the tail of each region into its holes (the layout
+ * stays dense with no indirection table), then moves the token at position
+ * t - W, if it survived, from the window to INT8: per (KV head, channel)
+ * a = |x|; if a > absmax the channel's stored codes become
+ * clamp(rne((code*s_old)/s_new)) and absmax = a; then code = clamp(rne(x/s)),
+ * s = absmax/127 (s = 0 gives code 0).
+ */
+int conf_compact_demote(const conf_params* p, conf_cache* c, int32_t layer, const uint8_t* keep,
+                        void* ws, conf_stream_t stream);
+
+/*
+ * One full decode step of every layer and sequence: conf_decode_attn(-1),
+ * conf_confidence, conf_rank_evict(-1), conf_compact_demote(-1).  c: fp32 [B]
+ * and budget: int32 [B][L] receive (a)'s results; the keep flags live in ws.
+ */
+int conf_step(const conf_params* p, conf_cache* c, const float* logits, const void* q,
+              const void* k_new, const void* v_new, float* out, float* conf, int32_t* budget,
+              void* ws, conf_stream_t stream);
+
+/*
+ * Copy one (layer, sequence) into plain row-major arrays in slot order, for
+ * inspection: k8, v8: int8 [cap8][Hkv][d]; k16, v16: 16-bit [cap16][Hkv][d].
+ * Slots beyond n8 / n16 hold whatever the cache held.
+ */
+int conf_cache_export(const conf_params* p, const conf_cache* c, int32_t layer, int32_t seq,
+                      int8_t* k8, int8_t* v8, void* k16, void* v16, conf_stream_t stream);
+
+/* Text of the last CONF_E_HIP error on this thread, or of a status code. */
+const char* conf_last_error(void);
+const char* conf_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CONFKV_H */

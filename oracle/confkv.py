@@ -465,6 +465,7 @@ def step_layer(st: LayerSeqState, q_bits, k_bits, v_bits, N: int, prm: OraclePar
     o, p = attention(q, K, V, prm.group)
     mass = token_mass(p)
     st.ema = ema_update(st.ema, mass, prm.ema_decay)
+    ema64 = st.ema.copy()
     e32 = st.ema.astype(F32) if ema32_override is None else np.asarray(ema32_override, F32)
     scores = composite_scores(e32, st.pos, st.t, prm.s_ema, prm.s_rec)
     keep = select_keep(scores, st.pos, st.t, prm.protect, N)
@@ -473,7 +474,7 @@ def step_layer(st: LayerSeqState, q_bits, k_bits, v_bits, N: int, prm: OraclePar
         st.ema = np.asarray(ema32_override, F64)
     st.evict(keep)
     st.demote(prm.window)
-    return dict(o=o, p=p, mass=mass, scores=scores, keep=keep, pos_before=pos_before)
+    return dict(o=o, p=p, mass=mass, ema=ema64, scores=scores, keep=keep, pos_before=pos_before)
 
 
 def decode_step(states, logits, q_bits, k_bits, v_bits, prm: OracleParams,

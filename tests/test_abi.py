@@ -1,0 +1,127 @@
+"""The C-ABI library loads, exports every symbol include/confkv.h declares, and
+rejects invalid arguments on the host with the documented codes.  No call here
+reaches a kernel launch, so these run without a GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from adaptive_kv_cache_amd import binding
+from adaptive_kv_cache_amd.workloads import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "confkv.h")
+E_INVALID, E_UNSUPPORTED, E_CAPACITY = -1, -2, -3
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(conf_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.skip("libconfkv.so not built (run __graft_entry__.build())")
+    return binding.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    decl = _declared()
+    assert len(decl) >= 12
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (conf_\w+)", out))
+    assert set(decl) <= exported, set(decl) - exported
+    assert set(binding.EXPORTED) == set(decl)
+    for name in decl:
+        assert hasattr(lib, name)
+
+
+def test_header_compiles_as_c():
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", HEADER],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def _p(**over):
+    return binding.params_from_workload(WORKLOADS["qwen32b_gqa_b8_32k"], **over)
+
+
+def _layout(lib, p):
+    out = binding.ConfCacheBytes()
+    return lib.conf_cache_layout(ctypes.byref(p), ctypes.byref(out)), out
+
+
+def test_layout_sizes(lib):
+    rc, out = _layout(lib, _p())
+    assert rc == 0
+    wl = WORKLOADS["qwen32b_gqa_b8_32k"]
+    U = wl.n_layers * wl.batch * wl.n_kv_heads
+    assert out.cap16 == 576                                   # W + 1 = 513 -> 9 tiles of 64
+    assert out.k8 == U * wl.cap8 * wl.head_dim
+    assert out.v16 == U * 576 * wl.head_dim * 2
+    assert out.n8 == wl.n_layers * wl.batch * 4
+    ws = ctypes.c_size_t()
+    assert lib.conf_workspace_bytes(ctypes.byref(_p()), ctypes.byref(ws)) == 0
+    assert ws.value % 256 == 0 and ws.value > 0
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(head_dim=96), E_UNSUPPORTED),
+    (dict(dtype16=7), E_UNSUPPORTED),
+    (dict(n_q_heads=40, n_kv_heads=2), E_UNSUPPORTED),        # group 20 > 16
+    (dict(n_q_heads=41), E_INVALID),                         # Hq % Hkv != 0
+    (dict(protect=600), E_INVALID),                          # P > W
+    (dict(n_high=5000), E_INVALID),                          # n_high > n_low
+    (dict(protect=256, n_high=300, pyramid=1), E_INVALID),   # P > pyramid-shrunk n_high
+    (dict(cap8=4096), E_CAPACITY),                           # cap8 <= n_low
+    (dict(cap8=4100), E_INVALID),                            # not a multiple of 64
+    (dict(vocab=1), E_INVALID),
+    (dict(ema_decay=1.5), E_INVALID),
+    (dict(s_ema=-0.1), E_INVALID),
+])
+def test_invalid_params(lib, over, code):
+    rc, _ = _layout(lib, _p(**over))
+    assert rc == code
+
+
+def test_null_pointers_rejected_before_launch(lib):
+    p = _p()
+    cache = binding.ConfCache()
+    null = ctypes.c_void_p(0)
+    assert lib.conf_confidence(ctypes.byref(p), null, null, null, null, null) == E_INVALID
+    assert lib.conf_decode_attn(ctypes.byref(p), ctypes.byref(cache), -1, null, null, null, null,
+                                null, null) == E_INVALID
+    assert lib.conf_rank_evict(ctypes.byref(p), ctypes.byref(cache), 0, null, null, null,
+                               null) == E_INVALID
+    assert lib.conf_compact_demote(ctypes.byref(p), ctypes.byref(cache), 0, null, null,
+                                   null) == E_INVALID
+    assert lib.conf_step(ctypes.byref(p), ctypes.byref(cache), *([null] * 9)) == E_INVALID
+    assert lib.conf_cache_reset(ctypes.byref(p), ctypes.byref(cache), null) == E_INVALID
+    assert lib.conf_status_string(E_CAPACITY) == b"capacity too small"
+
+
+def test_bad_layer_rejected(lib):
+    p = _p()
+    fake = ctypes.c_void_p(0x1000)           # never dereferenced: validation fails first
+    cache = binding.ConfCache(*([0x1000] * 14))
+    assert lib.conf_rank_evict(ctypes.byref(p), ctypes.byref(cache), 64, fake, fake, fake,
+                               null := ctypes.c_void_p(0)) == E_INVALID
+    assert lib.conf_cache_export(ctypes.byref(p), ctypes.byref(cache), 0, 8, fake, fake, fake,
+                                 fake, null) == E_INVALID
+    assert lib.conf_cache_ingest(ctypes.byref(p), ctypes.byref(cache), 0, fake, fake, 40000,
+                                 fake, null) == E_CAPACITY
+
+
+def test_package_has_no_fallback_path():
+    """The product package never imports the oracle."""
+    pkg = os.path.join(ROOT, "adaptive_kv_cache_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith(".py"):
+                src = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in re.findall(r"^\s*(?:from|import)\s+(\w+)", src, re.M), f

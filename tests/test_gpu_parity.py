@@ -1,0 +1,214 @@
+"""HIP library vs the oracle, element by element, on identical seeded inputs.
+
+Every call goes through the C ABI (libconfkv.so via the ctypes binding).  The
+oracle is run from a snapshot of the device state copied back before each step
+(teacher forcing), so every step is compared on identical inputs:
+  * confidence c: absolute error <= 1e-5; budgets exact unless |c - tau| <= 1e-5
+  * attention output: max over heads of ||o - o_ref||_inf / ||o_ref||_inf <= 2e-3
+  * EMA: relative error <= 1e-5 against the oracle's float64 EMA
+  * keep sets, INT8 codes, absmax, window bits, positions: bit-exact (the oracle's
+    selection is fed the device's fp32 EMA, so both rank identical score arrays)
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from adaptive_kv_cache_amd import synth
+from adaptive_kv_cache_amd.binding import Engine
+from adaptive_kv_cache_amd.workloads import Workload
+from parity_util import (assert_same_state, attn_rel_err, bits16, ema_by_pos, kept_positions,
+                         oracle_params, tiny_workloads, to_oracle_state)
+
+pytestmark = pytest.mark.gpu
+
+ATTN_TOL = 2e-3
+C_TOL = 1e-5
+EMA_RTOL = 1e-5
+SEED = 1234
+TINY = tiny_workloads()
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _ingest(eng, wl, seed):
+    pre = {}
+    for l in range(wl.n_layers):
+        k, v = synth.prefill_kv(wl, l, seed, device="cpu")
+        eng.ingest(l, k.cuda(), v.cuda())
+        pre[l] = (bits16(k), bits16(v))
+    return pre
+
+
+def _snap(eng, wl):
+    return [[eng.export(l, b) for b in range(wl.batch)] for l in range(wl.n_layers)]
+
+
+def _conf_wl(V, B, L=3, pyramid=True):
+    return Workload(name="conf", n_layers=L, batch=B, n_q_heads=2, n_kv_heads=1, head_dim=64,
+                    vocab=V, dtype16="f16", window=16, protect=4, n_high=100, n_low=200,
+                    prefill=0, steps=1, pyramid=pyramid)
+
+
+def _check_conf(c_gpu, budget_gpu, z, wl):
+    for b in range(z.shape[0]):
+        ref = O.confidence(z[b], wl.w_H, wl.w_m, wl.w_p)["c"]
+        if np.isnan(ref):
+            assert np.isnan(c_gpu[b])
+            N = wl.n_low
+        else:
+            assert abs(float(c_gpu[b]) - ref) <= C_TOL, (b, float(c_gpu[b]), ref)
+            N = O.budget(ref, wl.tau, wl.n_high, wl.n_low)
+            if abs(ref - wl.tau) <= C_TOL:               # either budget is correct
+                N = wl.n_high if c_gpu[b] >= wl.tau else wl.n_low
+        want = [O.layer_budget(N, l, wl.n_layers, wl.pyramid) for l in range(wl.n_layers)]
+        assert list(budget_gpu[b]) == want
+
+
+@pytest.mark.parametrize("V,B", [(1000, 3), (4097, 1), (50257, 2), (152064, 8), (201088, 4)])
+@pytest.mark.parametrize("T", [0.5, 2.0, 8.0])
+def test_confidence(V, B, T):
+    _say("confidence", V, B, T)
+    wl = _conf_wl(V, B)
+    eng = Engine(wl)
+    g = torch.Generator().manual_seed(V + B)
+    z = torch.randn(B, V, generator=g) * T
+    c, budget = eng.confidence(z.cuda())
+    _check_conf(c.cpu().numpy(), budget.cpu().numpy(), z.numpy().astype(np.float64), wl)
+
+
+def test_confidence_special_cases():
+    V, B = 50257, 5
+    wl = _conf_wl(V, B, L=1, pyramid=False)
+    eng = Engine(wl)
+    z = torch.zeros(B, V)
+    z[1, 77] = 100.0                                # one-hot, gap 100: c = 1
+    z[2, 5] = z[2, 9] = 3.0                         # tied maximum: margin 0
+    z[3, 11] = float("nan")                         # non-finite: NaN, loose budget
+    z[4, :] = torch.linspace(-50, 50, V)            # ramp
+    c, budget = eng.confidence(z.cuda())
+    c = c.cpu().numpy()
+    assert abs(c[0] - (0.15 + 0.3 / V)) <= C_TOL     # uniform closed form
+    assert abs(c[1] - 1.0) <= C_TOL
+    assert np.isnan(c[3]) and int(budget[3, 0]) == wl.n_low
+    _check_conf(c, budget.cpu().numpy(), z.numpy().astype(np.float64), wl)
+
+
+@pytest.mark.parametrize("name", [n for n, w in TINY.items() if w.prefill > 0])
+def test_ingest_bit_exact(name):
+    wl = TINY[name]
+    _say("ingest", name)
+    eng = Engine(wl)
+    pre = _ingest(eng, wl, SEED)
+    for l in range(wl.n_layers):
+        for b in range(wl.batch):
+            ex = eng.export(l, b)
+            ref = O.ingest(pre[l][0][b], pre[l][1][b], wl.window, wl.dtype16)
+            assert_same_state(to_oracle_state(ex, wl.dtype16), ref, ema_rtol=0, what=(l, b))
+    assert eng.status() == 0
+
+
+def _teacher_forced(wl, steps, seed=SEED):
+    prm = oracle_params(wl)
+    eng = Engine(wl)
+    if wl.prefill:
+        _ingest(eng, wl, seed)
+    cap8 = eng.cap8
+    worst = 0.0
+    for step in range(steps):
+        S0 = _snap(eng, wl)
+        z = synth.logits(wl, step, seed)
+        q = synth.q_new(wl, step, seed)
+        k, v = synth.kv_new(wl, step, seed)
+        out = eng.decode_attn(-1, q.cuda(), k.cuda(), v.cuda())
+        S1 = _snap(eng, wl)
+        c, budget = eng.confidence(z.cuda())
+        keep = eng.rank_evict(-1, budget)
+        eng.compact_demote(-1, keep)
+        keep = keep.cpu().numpy()
+        S2 = _snap(eng, wl)
+        out = out.cpu().numpy()
+        budget = budget.cpu().numpy()
+        _check_conf(c.cpu().numpy(), budget, z.numpy().astype(np.float64), wl)
+        qb, kb, vb = bits16(q), bits16(k), bits16(v)
+        for l in range(wl.n_layers):
+            for b in range(wl.batch):
+                what = (wl.name, step, l, b)
+                st = to_oracle_state(S0[l][b], wl.dtype16)
+                new_pos = np.append(st.pos, st.t + 1)
+                e_gpu = ema_by_pos(S1[l][b])
+                override = np.array([e_gpu[p] for p in new_pos.tolist()], np.float32)
+                r = O.step_layer(st, qb[l, b], kb[l, b], vb[l, b], int(budget[b, l]), prm,
+                                 ema32_override=override)
+                err = attn_rel_err(out[l, b], r["o"])
+                worst = max(worst, err)
+                assert err <= ATTN_TOL, (what, err)
+                np.testing.assert_allclose(override, r["ema"], rtol=EMA_RTOL, atol=1e-12,
+                                           err_msg=str(what))
+                got = kept_positions(S1[l][b], keep[l, b], cap8)
+                assert got == set(new_pos[r["keep"]].tolist()), what
+                assert_same_state(to_oracle_state(S2[l][b], wl.dtype16), st, ema_rtol=0, what=what)
+    assert eng.status() == 0
+    return worst
+
+
+@pytest.mark.parametrize("name", list(TINY))
+def test_teacher_forced_steps(name):
+    wl = TINY[name]
+    steps = 150 if wl.prefill == 0 else 12
+    _say("teacher-forced", name, steps)
+    worst = _teacher_forced(wl, steps)
+    _say("  worst attention rel err", worst)
+
+
+@pytest.mark.parametrize("name", ["gqa5_bf16_d128", "mha_f16_d64"])
+def test_conf_step_equals_the_four_calls(name):
+    """conf_step must be exactly decode_attn + confidence + rank_evict + compact_demote,
+    which the teacher-forced test holds to the oracle."""
+    wl = TINY[name]
+    _say("conf_step", name)
+    a, b = Engine(wl), Engine(wl)
+    if wl.prefill:
+        _ingest(a, wl, SEED)
+        _ingest(b, wl, SEED)
+    for step in range(12):
+        z = synth.logits(wl, step, SEED).cuda()
+        q = synth.q_new(wl, step, SEED).cuda()
+        k, v = (x.cuda() for x in synth.kv_new(wl, step, SEED))
+        out_a = a.decode_attn(-1, q, k, v)
+        c_a, bud_a = a.confidence(z)
+        a.compact_demote(-1, a.rank_evict(-1, bud_a))
+        out_b, c_b, bud_b = b.step(z, q, k, v)
+        assert torch.equal(out_a, out_b) and torch.equal(c_a, c_b) and torch.equal(bud_a, bud_b)
+        for l in range(wl.n_layers):
+            for s in range(wl.batch):
+                ea, eb = a.export(l, s), b.export(l, s)
+                for key in ea:
+                    assert np.array_equal(np.asarray(ea[key]), np.asarray(eb[key])), (step, l, s, key)
+
+
+def test_sawtooth_and_no_op_from_empty():
+    wl = TINY["mha_f16_d64"]
+    eng = Engine(wl)
+    sizes = np.zeros((wl.n_layers, wl.batch), np.int64)
+    saw = set()
+    for step in range(wl.steps):
+        z = synth.logits(wl, step, 7)
+        q = synth.q_new(wl, step, 7)
+        k, v = synth.kv_new(wl, step, 7)
+        _, c, budget = eng.step(z.cuda(), q.cuda(), k.cuda(), v.cuda())
+        n = (eng.t_n8 + eng.t_n16).cpu().numpy()
+        budget = budget.cpu().numpy()
+        for l in range(wl.n_layers):
+            for b in range(wl.batch):
+                want = min(sizes[l, b] + 1, budget[b, l])
+                assert n[l, b] == want, (step, l, b)
+                sizes[l, b] = want
+        saw |= set(budget[:, 0].tolist())
+        if step < min(wl.n_high, wl.n_low) // 2:
+            assert int(n.min()) == step + 1                 # no-op under budget
+    assert saw == {wl.n_high, wl.n_low}
+    assert int((eng.t_n16).max()) <= wl.window
+    assert eng.status() == 0
