@@ -1,33 +1,109 @@
-// (b)+(c) Decode attention over the mixed-precision cache, and the per-token
-// attention mass that feeds the EMA.
+// (b)+(c) Decode attention over the mixed-precision cache, the per-token
+// attention mass, and the EMA update, in one launch.
 //
 // CONF-KV explainer, Key contributions (system design): block-wise online-
 // softmax attention; Methodology, implementation: dequantisation fused into the
 // block-wise attention reads over a dense (compacted) layout; mixed-precision
 // storage: INT8 codes with one scale per (KV head, channel), so the key scale
-// folds into the query and the value scale into the output.
+// folds into the query and the value scale into the output; token ranking: the
+// EMA of each token's attention mass.
 //
 // One workgroup per unit (layer, sequence, KV head) covers the g = Hq/Hkv query
-// heads that share the unit's keys and values, over n = n8 INT8 tokens followed by
-// the n16 window tokens (the appended token is the last window slot).
+// heads sharing the unit's keys and values, over the n8 INT8 tokens, the window
+// tokens and this step's token (read from the caller's k_new / v_new rows and
+// also appended to the window).  Each unit writes the mass of its g heads per
+// token; the last unit of a (layer, sequence) to arrive (arrival counter, device-
+// scope fences) sums the KV heads in index order and applies the EMA.
 #include "common.hpp"
 
 namespace confkv {
 
 constexpr int kAttnThreads = 256;
 
+// Token view of one unit for this step: INT8 slots [0, n8), window slots
+// [0, nw), then the new token (index n8 + nw) if it was appended.
+struct UnitView {
+  const int8_t* k8;
+  const int8_t* v8;
+  const uint16_t* k16;
+  const uint16_t* v16;
+  const uint16_t* knew;  // [D] row of this step's key
+  const uint16_t* vnew;  // [D] row of this step's value
+  int n8, nw, n;         // n = n8 + nw + appended
+};
+
+// Appends this step's key/value to window slot `slot` of the unit (data only).
+__device__ inline void append_row(const Dims& dm, uint16_t* k16, uint16_t* v16, int slot,
+                                  const uint16_t* knew, const uint16_t* vnew) {
+  for (int ch = threadIdx.x; ch < dm.D; ch += blockDim.x) {
+    k16[(size_t)slot * dm.D + ch] = knew[ch];
+    v16[vtile_off(slot, ch, dm.D)] = vnew[ch];
+  }
+}
+
+// EMA of one (layer, sequence) from the per-KV-head mass rows, run by the last
+// unit to arrive.  mass_j = (sum over KV heads, in index order) / Hq;
+// e <- decay*e + (1-decay)*mass; the appended token starts from e = 0 and takes
+// position t+1; then n16 and t advance.
+__device__ void ema_update_lb(const conf_cache& c, const Dims& dm, int lb, int n8, int nw,
+                              int appended, int t, const float* mp) {
+#pragma clang fp contract(off)
+  const float hq = (float)dm.Hq;
+  for (int j = threadIdx.x; j < n8 + nw + appended; j += blockDim.x) {
+    const int idx = j < n8 ? j : dm.cap8 + (j - n8);
+    float a = 0.f;
+    for (int hk = 0; hk < dm.Hkv; ++hk) a += mp[(size_t)hk * dm.capt + idx];
+    a = a / hq;
+    if (j < n8) {
+      float* e = c.ema8 + (size_t)lb * dm.cap8 + j;
+      *e = dm.decay * (*e) + dm.one_minus_decay * a;
+    } else {
+      const int w = j - n8;
+      float* e = c.ema16 + (size_t)lb * dm.cap16 + w;
+      if (w == nw) {
+        *e = dm.one_minus_decay * a;  // decay * 0 + (1 - decay) * mass
+        c.pos16[(size_t)lb * dm.cap16 + w] = t + 1;
+      } else {
+        *e = dm.decay * (*e) + dm.one_minus_decay * a;
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    c.n16[lb] = nw + appended;
+    c.t[lb] = t + 1;
+    c.arrive[lb] = 0;
+  }
+}
+
+// Arrival protocol: every thread's mass stores are fenced at device scope
+// before thread 0 counts the unit in; the unit that completes the count fences
+// again (acquire) and runs the EMA for the (layer, sequence).
+__device__ inline bool arrive_last(const conf_cache& c, const Dims& dm, int lb) {
+  __shared__ int s_last;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = atomicAdd(c.arrive + lb, 1);
+    s_last = prev == dm.Hkv - 1;
+  }
+  __syncthreads();
+  const bool last = s_last != 0;
+  if (last) __threadfence();
+  return last;
+}
+
 // ---------------------------------------------------------------------------
-// Reference-structured kernel: two passes over the keys (pass A: per-head
-// log-sum-exp; pass B: probabilities, token mass and the value sum).  Used for
-// every shape the matrix-core kernel does not take.
+// Two-pass kernel (pass A: per-head log-sum-exp; pass B: probabilities, token
+// mass and the value sum), vector ALU only.
 // ---------------------------------------------------------------------------
 template <int D>
-__device__ inline void key_dot(const Dims& dm, int j, int n8, const int8_t* k8, const uint16_t* k16,
-                               const float (*q8)[D], const float (*qw)[D], float* sig) {
+__device__ inline void key_dot(const Dims& dm, const UnitView& uv, int j, const float (*q8)[D],
+                               const float (*qw)[D], float* sig) {
 #pragma unroll
   for (int h = 0; h < kMaxGroup; ++h) sig[h] = 0.f;
-  if (j < n8) {
-    const int8_t* row = k8 + (size_t)j * D;
+  if (j < uv.n8) {
+    const int8_t* row = uv.k8 + (size_t)j * D;
     for (int c0 = 0; c0 < D; c0 += 16) {
       const int4 v = *(const int4*)(row + c0);
       const int8_t* bytes = (const int8_t*)&v;
@@ -40,7 +116,7 @@ __device__ inline void key_dot(const Dims& dm, int j, int n8, const int8_t* k8, 
       }
     }
   } else {
-    const uint16_t* row = k16 + (size_t)(j - n8) * D;
+    const uint16_t* row = (j - uv.n8 < uv.nw) ? uv.k16 + (size_t)(j - uv.n8) * D : uv.knew;
     for (int c0 = 0; c0 < D; c0 += 8) {
       const int4 v = *(const int4*)(row + c0);
       const uint16_t* hs = (const uint16_t*)&v;
@@ -58,6 +134,8 @@ __device__ inline void key_dot(const Dims& dm, int j, int n8, const int8_t* k8, 
 template <int D>
 __global__ __launch_bounds__(kAttnThreads) void attn_ref_kernel(conf_cache c, Dims dm, int layer0,
                                                                 const uint16_t* __restrict__ q_all,
+                                                                const uint16_t* __restrict__ knew_all,
+                                                                const uint16_t* __restrict__ vnew_all,
                                                                 float* __restrict__ out_all,
                                                                 float* __restrict__ massp_all) {
   const int unit_local = blockIdx.x;
@@ -67,13 +145,25 @@ __global__ __launch_bounds__(kAttnThreads) void attn_ref_kernel(conf_cache c, Di
   const size_t u = (size_t)lb * dm.Hkv + hk;
   const int tid = threadIdx.x;
   const int G = dm.G;
-  const int n8 = c.n8[lb];
-  const int n16 = min(c.n16[lb] + 1, dm.cap16);
-  const int n = n8 + n16;
-  const int8_t* k8 = c.k8 + u * (size_t)dm.cap8 * D;
-  const int8_t* v8 = c.v8 + u * (size_t)dm.cap8 * D;
-  const uint16_t* k16 = (const uint16_t*)c.k16 + u * (size_t)dm.cap16 * D;
-  const uint16_t* v16 = (const uint16_t*)c.v16 + u * (size_t)dm.cap16 * D;
+  const int n8 = c.n8[lb], nw = c.n16[lb], t = c.t[lb];
+  const int appended = nw < dm.cap16;
+  UnitView uv;
+  uv.k8 = c.k8 + u * (size_t)dm.cap8 * D;
+  uv.v8 = c.v8 + u * (size_t)dm.cap8 * D;
+  uv.k16 = (const uint16_t*)c.k16 + u * (size_t)dm.cap16 * D;
+  uv.v16 = (const uint16_t*)c.v16 + u * (size_t)dm.cap16 * D;
+  uv.knew = knew_all + (size_t)unit_local * D;
+  uv.vnew = vnew_all + (size_t)unit_local * D;
+  uv.n8 = n8;
+  uv.nw = nw;
+  uv.n = n8 + nw + appended;
+  const int n = uv.n;
+  if (appended) {
+    append_row(dm, (uint16_t*)c.k16 + u * (size_t)dm.cap16 * D,
+               (uint16_t*)c.v16 + u * (size_t)dm.cap16 * D, nw, uv.knew, uv.vnew);
+  } else if (tid == 0 && hk == 0) {
+    atomicOr(c.status, (int)CONF_ST_WINDOW_FULL);
+  }
 
   __shared__ float qw[kMaxGroup][D];
   __shared__ float q8[kMaxGroup][D];
@@ -101,7 +191,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_ref_kernel(conf_cache c, Di
     s[h] = 0.f;
   }
   for (int j = tid; j < n; j += kAttnThreads) {
-    key_dot<D>(dm, j, n8, k8, k16, q8, qw, sig);
+    key_dot<D>(dm, uv, j, q8, qw, sig);
 #pragma unroll
     for (int h = 0; h < kMaxGroup; ++h) {
       if (h < G) {
@@ -114,7 +204,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_ref_kernel(conf_cache c, Di
       }
     }
   }
-  // reduce (max, sum) pairs: wave shuffles, then across waves
 #pragma unroll
   for (int h = 0; h < kMaxGroup; ++h) {
     if (h < G) {
@@ -152,11 +241,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_ref_kernel(conf_cache c, Di
     acc8[r] = 0.f;
     acc16[r] = 0.f;
   }
-  float* massp = massp_all + u * (size_t)dm.capt;
+  float* mp_lb = massp_all + (size_t)lb * dm.Hkv * dm.capt;
+  float* massp = mp_lb + (size_t)hk * dm.capt;
   for (int base = 0; base < n; base += kAttnThreads) {
     const int j = base + tid;
     if (j < n) {
-      key_dot<D>(dm, j, n8, k8, k16, q8, qw, sig);
+      key_dot<D>(dm, uv, j, q8, qw, sig);
       float mass = 0.f;
 #pragma unroll
       for (int h = 0; h < kMaxGroup; ++h) {
@@ -183,10 +273,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_ref_kernel(conf_cache c, Di
         for (int jj = 0; jj < cnt; ++jj) {
           const int tok = base + jj;
           const float p = pch[h][jj];
-          if (tok < n8)
-            a8 = fmaf(p, (float)v8[vtile_off(tok, ch, D)], a8);
-          else
-            a16 = fmaf(p, h16_to_f32(v16[vtile_off(tok - n8, ch, D)], dm.bf16), a16);
+          if (tok < n8) {
+            a8 = fmaf(p, (float)uv.v8[vtile_off(tok, ch, D)], a8);
+          } else {
+            const int w = tok - n8;
+            const uint16_t x = w < nw ? uv.v16[vtile_off(w, ch, D)] : uv.vnew[ch];
+            a16 = fmaf(p, h16_to_f32(x, dm.bf16), a16);
+          }
         }
         acc8[r] = a8;
         acc16[r] = a16;
@@ -203,17 +296,20 @@ __global__ __launch_bounds__(kAttnThreads) void attn_ref_kernel(conf_cache c, Di
       out[idx] = fmaf(acc8[r], sv[ch], acc16[r]);
     }
   }
+  if (arrive_last(c, dm, lb)) ema_update_lb(c, dm, lb, n8, nw, appended, t, mp_lb);
 }
 
-void launch_attn(const Dims& dm, const conf_cache& c, int layer0, int nl, const void* q, float* out,
-                 float* massp, hipStream_t st) {
+void launch_attn(const Dims& dm, const conf_cache& c, int layer0, int nl, const void* q,
+                 const void* k_new, const void* v_new, float* out, float* massp, hipStream_t st) {
   const dim3 grid(nl * dm.B * dm.Hkv);
   if (dm.D == 64)
     hipLaunchKernelGGL(attn_ref_kernel<64>, grid, dim3(kAttnThreads), 0, st, c, dm, layer0,
-                       (const uint16_t*)q, out, massp);
+                       (const uint16_t*)q, (const uint16_t*)k_new, (const uint16_t*)v_new, out,
+                       massp);
   else
     hipLaunchKernelGGL(attn_ref_kernel<128>, grid, dim3(kAttnThreads), 0, st, c, dm, layer0,
-                       (const uint16_t*)q, out, massp);
+                       (const uint16_t*)q, (const uint16_t*)k_new, (const uint16_t*)v_new, out,
+                       massp);
 }
 
 }  // namespace confkv

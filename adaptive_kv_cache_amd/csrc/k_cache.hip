@@ -1,5 +1,5 @@
-// Cache maintenance kernels: reset, append, EMA update, prefill ingest,
-// compaction + demotion, and export of one (layer, sequence).
+// Cache maintenance kernels: reset, prefill ingest, compaction + demotion, and
+// export of one (layer, sequence).
 //
 // CONF-KV explainer, Methodology, system integration: the newest W tokens stay
 // 16-bit, older kept tokens are INT8 per head and channel (mixed-precision
@@ -21,6 +21,7 @@ __global__ void reset_kernel(conf_cache c, Dims dm) {
     c.n8[i] = 0;
     c.n16[i] = 0;
     c.t[i] = -1;
+    c.arrive[i] = 0;
   }
   if (i < namax) {
     c.k_amax[i] = 0.f;
@@ -33,80 +34,6 @@ void launch_reset(const Dims& dm, const conf_cache& c, hipStream_t st) {
   const size_t n = (size_t)dm.L * dm.B * dm.Hkv * dm.D;
   const size_t blocks = (n + 255) / 256;
   hipLaunchKernelGGL(reset_kernel, dim3((unsigned)blocks), dim3(256), 0, st, c, dm);
-}
-
-// ---------------------------------------------------------------- append
-// Writes step t's key/value rows into window slot n16 (data only; the
-// position, EMA and counters are advanced by the EMA kernel after attention).
-__global__ void append_kernel(conf_cache c, Dims dm, int layer0, const uint16_t* __restrict__ knew,
-                              const uint16_t* __restrict__ vnew) {
-  const int unit_local = blockIdx.x;  // (l_local, b, hk)
-  const int hk = unit_local % dm.Hkv;
-  const int lbl = unit_local / dm.Hkv;
-  const int lb = layer0 * dm.B + lbl;
-  const int n16 = c.n16[lb];
-  if (n16 >= dm.cap16) {
-    if (threadIdx.x == 0) atomicOr(c.status, (int)CONF_ST_WINDOW_FULL);
-    return;
-  }
-  const size_t u = unit_of(dm, lb, hk);
-  uint16_t* k16 = (uint16_t*)c.k16 + u * (size_t)dm.cap16 * dm.D;
-  uint16_t* v16 = (uint16_t*)c.v16 + u * (size_t)dm.cap16 * dm.D;
-  const size_t src = (size_t)unit_local * dm.D;
-  for (int ch = threadIdx.x; ch < dm.D; ch += blockDim.x) {
-    k16[(size_t)n16 * dm.D + ch] = knew[src + ch];
-    v16[vtile_off(n16, ch, dm.D)] = vnew[src + ch];
-  }
-}
-
-void launch_append(const Dims& dm, const conf_cache& c, int layer0, int nl, const void* k,
-                   const void* v, hipStream_t st) {
-  hipLaunchKernelGGL(append_kernel, dim3(nl * dm.B * dm.Hkv), dim3(128), 0, st, c, dm, layer0,
-                     (const uint16_t*)k, (const uint16_t*)v);
-}
-
-// ---------------------------------------------------------------- EMA
-// mass_j = (sum over KV heads of the per-head-group mass) / Hq, summed in KV-head
-// order; e <- decay*e + (1-decay)*mass.  The appended token (window slot n16)
-// starts from e = 0 and gets position t+1; then n16 and t advance.
-__global__ __launch_bounds__(256) void ema_kernel(conf_cache c, Dims dm, int layer0,
-                                                  const float* __restrict__ massp) {
-#pragma clang fp contract(off)
-  const int lb = layer0 * dm.B + blockIdx.x;
-  const int n8 = c.n8[lb], n16 = c.n16[lb], t = c.t[lb];
-  const int appended = n16 < dm.cap16;
-  const int n16a = n16 + appended;
-  const float hq = (float)dm.Hq;
-  const float* mp = massp + (size_t)lb * dm.Hkv * dm.capt;
-  for (int j = threadIdx.x; j < n8 + n16a; j += blockDim.x) {
-    const int idx = j < n8 ? j : dm.cap8 + (j - n8);
-    float a = 0.f;
-    for (int hk = 0; hk < dm.Hkv; ++hk) a += mp[(size_t)hk * dm.capt + idx];
-    a = a / hq;
-    if (j < n8) {
-      float* e = c.ema8 + (size_t)lb * dm.cap8 + j;
-      *e = dm.decay * (*e) + dm.one_minus_decay * a;
-    } else {
-      const int w = j - n8;
-      float* e = c.ema16 + (size_t)lb * dm.cap16 + w;
-      if (w == n16) {
-        *e = dm.one_minus_decay * a;  // decay * 0 + (1 - decay) * mass
-        c.pos16[(size_t)lb * dm.cap16 + w] = t + 1;
-      } else {
-        *e = dm.decay * (*e) + dm.one_minus_decay * a;
-      }
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    c.n16[lb] = n16a;
-    c.t[lb] = t + 1;
-  }
-}
-
-void launch_ema(const Dims& dm, const conf_cache& c, int layer0, int nl, const float* massp,
-                hipStream_t st) {
-  hipLaunchKernelGGL(ema_kernel, dim3(nl * dm.B), dim3(256), 0, st, c, dm, layer0, massp);
 }
 
 // ---------------------------------------------------------------- ingest

@@ -1,0 +1,297 @@
+"""Decode-step benchmark of the CONF-KV hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 384] [--warmup 128] [--workload NAME]
+
+A step is one pass of the whole path over one batch: decode attention with
+append and EMA (conf_decode_attn), confidence + budgets (conf_confidence),
+rank + select (conf_rank_evict) and compaction + demotion (conf_compact_demote),
+for every layer and sequence.  Inputs (logits, q, k, v of every step) are
+generated on the device before the timed region; the prefilled context is
+ingested during set-up.  Default workload: the Qwen-32B-shaped GQA cache
+(64 layers, 40 query / 8 KV heads, head_dim 128, bf16, batch 8, 32768-token
+prefill with a planted needle, budgets 2048 / 4096, P 256, W 512).  The first
+128 steps (the one-off bulk eviction of the prefill and the first confident /
+unconfident phases) are warm-up; the timed steps are the steady state.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from adaptive_kv_cache_amd import synth  # noqa: E402
+from adaptive_kv_cache_amd.binding import Engine  # noqa: E402
+from adaptive_kv_cache_amd.workloads import WORKLOADS  # noqa: E402
+
+METRIC = "decode steps/s (attn+confidence+evict+compact), HBM GB/s vs peak, batch 8"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- byte model
+def attn_bytes(wl, n8, nw):
+    """Algorithmic bytes of one attention launch (every layer and sequence).
+
+    n8, nw: int64 tensors [L][B] of INT8 and window tokens before the append.
+    Per (layer, sequence): cached K and V (1 byte per INT8 element, e per 16-bit
+    element), this step's k and v read and appended, both absmax rows, q in and
+    o out (fp32), and every token's EMA read and written plus the new position.
+    """
+    e = 2
+    H, d, Hq = wl.n_kv_heads, wl.head_dim, wl.n_q_heads
+    kv = 2 * H * d * (n8 + e * nw)
+    per_lb = kv + 2 * H * d * e * 2 + 2 * H * d * 4 + Hq * d * (e + 4) + 8 * (n8 + nw + 1) + 4
+    return int(per_lb.sum())
+
+
+def step_bytes(wl, n8, nw, plan):
+    """Algorithmic bytes of one whole step: attention, logits, selection reads and
+    keep flags, hole-fill moves and the demotion (requantisation not counted)."""
+    H, d, e = wl.n_kv_heads, wl.head_dim, 2
+    n = n8 + nw + 1
+    b = attn_bytes(wl, n8, nw)
+    b += wl.batch * wl.vocab * 4
+    b += int((9 * n).sum())                                     # EMA + pos read, keep written
+    b += int(n.sum())                                           # keep read by the compaction
+    moves8, moves16, dest = plan[..., 1], plan[..., 3], plan[..., 5]
+    b += int((moves8 * (2 * 2 * H * d + 16)).sum())
+    b += int((moves16 * (2 * 2 * H * d * e + 16)).sum())
+    b += int(((dest >= 0).long() * (2 * H * d * (e + 1) + 8)).sum())
+    return b
+
+
+# ---------------------------------------------------------------- CPU baseline
+def cpu_baseline(wl, seed, budget_s=20.0):
+    """The oracle as it stands, on a bounded sample: every layer of one sequence
+    stepped from a steady-state-sized cache (N_high + 64 tokens, the top of the
+    confident-phase sawtooth) for as many steps as fit in about `budget_s`."""
+    import numpy as np
+
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas = 1
+    cores = len(os.sched_getaffinity(0))
+    prm = O.OracleParams(n_layers=wl.n_layers, n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads,
+                         head_dim=wl.head_dim, dtype16=wl.dtype16, window=wl.window,
+                         protect=wl.protect, n_high=wl.n_high, n_low=wl.n_low,
+                         pyramid=wl.pyramid, tau=wl.tau)
+    n0 = wl.n_high + 64
+    rng = np.random.default_rng(seed)
+    states = []
+    for l in range(wl.n_layers):
+        k = O.encode16(rng.standard_normal((wl.n_kv_heads, n0, wl.head_dim)), wl.dtype16)
+        v = O.encode16(rng.standard_normal((wl.n_kv_heads, n0, wl.head_dim)), wl.dtype16)
+        states.append([O.ingest(k, v, wl.window, wl.dtype16)])
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        z = synth.logits(wl.scaled(batch=1), 64 + steps, seed).numpy().astype(np.float64)
+        q = O.encode16(rng.standard_normal((wl.n_layers, 1, wl.n_q_heads, wl.head_dim)),
+                       wl.dtype16)
+        kk = O.encode16(rng.standard_normal((wl.n_layers, 1, wl.n_kv_heads, wl.head_dim)),
+                        wl.dtype16)
+        vv = O.encode16(rng.standard_normal((wl.n_layers, 1, wl.n_kv_heads, wl.head_dim)),
+                        wl.dtype16)
+        O.decode_step(states, z, q, kk, vv, prm)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or steps >= 64:
+            break
+    per_seq_step = el / steps
+    return {
+        "value": 1.0 / (per_seq_step * wl.batch), "unit": "steps/s", "cores": cores,
+        "blas_threads": blas, "kind": "oracle",
+        "sample": (f"{steps} steps x {wl.n_layers} layers x 1 sequence from a {n0}-token cache; "
+                   f"{per_seq_step:.3f} s per sequence-step, extrapolated to batch {wl.batch}"),
+    }
+
+
+# ---------------------------------------------------------------- GPU run
+def run(args):
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    total = args.warmup + args.steps
+    if total > wl.steps:
+        log(f"note: {total} steps exceed the workload's {wl.steps}; inputs are generated anyway")
+    log(f"set-up {wl.name}: cap8={wl.cap8} prefill={wl.prefill}")
+    eng = Engine(wl, dev)
+    t0 = time.perf_counter()
+    if wl.prefill:
+        for l in range(wl.n_layers):
+            k, v = synth.prefill_kv(wl, l, args.seed, device=dev)
+            eng.ingest(l, k, v)
+            del k, v
+    torch.cuda.synchronize()
+    log(f"ingest done in {time.perf_counter() - t0:.1f} s")
+    L, B = wl.n_layers, wl.batch
+    logits = torch.empty(total, B, wl.vocab, dtype=torch.float32, device=dev)
+    qs = torch.empty(total, L, B, wl.n_q_heads, wl.head_dim, dtype=eng.dtype16, device=dev)
+    ks = torch.empty(total, L, B, wl.n_kv_heads, wl.head_dim, dtype=eng.dtype16, device=dev)
+    vs = torch.empty_like(ks)
+    for s in range(total):
+        logits[s] = synth.logits(wl, s, args.seed, device=dev)
+        qs[s] = synth.q_new(wl, s, args.seed, device=dev)
+        ks[s], vs[s] = synth.kv_new(wl, s, args.seed, device=dev)
+    out = torch.empty(L, B, wl.n_q_heads, wl.head_dim, dtype=torch.float32, device=dev)
+    conf = torch.empty(total, B, dtype=torch.float32, device=dev)
+    budget = torch.empty(total, B, L, dtype=torch.int32, device=dev)
+    keep = torch.zeros(L, B, eng.cap8 + eng.cap16, dtype=torch.uint8, device=dev)
+    hist8 = torch.empty(args.steps, L, B, dtype=torch.int32, device=dev)
+    hist16 = torch.empty_like(hist8)
+    plan_off = _plan_offset(eng)
+    hplan = torch.empty(args.steps, L, B, 16, dtype=torch.int32, device=dev)
+    ws_plan = eng.ws[plan_off:plan_off + L * B * 16 * 4].view(torch.int32).view(L, B, 16)
+    torch.cuda.synchronize()
+    log("inputs resident; warm-up")
+
+    def one_step(s, ev=None, i=None):
+        if i is not None:
+            hist8[i].copy_(eng.t_n8)
+            hist16[i].copy_(eng.t_n16)
+        if ev is not None:
+            ev[0].record()
+        eng.decode_attn(-1, qs[s], ks[s], vs[s], out=out)
+        if ev is not None:
+            ev[1].record()
+        eng.confidence(logits[s], c=conf[s], budget=budget[s])
+        eng.rank_evict(-1, budget[s], keep=keep)
+        eng.compact_demote(-1, keep)
+        if i is not None:
+            hplan[i].copy_(ws_plan)
+
+    for s in range(args.warmup):
+        one_step(s)
+        if s % 32 == 0:
+            torch.cuda.synchronize()
+            log(f"  warm-up step {s}")
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"timed: {args.steps} steps")
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        one_step(args.warmup + i, evs[i], i)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    st = eng.status()
+    if st:
+        raise RuntimeError(f"cache status word {st}: a capacity was exceeded")
+    h8, h16, hp = hist8.cpu().long(), hist16.cpu().long(), hplan.cpu().long()
+    # the plan copied from the workspace must describe the cache the step left
+    n8_after = hp[-1][..., 0] + (hp[-1][..., 5] >= 0).long()
+    if not (torch.equal(n8_after, eng.t_n8.cpu().long())
+            and torch.equal(hp[-1][..., 2], eng.t_n16.cpu().long())):
+        raise RuntimeError("workspace plan offset does not match the library's layout")
+    a_bytes = [attn_bytes(wl, h8[i], h16[i]) for i in range(args.steps)]
+    s_bytes = [step_bytes(wl, h8[i], h16[i], hp[i]) for i in range(args.steps)]
+    attn_avg_ms = sum(attn_ms) / len(attn_ms)
+    attn_gbs = (sum(a_bytes) / len(a_bytes)) / (attn_avg_ms * 1e-3) / 1e9
+    sps = args.steps / (ms * 1e-3)
+    step_gbs = (sum(s_bytes) / len(s_bytes)) * sps / 1e9
+    n_mean = float((h8 + h16 + 1).float().mean())
+    res = {
+        "metric": METRIC, "value": round(sps, 3), "unit": "steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": L, "batch": B, "q_heads": wl.n_q_heads,
+                   "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "dtype16": wl.dtype16,
+                   "prefill": wl.prefill, "n_high": wl.n_high, "n_low": wl.n_low,
+                   "protect": wl.protect, "window": wl.window, "pyramid": wl.pyramid,
+                   "vocab": wl.vocab, "mean_tokens_attended": round(n_mean, 1)},
+        "roofline": {"bound": "hbm", "kernel": "conf_decode_attn (one launch)",
+                     "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(attn_avg_ms * 1e3, 2),
+                     "alg_bytes_per_launch": int(sum(a_bytes) / len(a_bytes))},
+        "step_roofline": {"achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                          "alg_bytes_per_step": int(sum(s_bytes) / len(s_bytes))},
+    }
+    return res, wl
+
+
+def _plan_offset(eng):
+    """Byte offset of the compaction plan inside the workspace (same arithmetic
+    as the library's workspace map: 256-byte aligned regions in a fixed order)."""
+    wl = eng.wl
+    LB = wl.n_layers * wl.batch
+    a = lambda x: (x + 255) & ~255  # noqa: E731
+    nch = -(-wl.vocab // (256 * 16))
+    off = a(wl.batch * nch * 8 * 4)
+    off = a(off + LB * wl.n_kv_heads * (eng.cap8 + eng.cap16) * 4)
+    off = a(off + LB * wl.n_q_heads * 4)
+    off = a(off + LB * (eng.cap8 + eng.cap16))
+    return off
+
+
+def rocpd_summary(db_path, timed_steps):
+    """Per-kernel durations from a rocprofv3 database of a bench run: every
+    dispatch, and the last `timed_steps` dispatches of each kernel (the timed
+    steady-state steps when the kernel runs once per step)."""
+    import sqlite3
+    db = sqlite3.connect(db_path)
+    rows = db.execute("select name, duration from kernels order by start").fetchall()
+    per = {}
+    for name, dur in rows:
+        short = name.split("(")[0].replace("void ", "").replace("confkv::", "")
+        per.setdefault(short[:70], []).append(dur)
+    lines = [f"rocpd database: {os.path.basename(db_path)}",
+             f"{'kernel':70s} {'calls':>6s} {'avg_us':>10s} {'min_us':>9s} {'max_us':>10s} "
+             f"{'last' + str(timed_steps) + '_avg_us':>14s}"]
+    for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        tail = v[-timed_steps:]
+        lines.append(f"{k:70s} {len(v):6d} {sum(v) / len(v) / 1e3:10.2f} {min(v) / 1e3:9.2f} "
+                     f"{max(v) / 1e3:10.2f} {sum(tail) / len(tail) / 1e3:14.2f}")
+    return "\n".join(lines)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=384)
+    ap.add_argument("--warmup", type=int, default=128)
+    ap.add_argument("--workload", default="qwen32b_gqa_b8_32k")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--rocpd-summary", metavar="DB",
+                    help="print per-kernel durations of a rocprofv3 database and exit")
+    args = ap.parse_args()
+    if args.rocpd_summary:
+        print(rocpd_summary(args.rocpd_summary, args.steps))
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(sharding is described in the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    res, wl = run(args)
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline(wl, args.seed, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -92,6 +92,8 @@ typedef struct conf_params {
  *   n8, n16        int32 [L][B]                   occupied slots (dense prefix)
  *   t              int32 [L][B]                   newest position (-1 = empty)
  *   status         int32 [1]                      CONF_ST_* bits
+ *   arrive         int32 [L][B]                   per-step arrival counters of the
+ *                                                 KV-head workgroups (0 between calls)
  * Inside a 64-token tile, slot s sits at column tile_col(s % 64), where for
  * j = 32u + 16a + 4g + b (u, a in {0,1}; g, b in 0..3) tile_col(j) = 16g + 8u + 4a + b.
  * (This order lets a wavefront feed the matrix cores straight from memory.)
@@ -113,10 +115,11 @@ typedef struct conf_cache {
   int32_t* n16;
   int32_t* t;
   int32_t* status;
+  int32_t* arrive;
 } conf_cache;
 
 typedef struct conf_cache_bytes_t {
-  size_t k8, v8, k16, v16, k_amax, v_amax, pos8, ema8, pos16, ema16, n8, n16, t, status;
+  size_t k8, v8, k16, v16, k_amax, v_amax, pos8, ema8, pos16, ema16, n8, n16, t, status, arrive;
   int32_t cap16;
 } conf_cache_bytes_t;
 
@@ -126,7 +129,8 @@ int conf_cache_layout(const conf_params* p, conf_cache_bytes_t* out);
 /* Workspace bytes every call below may use for `p`. */
 int conf_workspace_bytes(const conf_params* p, size_t* bytes);
 
-/* Empty every (layer, sequence): n8 = n16 = 0, t = -1, absmax = 0, status = 0.
+/* Empty every (layer, sequence): n8 = n16 = 0, t = -1, absmax = 0, status = 0,
+ * arrive = 0.
  * Fills with kernels (no memset nodes), so it may be graph-captured. */
 int conf_cache_reset(const conf_params* p, conf_cache* c, conf_stream_t stream);
 
