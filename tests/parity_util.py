@@ -105,4 +105,9 @@ def tiny_workloads() -> dict:
         name="gqa16_f16_d128", n_layers=1, batch=1, n_q_heads=16, n_kv_heads=1, head_dim=128,
         vocab=777, dtype16="f16", window=33, protect=5, n_high=40, n_low=90, prefill=200,
         steps=30)
+    # more scores than the LDS holds at the first step: exercises the two-pass path
+    w["gqa16_bf16_d64_long"] = Workload(
+        name="gqa16_bf16_d64_long", n_layers=1, batch=2, n_q_heads=16, n_kv_heads=1, head_dim=64,
+        vocab=500, dtype16="bf16", window=64, protect=8, n_high=100, n_low=300, prefill=2500,
+        steps=8)
     return w
