@@ -35,7 +35,7 @@ class ConfParams(ctypes.Structure):
 
 
 _CACHE_FIELDS = ("k8", "v8", "k16", "v16", "k_amax", "v_amax", "pos8", "ema8", "pos16", "ema16",
-                 "n8", "n16", "t", "status", "arrive")
+                 "n8", "n16", "t", "status")
 
 
 class ConfCache(ctypes.Structure):
@@ -148,7 +148,6 @@ class Engine:
         self.t_n16 = torch.zeros_like(self.t_n8)
         self.t_t = torch.zeros_like(self.t_n8)
         self.t_status = torch.zeros(1, dtype=torch.int32, device=dev)
-        self.t_arrive = torch.zeros(L, B, dtype=torch.int32, device=dev)
         for f in _CACHE_FIELDS:
             assert getattr(self, "t_" + f).numel() * getattr(self, "t_" + f).element_size() \
                 == getattr(sizes, f), f

@@ -13,7 +13,7 @@ int conf_vchunks(int V);
 void launch_confidence(const Dims&, const float*, float*, float*, int32_t*, hipStream_t);
 void launch_reset(const Dims&, const conf_cache&, hipStream_t);
 void launch_attn(const Dims&, const conf_cache&, int, int, const void*, const void*, const void*,
-                 float*, float*, hipStream_t);
+                 float*, float*, int32_t*, hipStream_t);
 void launch_ingest(const Dims&, const conf_cache&, int, int, int, const void*, const void*,
                    hipStream_t);
 void launch_select(const Dims&, const conf_cache&, int, int, const int32_t*, uint8_t*, hipStream_t);
@@ -107,6 +107,8 @@ WsMap make_ws(const Dims& d) {
   off = align256(off + LB * d.cap16 * sizeof(int32_t));
   w.wkeep = off;
   off = align256(off + LB * d.cap16);
+  w.snap = off;
+  off = align256(off + LB * 3 * sizeof(int32_t));
   w.total = off;
   return w;
 }
@@ -118,7 +120,7 @@ T* at(void* ws, size_t off) {
 
 bool cache_ok(const conf_cache* c) {
   return c && c->k8 && c->v8 && c->k16 && c->v16 && c->k_amax && c->v_amax && c->pos8 &&
-         c->ema8 && c->pos16 && c->ema16 && c->n8 && c->n16 && c->t && c->status && c->arrive;
+         c->ema8 && c->pos16 && c->ema16 && c->n8 && c->n16 && c->t && c->status;
 }
 
 // layer selector -> (first layer, layer count)
@@ -158,7 +160,6 @@ int conf_cache_layout(const conf_params* p, conf_cache_bytes_t* o) {
   o->n16 = o->n8;
   o->t = o->n8;
   o->status = sizeof(int32_t);
-  o->arrive = LB * sizeof(int32_t);
   o->cap16 = d.cap16;
   return CONF_OK;
 }
@@ -218,7 +219,8 @@ int conf_decode_attn(const conf_params* p, conf_cache* c, int32_t layer, const v
     return CONF_E_INVALID;
   const WsMap w = make_ws(d);
   hipStream_t st = (hipStream_t)stream;
-  launch_attn(d, *c, l0, nl, q, k_new, v_new, out, at<float>(ws, w.massp), st);
+  launch_attn(d, *c, l0, nl, q, k_new, v_new, out, at<float>(ws, w.massp), at<int32_t>(ws, w.snap),
+              st);
   return check_launch("conf_decode_attn");
 }
 
@@ -257,7 +259,8 @@ int conf_step(const conf_params* p, conf_cache* c, const float* logits, const vo
     return CONF_E_INVALID;
   const WsMap w = make_ws(d);
   hipStream_t st = (hipStream_t)stream;
-  launch_attn(d, *c, 0, d.L, q, k_new, v_new, out, at<float>(ws, w.massp), st);
+  launch_attn(d, *c, 0, d.L, q, k_new, v_new, out, at<float>(ws, w.massp), at<int32_t>(ws, w.snap),
+              st);
   launch_confidence(d, logits, at<float>(ws, w.conf_part), conf, budget, st);
   uint8_t* keep = at<uint8_t>(ws, w.keep);
   launch_select(d, *c, 0, d.L, budget, keep, st);

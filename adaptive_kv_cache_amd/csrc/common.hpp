@@ -31,21 +31,41 @@ struct WsMap {
   size_t mv8;         // int32 [L][B][cap8]       (src, dst) pairs, INT8 region
   size_t mv16;        // int32 [L][B][cap16]      (src, dst) pairs, window
   size_t wkeep;       // uint8 [L][B][cap16]      window keep flags minus the demotee
+  size_t snap;        // int32 [L][B][3]          (n8, n16, t) before the step's append
   size_t total;
   int n_vchunks;      // vocab chunks per sequence in the confidence reduction
 };
 
-// Slot -> column inside a 64-token value tile.  With s = 32u + 16a + 4g + b
-// the column is 16g + 8u + 4a + b: a 16-lane group of a wavefront then holds the
-// 16 tokens it contracts over in one contiguous 16-element run.
-__host__ __device__ inline int tile_col(int s) {
-  const int b = s & 3, g = (s >> 2) & 3, a = (s >> 4) & 1, u = (s >> 5) & 1;
-  return (g << 4) | (u << 3) | (a << 2) | b;
+// Tiled layouts of one unit (layer, sequence, KV head).  Every region is cut
+// into 64-token tiles of 64*d elements; inside a tile the order is chosen so that
+// each 16-byte-per-lane load of a wavefront reads one contiguous 1 KB run and
+// lands in the lane that feeds it to the matrix cores.  Write a slot as
+// j = 64*tile + 32u + 16a + 4g + b = 64*tile + 16r + row  (u, a in {0,1}; g, b, r in 0..3).
+//
+//   k8  (INT8 keys):    [r][c / 64][(c / 16) % 4][row][c % 16]
+//   v8  (INT8 values):  [c][16g + 8u + 4a + b]
+//   k16 (16-bit keys):  [u][r % 2][c / 32][(c / 8) % 4][row][c % 8]
+//   v16 (16-bit values):[u][c][8g + 4a + b]
+__host__ __device__ inline size_t k8_off(int slot, int c, int D) {
+  const int jj = slot & 63, r = jj >> 4, row = jj & 15;
+  return (size_t)(slot >> 6) * (size_t)(D * kTile) +
+         (size_t)((((r * (D >> 6) + (c >> 6)) * 4 + ((c >> 4) & 3)) * 16 + row) * 16 + (c & 15));
 }
-
-// Element offset of (slot, channel) in a tiled value region of one unit.
-__host__ __device__ inline size_t vtile_off(int slot, int c, int D) {
-  return (size_t)(slot >> 6) * (size_t)(D * kTile) + (size_t)c * kTile + tile_col(slot & 63);
+__host__ __device__ inline size_t k16_off(int slot, int c, int D) {
+  const int jj = slot & 31, rr = jj >> 4, row = jj & 15;
+  return (size_t)(slot >> 5) * (size_t)(D * 32) +
+         (size_t)((((rr * (D >> 5) + (c >> 5)) * 4 + ((c >> 3) & 3)) * 16 + row) * 8 + (c & 7));
+}
+__host__ __device__ inline size_t v8_off(int slot, int c, int D) {
+  const int s = slot & 63;
+  const int b = s & 3, g = (s >> 2) & 3, a = (s >> 4) & 1, u = (s >> 5) & 1;
+  return (size_t)(slot >> 6) * (size_t)(D * kTile) + (size_t)c * kTile +
+         (size_t)((g << 4) | (u << 3) | (a << 2) | b);
+}
+__host__ __device__ inline size_t v16_off(int slot, int c, int D) {
+  const int s = slot & 31;
+  const int b = s & 3, g = (s >> 2) & 3, a = (s >> 4) & 1;
+  return (size_t)(slot >> 5) * (size_t)(D * 32) + (size_t)c * 32 + (size_t)((g << 3) | (a << 2) | b);
 }
 
 __device__ inline float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }

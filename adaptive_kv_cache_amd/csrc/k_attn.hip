@@ -1,90 +1,46 @@
-// (b)+(c) Decode attention on the CDNA4 matrix cores, with the per-token
-// attention mass and the EMA update, in one launch per step.
+// (b)+(c) Decode attention on the CDNA4 matrix cores, the per-token attention
+// mass and the EMA update.
 //
 // CONF-KV explainer, Key contributions (system design): block-wise online-
 // softmax attention; Methodology, implementation: dequantisation fused into the
 // block-wise attention reads over a dense (compacted) layout; mixed-precision
-// storage: INT8 codes with one scale per (KV head, channel).
+// storage: INT8 codes with one scale per (KV head, channel); token ranking: the
+// EMA of each token's attention mass.
 //
-// Work split: one workgroup (4 wavefronts) per unit (layer, sequence, KV head);
-// a wavefront takes whole 64-token blocks, round-robin.  For a block it forms
-//   S^T[16 tokens x 16 heads] = K[16 x d] . Q^T[d x 16]   (v_mfma_f32_16x16x32)
-// four times (64 tokens), so each lane holds one query head (lane % 16) and four
-// tokens per 16-token row block; that is exactly the A-operand layout of
+// Two launches.  The attention kernel writes, per unit, the mass of its query
+// group for every token to the workspace; a small kernel then sums the KV heads
+// in index order and applies the EMA.  (A kernel boundary is the cheap way to
+// order that: a device-scope fence per workgroup would write back the per-XCD
+// L2 caches.)
+//
+// Work split.  One workgroup (4 wavefronts) per unit (layer, sequence, KV head)
+// covers the g = Hq/Hkv query heads that share the unit's keys and values.  The
+// unit's tokens are cut into work items of equal byte size: 64-token INT8 blocks
+// and 32-token halves of the 64-token window tiles.  Wavefront w takes items w,
+// w+4, ...; while it computes item i, the values of item i and the keys of
+// item i+4 are in flight.  For an item it forms
+//   S^T[16 tokens x 16 heads] = K[16 x d] . Q^T[d x 16]          (v_mfma_f32_16x16x32)
+// per 16-token row block, so a lane holds one query head (lane % 16) and four
+// tokens per row block; that is the A-operand layout of
 //   O[16 heads x 16 channels] += P[16 x 32 tokens] . V[32 tokens x 16 channels]
-// so P never leaves registers, and the tiled value layout (see tile_col) hands
-// each lane its 16 tokens of one channel in one 16-byte load.  Heads beyond
-// g = Hq/Hkv are zero padding of the 16-wide tile.
+// so P never leaves registers, and the tiled value layout hands each lane its
+// tokens of one channel in one 16-byte load.  Heads beyond g are zero padding.
 //
 // Precision.  INT8 codes become fp16 exactly.  The key scale folds into the
-// query: q' = q * amax_K/127, scaled by a power of two per head so its largest
-// entry sits in [2^14, 2^15), then split into fp16 hi + lo parts (two MFMAs,
-// ~22 significant bits).  Window keys meet the 16-bit query as stored (exact
-// products).  P is rounded to fp16 for INT8 values and fp16 windows; for
-// bfloat16 windows it is split into bf16 hi + lo parts.  All sums are fp32.
+// query: q' = q * amax_K/127, times a power of two per head that puts its largest
+// entry in [2^14, 2^15), split into fp16 hi + lo parts (two MFMAs, ~22 bits).
+// Window keys meet the 16-bit query as stored (exact products).  P is rounded to
+// fp16 for INT8 values and fp16 windows, and split into bf16 hi + lo for bfloat16
+// windows.  Accumulation is fp32 throughout.  The INT8 value scale multiplies the
+// accumulator once, between a wavefront's INT8 items and its window items.
 //
-// Scores of the whole unit stay in LDS (fp32) when they fit; then the per-token
-// mass is formed after the softmax normaliser is final.  Otherwise (the first
-// step after a long prefill) the kernel makes two passes over the keys: the
-// first finds each head's log-sum-exp, the second forms probabilities, mass and
-// the value sums directly.
+// Scores of the whole unit stay in LDS (fp32) when they fit, and the per-token
+// mass is formed once the softmax normaliser is final.  Otherwise (the first step
+// after a long prefill) the kernel makes two passes over the keys: the first
+// finds each head's log-sum-exp, the second forms probabilities, mass and values.
 #include "common.hpp"
 
 namespace confkv {
-
-// EMA of one (layer, sequence) from the per-KV-head mass rows, run by the last
-// unit to arrive.  mass_j = (sum over KV heads, in index order) / Hq;
-// e <- decay*e + (1-decay)*mass; the appended token starts from e = 0 and takes
-// position t+1; then n16 and t advance.
-__device__ void ema_update_lb(const conf_cache& c, const Dims& dm, int lb, int n8, int nw,
-                              int appended, int t, const float* mp) {
-#pragma clang fp contract(off)
-  const float hq = (float)dm.Hq;
-  for (int j = threadIdx.x; j < n8 + nw + appended; j += blockDim.x) {
-    const int idx = j < n8 ? j : dm.cap8 + (j - n8);
-    float a = 0.f;
-    for (int hk = 0; hk < dm.Hkv; ++hk) a += mp[(size_t)hk * dm.capt + idx];
-    a = a / hq;
-    if (j < n8) {
-      float* e = c.ema8 + (size_t)lb * dm.cap8 + j;
-      *e = dm.decay * (*e) + dm.one_minus_decay * a;
-    } else {
-      const int w = j - n8;
-      float* e = c.ema16 + (size_t)lb * dm.cap16 + w;
-      if (w == nw) {
-        *e = dm.one_minus_decay * a;  // decay * 0 + (1 - decay) * mass
-        c.pos16[(size_t)lb * dm.cap16 + w] = t + 1;
-      } else {
-        *e = dm.decay * (*e) + dm.one_minus_decay * a;
-      }
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    c.n16[lb] = nw + appended;
-    c.t[lb] = t + 1;
-    c.arrive[lb] = 0;
-  }
-}
-
-// Arrival protocol: every thread's mass stores are fenced at device scope
-// before thread 0 counts the unit in; the unit that completes the count fences
-// again (acquire) and runs the EMA for the (layer, sequence).
-__device__ inline bool arrive_last(const conf_cache& c, const Dims& dm, int lb) {
-  __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = atomicAdd(c.arrive + lb, 1);
-    s_last = prev == dm.Hkv - 1;
-  }
-  __syncthreads();
-  const bool last = s_last != 0;
-  if (last) __threadfence();
-  return last;
-}
-
-
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
@@ -93,8 +49,8 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
-constexpr int kMfmaThreads = kWaves * 64;
-constexpr int kLdsScoreBytes = 76 * 1024;  // dynamic LDS budget of one workgroup
+constexpr int kAttnThreads = kWaves * 64;
+constexpr int kLdsDynBytes = 76 * 1024;  // dynamic LDS of one workgroup (two fit a CU)
 
 enum { MODE_ONLINE = 0, MODE_LSE = 1, MODE_FINAL = 2 };
 
@@ -125,73 +81,137 @@ __device__ inline void codes_to_f16(u4 raw, h8& a0, h8& a1) {
 
 __device__ inline u4 ld16(const void* p) { return *(const u4*)p; }
 
+// ---------------------------------------------------------------- work items
+template <int D>
+struct Raw {
+  u4 k[D / 16];   // INT8 block: [row block r][64-channel half hh]; window half: [r][32-ch step s]
+  u4 v[D / 16];   // [16-channel block cb]
+};
+
 template <int D>
 struct WaveAcc {
-  float m;             // running max of this lane's head
-  float l;             // running sum
-  f4 o[D / 16];        // O tile: lane = channel 16*cb + lane%16, rows = heads 4*(lane/16)+i
+  float m;        // running max of this lane's head
+  float l;        // running sum
+  f4 o[D / 16];   // O: lane holds channel 16*cb + lane%16, heads 4*(lane/16) + i
 };
 
+// Query operands of one lane (head lane%16, lane group lane/16), kept in LDS as
+// [32-channel step s][3] x 16 bytes: the 16-bit query as stored (window keys),
+// then the fp16 hi and lo parts of the scaled query (INT8 keys).  Lanes of
+// padding heads point at a shared all-zero block.
 template <int D, bool BF16>
 struct QOps {
-  u4 qw[D / 32];       // 16-bit query as stored, for window keys
-  h8 qh[D / 32];       // fp16 hi part of the scaled INT8 query
-  h8 ql[D / 32];       // fp16 lo part
+  const u4* p;
+  __device__ u4 qw(int s) const { return p[3 * s]; }
+  __device__ h8 qh(int s) const { return __builtin_bit_cast(h8, p[3 * s + 1]); }
+  __device__ h8 ql(int s) const { return __builtin_bit_cast(h8, p[3 * s + 2]); }
+};
+template <int D>
+__host__ __device__ constexpr int qops_u4(int G) { return (4 * G + 1) * (D / 32) * 3; }
+
+struct Item {
+  bool i8;        // INT8 block (64 tokens) or window half-tile (32 tokens)
+  int blk;        // INT8 block index, or window item index j (tokens 32j .. 32j+31)
+  int n_valid;    // valid tokens in the item
+  int tok0;       // unit token index of the first slot (scores in LDS)
+  int mass0;      // mass-row index of the first slot
 };
 
-// S^T of one 64-token block: acc[r][i] = score of token 16r + 4*(lane/16) + i
-// for head lane%16 (before scaling).
+__device__ inline Item item_of(int it, int nb8, int n8, int nw, int cap8) {
+  Item I;
+  if (it < nb8) {
+    I.i8 = true;
+    I.blk = it;
+    I.n_valid = min(kTile, n8 - it * kTile);
+    I.tok0 = it * kTile;
+    I.mass0 = it * kTile;
+  } else {
+    const int j = it - nb8;
+    I.i8 = false;
+    I.blk = j;
+    I.n_valid = min(32, nw - 32 * j);
+    I.tok0 = n8 + 32 * j;
+    I.mass0 = cap8 + 32 * j;
+  }
+  return I;
+}
+
+template <int D>
+__device__ inline void load_k(const Item& I, const int8_t* k8, const uint16_t* k16, Raw<D>& R) {
+  const int lane = threadIdx.x & 63;
+  if (I.i8) {
+    const int8_t* base = k8 + (size_t)I.blk * kTile * D;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int hh = 0; hh < D / 64; ++hh)
+        R.k[r * (D / 64) + hh] = ld16(base + ((r * (D / 64) + hh) * 64 + lane) * 16);
+  } else {
+    const uint16_t* base = k16 + (size_t)I.blk * 32 * D;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s)
+        R.k[r * (D / 32) + s] = ld16(base + ((r * (D / 32) + s) * 64 + lane) * 8);
+  }
+}
+
+template <int D>
+__device__ inline void load_v(const Item& I, const int8_t* v8, const uint16_t* v16, Raw<D>& R) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, col = lane & 15;
+  if (I.i8) {
+    const int8_t* base = v8 + (size_t)I.blk * kTile * D;
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb) R.v[cb] = ld16(base + (16 * cb + col) * kTile + 16 * g);
+  } else {
+    const uint16_t* base = v16 + (size_t)I.blk * 32 * D;
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb) R.v[cb] = ld16(base + (16 * cb + col) * 32 + 8 * g);
+  }
+}
+
+// Raw S^T: acc[r][i] is the score of item token 16r + 4*(lane/16) + i for head lane%16.
 template <int D, bool BF16>
-__device__ inline void block_scores_i8(const int8_t* k8blk, const QOps<D, BF16>& q, f4 acc[4]) {
-  const int lane = threadIdx.x & 63, g = lane >> 4, row = lane & 15;
-  u4 raw[4][D / 64];
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int hh = 0; hh < D / 64; ++hh) raw[r][hh] = ld16(k8blk + (16 * r + row) * D + 64 * hh + 16 * g);
+__device__ inline void scores_i8(const Raw<D>& R, const QOps<D, BF16>& q, f4 acc[4]) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     f4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int hh = 0; hh < D / 64; ++hh) {
       h8 k0, k1;
-      codes_to_f16(raw[r][hh], k0, k1);
-      a = mma_f16(k0, q.qh[2 * hh], a);
-      a = mma_f16(k0, q.ql[2 * hh], a);
-      a = mma_f16(k1, q.qh[2 * hh + 1], a);
-      a = mma_f16(k1, q.ql[2 * hh + 1], a);
+      codes_to_f16(R.k[r * (D / 64) + hh], k0, k1);
+      a = mma_f16(k0, q.qh(2 * hh), a);
+      a = mma_f16(k0, q.ql(2 * hh), a);
+      a = mma_f16(k1, q.qh(2 * hh + 1), a);
+      a = mma_f16(k1, q.ql(2 * hh + 1), a);
     }
     acc[r] = a;
+    // keep one row block's converted codes live at a time
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 template <int D, bool BF16>
-__device__ inline void block_scores_16(const uint16_t* k16blk, const QOps<D, BF16>& q, f4 acc[4]) {
-  const int lane = threadIdx.x & 63, g = lane >> 4, row = lane & 15;
-  u4 raw[4][D / 32];
+__device__ inline void scores_16(const Raw<D>& R, const QOps<D, BF16>& q, f4 acc[2]) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s) raw[r][s] = ld16(k16blk + (16 * r + row) * D + 32 * s + 8 * g);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
+  for (int r = 0; r < 2; ++r) {
     f4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
       if constexpr (BF16)
-        a = mma_bf16(__builtin_bit_cast(bf8, raw[r][s]), __builtin_bit_cast(bf8, q.qw[s]), a);
+        a = mma_bf16(__builtin_bit_cast(bf8, R.k[r * (D / 32) + s]), __builtin_bit_cast(bf8, q.qw(s)),
+                     a);
       else
-        a = mma_f16(__builtin_bit_cast(h8, raw[r][s]), __builtin_bit_cast(h8, q.qw[s]), a);
+        a = mma_f16(__builtin_bit_cast(h8, R.k[r * (D / 32) + s]), __builtin_bit_cast(h8, q.qw(s)), a);
     }
     acc[r] = a;
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// O += P . V for one 64-token block.  p[r][i]: probability of token
-// 16r + 4g + i for head lane%16 (already 0 for masked tokens and padding heads).
+// O += P . V.  p[r][i]: probability of item token 16r + 4g + i for head lane%16.
 template <int D>
-__device__ inline void block_pv_i8(const int8_t* v8blk, const float p[4][4], f4* o) {
-  const int lane = threadIdx.x & 63, g = lane >> 4, col = lane & 15;
+__device__ inline void pv_i8(const Raw<D>& R, const float p[4][4], f4* o) {
   h8 pa[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u)
@@ -199,50 +219,38 @@ __device__ inline void block_pv_i8(const int8_t* v8blk, const float p[4][4], f4*
     for (int e = 0; e < 8; ++e) pa[u][e] = (_Float16)p[2 * u + (e >> 2)][e & 3];
 #pragma unroll
   for (int cb = 0; cb < D / 16; ++cb) {
-    const u4 raw = ld16(v8blk + (16 * cb + col) * kTile + 16 * g);
     h8 v0, v1;
-    codes_to_f16(raw, v0, v1);
+    codes_to_f16(R.v[cb], v0, v1);
     o[cb] = mma_f16(pa[0], v0, o[cb]);
     o[cb] = mma_f16(pa[1], v1, o[cb]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 template <int D, bool BF16>
-__device__ inline void block_pv_16(const uint16_t* v16blk, const float p[4][4], f4* o) {
-  const int lane = threadIdx.x & 63, g = lane >> 4, col = lane & 15;
+__device__ inline void pv_16(const Raw<D>& R, const float p[2][4], f4* o) {
   if constexpr (BF16) {
-    bf8 ph[2], pl[2];
+    bf8 ph, pl;
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = p[2 * u + (e >> 2)][e & 3];
-        const __bf16 hi = (__bf16)x;
-        ph[u][e] = hi;
-        pl[u][e] = (__bf16)(x - (float)hi);
-      }
+    for (int e = 0; e < 8; ++e) {
+      const float x = p[e >> 2][e & 3];
+      const __bf16 hi = (__bf16)x;
+      ph[e] = hi;
+      pl[e] = (__bf16)(x - (float)hi);
+    }
 #pragma unroll
     for (int cb = 0; cb < D / 16; ++cb) {
-      const uint16_t* rowp = v16blk + (16 * cb + col) * kTile + 16 * g;
-      const bf8 v0 = __builtin_bit_cast(bf8, ld16(rowp));
-      const bf8 v1 = __builtin_bit_cast(bf8, ld16(rowp + 8));
-      o[cb] = mma_bf16(ph[0], v0, o[cb]);
-      o[cb] = mma_bf16(pl[0], v0, o[cb]);
-      o[cb] = mma_bf16(ph[1], v1, o[cb]);
-      o[cb] = mma_bf16(pl[1], v1, o[cb]);
+      const bf8 v = __builtin_bit_cast(bf8, R.v[cb]);
+      o[cb] = mma_bf16(ph, v, o[cb]);
+      o[cb] = mma_bf16(pl, v, o[cb]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   } else {
-    h8 pa[2];
+    h8 pa;
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int e = 0; e < 8; ++e) pa[e] = (_Float16)p[e >> 2][e & 3];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pa[u][e] = (_Float16)p[2 * u + (e >> 2)][e & 3];
-#pragma unroll
-    for (int cb = 0; cb < D / 16; ++cb) {
-      const uint16_t* rowp = v16blk + (16 * cb + col) * kTile + 16 * g;
-      o[cb] = mma_f16(pa[0], __builtin_bit_cast(h8, ld16(rowp)), o[cb]);
-      o[cb] = mma_f16(pa[1], __builtin_bit_cast(h8, ld16(rowp + 8)), o[cb]);
-    }
+    for (int cb = 0; cb < D / 16; ++cb) o[cb] = mma_f16(pa, __builtin_bit_cast(h8, R.v[cb]), o[cb]);
   }
 }
 
@@ -262,59 +270,50 @@ __device__ inline float group_sum(float x) {
   x += __shfl_xor(x, 4);
   return x + __shfl_xor(x, 8);
 }
+__device__ inline float wave_sum(float x) {
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+__device__ inline float wave_max(float x) {
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
 
-struct BlockCtx {
-  int n_valid;     // valid tokens in this block (1..64)
-  int tok0;        // unit-level token index of the block's first slot
-  int mass_idx0;   // massp index of the block's first slot
-  float scale;     // score scale of this lane's head
-  int head_ok;     // lane's head < g
-};
-
-// One 64-token block in the given mode.  sc: LDS scores [h][stride] (MODE_ONLINE);
-// lse: this lane's head log-sum-exp (MODE_FINAL).
-template <int D, bool BF16, bool INT8, int MODE>
-__device__ inline void do_block(const void* kblk, const void* vblk, const QOps<D, BF16>& q,
-                                const BlockCtx& bc, WaveAcc<D>& wa, float* sc, int stride,
-                                float lse, float* massp) {
+// Softmax bookkeeping of one item with R row blocks (R = 4 INT8, 2 window).
+// MODE_ONLINE: update the running (max, sum), store the scores, rescale O, fill p.
+// MODE_LSE:    update the running (max, sum) only.
+// MODE_FINAL:  p = exp(score - lse); write the group mass of each token.
+template <int R, int MODE, int D>
+__device__ inline void softmax_item(const f4* acc, float scale, bool head_ok, const Item& I,
+                                    WaveAcc<D>& wa, float* sc, int stride, float lse, float* massp,
+                                    float p[R][4]) {
   const int lane = threadIdx.x & 63, g = lane >> 4, h = lane & 15;
-  f4 acc[4];
-  if constexpr (INT8)
-    block_scores_i8<D, BF16>((const int8_t*)kblk, q, acc);
-  else
-    block_scores_16<D, BF16>((const uint16_t*)kblk, q, acc);
-  float sig[4][4];
+  float sig[R][4];
   float mloc = -INFINITY;
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tk = 16 * r + 4 * g + i;
-      const bool ok = bc.head_ok && tk < bc.n_valid;
-      sig[r][i] = ok ? acc[r][i] * bc.scale : -INFINITY;
+      sig[r][i] = (head_ok && tk < I.n_valid) ? acc[r][i] * scale : -INFINITY;
       mloc = fmaxf(mloc, sig[r][i]);
     }
-  float p[4][4];
   if constexpr (MODE == MODE_FINAL) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p[r][i] = sig[r][i] > -INFINITY ? __expf(sig[r][i] - lse) : 0.f;
-    // token mass of this KV head's query group: sum over the 16 lanes of the group
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        p[r][i] = sig[r][i] > -INFINITY ? __expf(sig[r][i] - lse) : 0.f;
         const float s = group_sum(p[r][i]);
         const int tk = 16 * r + 4 * g + i;
-        if (h == 0 && tk < bc.n_valid) massp[bc.mass_idx0 + tk] = s;
+        if (h == 0 && tk < I.n_valid) massp[I.mass0 + tk] = s;
       }
   } else {
     const float mnew = fmaxf(wa.m, head_max(mloc));
     const float corr = wa.m > -INFINITY ? __expf(wa.m - mnew) : 0.f;
     float lsum = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         p[r][i] = sig[r][i] > -INFINITY ? __expf(sig[r][i] - mnew) : 0.f;
@@ -322,60 +321,122 @@ __device__ inline void do_block(const void* kblk, const void* vblk, const QOps<D
       }
     wa.l = wa.l * corr + head_sum(lsum);
     wa.m = mnew;
-    if constexpr (MODE == MODE_LSE) return;
-    // keep the raw scores for the mass pass
-    if (bc.head_ok) {
+    if constexpr (MODE == MODE_ONLINE) {
+      if (head_ok) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+        for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tk = 16 * r + 4 * g + i;
-          if (tk < bc.n_valid) sc[h * stride + bc.tok0 + tk] = sig[r][i];
-        }
+          for (int i = 0; i < 4; ++i) {
+            const int tk = 16 * r + 4 * g + i;
+            if (tk < I.n_valid) sc[h * stride + I.tok0 + tk] = sig[r][i];
+          }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ci = __shfl(corr, 4 * g + i);
+#pragma unroll
+        for (int cb = 0; cb < D / 16; ++cb) wa.o[cb][i] *= ci;
+      }
     }
-    // rescale O rows (heads 4g+i) by their head's correction
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float ci = __shfl(corr, 4 * g + i);
-#pragma unroll
-      for (int cb = 0; cb < D / 16; ++cb) wa.o[cb][i] *= ci;
-    }
-  }
-  if constexpr (INT8)
-    block_pv_i8<D>((const int8_t*)vblk, p, wa.o);
-  else
-    block_pv_16<D, BF16>((const uint16_t*)vblk, p, wa.o);
-}
-
-// Appends this step's key/value to window slot `slot` of the unit (data only).
-__device__ inline void append_row_m(int D, uint16_t* k16, uint16_t* v16, int slot,
-                                    const uint16_t* knew, const uint16_t* vnew) {
-  for (int ch = threadIdx.x; ch < D; ch += blockDim.x) {
-    k16[(size_t)slot * D + ch] = knew[ch];
-    v16[vtile_off(slot, ch, D)] = vnew[ch];
   }
 }
 
+template <int D, bool BF16, int MODE>
+__device__ inline void compute_item(const Item& I, const Raw<D>& Rw, const QOps<D, BF16>& q,
+                                    float scale8, float scale16, bool head_ok, WaveAcc<D>& wa,
+                                    float* sc, int stride, float lse, float* massp) {
+  // Re-read the query operands from LDS for every item instead of letting the
+  // compiler hoist 48 registers' worth of them out of the item loop.
+  QOps<D, BF16> ql = q;
+  __asm__ volatile("" : "+v"(ql.p));
+  if (I.i8) {
+    f4 acc[4];
+    scores_i8<D, BF16>(Rw, ql, acc);
+    float p[4][4];
+    softmax_item<4, MODE, D>(acc, scale8, head_ok, I, wa, sc, stride, lse, massp, p);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (MODE != MODE_LSE) pv_i8<D>(Rw, p, wa.o);
+  } else {
+    f4 acc[2];
+    scores_16<D, BF16>(Rw, ql, acc);
+    float p[2][4];
+    softmax_item<2, MODE, D>(acc, scale16, head_ok, I, wa, sc, stride, lse, massp, p);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (MODE != MODE_LSE) pv_16<D, BF16>(Rw, p, wa.o);
+  }
+}
 
-// value scale of the INT8 part: lane's O channels are 16*cb + lane%16
+// value scale of the INT8 part: the lane's O channels are 16*cb + lane%16
 template <int D>
 __device__ inline void apply_vscale(WaveAcc<D>& wa, const float* sv) {
   const int hl = threadIdx.x & 15;
 #pragma unroll
-  for (int cb = 0; cb < D / 16; ++cb) {
-    const float s = sv[16 * cb + hl];
-    wa.o[cb] *= s;
+  for (int cb = 0; cb < D / 16; ++cb) wa.o[cb] *= sv[16 * cb + hl];
+}
+
+// One pass of a wavefront over its items (it = wave, wave + 4, ...), software
+// pipelined: the values of item i and the keys of item i+4 load while item i's
+// scores are formed.  If `preloaded`, `cur` already holds (or is receiving) the
+// keys of item `wave`.
+template <int D, bool BF16, int MODE>
+__device__ inline void wave_pass(int nitems, int nb8, int n8, int nw, int cap8, const int8_t* k8,
+                                 const int8_t* v8, const uint16_t* k16, const uint16_t* v16,
+                                 const QOps<D, BF16>& q, float scale8, float scale16, bool head_ok,
+                                 WaveAcc<D>& wa, bool& vscaled, const float* sv, float* sc,
+                                 int stride, float lse, float* massp, Raw<D>& cur, bool preloaded) {
+  const int wave = threadIdx.x >> 6;
+  int it = wave;
+  if (it >= nitems) return;
+  Item I = item_of(it, nb8, n8, nw, cap8);
+  if (!preloaded) load_k<D>(I, k8, k16, cur);
+  for (;;) {
+    if constexpr (MODE != MODE_LSE) load_v<D>(I, v8, v16, cur);
+    const int nt = it + kWaves;
+    Raw<D> nxt;
+    Item J = I;
+    const bool more = nt < nitems;
+    if (more) {
+      J = item_of(nt, nb8, n8, nw, cap8);
+      load_k<D>(J, k8, k16, nxt);
+    }
+    if constexpr (MODE != MODE_LSE) {
+      if (!I.i8 && !vscaled) {
+        apply_vscale<D>(wa, sv);
+        vscaled = true;
+      }
+    }
+    compute_item<D, BF16, MODE>(I, cur, q, scale8, scale16, head_ok, wa, sc, stride, lse, massp);
+    if (!more) break;
+#pragma unroll
+    for (int x = 0; x < D / 16; ++x) cur.k[x] = nxt.k[x];
+    I = J;
+    it = nt;
   }
 }
 
+// Appends this step's key/value to window slot `slot` of the unit (data only).
+__device__ inline void append_row(int D, uint16_t* k16, uint16_t* v16, int slot,
+                                  const uint16_t* knew, const uint16_t* vnew) {
+  for (int ch = threadIdx.x; ch < D; ch += blockDim.x) {
+    k16[k16_off(slot, ch, D)] = knew[ch];
+    v16[v16_off(slot, ch, D)] = vnew[ch];
+  }
+}
+
+// One workgroup per unit.  The unit of KV head 0 also records the (layer,
+// sequence)'s sizes before this step in `snap` [L][B][3] = (n8, n16, t) for the
+// EMA kernel, which must not read the counters it advances.
 template <int D, bool BF16>
-__global__ __launch_bounds__(kMfmaThreads, 2) void attn_mfma_kernel(
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     conf_cache c, Dims dm, int layer0, const uint16_t* __restrict__ q_all,
     const uint16_t* __restrict__ knew_all, const uint16_t* __restrict__ vnew_all,
-    float* __restrict__ out_all, float* __restrict__ massp_all, int score_cap) {
-  // Dynamic LDS: first the fp32 query staging [G][D], then (after the operands
-  // are in registers) the scores [G][score_cap + 1], then the O merge buffer.
-  extern __shared__ float smem[];
+    float* __restrict__ out_all, float* __restrict__ massp_all, int32_t* __restrict__ snap,
+    int score_cap) {
+  // Dynamic LDS: the query operands, then one region reused as query staging
+  // [G + 1][D], scores [G][stride] and the O merge buffer [4][G][D].
+  extern __shared__ float dyn_lds[];
+  u4* s_qops = (u4*)dyn_lds;
+  float* smem = dyn_lds + 4 * qops_u4<D>(dm.G);
   __shared__ float s_qscale[kMaxGroup];    // power-of-two scale of the INT8 query
   __shared__ float s_snew[kMaxGroup];      // score of this step's token
   __shared__ float s_m[kWaves][kMaxGroup], s_l[kWaves][kMaxGroup];
@@ -392,6 +453,10 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void attn_mfma_kernel(
   const int n8 = c.n8[lb], nw = c.n16[lb], t = c.t[lb];
   const int appended = nw < dm.cap16;
   const int n = n8 + nw + appended;
+  const int nb8 = (n8 + kTile - 1) / kTile;
+  const int nitems = nb8 + (nw + 31) / 32;
+  const int stride = score_cap | 1;
+  const bool in_lds = n <= score_cap;
   const int8_t* k8 = c.k8 + u * (size_t)dm.cap8 * D;
   const int8_t* v8 = c.v8 + u * (size_t)dm.cap8 * D;
   uint16_t* k16 = (uint16_t*)c.k16 + u * (size_t)dm.cap16 * D;
@@ -399,116 +464,108 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void attn_mfma_kernel(
   const uint16_t* knew = knew_all + (size_t)unit_local * D;
   const uint16_t* vnew = vnew_all + (size_t)unit_local * D;
   const uint16_t* qsrc = q_all + ((size_t)lbl * dm.Hq + (size_t)hk * G) * D;
-  float* mp_lb = massp_all + (size_t)lb * dm.Hkv * dm.capt;
-  float* massp = mp_lb + (size_t)hk * dm.capt;
+  float* massp = massp_all + u * dm.capt;
   const float rs = 1.0f / sqrtf((float)D);
+  const bool head_ok = hl < G;
 
+  // the keys of this wavefront's first item start loading now, under the set-up
+  Raw<D> cur;
+  if (wave < nitems) load_k<D>(item_of(wave, nb8, n8, nw, dm.cap8), k8, k16, cur);
+
+  if (hk == 0 && tid == 0) {
+    snap[3 * lb] = n8;
+    snap[3 * lb + 1] = nw;
+    snap[3 * lb + 2] = t;
+  }
   if (appended)
-    append_row_m(D, k16, v16, nw, knew, vnew);
+    append_row(D, k16, v16, nw, knew, vnew);
   else if (tid == 0 && hk == 0)
     atomicOr(c.status, (int)CONF_ST_WINDOW_FULL);
 
-  // ---- query set-up
-  float* s_q = smem;
-  for (int i = tid; i < G * D; i += kMfmaThreads) s_q[i] = h16_to_f32(qsrc[i], dm.bf16);
-  for (int ch = tid; ch < D; ch += kMfmaThreads) s_sv[ch] = c.v_amax[u * D + ch] / 127.0f;
+  // ---- query set-up: one round of global loads, then wavefront reductions
+  float* s_q = smem;           // [G][D] query as fp32
+  float* s_ka = smem + G * D;  // [D] key scale amax_K / 127
+  for (int i = tid; i < G * D; i += kAttnThreads) s_q[i] = h16_to_f32(qsrc[i], dm.bf16);
+  for (int ch = tid; ch < D; ch += kAttnThreads) {
+    s_ka[ch] = c.k_amax[u * D + ch] / 127.0f;
+    s_sv[ch] = c.v_amax[u * D + ch] / 127.0f;
+  }
+  float kn[D / 64];
+#pragma unroll
+  for (int y = 0; y < D / 64; ++y) kn[y] = h16_to_f32(knew[lane + 64 * y], dm.bf16);
   __syncthreads();
-  if (tid < G) {
-    float s = 0.f;
-    for (int ch = 0; ch < D; ++ch) s = fmaf(s_q[tid * D + ch], h16_to_f32(knew[ch], dm.bf16), s);
-    s_snew[tid] = s * rs;
+  // per head: the new token's score and the power-of-two scale of q * amax_K / 127
+  for (int h = wave; h < G; h += kWaves) {
+    float s = 0.f, mx = 0.f;
+#pragma unroll
+    for (int y = 0; y < D / 64; ++y) {
+      const float qv = s_q[h * D + lane + 64 * y];
+      s = fmaf(qv, kn[y], s);
+      mx = fmaxf(mx, fabsf(qv * s_ka[lane + 64 * y]));
+    }
+    s = wave_sum(s);
+    mx = wave_max(mx);
+    if (lane == 0) {
+      s_snew[h] = s * rs;
+      s_qscale[h] = mx > 0.f ? ldexpf(1.0f, 14 - ilogbf(mx)) : 1.0f;
+    }
   }
   __syncthreads();
-  for (int i = tid; i < G * D; i += kMfmaThreads) s_q[i] *= c.k_amax[u * D + i % D] / 127.0f;
-  __syncthreads();
-  if (tid < G) {
-    float mx = 0.f;
-    for (int ch = 0; ch < D; ++ch) mx = fmaxf(mx, fabsf(s_q[tid * D + ch]));
-    s_qscale[tid] = mx > 0.f ? ldexpf(1.0f, 14 - ilogbf(mx)) : 1.0f;
-  }
-  __syncthreads();
-  const int head_ok = hl < G;
-  QOps<D, BF16> q;
-  {
+  if (wave == 0) {
+    // one wavefront writes every lane's operands (the other three read the same)
+    u4* dst = head_ok ? s_qops + (hl * 4 + g) * (D / 32) * 3 : s_qops + 4 * G * (D / 32) * 3;
     const float al = head_ok ? s_qscale[hl] : 1.0f;
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
-      q.qw[s] = head_ok ? ld16(qsrc + (size_t)hl * D + 32 * s + 8 * g) : (u4){0u, 0u, 0u, 0u};
+      // 16-bit query for window keys: the fp32 staging value converts back exactly
+      uint16_t w16[8];
+      h8 hi8, lo8;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
+        const float xq = head_ok ? s_q[hl * D + 32 * s + 8 * g + e] : 0.f;
+        if constexpr (BF16)
+          w16[e] = (uint16_t)(__float_as_uint(xq) >> 16);
+        else
+          w16[e] = __builtin_bit_cast(uint16_t, (_Float16)xq);
+        // channel order of the INT8 key loads: 64*(s/2) + 16*g + 8*(s%2) + e
         const int ch = 64 * (s >> 1) + 16 * g + 8 * (s & 1) + e;
-        const float x = head_ok ? s_q[hl * D + ch] * al : 0.f;
-        const _Float16 hi = (_Float16)x;
-        q.qh[s][e] = hi;
-        q.ql[s][e] = (_Float16)(x - (float)hi);
+        const float x8 = head_ok ? (s_q[hl * D + ch] * s_ka[ch]) * al : 0.f;
+        const _Float16 hi = (_Float16)x8;
+        hi8[e] = hi;
+        lo8[e] = (_Float16)(x8 - (float)hi);
+      }
+      if (head_ok || g == 0) {
+        dst[3 * s] = (u4){w16[0] | ((uint32_t)w16[1] << 16), w16[2] | ((uint32_t)w16[3] << 16),
+                          w16[4] | ((uint32_t)w16[5] << 16), w16[6] | ((uint32_t)w16[7] << 16)};
+        dst[3 * s + 1] = __builtin_bit_cast(u4, hi8);
+        dst[3 * s + 2] = __builtin_bit_cast(u4, lo8);
       }
     }
   }
+  const QOps<D, BF16> q{head_ok ? s_qops + (hl * 4 + g) * (D / 32) * 3
+                                : s_qops + 4 * G * (D / 32) * 3};
   const float scale8 = head_ok ? rs / s_qscale[hl] : 0.f;
   const float scale16 = head_ok ? rs : 0.f;
   __syncthreads();  // the staging area becomes the score store
 
-  const int nb8 = (n8 + kTile - 1) / kTile, nbw = (nw + kTile - 1) / kTile;
-  const int nblk = nb8 + nbw;
-  const int stride = score_cap + 1;
-  const bool in_lds = n <= score_cap;
   WaveAcc<D> wa;
   wa.m = -INFINITY;
   wa.l = 0.f;
 #pragma unroll
   for (int cb = 0; cb < D / 16; ++cb) wa.o[cb] = (f4){0.f, 0.f, 0.f, 0.f};
-
-  auto ctx = [&](int bi, BlockCtx& bc) {
-    if (bi < nb8) {
-      bc.n_valid = min(kTile, n8 - bi * kTile);
-      bc.tok0 = bi * kTile;
-      bc.mass_idx0 = bi * kTile;
-      bc.scale = scale8;
-    } else {
-      const int wb = bi - nb8;
-      bc.n_valid = min(kTile, nw - wb * kTile);
-      bc.tok0 = n8 + wb * kTile;
-      bc.mass_idx0 = dm.cap8 + wb * kTile;
-      bc.scale = scale16;
-    }
-    bc.head_ok = head_ok;
-  };
-  // Each wavefront meets its INT8 blocks before its window blocks; the value
-  // scale of the INT8 codes is applied to the accumulator once, in between.
   bool vscaled = false;
 
   if (in_lds) {
-    float* sc = smem;
-    for (int bi = wave; bi < nblk; bi += kWaves) {
-      BlockCtx bc;
-      ctx(bi, bc);
-      if (bi < nb8) {
-        do_block<D, BF16, true, MODE_ONLINE>(k8 + (size_t)bi * kTile * D, v8 + (size_t)bi * kTile * D,
-                                              q, bc, wa, sc, stride, 0.f, nullptr);
-      } else {
-        if (!vscaled) {
-          apply_vscale<D>(wa, s_sv);
-          vscaled = true;
-        }
-        do_block<D, BF16, false, MODE_ONLINE>(k16 + (size_t)(bi - nb8) * kTile * D,
-                                               v16 + (size_t)(bi - nb8) * kTile * D, q, bc, wa, sc,
-                                               stride, 0.f, nullptr);
-      }
-    }
-    if (appended && tid < G) sc[tid * stride + n - 1] = s_snew[tid];
+    wave_pass<D, BF16, MODE_ONLINE>(nitems, nb8, n8, nw, dm.cap8, k8, v8, k16, v16, q, scale8,
+                                     scale16, head_ok, wa, vscaled, s_sv, smem, stride, 0.f, nullptr,
+                                     cur, true);
+    if (appended && tid < G) smem[tid * stride + n - 1] = s_snew[tid];
   } else {
-    for (int bi = wave; bi < nblk; bi += kWaves) {
-      BlockCtx bc;
-      ctx(bi, bc);
-      if (bi < nb8)
-        do_block<D, BF16, true, MODE_LSE>(k8 + (size_t)bi * kTile * D, nullptr, q, bc, wa, nullptr,
-                                           0, 0.f, nullptr);
-      else
-        do_block<D, BF16, false, MODE_LSE>(k16 + (size_t)(bi - nb8) * kTile * D, nullptr, q, bc, wa,
-                                            nullptr, 0, 0.f, nullptr);
-    }
+    wave_pass<D, BF16, MODE_LSE>(nitems, nb8, n8, nw, dm.cap8, k8, v8, k16, v16, q, scale8,
+                                  scale16, head_ok, wa, vscaled, s_sv, nullptr, 0, 0.f, nullptr,
+                                  cur, true);
   }
-  // ---- merge the running (max, sum) of the waves and add this step's token
+  // ---- merge the waves' running (max, sum) and add this step's token
   if (lane < 16) {
     s_m[wave][lane] = wa.m;
     s_l[wave][lane] = wa.l;
@@ -525,7 +582,6 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void attn_mfma_kernel(
     const float lse = M + logf(S);
     s_lse[tid] = lse;
     s_pnew[tid] = appended ? expf(s_snew[tid] - lse) : 0.f;
-    // weight of each wave's O in the final, normalised sum
     for (int w = 0; w < kWaves; ++w)
       s_f[w][tid] = s_m[w][tid] > -INFINITY ? expf(s_m[w][tid] - lse) : 0.f;
   }
@@ -533,32 +589,18 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void attn_mfma_kernel(
 
   if (in_lds) {
     // per-token mass of this query group from the stored scores
-    const float* sc = smem;
-    for (int j = tid; j < n; j += kMfmaThreads) {
+    for (int j = tid; j < n; j += kAttnThreads) {
       float s = 0.f;
-      for (int h = 0; h < G; ++h) s += __expf(sc[h * stride + j] - s_lse[h]);
+      for (int h = 0; h < G; ++h) s += __expf(smem[h * stride + j] - s_lse[h]);
       massp[j < n8 ? j : dm.cap8 + (j - n8)] = s;
     }
     __syncthreads();
   } else {
     // second pass: probabilities with the final normaliser, mass and values
     const float lse = head_ok ? s_lse[hl] : 0.f;
-    for (int bi = wave; bi < nblk; bi += kWaves) {
-      BlockCtx bc;
-      ctx(bi, bc);
-      if (bi < nb8) {
-        do_block<D, BF16, true, MODE_FINAL>(k8 + (size_t)bi * kTile * D, v8 + (size_t)bi * kTile * D,
-                                             q, bc, wa, nullptr, 0, lse, massp);
-      } else {
-        if (!vscaled) {
-          apply_vscale<D>(wa, s_sv);
-          vscaled = true;
-        }
-        do_block<D, BF16, false, MODE_FINAL>(k16 + (size_t)(bi - nb8) * kTile * D,
-                                              v16 + (size_t)(bi - nb8) * kTile * D, q, bc, wa,
-                                              nullptr, 0, lse, massp);
-      }
-    }
+    wave_pass<D, BF16, MODE_FINAL>(nitems, nb8, n8, nw, dm.cap8, k8, v8, k16, v16, q, scale8,
+                                    scale16, head_ok, wa, vscaled, s_sv, nullptr, 0, lse, massp,
+                                    cur, false);
     if (appended && tid == 0) {
       float s = 0.f;
       for (int h = 0; h < G; ++h) s += s_pnew[h];
@@ -580,49 +622,107 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void attn_mfma_kernel(
   }
   __syncthreads();
   float* out = out_all + ((size_t)lbl * dm.Hq + (size_t)hk * G) * D;
-  for (int i = tid; i < G * D; i += kMfmaThreads) {
+  for (int i = tid; i < G * D; i += kAttnThreads) {
     const int hh = i / D, ch = i % D;
     float s = 0.f;
     for (int w = 0; w < kWaves; ++w) s += ob[(w * G + hh) * D + ch];
     out[i] = fmaf(s_pnew[hh], h16_to_f32(vnew[ch], dm.bf16), s);
   }
-  if (arrive_last(c, dm, lb)) ema_update_lb(c, dm, lb, n8, nw, appended, t, mp_lb);
+}
+
+// EMA of every token once all KV heads' mass rows exist (kernel boundary).
+// mass_j = (sum of the KV heads' rows, in index order) / Hq;
+// e <- decay*e + (1-decay)*mass; the appended token starts from e = 0 and takes
+// position t+1.  Each (layer, sequence) is spread over gridDim.y workgroups that
+// read the sizes from the attention kernel's snapshot; workgroup y = 0 then
+// advances n16 and t.
+constexpr int kEmaThreads = 256;
+
+__global__ __launch_bounds__(kEmaThreads) void ema_kernel(conf_cache c, Dims dm, int layer0,
+                                                          const float* __restrict__ massp_all,
+                                                          const int32_t* __restrict__ snap) {
+#pragma clang fp contract(off)
+  const int lb = layer0 * dm.B + blockIdx.x;
+  const int n8 = snap[3 * lb], nw = snap[3 * lb + 1], t = snap[3 * lb + 2];
+  const int appended = nw < dm.cap16;
+  const float* rows = massp_all + (size_t)lb * dm.Hkv * dm.capt;
+  const float hq = (float)dm.Hq;
+  for (int j = blockIdx.y * kEmaThreads + threadIdx.x; j < n8 + nw + appended;
+       j += gridDim.y * kEmaThreads) {
+    const int idx = j < n8 ? j : dm.cap8 + (j - n8);
+    float a = 0.f;
+    for (int hk = 0; hk < dm.Hkv; ++hk) a += rows[(size_t)hk * dm.capt + idx];
+    a = a / hq;
+    if (j < n8) {
+      float* e = c.ema8 + (size_t)lb * dm.cap8 + j;
+      *e = dm.decay * (*e) + dm.one_minus_decay * a;
+    } else {
+      const int w = j - n8;
+      float* e = c.ema16 + (size_t)lb * dm.cap16 + w;
+      if (w == nw) {
+        *e = dm.one_minus_decay * a;  // decay * 0 + (1 - decay) * mass
+        c.pos16[(size_t)lb * dm.cap16 + w] = t + 1;
+      } else {
+        *e = dm.decay * (*e) + dm.one_minus_decay * a;
+      }
+    }
+  }
+  if (blockIdx.y == 0 && threadIdx.x == 0) {
+    c.n16[lb] = nw + appended;
+    c.t[lb] = t + 1;
+  }
+}
+
+// Scores one workgroup keeps in LDS (G rows of stride cap | 1, odd so that the
+// 16 heads of a store spread over banks), next to the query operands.
+static int qops_bytes(const Dims& dm) {
+  return 16 * (dm.D == 64 ? qops_u4<64>(dm.G) : qops_u4<128>(dm.G));
 }
 
 int attn_score_cap(const Dims& dm) {
-  const int cap = kLdsScoreBytes / (4 * dm.G) - 1;
-  return cap < dm.capt + 1 ? cap : dm.capt + 1;
+  int cap = (kLdsDynBytes - qops_bytes(dm)) / (4 * dm.G) - 1;
+  cap &= ~1;
+  return cap < dm.capt + 2 ? cap : dm.capt + 2;
 }
 
 size_t attn_dyn_lds(const Dims& dm) {
-  const size_t sc = (size_t)dm.G * (attn_score_cap(dm) + 1) * 4;
-  const size_t ob = (size_t)kWaves * dm.G * dm.D * 4;
-  return sc > ob ? sc : ob;
+  const size_t sc = (size_t)dm.G * (attn_score_cap(dm) | 1);
+  const size_t ob = (size_t)kWaves * dm.G * dm.D;  // also covers the [G + 1][D] staging
+  return (size_t)qops_bytes(dm) + 4 * (sc > ob ? sc : ob);
 }
 
 template <int D, bool BF16>
 static void launch_t(const Dims& dm, const conf_cache& c, int layer0, int nl, const void* q,
-                     const void* k_new, const void* v_new, float* out, float* massp, hipStream_t st) {
-  const size_t lds = attn_dyn_lds(dm);
+                     const void* k_new, const void* v_new, float* out, float* massp,
+                     int32_t* snap, hipStream_t st) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipFuncSetAttribute((const void*)attn_mfma_kernel<D, BF16>,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsScoreBytes);
+    (void)hipFuncSetAttribute((const void*)attn_kernel<D, BF16>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kLdsDynBytes);
     attr_set = true;
   }
-  hipLaunchKernelGGL((attn_mfma_kernel<D, BF16>), dim3(nl * dm.B * dm.Hkv), dim3(kMfmaThreads), lds,
-                     st, c, dm, layer0, (const uint16_t*)q, (const uint16_t*)k_new,
-                     (const uint16_t*)v_new, out, massp, attn_score_cap(dm));
+  hipLaunchKernelGGL((attn_kernel<D, BF16>), dim3(nl * dm.B * dm.Hkv), dim3(kAttnThreads),
+                     attn_dyn_lds(dm), st, c, dm, layer0, (const uint16_t*)q,
+                     (const uint16_t*)k_new, (const uint16_t*)v_new, out, massp, snap,
+                     attn_score_cap(dm));
+  // token chunks per (layer, sequence): enough for the largest budget plus the
+  // window growth of one phase; larger caches loop inside the workgroups
+  const int typical = (dm.n_low > dm.n_high ? dm.n_low : dm.n_high) + dm.W + 1;
+  const int cap = dm.capt < typical ? dm.capt : typical;
+  const int chunks = (cap + kEmaThreads - 1) / kEmaThreads;
+  hipLaunchKernelGGL(ema_kernel, dim3(nl * dm.B, chunks), dim3(kEmaThreads), 0, st, c, dm, layer0,
+                     massp, snap);
 }
 
 void launch_attn(const Dims& dm, const conf_cache& c, int layer0, int nl, const void* q,
-                 const void* k_new, const void* v_new, float* out, float* massp, hipStream_t st) {
+                 const void* k_new, const void* v_new, float* out, float* massp, int32_t* snap,
+                 hipStream_t st) {
   if (dm.D == 64) {
-    if (dm.bf16) launch_t<64, true>(dm, c, layer0, nl, q, k_new, v_new, out, massp, st);
-    else launch_t<64, false>(dm, c, layer0, nl, q, k_new, v_new, out, massp, st);
+    if (dm.bf16) launch_t<64, true>(dm, c, layer0, nl, q, k_new, v_new, out, massp, snap, st);
+    else launch_t<64, false>(dm, c, layer0, nl, q, k_new, v_new, out, massp, snap, st);
   } else {
-    if (dm.bf16) launch_t<128, true>(dm, c, layer0, nl, q, k_new, v_new, out, massp, st);
-    else launch_t<128, false>(dm, c, layer0, nl, q, k_new, v_new, out, massp, st);
+    if (dm.bf16) launch_t<128, true>(dm, c, layer0, nl, q, k_new, v_new, out, massp, snap, st);
+    else launch_t<128, false>(dm, c, layer0, nl, q, k_new, v_new, out, massp, snap, st);
   }
 }
 

@@ -21,7 +21,6 @@ __global__ void reset_kernel(conf_cache c, Dims dm) {
     c.n8[i] = 0;
     c.n16[i] = 0;
     c.t[i] = -1;
-    c.arrive[i] = 0;
   }
   if (i < namax) {
     c.k_amax[i] = 0.f;
@@ -84,16 +83,16 @@ __global__ __launch_bounds__(256) void ingest_kernel(conf_cache c, Dims dm, int 
   int8_t* v8 = c.v8 + u * (size_t)dm.cap8 * D;
   for (size_t i = threadIdx.x; i < (size_t)n8 * D; i += blockDim.x) {
     const int tok = (int)(i / D), cc = (int)(i % D);
-    k8[i] = quant_code(h16_to_f32(ksrc[i], dm.bf16), sk[cc]);
-    v8[vtile_off(tok, cc, D)] = quant_code(h16_to_f32(vsrc[i], dm.bf16), sv[cc]);
+    k8[k8_off(tok, cc, D)] = quant_code(h16_to_f32(ksrc[i], dm.bf16), sk[cc]);
+    v8[v8_off(tok, cc, D)] = quant_code(h16_to_f32(vsrc[i], dm.bf16), sv[cc]);
   }
   uint16_t* k16 = (uint16_t*)c.k16 + u * (size_t)dm.cap16 * D;
   uint16_t* v16 = (uint16_t*)c.v16 + u * (size_t)dm.cap16 * D;
   for (size_t i = threadIdx.x; i < (size_t)nw * D; i += blockDim.x) {
     const int w = (int)(i / D), cc = (int)(i % D);
     const size_t s = (size_t)(n8 + w) * D + cc;
-    k16[i] = ksrc[s];
-    v16[vtile_off(w, cc, D)] = vsrc[s];
+    k16[k16_off(w, cc, D)] = ksrc[s];
+    v16[v16_off(w, cc, D)] = vsrc[s];
   }
   if (hk == 0) {
     for (int i = threadIdx.x; i < n8; i += blockDim.x) {
@@ -279,8 +278,8 @@ __global__ __launch_bounds__(256) void move_kernel(conf_cache c, Dims dm, int la
   }
   if (dest >= 0) {
     for (int ch = threadIdx.x; ch < D; ch += blockDim.x) {
-      xk[ch] = h16_to_f32(k16[(size_t)jd * D + ch], dm.bf16);
-      xv[ch] = h16_to_f32(v16[vtile_off(jd, ch, D)], dm.bf16);
+      xk[ch] = h16_to_f32(k16[k16_off(jd, ch, D)], dm.bf16);
+      xv[ch] = h16_to_f32(v16[v16_off(jd, ch, D)], dm.bf16);
     }
   }
   __syncthreads();
@@ -288,15 +287,15 @@ __global__ __launch_bounds__(256) void move_kernel(conf_cache c, Dims dm, int la
   for (int i = threadIdx.x; i < nm8 * D; i += blockDim.x) {
     const int k = i / D, ch = i % D;
     const int src = mv8[2 * k], dst = mv8[2 * k + 1];
-    k8[(size_t)dst * D + ch] = k8[(size_t)src * D + ch];
-    v8[vtile_off(dst, ch, D)] = v8[vtile_off(src, ch, D)];
+    k8[k8_off(dst, ch, D)] = k8[k8_off(src, ch, D)];
+    v8[v8_off(dst, ch, D)] = v8[v8_off(src, ch, D)];
   }
   const int32_t* mv16 = mv16_all + (size_t)lb * dm.cap16;
   for (int i = threadIdx.x; i < nm16 * D; i += blockDim.x) {
     const int k = i / D, ch = i % D;
     const int src = mv16[2 * k], dst = mv16[2 * k + 1];
-    k16[(size_t)dst * D + ch] = k16[(size_t)src * D + ch];
-    v16[vtile_off(dst, ch, D)] = v16[vtile_off(src, ch, D)];
+    k16[k16_off(dst, ch, D)] = k16[k16_off(src, ch, D)];
+    v16[v16_off(dst, ch, D)] = v16[v16_off(src, ch, D)];
   }
   __syncthreads();
   if (dest < 0) return;
@@ -316,20 +315,20 @@ __global__ __launch_bounds__(256) void move_kernel(conf_cache c, Dims dm, int la
     if (gv) grown_v[atomicAdd(&n_grown_v, 1)] = ch;
     *ak = nk;
     *av = nv;
-    k8[(size_t)dest * D + ch] = quant_code(xk[ch], sk);
-    v8[vtile_off(dest, ch, D)] = quant_code(xv[ch], sv);
+    k8[k8_off(dest, ch, D)] = quant_code(xk[ch], sk);
+    v8[v8_off(dest, ch, D)] = quant_code(xv[ch], sv);
   }
   __syncthreads();
   // Requantise the stored codes (slots < n8n) of every channel whose absmax grew.
   const int ngk = n_grown_k, ngv = n_grown_v;
   for (int i = threadIdx.x; i < n8n * ngk; i += blockDim.x) {
     const int tok = i / ngk, ch = grown_k[i % ngk];
-    int8_t* p = k8 + (size_t)tok * D + ch;
+    int8_t* p = k8 + k8_off(tok, ch, D);
     *p = quant_code((float)(*p) * s_old_k[ch], s_new_k[ch]);
   }
   for (int i = threadIdx.x; i < n8n * ngv; i += blockDim.x) {
     const int tok = i / ngv, ch = grown_v[i % ngv];
-    int8_t* p = v8 + vtile_off(tok, ch, D);
+    int8_t* p = v8 + v8_off(tok, ch, D);
     *p = quant_code((float)(*p) * s_old_v[ch], s_new_v[ch]);
   }
 }
@@ -354,16 +353,16 @@ __global__ void export_kernel(conf_cache c, Dims dm, int lb, int8_t* ok8, int8_t
       const int hk = (int)((i / dm.D) % dm.Hkv);
       const int s = (int)(i / ((size_t)dm.D * dm.Hkv));
       const size_t u = unit_of(dm, lb, hk);
-      ok8[i] = c.k8[(u * dm.cap8 + s) * dm.D + ch];
-      ov8[i] = c.v8[u * dm.cap8 * dm.D + vtile_off(s, ch, dm.D)];
+      ok8[i] = c.k8[u * dm.cap8 * dm.D + k8_off(s, ch, dm.D)];
+      ov8[i] = c.v8[u * dm.cap8 * dm.D + v8_off(s, ch, dm.D)];
     } else {
       const size_t j = i - n8tot;
       const int ch = (int)(j % dm.D);
       const int hk = (int)((j / dm.D) % dm.Hkv);
       const int s = (int)(j / ((size_t)dm.D * dm.Hkv));
       const size_t u = unit_of(dm, lb, hk);
-      ok16[j] = ((const uint16_t*)c.k16)[(u * dm.cap16 + s) * dm.D + ch];
-      ov16[j] = ((const uint16_t*)c.v16)[u * dm.cap16 * dm.D + vtile_off(s, ch, dm.D)];
+      ok16[j] = ((const uint16_t*)c.k16)[u * dm.cap16 * dm.D + k16_off(s, ch, dm.D)];
+      ov16[j] = ((const uint16_t*)c.v16)[u * dm.cap16 * dm.D + v16_off(s, ch, dm.D)];
     }
   }
 }

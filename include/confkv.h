@@ -81,22 +81,24 @@ typedef struct conf_params {
  * The dense mixed-precision cache [storage][impl].  All arrays are caller-
  * allocated device memory of the sizes conf_cache_layout() reports.  With
  * cap16 = W+1 rounded up to 64 and U = L*B*Hkv units:
- *   k8     int8  [L][B][Hkv][cap8][d]             INT8 key codes, token-major rows
- *   v8     int8  [L][B][Hkv][cap8/64][d][64]      INT8 value codes, 64-token tiles,
- *                                                 channel-major inside a tile
- *   k16    16-bit[L][B][Hkv][cap16][d]            window keys, token-major rows
- *   v16    16-bit[L][B][Hkv][cap16/64][d][64]     window values, tiled like v8
+ *   k8     int8  [L][B][Hkv][cap8/64][64*d]       INT8 key codes, 64-token tiles
+ *   v8     int8  [L][B][Hkv][cap8/64][64*d]       INT8 value codes, 64-token tiles
+ *   k16    16-bit[L][B][Hkv][cap16/64][64*d]      window keys, 64-token tiles
+ *   v16    16-bit[L][B][Hkv][cap16/64][64*d]      window values, 64-token tiles
  *   k_amax, v_amax fp32 [L][B][Hkv][d]            running absmax; scale = amax/127
  *   pos8, ema8     [L][B][cap8]  int32 / fp32     position and EMA of INT8 slots
  *   pos16, ema16   [L][B][cap16] int32 / fp32     position and EMA of window slots
  *   n8, n16        int32 [L][B]                   occupied slots (dense prefix)
  *   t              int32 [L][B]                   newest position (-1 = empty)
  *   status         int32 [1]                      CONF_ST_* bits
- *   arrive         int32 [L][B]                   per-step arrival counters of the
- *                                                 KV-head workgroups (0 between calls)
- * Inside a 64-token tile, slot s sits at column tile_col(s % 64), where for
- * j = 32u + 16a + 4g + b (u, a in {0,1}; g, b in 0..3) tile_col(j) = 16g + 8u + 4a + b.
- * (This order lets a wavefront feed the matrix cores straight from memory.)
+ * Inside a tile, write a slot's index j (mod 64) as j = 32u + 16a + 4g + b =
+ * 16r + row (u, a in {0,1}; g, b, r in 0..3; row in 0..15) and a channel c.
+ * The element order of a tile is
+ *   k8:  [r][c/64][(c/16)%4][row][c%16]         v8:  [c][16g + 8u + 4a + b]
+ *   k16: [u][r%2][c/32][(c/8)%4][row][c%8]      v16: [u][c][8g + 4a + b]
+ * so that every wavefront load of the attention kernel reads one contiguous
+ * 1 KB run and lands in the lane that feeds it to the matrix cores.
+ * conf_cache_export() returns plain row-major copies.
  * Slot order inside a region is arbitrary: compaction fills holes, so a token's
  * identity is its stored position.
  */
@@ -115,11 +117,10 @@ typedef struct conf_cache {
   int32_t* n16;
   int32_t* t;
   int32_t* status;
-  int32_t* arrive;
 } conf_cache;
 
 typedef struct conf_cache_bytes_t {
-  size_t k8, v8, k16, v16, k_amax, v_amax, pos8, ema8, pos16, ema16, n8, n16, t, status, arrive;
+  size_t k8, v8, k16, v16, k_amax, v_amax, pos8, ema8, pos16, ema16, n8, n16, t, status;
   int32_t cap16;
 } conf_cache_bytes_t;
 
@@ -129,8 +130,7 @@ int conf_cache_layout(const conf_params* p, conf_cache_bytes_t* out);
 /* Workspace bytes every call below may use for `p`. */
 int conf_workspace_bytes(const conf_params* p, size_t* bytes);
 
-/* Empty every (layer, sequence): n8 = n16 = 0, t = -1, absmax = 0, status = 0,
- * arrive = 0.
+/* Empty every (layer, sequence): n8 = n16 = 0, t = -1, absmax = 0, status = 0.
  * Fills with kernels (no memset nodes), so it may be graph-captured. */
 int conf_cache_reset(const conf_params* p, conf_cache* c, conf_stream_t stream);
 

@@ -108,7 +108,7 @@ def test_null_pointers_rejected_before_launch(lib):
 def test_bad_layer_rejected(lib):
     p = _p()
     fake = ctypes.c_void_p(0x1000)           # never dereferenced: validation fails first
-    cache = binding.ConfCache(*([0x1000] * 15))
+    cache = binding.ConfCache(*([0x1000] * 14))
     assert lib.conf_rank_evict(ctypes.byref(p), ctypes.byref(cache), 64, fake, fake, fake,
                                null := ctypes.c_void_p(0)) == E_INVALID
     assert lib.conf_cache_export(ctypes.byref(p), ctypes.byref(cache), 0, 8, fake, fake, fake,
