@@ -117,70 +117,59 @@ void launch_ingest(const Dims& dm, const conf_cache& c, int layer0, int nl, int 
                      (const uint16_t*)k, (const uint16_t*)v);
 }
 
-// ---------------------------------------------------------------- compaction plan
-// One workgroup per (layer, sequence).  Window keep flags exclude the token at
-// position t - W (it is demoted, not kept in place).  In each region the k-th
-// hole below the new end receives the k-th survivor above it.  Metadata moves
-// happen here; the plan tells the data kernel what to move.
-// plan: [0] n8 new (before demotion) [1] moves8 [2] n16 new [3] moves16
-//       [4] window slot of the demotee or -1 [5] INT8 slot it goes to or -1
-constexpr int kPlanThreads = 256;
+// ---------------------------------------------------------------- compaction + demotion
+// One workgroup of 1024 threads per (layer, sequence).
+//  1. Window keep flags exclude the token at position t - W (it is demoted, not
+//     kept in place).  In each region the k-th hole below the new end receives
+//     the k-th survivor above it (both in slot order), so the layout stays dense.
+//  2. Positions and EMAs move; the demotee's metadata lands in INT8 slot n8'.
+//  3. Key/value data of every KV head move the same way.
+//  4. Per (KV head, channel), one thread quantises the demotee under the running
+//     absmax; channels whose absmax grows first requantise their stored codes.
+// plan: [0] n8' [1] INT8 moves [2] n16' [3] window moves [4] demotee's window
+//       slot or -1 [5] its INT8 slot or -1  (kept in the workspace for inspection)
+constexpr int kCompThreads = 1024;
+constexpr int kCompWaves = kCompThreads / 64;
+constexpr int kMaxGrown = 512;  // grown channels requantised by the whole workgroup
 
-__device__ inline int block_excl_scan(int v, int* sh, int& total) {
-  // Inclusive Hillis-Steele scan over 256 threads in shared memory.
-  const int tid = threadIdx.x;
-  sh[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kPlanThreads; off <<= 1) {
-    const int x = tid >= off ? sh[tid - off] : 0;
+// Ordered ranks of the slots of [lo, hi) whose keep flag equals `want`:
+// out[2*rank + off] = slot.  Returns their number.  Every thread must call it.
+__device__ int rank_slots(int lo, int hi, const uint8_t* keep, bool want, int32_t* out, int off,
+                          int* s_wcnt) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int base = 0;
+  for (int c0 = lo; c0 < hi; c0 += kCompThreads) {
+    const int i = c0 + tid;
+    const bool f = i < hi && ((keep[i] != 0) == want);
+    const unsigned long long bal = __ballot(f);
+    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) s_wcnt[wave] = __popcll(bal);
     __syncthreads();
-    sh[tid] += x;
+    int woff = 0, tot = 0;
+    for (int w = 0; w < kCompWaves; ++w) {
+      const int cw = s_wcnt[w];
+      woff += w < wave ? cw : 0;
+      tot += cw;
+    }
+    if (f) out[2 * (base + woff + before) + off] = i;
+    base += tot;
     __syncthreads();
   }
-  total = sh[kPlanThreads - 1];
-  const int r = sh[tid] - v;
-  __syncthreads();
-  return r;
+  return base;
 }
 
-__device__ void plan_region(const uint8_t* keep, int n, int n_new, int* mv, int* sh,
-                            int32_t* pos, float* ema, int& n_moves_out) {
-  // holes: i < n_new with !keep[i];  movers: n_new <= i < n with keep[i]
-  int hole_base = 0;
-  for (int base = 0; base < n_new; base += kPlanThreads) {
-    const int i = base + threadIdx.x;
-    const int is_hole = (i < n_new) && !keep[i];
-    int tot;
-    const int r = block_excl_scan(is_hole, sh, tot);
-    if (is_hole) mv[2 * (hole_base + r) + 1] = i;
-    hole_base += tot;
-  }
-  int mover_base = 0;
-  for (int base = n_new; base < n; base += kPlanThreads) {
-    const int i = base + threadIdx.x;
-    const int is_mv = (i < n) && keep[i];
-    int tot;
-    const int r = block_excl_scan(is_mv, sh, tot);
-    if (is_mv) mv[2 * (mover_base + r)] = i;
-    mover_base += tot;
-  }
-  __syncthreads();
-  n_moves_out = hole_base;  // == mover_base
-  for (int k = threadIdx.x; k < hole_base; k += kPlanThreads) {
-    const int src = mv[2 * k], dst = mv[2 * k + 1];
-    pos[dst] = pos[src];
-    ema[dst] = ema[src];
-  }
-}
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(conf_cache c, Dims dm, int layer0,
-                                                            const uint8_t* __restrict__ keep_all,
-                                                            int32_t* __restrict__ plan_all,
-                                                            int32_t* __restrict__ mv8_all,
-                                                            int32_t* __restrict__ mv16_all,
-                                                            uint8_t* __restrict__ wkeep_all) {
+__global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dims dm, int layer0,
+                                                               const uint8_t* __restrict__ keep_all,
+                                                               int32_t* __restrict__ plan_all,
+                                                               int32_t* __restrict__ mv8_all,
+                                                               int32_t* __restrict__ mv16_all,
+                                                               uint8_t* __restrict__ wkeep_all) {
+#pragma clang fp contract(off)
   const int lb = layer0 * dm.B + blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n8 = c.n8[lb], n16 = c.n16[lb], t = c.t[lb];
+  const int D = dm.D;
   const uint8_t* keep8 = keep_all + (size_t)lb * dm.capt;
   const uint8_t* keep16 = keep8 + dm.cap8;
   uint8_t* wkeep = wkeep_all + (size_t)lb * dm.cap16;
@@ -188,18 +177,21 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(conf_cache c, Dims d
   float* ema8 = c.ema8 + (size_t)lb * dm.cap8;
   int32_t* pos16 = c.pos16 + (size_t)lb * dm.cap16;
   float* ema16 = c.ema16 + (size_t)lb * dm.cap16;
-  __shared__ int sh[kPlanThreads];
-  __shared__ int s_cnt8, s_cnt16, s_jd;
-  if (threadIdx.x == 0) {
-    s_cnt8 = 0;
-    s_cnt16 = 0;
-    s_jd = -1;
-  }
+  int32_t* mv8 = mv8_all + (size_t)lb * dm.cap8;
+  int32_t* mv16 = mv16_all + (size_t)lb * dm.cap16;
+  __shared__ int s_wcnt[kCompWaves];
+  __shared__ int s_c8[kCompWaves], s_c16[kCompWaves];
+  __shared__ int s_jd;
+  __shared__ int s_ngrown;
+  __shared__ int s_grown[kMaxGrown];
+  __shared__ float s_gold[kMaxGrown], s_gnew[kMaxGrown];
+  if (tid == 0) s_jd = -1;
   __syncthreads();
+  // ---- 1. counts, the demotee, window keep flags
   const int target = t - dm.W;
   int c8 = 0, c16 = 0;
-  for (int i = threadIdx.x; i < n8; i += kPlanThreads) c8 += keep8[i] ? 1 : 0;
-  for (int w = threadIdx.x; w < n16; w += kPlanThreads) {
+  for (int i = tid; i < n8; i += kCompThreads) c8 += keep8[i] ? 1 : 0;
+  for (int w = tid; w < n16; w += kCompThreads) {
     int k = keep16[w] ? 1 : 0;
     if (k && target >= 0 && pos16[w] == target) {
       s_jd = w;  // at most one slot holds this position
@@ -208,33 +200,120 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(conf_cache c, Dims d
     wkeep[w] = (uint8_t)k;
     c16 += k;
   }
-  atomicAdd(&s_cnt8, c8);
-  atomicAdd(&s_cnt16, c16);
+  for (int off = 32; off > 0; off >>= 1) {
+    c8 += __shfl_xor(c8, off);
+    c16 += __shfl_xor(c16, off);
+  }
+  if (lane == 0) {
+    s_c8[wave] = c8;
+    s_c16[wave] = c16;
+  }
   __syncthreads();
-  const int n8n = s_cnt8, n16n = s_cnt16, jd = s_jd;
+  int n8n = 0, n16n = 0;
+  for (int w = 0; w < kCompWaves; ++w) {
+    n8n += s_c8[w];
+    n16n += s_c16[w];
+  }
+  const int jd = s_jd;
+  const int dest = (jd >= 0 && n8n < dm.cap8) ? n8n : -1;
   int dpos = 0;
   float dema = 0.f;
-  if (jd >= 0) {
+  if (jd >= 0) {  // read before the window metadata moves
     dpos = pos16[jd];
     dema = ema16[jd];
   }
+  // ---- 2. move lists: k-th hole below the new end <- k-th survivor above it
+  const int nm8 = rank_slots(0, n8n, keep8, false, mv8, 1, s_wcnt);
+  rank_slots(n8n, n8, keep8, true, mv8, 0, s_wcnt);
+  const int nm16 = rank_slots(0, n16n, wkeep, false, mv16, 1, s_wcnt);
+  rank_slots(n16n, n16, wkeep, true, mv16, 0, s_wcnt);
+  __syncthreads();  // move lists complete (same workgroup: visible after the barrier)
+  // ---- 3. metadata moves (holes and movers are disjoint slots)
+  for (int k = tid; k < nm8; k += kCompThreads) {
+    const int src = mv8[2 * k], dst = mv8[2 * k + 1];
+    pos8[dst] = pos8[src];
+    ema8[dst] = ema8[src];
+  }
+  for (int k = tid; k < nm16; k += kCompThreads) {
+    const int src = mv16[2 * k], dst = mv16[2 * k + 1];
+    pos16[dst] = pos16[src];
+    ema16[dst] = ema16[src];
+  }
+  // ---- 4. INT8 data of every KV head (slot n8' is free once its mover has left)
+  const int per = dm.Hkv * D;
+  for (int i = tid; i < nm8 * per; i += kCompThreads) {
+    const int k = i / per, r = i % per, hk = r / D, ch = r % D;
+    const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap8 * D;
+    const int src = mv8[2 * k], dst = mv8[2 * k + 1];
+    c.k8[ub + k8_off(dst, ch, D)] = c.k8[ub + k8_off(src, ch, D)];
+    c.v8[ub + v8_off(dst, ch, D)] = c.v8[ub + v8_off(src, ch, D)];
+  }
   __syncthreads();
-  int nm8 = 0, nm16 = 0;
-  plan_region(keep8, n8, n8n, mv8_all + (size_t)lb * dm.cap8, sh, pos8, ema8, nm8);
-  __syncthreads();
-  plan_region(wkeep, n16, n16n, mv16_all + (size_t)lb * dm.cap16, sh, pos16, ema16, nm16);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int dest = -1;
-    if (jd >= 0) {
-      if (n8n < dm.cap8) {
-        dest = n8n;
-        pos8[dest] = dpos;
-        ema8[dest] = dema;
-      } else {
-        atomicOr(c.status, (int)CONF_ST_INT8_FULL);
-      }
+  // ---- 5. demotion into INT8 slot `dest`, read from the untouched window slot jd.
+  // One thread per (KV head, channel) and kind: a = |x|; a new maximum first
+  // requantises that channel's stored codes (slots < n8'), then the token is coded
+  // at the channel's absmax / 127.  Grown channels are listed in LDS and their
+  // codes requantised by the whole workgroup (a list overflow, only possible when
+  // very many channels grow at once, is handled by the owning thread).
+  if (dest >= 0) {
+    if (tid == 0) {
+      pos8[dest] = dpos;
+      ema8[dest] = dema;
+      s_ngrown = 0;
     }
+    __syncthreads();
+    for (int pi = tid; pi < 2 * per; pi += kCompThreads) {
+      const int kind = pi / per, hc = pi % per, hk = hc / D, ch = hc % D;
+      const size_t u = (size_t)lb * dm.Hkv + hk;
+      const float x = h16_to_f32(
+          kind == 0 ? ((const uint16_t*)c.k16)[u * (size_t)dm.cap16 * D + k16_off(jd, ch, D)]
+                    : ((const uint16_t*)c.v16)[u * (size_t)dm.cap16 * D + v16_off(jd, ch, D)],
+          dm.bf16);
+      int8_t* base = (kind == 0 ? c.k8 : c.v8) + u * (size_t)dm.cap8 * D;
+      float* am = (kind == 0 ? c.k_amax : c.v_amax) + u * D + ch;
+      const float old = *am, a = fabsf(x);
+      const float amax = a > old ? a : old;
+      const float s_new = amax / 127.0f;
+      if (a > old) {
+        *am = amax;
+        const float s_old = old / 127.0f;
+        const int slot = atomicAdd(&s_ngrown, 1);
+        if (slot < kMaxGrown) {
+          s_grown[slot] = pi;
+          s_gold[slot] = s_old;
+          s_gnew[slot] = s_new;
+        } else {
+          for (int tok = 0; tok < n8n; ++tok) {
+            int8_t* p = base + (kind == 0 ? k8_off(tok, ch, D) : v8_off(tok, ch, D));
+            *p = quant_code((float)(*p) * s_old, s_new);
+          }
+        }
+      }
+      base[kind == 0 ? k8_off(dest, ch, D) : v8_off(dest, ch, D)] = quant_code(x, s_new);
+    }
+    __syncthreads();
+    const int ng = min(s_ngrown, kMaxGrown);
+    for (int i = tid; i < ng * n8n; i += kCompThreads) {
+      const int e = i % ng, tok = i / ng;
+      const int pi = s_grown[e], kind = pi / per, hc = pi % per, hk = hc / D, ch = hc % D;
+      const size_t u = (size_t)lb * dm.Hkv + hk;
+      int8_t* p = (kind == 0 ? c.k8 + u * (size_t)dm.cap8 * D + k8_off(tok, ch, D)
+                             : c.v8 + u * (size_t)dm.cap8 * D + v8_off(tok, ch, D));
+      *p = quant_code((float)(*p) * s_gold[e], s_gnew[e]);
+    }
+  }
+  __syncthreads();
+  // ---- 6. window data of every KV head
+  for (int i = tid; i < nm16 * per; i += kCompThreads) {
+    const int k = i / per, r = i % per, hk = r / D, ch = r % D;
+    const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap16 * D;
+    const int src = mv16[2 * k], dst = mv16[2 * k + 1];
+    uint16_t* k16 = (uint16_t*)c.k16 + ub;
+    uint16_t* v16 = (uint16_t*)c.v16 + ub;
+    k16[k16_off(dst, ch, D)] = k16[k16_off(src, ch, D)];
+    v16[v16_off(dst, ch, D)] = v16[v16_off(src, ch, D)];
+  }
+  if (tid == 0) {
     int32_t* pl = plan_all + (size_t)lb * 16;
     pl[0] = n8n;
     pl[1] = nm8;
@@ -242,103 +321,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(conf_cache c, Dims d
     pl[3] = nm16;
     pl[4] = jd;
     pl[5] = dest;
+    if (jd >= 0 && dest < 0) atomicOr(c.status, (int)CONF_ST_INT8_FULL);
     c.n8[lb] = n8n + (dest >= 0 ? 1 : 0);
     c.n16[lb] = n16n;
   }
 }
 
-// ---------------------------------------------------------------- data moves + demotion
-// One workgroup per unit.  Reads the demotee's 16-bit row first (a window move
-// may overwrite its slot), moves INT8 and window rows/columns, then quantises the
-// demotee into INT8 slot `dest` under the running absmax, requantising the
-// channels whose absmax grows.
-__global__ __launch_bounds__(256) void move_kernel(conf_cache c, Dims dm, int layer0,
-                                                   const int32_t* __restrict__ plan_all,
-                                                   const int32_t* __restrict__ mv8_all,
-                                                   const int32_t* __restrict__ mv16_all) {
-#pragma clang fp contract(off)
-  const int unit_local = blockIdx.x;
-  const int hk = unit_local % dm.Hkv;
-  const int lb = layer0 * dm.B + unit_local / dm.Hkv;
-  const size_t u = unit_of(dm, lb, hk);
-  const int D = dm.D;
-  const int32_t* pl = plan_all + (size_t)lb * 16;
-  const int n8n = pl[0], nm8 = pl[1], nm16 = pl[3], jd = pl[4], dest = pl[5];
-  int8_t* k8 = c.k8 + u * (size_t)dm.cap8 * D;
-  int8_t* v8 = c.v8 + u * (size_t)dm.cap8 * D;
-  uint16_t* k16 = (uint16_t*)c.k16 + u * (size_t)dm.cap16 * D;
-  uint16_t* v16 = (uint16_t*)c.v16 + u * (size_t)dm.cap16 * D;
-  __shared__ float xk[128], xv[128];
-  __shared__ float s_old_k[128], s_new_k[128], s_old_v[128], s_new_v[128];
-  __shared__ int grown_k[128], grown_v[128];
-  __shared__ int n_grown_k, n_grown_v;
-  if (threadIdx.x == 0) {
-    n_grown_k = 0;
-    n_grown_v = 0;
-  }
-  if (dest >= 0) {
-    for (int ch = threadIdx.x; ch < D; ch += blockDim.x) {
-      xk[ch] = h16_to_f32(k16[k16_off(jd, ch, D)], dm.bf16);
-      xv[ch] = h16_to_f32(v16[v16_off(jd, ch, D)], dm.bf16);
-    }
-  }
-  __syncthreads();
-  const int32_t* mv8 = mv8_all + (size_t)lb * dm.cap8;
-  for (int i = threadIdx.x; i < nm8 * D; i += blockDim.x) {
-    const int k = i / D, ch = i % D;
-    const int src = mv8[2 * k], dst = mv8[2 * k + 1];
-    k8[k8_off(dst, ch, D)] = k8[k8_off(src, ch, D)];
-    v8[v8_off(dst, ch, D)] = v8[v8_off(src, ch, D)];
-  }
-  const int32_t* mv16 = mv16_all + (size_t)lb * dm.cap16;
-  for (int i = threadIdx.x; i < nm16 * D; i += blockDim.x) {
-    const int k = i / D, ch = i % D;
-    const int src = mv16[2 * k], dst = mv16[2 * k + 1];
-    k16[k16_off(dst, ch, D)] = k16[k16_off(src, ch, D)];
-    v16[v16_off(dst, ch, D)] = v16[v16_off(src, ch, D)];
-  }
-  __syncthreads();
-  if (dest < 0) return;
-  for (int ch = threadIdx.x; ch < D; ch += blockDim.x) {
-    float* ak = c.k_amax + u * D + ch;
-    float* av = c.v_amax + u * D + ch;
-    const float ok = *ak, ov = *av;
-    const float a_k = fabsf(xk[ch]), a_v = fabsf(xv[ch]);
-    const int gk = a_k > ok, gv = a_v > ov;
-    const float nk = gk ? a_k : ok, nv = gv ? a_v : ov;
-    const float sk = nk / 127.0f, sv = nv / 127.0f;
-    s_old_k[ch] = ok / 127.0f;
-    s_new_k[ch] = sk;
-    s_old_v[ch] = ov / 127.0f;
-    s_new_v[ch] = sv;
-    if (gk) grown_k[atomicAdd(&n_grown_k, 1)] = ch;
-    if (gv) grown_v[atomicAdd(&n_grown_v, 1)] = ch;
-    *ak = nk;
-    *av = nv;
-    k8[k8_off(dest, ch, D)] = quant_code(xk[ch], sk);
-    v8[v8_off(dest, ch, D)] = quant_code(xv[ch], sv);
-  }
-  __syncthreads();
-  // Requantise the stored codes (slots < n8n) of every channel whose absmax grew.
-  const int ngk = n_grown_k, ngv = n_grown_v;
-  for (int i = threadIdx.x; i < n8n * ngk; i += blockDim.x) {
-    const int tok = i / ngk, ch = grown_k[i % ngk];
-    int8_t* p = k8 + k8_off(tok, ch, D);
-    *p = quant_code((float)(*p) * s_old_k[ch], s_new_k[ch]);
-  }
-  for (int i = threadIdx.x; i < n8n * ngv; i += blockDim.x) {
-    const int tok = i / ngv, ch = grown_v[i % ngv];
-    int8_t* p = v8 + v8_off(tok, ch, D);
-    *p = quant_code((float)(*p) * s_old_v[ch], s_new_v[ch]);
-  }
-}
-
 void launch_compact(const Dims& dm, const conf_cache& c, int layer0, int nl, const uint8_t* keep,
                     int32_t* plan, int32_t* mv8, int32_t* mv16, uint8_t* wkeep, hipStream_t st) {
-  hipLaunchKernelGGL(plan_kernel, dim3(nl * dm.B), dim3(kPlanThreads), 0, st, c, dm, layer0, keep,
-                     plan, mv8, mv16, wkeep);
-  hipLaunchKernelGGL(move_kernel, dim3(nl * dm.B * dm.Hkv), dim3(256), 0, st, c, dm, layer0, plan,
-                     mv8, mv16);
+  hipLaunchKernelGGL(compact_kernel, dim3(nl * dm.B), dim3(kCompThreads), 0, st, c, dm, layer0,
+                     keep, plan, mv8, mv16, wkeep);
 }
 
 // ---------------------------------------------------------------- export

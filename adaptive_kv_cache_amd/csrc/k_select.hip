@@ -10,13 +10,16 @@
 // rounding per operation (contraction off).  s >= 0, so its IEEE bits order like
 // the value; the 64-bit key (bits(s) << 32 | pos) is unique per token and orders
 // exactly as (s desc, pos desc).  The K-th largest candidate key is found by an
-// MSB-first radix select (8 passes of 8 bits) with a 256-bin histogram in LDS;
-// every candidate whose key is >= it is kept.
+// MSB-first radix select over 8-bit digits: a 256-bin histogram in LDS per pass,
+// the bin holding the K-th key found by one wavefront's suffix scan, and an early
+// stop as soon as that bin's keys are all kept.  Keys live in LDS when the cache
+// fits (the steady state); otherwise each pass recomputes them from the cache.
 #include "common.hpp"
 
 namespace confkv {
 
-constexpr int kSelThreads = 256;
+constexpr int kSelThreads = 1024;
+constexpr int kSelLdsKeys = 6144;  // keys cached in LDS (48 KB)
 
 __device__ inline uint64_t sel_key(float e, float emax, int pos, int t, float s_ema, float s_rec) {
 #pragma clang fp contract(off)
@@ -42,23 +45,36 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(conf_cache c, Dims 
   const float* ema8 = c.ema8 + (size_t)lb * dm.cap8;
   const int32_t* pos16 = c.pos16 + (size_t)lb * dm.cap16;
   const float* ema16 = c.ema16 + (size_t)lb * dm.cap16;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (n <= N) {
     for (int j = tid; j < n8; j += kSelThreads) keep8[j] = 1;
     for (int j = tid; j < n16; j += kSelThreads) keep16[j] = 1;
     return;
   }
+  __shared__ uint64_t s_key[kSelLdsKeys];
   __shared__ unsigned hist[256];
-  __shared__ float s_emax;
-  __shared__ int s_nprot;
+  __shared__ float s_wmax[kSelThreads / 64];
+  __shared__ int s_wprot[kSelThreads / 64];
   __shared__ unsigned long long s_prefix, s_mask;
-  __shared__ int s_rem;
+  __shared__ int s_rem, s_done;
   const int prot_lo = t - dm.P;  // protected: pos > prot_lo
+  const bool cached = n <= kSelLdsKeys;
+  auto tok = [&](int j, float& e, int& p) {
+    if (j < n8) {
+      e = ema8[j];
+      p = pos8[j];
+    } else {
+      e = ema16[j - n8];
+      p = pos16[j - n8];
+    }
+  };
+  // e_max over every cached token and the protected count
   float emax = 0.f;
   int nprot = 0;
   for (int j = tid; j < n; j += kSelThreads) {
-    const float e = j < n8 ? ema8[j] : ema16[j - n8];
-    const int p = j < n8 ? pos8[j] : pos16[j - n8];
+    float e;
+    int p;
+    tok(j, e, p);
     emax = fmaxf(emax, e);
     nprot += p > prot_lo;
   }
@@ -66,60 +82,89 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(conf_cache c, Dims 
     emax = fmaxf(emax, __shfl_xor(emax, off));
     nprot += __shfl_xor(nprot, off);
   }
+  if (lane == 0) {
+    s_wmax[wave] = emax;
+    s_wprot[wave] = nprot;
+  }
+  __syncthreads();
+  float em = 0.f;
+  int np = 0;
+  for (int w = 0; w < kSelThreads / 64; ++w) {
+    em = fmaxf(em, s_wmax[w]);
+    np += s_wprot[w];
+  }
+  int K = N - np;
+  if (K < 0) K = 0;
+  // candidate keys; protected tokens get key 0, which no candidate can have
+  // (pos + 1 > 0 is folded in below so that 0 stays reserved)
+  auto key_of = [&](int j) -> uint64_t {
+    float e;
+    int p;
+    tok(j, e, p);
+    if (p > prot_lo) return 0ull;
+    return sel_key(e, em, p, t, dm.s_ema, dm.s_rec) + 1ull;
+  };
+  if (cached)
+    for (int j = tid; j < n; j += kSelThreads) s_key[j] = key_of(j);
   if (tid == 0) {
-    s_emax = 0.f;
-    s_nprot = 0;
     s_prefix = 0ull;
     s_mask = 0ull;
+    s_rem = K;
+    s_done = K == 0;
   }
   __syncthreads();
-  if ((tid & 63) == 0) {
-    atomicMax((unsigned*)&s_emax, __float_as_uint(emax));  // e >= 0: bits order like values
-    atomicAdd(&s_nprot, nprot);
-  }
-  __syncthreads();
-  const float em = s_emax;
-  int K = N - s_nprot;
-  if (K < 0) K = 0;
-  if (tid == 0) s_rem = K;
-  for (int shift = 56; shift >= 0; shift -= 8) {
-    hist[tid] = 0u;
+  for (int shift = 56; shift >= 0 && !s_done; shift -= 8) {
+    if (tid < 256) hist[tid] = 0u;
     __syncthreads();
     const unsigned long long pre = s_prefix, msk = s_mask;
     for (int j = tid; j < n; j += kSelThreads) {
-      const int p = j < n8 ? pos8[j] : pos16[j - n8];
-      if (p > prot_lo) continue;
-      const float e = j < n8 ? ema8[j] : ema16[j - n8];
-      const uint64_t key = sel_key(e, em, p, t, dm.s_ema, dm.s_rec);
-      if ((key & msk) == pre) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      const uint64_t key = cached ? s_key[j] : key_of(j);
+      if (key != 0ull && (key & msk) == pre) atomicAdd(&hist[(key >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (tid == 0) {
-      int rem = s_rem;
-      unsigned cum = 0;
-      int d = 255;
-      for (; d > 0; --d) {
-        if ((int)(cum + hist[d]) >= rem) break;
-        cum += hist[d];
+    if (wave == 0) {
+      // lane l covers bins 255-4l .. 252-4l; suffix sums from the top bin down
+      unsigned hb[4], sum = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hb[i] = hist[255 - 4 * lane - i];
+        sum += hb[i];
       }
-      s_rem = rem - (int)cum;
-      s_prefix = pre | ((unsigned long long)d << shift);
-      s_mask = msk | (0xFFull << shift);
+      unsigned incl = sum;
+      for (int off = 1; off < 64; off <<= 1) {
+        const unsigned y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      const unsigned excl = incl - sum;
+      const unsigned rem = (unsigned)s_rem;
+      if (excl < rem && rem <= incl) {
+        unsigned cum = excl;
+        int d = 255 - 4 * lane - 3;
+        unsigned cnt = hb[3];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (cum + hb[i] >= rem) {
+            d = 255 - 4 * lane - i;
+            cnt = hb[i];
+            break;
+          }
+          cum += hb[i];
+        }
+        const int rem2 = (int)(rem - cum);
+        s_prefix = pre | ((unsigned long long)d << shift);
+        s_mask = msk | (0xFFull << shift);
+        s_rem = rem2;
+        s_done = (rem2 == (int)cnt) || shift == 0;  // the whole bin is kept
+      }
     }
     __syncthreads();
   }
+  // keep every candidate whose key is >= the threshold prefix (its undecided low
+  // bits at zero); when K = 0 no candidate is kept
   const unsigned long long kth = s_prefix;
   for (int j = tid; j < n; j += kSelThreads) {
-    const int p = j < n8 ? pos8[j] : pos16[j - n8];
-    int k = 1;
-    if (p <= prot_lo) {
-      if (K == 0) {
-        k = 0;
-      } else {
-        const float e = j < n8 ? ema8[j] : ema16[j - n8];
-        k = sel_key(e, em, p, t, dm.s_ema, dm.s_rec) >= kth;
-      }
-    }
+    const uint64_t key = cached ? s_key[j] : key_of(j);
+    const int k = key == 0ull ? 1 : (K > 0 && key >= kth);
     if (j < n8)
       keep8[j] = (uint8_t)k;
     else
