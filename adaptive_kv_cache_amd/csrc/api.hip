@@ -56,6 +56,9 @@ int make_dims(const conf_params* p, Dims* d) {
   if (p->protect > min_budget) return CONF_E_INVALID;
   if (p->cap8 < 64 || p->cap8 % 64) return CONF_E_INVALID;
   if (p->cap8 <= p->n_low) return CONF_E_CAPACITY;
+  // a unit's INT8 region (cap8 * head_dim bytes) is addressed through a 32-bit
+  // buffer range: keep it at or below 1 GiB
+  if ((int64_t)p->cap8 * p->head_dim > ((int64_t)1 << 30)) return CONF_E_INVALID;
   if (!(p->ema_decay >= 0.f && p->ema_decay <= 1.f)) return CONF_E_INVALID;
   if (!(p->s_ema >= 0.f && p->s_rec >= 0.f)) return CONF_E_INVALID;
   if (p->pyramid != 0 && p->pyramid != 1) return CONF_E_INVALID;
@@ -118,9 +121,13 @@ T* at(void* ws, size_t off) {
   return (T*)((char*)ws + off);
 }
 
+// non-null and 16-byte aligned (the kernels read these with 16-byte loads)
+bool a16(const void* x) { return x && ((uintptr_t)x & 15u) == 0; }
+
 bool cache_ok(const conf_cache* c) {
-  return c && c->k8 && c->v8 && c->k16 && c->v16 && c->k_amax && c->v_amax && c->pos8 &&
-         c->ema8 && c->pos16 && c->ema16 && c->n8 && c->n16 && c->t && c->status;
+  return c && a16(c->k8) && a16(c->v8) && a16(c->k16) && a16(c->v16) && a16(c->k_amax) &&
+         a16(c->v_amax) && c->pos8 && c->ema8 && c->pos16 && c->ema16 && c->n8 && c->n16 && c->t &&
+         c->status;
 }
 
 // layer selector -> (first layer, layer count)
@@ -215,7 +222,8 @@ int conf_decode_attn(const conf_params* p, conf_cache* c, int32_t layer, const v
   int rc = make_dims(p, &d);
   if (rc) return rc;
   int l0, nl;
-  if (!cache_ok(c) || !q || !k_new || !v_new || !out || !ws || !layer_range(d, layer, &l0, &nl))
+  if (!cache_ok(c) || !a16(q) || !a16(k_new) || !a16(v_new) || !out || !ws ||
+      !layer_range(d, layer, &l0, &nl))
     return CONF_E_INVALID;
   const WsMap w = make_ws(d);
   hipStream_t st = (hipStream_t)stream;
@@ -255,7 +263,8 @@ int conf_step(const conf_params* p, conf_cache* c, const float* logits, const vo
   Dims d;
   int rc = make_dims(p, &d);
   if (rc) return rc;
-  if (!cache_ok(c) || !logits || !q || !k_new || !v_new || !out || !conf || !budget || !ws)
+  if (!cache_ok(c) || !logits || !a16(q) || !a16(k_new) || !a16(v_new) || !out || !conf ||
+      !budget || !ws)
     return CONF_E_INVALID;
   const WsMap w = make_ws(d);
   hipStream_t st = (hipStream_t)stream;

@@ -24,6 +24,8 @@
  *   - A call validates its arguments on the host, enqueues kernels on `stream`
  *     (a hipStream_t; NULL is the null stream) and returns without waiting for
  *     the device.  Results are valid once the stream has been synchronised.
+ *   - q, k_new, v_new and the cache's k8, v8, k16, v16, k_amax, v_amax must be
+ *     16-byte aligned (CONF_E_INVALID otherwise); PyTorch allocations are.
  *   - Return value: CONF_OK (0) or a negative CONF_E_* code; nothing is
  *     enqueued when validation fails.  No C++ exception crosses the ABI.
  *   - `layer` = -1 processes every layer in one launch per kernel; then per-
@@ -69,7 +71,8 @@ typedef struct conf_params {
   int32_t window;           /* W: positions (t-W, t] stay 16-bit [storage] */
   int32_t protect;          /* P: positions (t-P, t] are never evicted [ranking]; P <= W */
   int32_t n_high, n_low;    /* budgets for c >= tau and c < tau [budget]; P <= n_high <= n_low */
-  int32_t cap8;             /* INT8 slots per (layer, sequence): multiple of 64, > n_low */
+  int32_t cap8;             /* INT8 slots per (layer, sequence): multiple of 64, > n_low,
+                               cap8 * head_dim <= 2^30 */
   int32_t pyramid;          /* 1: N_l = floor(N (2(L-1)-l) / (2(L-1))) [pyramid]; 0: N_l = N */
   float tau;                /* confidence threshold [budget] */
   float w_H, w_m, w_p;      /* confidence weights; the pages use 0.4, 0.3, 0.3 [confidence] */

@@ -7,6 +7,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 from adaptive_kv_cache_amd import binding
 from adaptive_kv_cache_amd.workloads import WORKLOADS
@@ -80,6 +81,7 @@ def test_layout_sizes(lib):
     (dict(protect=256, n_high=300, pyramid=1), E_INVALID),   # P > pyramid-shrunk n_high
     (dict(cap8=4096), E_CAPACITY),                           # cap8 <= n_low
     (dict(cap8=4100), E_INVALID),                            # not a multiple of 64
+    (dict(cap8=(1 << 23) + 64), E_INVALID),                  # cap8 * head_dim over 2^30
     (dict(vocab=1), E_INVALID),
     (dict(ema_decay=1.5), E_INVALID),
     (dict(s_ema=-0.1), E_INVALID),
@@ -115,6 +117,27 @@ def test_bad_layer_rejected(lib):
                                  fake, null) == E_INVALID
     assert lib.conf_cache_ingest(ctypes.byref(p), ctypes.byref(cache), 0, fake, fake, 40000,
                                  fake, null) == E_CAPACITY
+
+
+@pytest.mark.skipif(torch.cuda.is_available(),
+                    reason="passes fake device pointers: run where no GPU could receive a launch")
+def test_misaligned_pointers_rejected(lib):
+    """The kernels read q, k_new, v_new, the tiles and the absmax rows with 16-byte loads."""
+    p = _p()
+    fake = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1008)
+    cache = binding.ConfCache(*([0x1000] * 14))
+    args = [fake] * 6
+    for i in range(3):                       # q, k_new, v_new
+        a = list(args)
+        a[i] = odd
+        assert lib.conf_decode_attn(ctypes.byref(p), ctypes.byref(cache), -1, *a[:3], fake, fake,
+                                    ctypes.c_void_p(0)) == E_INVALID
+    for field in ("k8", "v8", "k16", "v16", "k_amax", "v_amax"):
+        bad = binding.ConfCache(*([0x1000] * 14))
+        setattr(bad, field, 0x1004)
+        assert lib.conf_decode_attn(ctypes.byref(p), ctypes.byref(bad), -1, fake, fake, fake, fake,
+                                    fake, ctypes.c_void_p(0)) == E_INVALID
 
 
 def test_package_has_no_fallback_path():
