@@ -118,46 +118,86 @@ void launch_ingest(const Dims& dm, const conf_cache& c, int layer0, int nl, int 
 }
 
 // ---------------------------------------------------------------- compaction + demotion
-// One workgroup of 1024 threads per (layer, sequence).
-//  1. Window keep flags exclude the token at position t - W (it is demoted, not
-//     kept in place).  In each region the k-th hole below the new end receives
-//     the k-th survivor above it (both in slot order), so the layout stays dense.
-//  2. Positions and EMAs move; the demotee's metadata lands in INT8 slot n8'.
-//  3. Key/value data of every KV head move the same way.
-//  4. Per (KV head, channel), one thread quantises the demotee under the running
-//     absmax; channels whose absmax grows first requantise their stored codes.
+// One workgroup of 512 threads per (layer, sequence), built to need few global
+// round trips (one token or so moves per step in the steady state):
+//  1. Keep flags are read once (into LDS).  The window flag of the token at
+//     position t - W is cleared: it is demoted, not kept in place.
+//  2. In each region the k-th hole below the new end receives the k-th survivor
+//     above it (both in slot order), so the layout stays dense.  The move lists
+//     come from ballot ranks, in LDS (the workspace holds what does not fit).
+//  3. INT8 moves (data, position, EMA) run while every (KV head, channel, K|V)
+//     thread of the demotion reads its 16-bit value and absmax and works out the
+//     new absmax and code.
+//  4. After a barrier: the demotee's codes and metadata land in INT8 slot n8',
+//     window moves (data, position, EMA; the demotee's window slot has been
+//     read), and channels whose absmax grew requantise their stored codes
+//     (listed in LDS and spread over the workgroup; an overflow of the list is
+//     handled by the owning threads).
 // plan: [0] n8' [1] INT8 moves [2] n16' [3] window moves [4] demotee's window
 //       slot or -1 [5] its INT8 slot or -1  (kept in the workspace for inspection)
-constexpr int kCompThreads = 1024;
+constexpr int kCompThreads = 512;  // every (layer, sequence) workgroup resident at once
 constexpr int kCompWaves = kCompThreads / 64;
-constexpr int kMaxGrown = 512;  // grown channels requantised by the whole workgroup
+constexpr int kMaxGrown = 512;    // grown channels requantised by the whole workgroup
+constexpr int kLdsFlags8 = 8192;  // INT8 keep flags cached in LDS (beyond: re-read)
+constexpr int kLdsFlags16 = 2048; // window keep flags cached in LDS (beyond: workspace)
+constexpr int kLdsMoves = 2048;   // move-list pairs per region kept in LDS (beyond: workspace)
 
-// Ordered ranks of the slots of [lo, hi) whose keep flag equals `want`:
-// out[2*rank + off] = slot.  Returns their number.  Every thread must call it.
-__device__ int rank_slots(int lo, int hi, const uint8_t* keep, bool want, int32_t* out, int off,
-                          int* s_wcnt) {
+struct CompLds {
+  uint8_t k8[kLdsFlags8];
+  uint8_t k16[kLdsFlags16];
+  int mv8[2 * kLdsMoves];   // (source, destination) pairs
+  int mv16[2 * kLdsMoves];
+  int wcnt[2][kCompWaves];
+  int c8[kCompWaves], c16[kCompWaves];
+  int grown[kMaxGrown];
+  float gold[kMaxGrown], gnew[kMaxGrown];
+  int jd, ngrown;
+};
+
+// Ordered ranks of the slots of [0, n) that are holes (slot < nnew, flag 0) or
+// survivors (slot >= nnew, flag 1): hole k -> pair k's destination, survivor k ->
+// its source.  `flag(i)` reads slot i's keep flag.  Every thread must call it.
+template <typename Flag>
+__device__ int build_moves(int n, int nnew, Flag flag, int* lds_mv, int32_t* gl_mv, int (*wcnt)[kCompWaves]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int base = 0;
-  for (int c0 = lo; c0 < hi; c0 += kCompThreads) {
+  int hb = 0, sb = 0;
+  for (int c0 = 0; c0 < n; c0 += kCompThreads) {
     const int i = c0 + tid;
-    const bool f = i < hi && ((keep[i] != 0) == want);
-    const unsigned long long bal = __ballot(f);
-    const int before = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) s_wcnt[wave] = __popcll(bal);
-    __syncthreads();
-    int woff = 0, tot = 0;
-    for (int w = 0; w < kCompWaves; ++w) {
-      const int cw = s_wcnt[w];
-      woff += w < wave ? cw : 0;
-      tot += cw;
+    const bool k = i < n && flag(i);
+    const bool hole = i < nnew && !k, surv = i >= nnew && k;
+    const unsigned long long bh = __ballot(hole), bs = __ballot(surv);
+    const unsigned long long below = (1ull << lane) - 1ull;
+    if (lane == 0) {
+      wcnt[0][wave] = __popcll(bh);
+      wcnt[1][wave] = __popcll(bs);
     }
-    if (f) out[2 * (base + woff + before) + off] = i;
-    base += tot;
+    __syncthreads();
+    int oh = 0, os = 0, th = 0, ts = 0;
+    for (int w = 0; w < kCompWaves; ++w) {
+      const int ch = wcnt[0][w], cs = wcnt[1][w];
+      oh += w < wave ? ch : 0;
+      os += w < wave ? cs : 0;
+      th += ch;
+      ts += cs;
+    }
+    if (hole) {
+      const int r = hb + oh + __popcll(bh & below);
+      if (r < kLdsMoves) lds_mv[2 * r + 1] = i; else gl_mv[2 * r + 1] = i;
+    }
+    if (surv) {
+      const int r = sb + os + __popcll(bs & below);
+      if (r < kLdsMoves) lds_mv[2 * r] = i; else gl_mv[2 * r] = i;
+    }
+    hb += th;
+    sb += ts;
     __syncthreads();
   }
-  return base;
+  return hb;  // holes below the new end = survivors above it
 }
 
+__device__ inline int mv_at(const int* lds_mv, const int32_t* gl_mv, int e) {
+  return e < 2 * kLdsMoves ? lds_mv[e] : gl_mv[e];
+}
 
 __global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dims dm, int layer0,
                                                                const uint8_t* __restrict__ keep_all,
@@ -166,6 +206,7 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dim
                                                                int32_t* __restrict__ mv16_all,
                                                                uint8_t* __restrict__ wkeep_all) {
 #pragma clang fp contract(off)
+  __shared__ CompLds S;
   const int lb = layer0 * dm.B + blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n8 = c.n8[lb], n16 = c.n16[lb], t = c.t[lb];
@@ -179,25 +220,26 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dim
   float* ema16 = c.ema16 + (size_t)lb * dm.cap16;
   int32_t* mv8 = mv8_all + (size_t)lb * dm.cap8;
   int32_t* mv16 = mv16_all + (size_t)lb * dm.cap16;
-  __shared__ int s_wcnt[kCompWaves];
-  __shared__ int s_c8[kCompWaves], s_c16[kCompWaves];
-  __shared__ int s_jd;
-  __shared__ int s_ngrown;
-  __shared__ int s_grown[kMaxGrown];
-  __shared__ float s_gold[kMaxGrown], s_gnew[kMaxGrown];
-  if (tid == 0) s_jd = -1;
+  if (tid == 0) {
+    S.jd = -1;
+    S.ngrown = 0;
+  }
   __syncthreads();
-  // ---- 1. counts, the demotee, window keep flags
+  // ---- 1. keep flags (one read), counts, the demotee
   const int target = t - dm.W;
   int c8 = 0, c16 = 0;
-  for (int i = tid; i < n8; i += kCompThreads) c8 += keep8[i] ? 1 : 0;
+  for (int i = tid; i < n8; i += kCompThreads) {
+    const uint8_t k = keep8[i] ? 1 : 0;
+    if (i < kLdsFlags8) S.k8[i] = k;
+    c8 += k;
+  }
   for (int w = tid; w < n16; w += kCompThreads) {
-    int k = keep16[w] ? 1 : 0;
+    uint8_t k = keep16[w] ? 1 : 0;
     if (k && target >= 0 && pos16[w] == target) {
-      s_jd = w;  // at most one slot holds this position
+      S.jd = w;  // at most one slot holds this position
       k = 0;
     }
-    wkeep[w] = (uint8_t)k;
+    if (w < kLdsFlags16) S.k16[w] = k; else wkeep[w] = k;
     c16 += k;
   }
   for (int off = 32; off > 0; off >>= 1) {
@@ -205,113 +247,216 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dim
     c16 += __shfl_xor(c16, off);
   }
   if (lane == 0) {
-    s_c8[wave] = c8;
-    s_c16[wave] = c16;
+    S.c8[wave] = c8;
+    S.c16[wave] = c16;
   }
   __syncthreads();
   int n8n = 0, n16n = 0;
   for (int w = 0; w < kCompWaves; ++w) {
-    n8n += s_c8[w];
-    n16n += s_c16[w];
+    n8n += S.c8[w];
+    n16n += S.c16[w];
   }
-  const int jd = s_jd;
+  const int jd = S.jd;
   const int dest = (jd >= 0 && n8n < dm.cap8) ? n8n : -1;
+  // ---- 2. move lists
+  const int nm8 = build_moves(
+      n8, n8n, [&](int i) { return i < kLdsFlags8 ? S.k8[i] != 0 : keep8[i] != 0; }, S.mv8, mv8,
+      S.wcnt);
+  const int nm16 = build_moves(
+      n16, n16n, [&](int w) { return w < kLdsFlags16 ? S.k16[w] != 0 : wkeep[w] != 0; }, S.mv16,
+      mv16, S.wcnt);
+  // ---- 3. INT8 moves; the demotion's reads and arithmetic; window-move reads.
+  // Steady state (a move or so per region): every load is issued before any
+  // store, from registers.  Bulk steps (step 0 after a long prefill) loop.
+  const int per = dm.Hkv * D;
+  constexpr int kMv = 2;       // move elements per thread in the register path
+  constexpr int kDemPer = 4;   // (K|V, KV head, channel) triples per thread (<= 2048, host-checked)
+  const bool fast = nm8 * per <= kMv * kCompThreads && nm16 * per <= kMv * kCompThreads &&
+                    nm8 <= kCompThreads && nm16 <= kCompThreads;
+  int8_t mk[kMv], mvv[kMv];
+  uint16_t wk[kMv], wv[kMv];
+  int32_t mp8 = 0, mp16 = 0;
+  float me8 = 0.f, me16 = 0.f;
+  if (fast) {
+#pragma unroll
+    for (int e = 0; e < kMv; ++e) {
+      const int i = tid + e * kCompThreads;
+      if (i < nm8 * per) {
+        const int k = i / per, r = i % per, hk = r / D, ch = r % D;
+        const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap8 * D;
+        const int src = mv_at(S.mv8, mv8, 2 * k);
+        mk[e] = c.k8[ub + k8_off(src, ch, D)];
+        mvv[e] = c.v8[ub + v8_off(src, ch, D)];
+      }
+      if (i < nm16 * per) {
+        const int k = i / per, r = i % per, hk = r / D, ch = r % D;
+        const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap16 * D;
+        const int src = mv_at(S.mv16, mv16, 2 * k);
+        wk[e] = ((const uint16_t*)c.k16)[ub + k16_off(src, ch, D)];
+        wv[e] = ((const uint16_t*)c.v16)[ub + v16_off(src, ch, D)];
+      }
+    }
+    if (tid < nm8) {
+      const int src = mv_at(S.mv8, mv8, 2 * tid);
+      mp8 = pos8[src];
+      me8 = ema8[src];
+    }
+    if (tid < nm16) {
+      const int src = mv_at(S.mv16, mv16, 2 * tid);
+      mp16 = pos16[src];
+      me16 = ema16[src];
+    }
+  } else {
+    for (int k = tid; k < nm8; k += kCompThreads) {
+      const int src = mv_at(S.mv8, mv8, 2 * k), dst = mv_at(S.mv8, mv8, 2 * k + 1);
+      pos8[dst] = pos8[src];
+      ema8[dst] = ema8[src];
+    }
+    for (int i = tid; i < nm8 * per; i += kCompThreads) {
+      const int k = i / per, r = i % per, hk = r / D, ch = r % D;
+      const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap8 * D;
+      const int src = mv_at(S.mv8, mv8, 2 * k), dst = mv_at(S.mv8, mv8, 2 * k + 1);
+      c.k8[ub + k8_off(dst, ch, D)] = c.k8[ub + k8_off(src, ch, D)];
+      c.v8[ub + v8_off(dst, ch, D)] = c.v8[ub + v8_off(src, ch, D)];
+    }
+  }
+  int8_t code[kDemPer];
+  float amax_new[kDemPer], s_old[kDemPer];
+  bool grew[kDemPer], listed[kDemPer];
   int dpos = 0;
   float dema = 0.f;
-  if (jd >= 0) {  // read before the window metadata moves
-    dpos = pos16[jd];
-    dema = ema16[jd];
+  if (dest >= 0) {
+    if (tid == 0) {  // read before the window metadata moves of phase 4
+      dpos = pos16[jd];
+      dema = ema16[jd];
+    }
+#pragma unroll
+    for (int e = 0; e < kDemPer; ++e) {
+      const int pi = tid + e * kCompThreads;
+      grew[e] = false;
+      listed[e] = false;
+      if (pi < 2 * per) {
+        const int kind = pi / per, hc = pi % per, hk = hc / D, ch = hc % D;
+        const size_t u = (size_t)lb * dm.Hkv + hk;
+        const float x = h16_to_f32(
+            kind == 0 ? ((const uint16_t*)c.k16)[u * (size_t)dm.cap16 * D + k16_off(jd, ch, D)]
+                      : ((const uint16_t*)c.v16)[u * (size_t)dm.cap16 * D + v16_off(jd, ch, D)],
+            dm.bf16);
+        const float old = (kind == 0 ? c.k_amax : c.v_amax)[u * D + ch];
+        const float a = fabsf(x);
+        const float am = a > old ? a : old;
+        amax_new[e] = am;
+        code[e] = quant_code(x, am / 127.0f);
+        s_old[e] = old / 127.0f;
+        if (a > old) {
+          grew[e] = true;
+          const int slot = atomicAdd(&S.ngrown, 1);
+          if (slot < kMaxGrown) {
+            listed[e] = true;
+            S.grown[slot] = pi;
+            S.gold[slot] = s_old[e];
+            S.gnew[slot] = am / 127.0f;
+          }
+        }
+      }
+    }
   }
-  // ---- 2. move lists: k-th hole below the new end <- k-th survivor above it
-  const int nm8 = rank_slots(0, n8n, keep8, false, mv8, 1, s_wcnt);
-  rank_slots(n8n, n8, keep8, true, mv8, 0, s_wcnt);
-  const int nm16 = rank_slots(0, n16n, wkeep, false, mv16, 1, s_wcnt);
-  rank_slots(n16n, n16, wkeep, true, mv16, 0, s_wcnt);
-  __syncthreads();  // move lists complete (same workgroup: visible after the barrier)
-  // ---- 3. metadata moves (holes and movers are disjoint slots)
-  for (int k = tid; k < nm8; k += kCompThreads) {
-    const int src = mv8[2 * k], dst = mv8[2 * k + 1];
-    pos8[dst] = pos8[src];
-    ema8[dst] = ema8[src];
+  if (fast) {
+    // INT8 stores go to holes below n8', which no load of this phase reads
+#pragma unroll
+    for (int e = 0; e < kMv; ++e) {
+      const int i = tid + e * kCompThreads;
+      if (i < nm8 * per) {
+        const int k = i / per, r = i % per, hk = r / D, ch = r % D;
+        const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap8 * D;
+        const int dst = mv_at(S.mv8, mv8, 2 * k + 1);
+        c.k8[ub + k8_off(dst, ch, D)] = mk[e];
+        c.v8[ub + v8_off(dst, ch, D)] = mvv[e];
+      }
+    }
+    if (tid < nm8) {
+      const int dst = mv_at(S.mv8, mv8, 2 * tid + 1);
+      pos8[dst] = mp8;
+      ema8[dst] = me8;
+    }
   }
-  for (int k = tid; k < nm16; k += kCompThreads) {
-    const int src = mv16[2 * k], dst = mv16[2 * k + 1];
-    pos16[dst] = pos16[src];
-    ema16[dst] = ema16[src];
-  }
-  // ---- 4. INT8 data of every KV head (slot n8' is free once its mover has left)
-  const int per = dm.Hkv * D;
-  for (int i = tid; i < nm8 * per; i += kCompThreads) {
-    const int k = i / per, r = i % per, hk = r / D, ch = r % D;
-    const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap8 * D;
-    const int src = mv8[2 * k], dst = mv8[2 * k + 1];
-    c.k8[ub + k8_off(dst, ch, D)] = c.k8[ub + k8_off(src, ch, D)];
-    c.v8[ub + v8_off(dst, ch, D)] = c.v8[ub + v8_off(src, ch, D)];
-  }
-  __syncthreads();
-  // ---- 5. demotion into INT8 slot `dest`, read from the untouched window slot jd.
-  // One thread per (KV head, channel) and kind: a = |x|; a new maximum first
-  // requantises that channel's stored codes (slots < n8'), then the token is coded
-  // at the channel's absmax / 127.  Grown channels are listed in LDS and their
-  // codes requantised by the whole workgroup (a list overflow, only possible when
-  // very many channels grow at once, is handled by the owning thread).
+  __syncthreads();  // INT8 moves done, the demotee's window slot read
+  // ---- 4. demotee codes and metadata; window moves; requantisation of grown channels
   if (dest >= 0) {
     if (tid == 0) {
       pos8[dest] = dpos;
       ema8[dest] = dema;
-      s_ngrown = 0;
     }
-    __syncthreads();
-    for (int pi = tid; pi < 2 * per; pi += kCompThreads) {
-      const int kind = pi / per, hc = pi % per, hk = hc / D, ch = hc % D;
-      const size_t u = (size_t)lb * dm.Hkv + hk;
-      const float x = h16_to_f32(
-          kind == 0 ? ((const uint16_t*)c.k16)[u * (size_t)dm.cap16 * D + k16_off(jd, ch, D)]
-                    : ((const uint16_t*)c.v16)[u * (size_t)dm.cap16 * D + v16_off(jd, ch, D)],
-          dm.bf16);
-      int8_t* base = (kind == 0 ? c.k8 : c.v8) + u * (size_t)dm.cap8 * D;
-      float* am = (kind == 0 ? c.k_amax : c.v_amax) + u * D + ch;
-      const float old = *am, a = fabsf(x);
-      const float amax = a > old ? a : old;
-      const float s_new = amax / 127.0f;
-      if (a > old) {
-        *am = amax;
-        const float s_old = old / 127.0f;
-        const int slot = atomicAdd(&s_ngrown, 1);
-        if (slot < kMaxGrown) {
-          s_grown[slot] = pi;
-          s_gold[slot] = s_old;
-          s_gnew[slot] = s_new;
-        } else {
-          for (int tok = 0; tok < n8n; ++tok) {
-            int8_t* p = base + (kind == 0 ? k8_off(tok, ch, D) : v8_off(tok, ch, D));
-            *p = quant_code((float)(*p) * s_old, s_new);
-          }
-        }
+#pragma unroll
+    for (int e = 0; e < kDemPer; ++e) {
+      const int pi = tid + e * kCompThreads;
+      if (pi < 2 * per) {
+        const int kind = pi / per, hc = pi % per, hk = hc / D, ch = hc % D;
+        const size_t u = (size_t)lb * dm.Hkv + hk;
+        int8_t* base = (kind == 0 ? c.k8 : c.v8) + u * (size_t)dm.cap8 * D;
+        base[kind == 0 ? k8_off(dest, ch, D) : v8_off(dest, ch, D)] = code[e];
+        if (grew[e]) (kind == 0 ? c.k_amax : c.v_amax)[u * D + ch] = amax_new[e];
       }
-      base[kind == 0 ? k8_off(dest, ch, D) : v8_off(dest, ch, D)] = quant_code(x, s_new);
     }
-    __syncthreads();
-    const int ng = min(s_ngrown, kMaxGrown);
-    for (int i = tid; i < ng * n8n; i += kCompThreads) {
-      const int e = i % ng, tok = i / ng;
-      const int pi = s_grown[e], kind = pi / per, hc = pi % per, hk = hc / D, ch = hc % D;
+  }
+  if (fast) {
+#pragma unroll
+    for (int e = 0; e < kMv; ++e) {
+      const int i = tid + e * kCompThreads;
+      if (i < nm16 * per) {
+        const int k = i / per, r = i % per, hk = r / D, ch = r % D;
+        const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap16 * D;
+        const int dst = mv_at(S.mv16, mv16, 2 * k + 1);
+        ((uint16_t*)c.k16)[ub + k16_off(dst, ch, D)] = wk[e];
+        ((uint16_t*)c.v16)[ub + v16_off(dst, ch, D)] = wv[e];
+      }
+    }
+    if (tid < nm16) {
+      const int dst = mv_at(S.mv16, mv16, 2 * tid + 1);
+      pos16[dst] = mp16;
+      ema16[dst] = me16;
+    }
+  } else {
+    for (int k = tid; k < nm16; k += kCompThreads) {
+      const int src = mv_at(S.mv16, mv16, 2 * k), dst = mv_at(S.mv16, mv16, 2 * k + 1);
+      pos16[dst] = pos16[src];
+      ema16[dst] = ema16[src];
+    }
+    for (int i = tid; i < nm16 * per; i += kCompThreads) {
+      const int k = i / per, r = i % per, hk = r / D, ch = r % D;
+      const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap16 * D;
+      const int src = mv_at(S.mv16, mv16, 2 * k), dst = mv_at(S.mv16, mv16, 2 * k + 1);
+      uint16_t* k16 = (uint16_t*)c.k16 + ub;
+      uint16_t* v16 = (uint16_t*)c.v16 + ub;
+      k16[k16_off(dst, ch, D)] = k16[k16_off(src, ch, D)];
+      v16[v16_off(dst, ch, D)] = v16[v16_off(src, ch, D)];
+    }
+  }
+  if (dest >= 0) {
+    // codes of slots < n8' of every grown channel: c = clamp(rne((c * s_old) / s_new))
+    const int ng = S.ngrown;
+    const int ngl = ng < kMaxGrown ? ng : kMaxGrown;
+    for (int i = tid; i < ngl * n8n; i += kCompThreads) {
+      const int e = i % ngl, tok = i / ngl;
+      const int pi = S.grown[e], kind = pi / per, hc = pi % per, hk = hc / D, ch = hc % D;
       const size_t u = (size_t)lb * dm.Hkv + hk;
       int8_t* p = (kind == 0 ? c.k8 + u * (size_t)dm.cap8 * D + k8_off(tok, ch, D)
                              : c.v8 + u * (size_t)dm.cap8 * D + v8_off(tok, ch, D));
-      *p = quant_code((float)(*p) * s_gold[e], s_gnew[e]);
+      *p = quant_code((float)(*p) * S.gold[e], S.gnew[e]);
     }
-  }
-  __syncthreads();
-  // ---- 6. window data of every KV head
-  for (int i = tid; i < nm16 * per; i += kCompThreads) {
-    const int k = i / per, r = i % per, hk = r / D, ch = r % D;
-    const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap16 * D;
-    const int src = mv16[2 * k], dst = mv16[2 * k + 1];
-    uint16_t* k16 = (uint16_t*)c.k16 + ub;
-    uint16_t* v16 = (uint16_t*)c.v16 + ub;
-    k16[k16_off(dst, ch, D)] = k16[k16_off(src, ch, D)];
-    v16[v16_off(dst, ch, D)] = v16[v16_off(src, ch, D)];
+    // a list overflow (very many channels grew at once): the owner requantises
+#pragma unroll
+    for (int e = 0; e < kDemPer; ++e) {
+      if (!grew[e] || listed[e]) continue;
+      const int pi = tid + e * kCompThreads;
+      const int kind = pi / per, hc = pi % per, hk = hc / D, ch = hc % D;
+      int8_t* base = (kind == 0 ? c.k8 : c.v8) + ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap8 * D;
+      const float s_new = amax_new[e] / 127.0f;
+      for (int tok = 0; tok < n8n; ++tok) {
+        int8_t* q = base + (kind == 0 ? k8_off(tok, ch, D) : v8_off(tok, ch, D));
+        *q = quant_code((float)(*q) * s_old[e], s_new);
+      }
+    }
   }
   if (tid == 0) {
     int32_t* pl = plan_all + (size_t)lb * 16;

@@ -51,7 +51,8 @@ typedef void* conf_stream_t; /* hipStream_t */
 enum {
   CONF_OK = 0,
   CONF_E_INVALID = -1,     /* null pointer, inconsistent sizes, P > W, P > budget, ... */
-  CONF_E_UNSUPPORTED = -2, /* head_dim not 64/128, group > 16, unknown dtype */
+  CONF_E_UNSUPPORTED = -2, /* head_dim not 64/128, group > 16, n_kv_heads * head_dim > 2048,
+                              unknown dtype */
   CONF_E_CAPACITY = -3,    /* cap8 too small for the budgets or the prefill */
   CONF_E_HIP = -4          /* a HIP launch failed; see conf_last_error() */
 };

@@ -105,6 +105,12 @@ def tiny_workloads() -> dict:
         name="gqa16_f16_d128", n_layers=1, batch=1, n_q_heads=16, n_kv_heads=1, head_dim=128,
         vocab=777, dtype16="f16", window=33, protect=5, n_high=40, n_low=90, prefill=200,
         steps=30)
+    # from empty with 2 x 8 x 128 (K|V, KV head, channel) triples: the early demotions grow
+    # more than 512 channels of a non-empty INT8 region (the requantisation list overflows)
+    w["mha_bf16_d128_empty"] = Workload(
+        name="mha_bf16_d128_empty", n_layers=1, batch=2, n_q_heads=8, n_kv_heads=8, head_dim=128,
+        vocab=500, dtype16="bf16", window=24, protect=6, n_high=40, n_low=70, prefill=0,
+        steps=150)
     # more scores than the LDS holds at the first step: exercises the two-pass path
     w["gqa16_bf16_d64_long"] = Workload(
         name="gqa16_bf16_d64_long", n_layers=1, batch=2, n_q_heads=16, n_kv_heads=1, head_dim=64,

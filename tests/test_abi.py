@@ -81,6 +81,7 @@ def test_layout_sizes(lib):
     (dict(protect=256, n_high=300, pyramid=1), E_INVALID),   # P > pyramid-shrunk n_high
     (dict(cap8=4096), E_CAPACITY),                           # cap8 <= n_low
     (dict(cap8=4100), E_INVALID),                            # not a multiple of 64
+    (dict(n_q_heads=32, n_kv_heads=32), E_UNSUPPORTED),      # KV heads x head_dim over 2048
     (dict(cap8=(1 << 23) + 64), E_INVALID),                  # cap8 * head_dim over 2^30
     (dict(vocab=1), E_INVALID),
     (dict(ema_decay=1.5), E_INVALID),
