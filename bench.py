@@ -153,8 +153,8 @@ def run(args):
     conf = torch.empty(total, B, dtype=torch.float32, device=dev)
     budget = torch.empty(total, B, L, dtype=torch.int32, device=dev)
     keep = torch.zeros(L, B, eng.cap8 + eng.cap16, dtype=torch.uint8, device=dev)
-    hist8 = torch.empty(args.steps, L, B, dtype=torch.int32, device=dev)
-    hist16 = torch.empty_like(hist8)
+    n8_first = torch.empty(L, B, dtype=torch.int32, device=dev)
+    n16_first = torch.empty_like(n8_first)
     plan_off = _plan_offset(eng)
     hplan = torch.empty(args.steps, L, B, 16, dtype=torch.int32, device=dev)
     ws_plan = eng.ws[plan_off:plan_off + L * B * 16 * 4].view(torch.int32).view(L, B, 16)
@@ -162,9 +162,6 @@ def run(args):
     log("inputs resident; warm-up")
 
     def one_step(s, ev=None, i=None):
-        if i is not None:
-            hist8[i].copy_(eng.t_n8)
-            hist16[i].copy_(eng.t_n16)
         if ev is not None:
             ev[0].record()
         eng.decode_attn(-1, qs[s], ks[s], vs[s], out=out)
@@ -186,6 +183,9 @@ def run(args):
            for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"timed: {args.steps} steps")
+    # the sizes before the first timed step; later ones follow from each step's plan
+    n8_first.copy_(eng.t_n8)
+    n16_first.copy_(eng.t_n16)
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
@@ -197,12 +197,16 @@ def run(args):
     st = eng.status()
     if st:
         raise RuntimeError(f"cache status word {st}: a capacity was exceeded")
-    h8, h16, hp = hist8.cpu().long(), hist16.cpu().long(), hplan.cpu().long()
-    # the plan copied from the workspace must describe the cache the step left
-    n8_after = hp[-1][..., 0] + (hp[-1][..., 5] >= 0).long()
-    if not (torch.equal(n8_after, eng.t_n8.cpu().long())
-            and torch.equal(hp[-1][..., 2], eng.t_n16.cpu().long())):
+    hp = hplan.cpu().long()
+    # sizes after each step: n8 = plan n8' (+1 if a token was demoted), n16 = plan n16'
+    n8_after = hp[..., 0] + (hp[..., 5] >= 0).long()
+    n16_after = hp[..., 2]
+    # the plan copied from the workspace must describe the cache the last step left
+    if not (torch.equal(n8_after[-1], eng.t_n8.cpu().long())
+            and torch.equal(n16_after[-1], eng.t_n16.cpu().long())):
         raise RuntimeError("workspace plan offset does not match the library's layout")
+    h8 = torch.cat([n8_first.cpu().long()[None], n8_after[:-1]])
+    h16 = torch.cat([n16_first.cpu().long()[None], n16_after[:-1]])
     a_bytes = [attn_bytes(wl, h8[i], h16[i]) for i in range(args.steps)]
     s_bytes = [step_bytes(wl, h8[i], h16[i], hp[i]) for i in range(args.steps)]
     attn_avg_ms = sum(attn_ms) / len(attn_ms)
@@ -213,7 +217,8 @@ def run(args):
     res = {
         "metric": METRIC, "value": round(sps, 3), "unit": "steps/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms / args.steps, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": f"int8+{wl.dtype16} operands, f32 accumulate",
         "data": "synthetic",
         "config": {"workload": wl.name, "layers": L, "batch": B, "q_heads": wl.n_q_heads,
                    "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "dtype16": wl.dtype16,
@@ -222,7 +227,8 @@ def run(args):
                    "vocab": wl.vocab, "mean_tokens_attended": round(n_mean, 1)},
         "roofline": {"bound": "hbm", "kernel": "conf_decode_attn (one launch)",
                      "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": stored_traffic(wl.name),
                      "avg_launch_us": round(attn_avg_ms * 1e3, 2),
                      "alg_bytes_per_launch": int(sum(a_bytes) / len(a_bytes))},
         "step_roofline": {"achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -267,6 +273,68 @@ def rocpd_summary(db_path, timed_steps):
     return "\n".join(lines)
 
 
+# ---------------------------------------------------------------- counters
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_qwen32b_b8_32k.md")
+ATTN_SOURCES = ("adaptive_kv_cache_amd/csrc/k_attn.hip", "adaptive_kv_cache_amd/csrc/common.hpp")
+
+
+def attn_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload):
+    """HBM bytes per conf_decode_attn launch from the committed counter summary, or
+    None when it is missing, for another workload, or taken on other kernel source."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        if line.startswith("traffic:"):
+            for kv in line[len("traffic:"):].split():
+                k, _, v = kv.partition("=")
+                vals[k] = v
+    if vals.get("workload") != workload or vals.get("source") != attn_source_hash():
+        return None
+    return int(vals["bytes_per_launch"])
+
+
+def copy_calibration(mib, reps):
+    """A plain copy kernel of known size (reads and writes `mib` MiB each time), run
+    under a counter pass to scale FETCH_SIZE / WRITE_SIZE to bytes."""
+    dev = torch.device("cuda", 0)
+    n = mib * (1 << 20) // 4
+    src = torch.randn(n, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4,
+                      "reps": reps}))
+
+
+def pmc_summary(csv_path, last):
+    """Mean counter value per dispatch of each kernel (its last `last` dispatches)
+    from a rocprofv3 --pmc counter_collection.csv."""
+    import csv
+    per = {}
+    with open(csv_path) as fh:
+        for row in csv.DictReader(fh):
+            name = row["Kernel_Name"].split("(")[0].replace("void ", "").replace("confkv::", "")
+            per.setdefault((name[:70], row["Counter_Name"]), []).append(float(row["Counter_Value"]))
+    lines = [f"{'kernel':70s} {'counter':12s} {'dispatches':>10s} {'mean_last':>14s}"]
+    for (k, ctr), v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        tail = v[-last:]
+        lines.append(f"{k:70s} {ctr:12s} {len(v):10d} {sum(tail) / len(tail):14.1f}")
+    return "\n".join(lines)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,9 +346,19 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--rocpd-summary", metavar="DB",
                     help="print per-kernel durations of a rocprofv3 database and exit")
+    ap.add_argument("--pmc-summary", metavar="CSV",
+                    help="print per-kernel mean counter values of a rocprofv3 --pmc csv and exit")
+    ap.add_argument("--copy-calibration", metavar="MIB", type=int,
+                    help="run a plain copy kernel of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.rocpd_summary:
         print(rocpd_summary(args.rocpd_summary, args.steps))
+        return
+    if args.pmc_summary:
+        print(pmc_summary(args.pmc_summary, args.steps))
+        return
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, 8)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "

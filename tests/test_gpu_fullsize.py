@@ -1,0 +1,111 @@
+"""Full-size parity on sampled (layer, sequence) pairs.
+
+The Qwen-32B-shaped cache the benchmark runs: 64 layers, 40 query / 8 KV heads,
+head_dim 128, bf16, batch 8, a 32768-token prefill with the planted needle,
+budgets 2048 / 4096, P 256, W 512.  The library is driven exactly as the
+benchmark drives it: every layer and sequence in one launch per kernel, the
+benchmark's seed.  The oracle cannot run all 512 (layer, sequence) pairs, so it
+re-runs sampled pairs one by one from a snapshot of their device state
+(teacher forcing), at three kinds of step:
+  * step 0: the one-off cut of the prefilled 32769 tokens to the budget (the
+    scores exceed the LDS, so the kernel takes its two-pass path);
+  * step 1: a loose-budget step with 4097 tokens (also two-pass);
+  * step 66: after the first confident phase, about 2050 tokens (single pass,
+    scores in LDS), the steady state the benchmark times.
+Tolerances are those of the small-shape parity tests.  Confidence and budgets are
+checked for every sequence at every checked step.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from adaptive_kv_cache_amd import synth
+from adaptive_kv_cache_amd.binding import Engine
+from adaptive_kv_cache_amd.workloads import WORKLOADS
+from parity_util import (assert_same_state, attn_rel_err, bits16, ema_by_pos, kept_positions,
+                         oracle_params, to_oracle_state)
+
+pytestmark = pytest.mark.gpu
+
+ATTN_TOL = 2e-3
+C_TOL = 1e-5
+EMA_RTOL = 1e-5
+SEED = 0                                   # the benchmark's seed
+SAMPLES = [(0, 0), (37, 5), (63, 7)]       # (layer, sequence)
+CHECKED = (0, 1, 66)
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _check_conf(c_gpu, budget_gpu, z, wl):
+    for b in range(z.shape[0]):
+        ref = O.confidence(z[b], wl.w_H, wl.w_m, wl.w_p)["c"]
+        assert abs(float(c_gpu[b]) - ref) <= C_TOL, (b, float(c_gpu[b]), ref)
+        N = O.budget(ref, wl.tau, wl.n_high, wl.n_low)
+        if abs(ref - wl.tau) <= C_TOL:
+            N = wl.n_high if c_gpu[b] >= wl.tau else wl.n_low
+        assert list(budget_gpu[b]) == [O.layer_budget(N, l, wl.n_layers, wl.pyramid)
+                                       for l in range(wl.n_layers)]
+
+
+def test_qwen32b_b8_32k_sampled_pairs():
+    wl = WORKLOADS["qwen32b_gqa_b8_32k"]
+    prm = oracle_params(wl)
+    dev = torch.device("cuda", 0)
+    _say("full size: allocating and ingesting", wl.name)
+    eng = Engine(wl, dev)
+    for l in range(wl.n_layers):
+        k, v = synth.prefill_kv(wl, l, SEED, device=dev)
+        eng.ingest(l, k, v)
+        if l in {s[0] for s in SAMPLES}:
+            # the ingest itself, for the sampled pairs
+            for (sl, b) in SAMPLES:
+                if sl != l:
+                    continue
+                ref = O.ingest(bits16(k[b]), bits16(v[b]), wl.window, wl.dtype16)
+                assert_same_state(to_oracle_state(eng.export(l, b), wl.dtype16), ref,
+                                  ema_rtol=0, what=("ingest", l, b))
+        del k, v
+    worst = 0.0
+    for step in range(max(CHECKED) + 1):
+        check = step in CHECKED
+        z = synth.logits(wl, step, SEED, device=dev)
+        q = synth.q_new(wl, step, SEED, device=dev)
+        k, v = synth.kv_new(wl, step, SEED, device=dev)
+        S0 = {s: eng.export(*s) for s in SAMPLES} if check else None
+        out = eng.decode_attn(-1, q, k, v)
+        S1 = {s: eng.export(*s) for s in SAMPLES} if check else None
+        c, budget = eng.confidence(z)
+        keep = eng.rank_evict(-1, budget)
+        eng.compact_demote(-1, keep)
+        if not check:
+            continue
+        _say("  checking step", step)
+        S2 = {s: eng.export(*s) for s in SAMPLES}
+        budget_h = budget.cpu().numpy()
+        _check_conf(c.cpu().numpy(), budget_h, z.cpu().numpy().astype(np.float64), wl)
+        keep_h = keep.cpu().numpy()
+        out_h = out.cpu().numpy()
+        qb, kb, vb = bits16(q), bits16(k), bits16(v)
+        for (l, b) in SAMPLES:
+            what = (wl.name, step, l, b)
+            st = to_oracle_state(S0[(l, b)], wl.dtype16)
+            new_pos = np.append(st.pos, st.t + 1)
+            e_gpu = ema_by_pos(S1[(l, b)])
+            override = np.array([e_gpu[p] for p in new_pos.tolist()], np.float32)
+            r = O.step_layer(st, qb[l, b], kb[l, b], vb[l, b], int(budget_h[b, l]), prm,
+                             ema32_override=override)
+            err = attn_rel_err(out_h[l, b], r["o"])
+            worst = max(worst, err)
+            assert err <= ATTN_TOL, (what, err)
+            np.testing.assert_allclose(override, r["ema"], rtol=EMA_RTOL, atol=1e-12,
+                                       err_msg=str(what))
+            assert kept_positions(S1[(l, b)], keep_h[l, b], eng.cap8) == \
+                set(new_pos[r["keep"]].tolist()), what
+            assert_same_state(to_oracle_state(S2[(l, b)], wl.dtype16), st, ema_rtol=0, what=what)
+            _say(f"    {what}: n={len(new_pos)} attention rel err {err:.2e}")
+    assert eng.status() == 0
+    _say("  worst attention rel err", worst)
