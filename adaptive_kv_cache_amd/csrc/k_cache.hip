@@ -123,18 +123,20 @@ void launch_ingest(const Dims& dm, const conf_cache& c, int layer0, int nl, int 
 //  1. Keep flags are read once (into LDS).  The window flag of the token at
 //     position t - W is cleared: it is demoted, not kept in place.
 //  2. In each region the k-th hole below the new end receives the k-th survivor
-//     above it (both in slot order), so the layout stays dense.  The move lists
-//     come from ballot ranks, in LDS (the workspace holds what does not fit).
+//     above it (both in slot order), so the layout stays dense; a demotee takes
+//     the first INT8 hole itself.  The move lists come from ballot ranks, in LDS
+//     (the workspace holds what does not fit).
 //  3. INT8 moves (data, position, EMA) run while every (KV head, channel, K|V)
 //     thread of the demotion reads its 16-bit value and absmax and works out the
 //     new absmax and code.
-//  4. After a barrier: the demotee's codes and metadata land in INT8 slot n8',
+//  4. After a barrier: the demotee's codes and metadata land in its INT8 slot,
 //     window moves (data, position, EMA; the demotee's window slot has been
 //     read), and channels whose absmax grew requantise their stored codes
 //     (listed in LDS and spread over the workgroup; an overflow of the list is
 //     handled by the owning threads).
-// plan: [0] n8' [1] INT8 moves [2] n16' [3] window moves [4] demotee's window
-//       slot or -1 [5] its INT8 slot or -1  (kept in the workspace for inspection)
+// plan: [0] n8' (kept INT8 tokens) [1] INT8 moves [2] n16' [3] window moves
+//       [4] demotee's window slot or -1 [5] its INT8 slot or -1  (kept in the
+//       workspace for inspection; the INT8 region ends at n8' + (demoted))
 constexpr int kCompThreads = 512;  // every (layer, sequence) workgroup resident at once
 constexpr int kCompWaves = kCompThreads / 64;
 constexpr int kMaxGrown = 512;    // grown channels requantised by the whole workgroup
@@ -151,17 +153,22 @@ struct CompLds {
   int c8[kCompWaves], c16[kCompWaves];
   int grown[kMaxGrown];
   float gold[kMaxGrown], gnew[kMaxGrown];
-  int jd, ngrown;
+  int jd, ngrown, first_hole;
 };
 
-// Ordered ranks of the slots of [0, n) that are holes (slot < nnew, flag 0) or
-// survivors (slot >= nnew, flag 1): hole k -> pair k's destination, survivor k ->
-// its source.  `flag(i)` reads slot i's keep flag.  Every thread must call it.
+// Ordered ranks of the slots of [0, max(n, nnew)) that are holes (slot < nnew,
+// not kept; slots >= n count as not kept) or survivors (slot >= nnew, kept).  The
+// first `skip` holes are set aside (the first one's slot goes to *first_hole);
+// hole skip + k receives survivor k: pair k = (survivor k, hole skip + k).
+// `flag(i)` reads slot i's keep flag (i < n).  Returns the number of pairs.
+// Every thread must call it.
 template <typename Flag>
-__device__ int build_moves(int n, int nnew, Flag flag, int* lds_mv, int32_t* gl_mv, int (*wcnt)[kCompWaves]) {
+__device__ int build_moves(int n, int nnew, int skip, Flag flag, int* lds_mv, int32_t* gl_mv,
+                           int (*wcnt)[kCompWaves], int* first_hole) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int end = n > nnew ? n : nnew;
   int hb = 0, sb = 0;
-  for (int c0 = 0; c0 < n; c0 += kCompThreads) {
+  for (int c0 = 0; c0 < end; c0 += kCompThreads) {
     const int i = c0 + tid;
     const bool k = i < n && flag(i);
     const bool hole = i < nnew && !k, surv = i >= nnew && k;
@@ -181,8 +188,14 @@ __device__ int build_moves(int n, int nnew, Flag flag, int* lds_mv, int32_t* gl_
       ts += cs;
     }
     if (hole) {
-      const int r = hb + oh + __popcll(bh & below);
-      if (r < kLdsMoves) lds_mv[2 * r + 1] = i; else gl_mv[2 * r + 1] = i;
+      const int r = hb + oh + __popcll(bh & below) - skip;
+      if (r < 0) {
+        if (r == -skip) *first_hole = i;
+      } else if (r < kLdsMoves) {
+        lds_mv[2 * r + 1] = i;
+      } else {
+        gl_mv[2 * r + 1] = i;
+      }
     }
     if (surv) {
       const int r = sb + os + __popcll(bs & below);
@@ -192,7 +205,7 @@ __device__ int build_moves(int n, int nnew, Flag flag, int* lds_mv, int32_t* gl_
     sb += ts;
     __syncthreads();
   }
-  return hb;  // holes below the new end = survivors above it
+  return hb - skip;  // holes below the new end, less those set aside = survivors above it
 }
 
 __device__ inline int mv_at(const int* lds_mv, const int32_t* gl_mv, int e) {
@@ -257,14 +270,19 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dim
     n16n += S.c16[w];
   }
   const int jd = S.jd;
-  const int dest = (jd >= 0 && n8n < dm.cap8) ? n8n : -1;
-  // ---- 2. move lists
+  // ---- 2. move lists.  With a demotee, the INT8 region grows to n8' + 1 and the
+  // demotee takes its first hole (in the steady state: the slot of the evicted
+  // INT8 token, so nothing moves); without one it ends at n8'.
+  const bool demote = jd >= 0 && n8n < dm.cap8;
+  const int n8end = n8n + (demote ? 1 : 0);
   const int nm8 = build_moves(
-      n8, n8n, [&](int i) { return i < kLdsFlags8 ? S.k8[i] != 0 : keep8[i] != 0; }, S.mv8, mv8,
-      S.wcnt);
+      n8, n8end, demote ? 1 : 0,
+      [&](int i) { return i < kLdsFlags8 ? S.k8[i] != 0 : keep8[i] != 0; }, S.mv8, mv8, S.wcnt,
+      &S.first_hole);
   const int nm16 = build_moves(
-      n16, n16n, [&](int w) { return w < kLdsFlags16 ? S.k16[w] != 0 : wkeep[w] != 0; }, S.mv16,
-      mv16, S.wcnt);
+      n16, n16n, 0, [&](int w) { return w < kLdsFlags16 ? S.k16[w] != 0 : wkeep[w] != 0; },
+      S.mv16, mv16, S.wcnt, &S.first_hole);
+  const int dest = demote ? S.first_hole : -1;  // written by build_moves before its last barrier
   // ---- 3. INT8 moves; the demotion's reads and arithmetic; window-move reads.
   // Steady state (a move or so per region): every load is issued before any
   // store, from registers.  Bulk steps (step 0 after a long prefill) loop.
@@ -433,11 +451,12 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dim
     }
   }
   if (dest >= 0) {
-    // codes of slots < n8' of every grown channel: c = clamp(rne((c * s_old) / s_new))
+    // codes of every other INT8 slot of each grown channel: c = clamp(rne((c * s_old) / s_new))
     const int ng = S.ngrown;
     const int ngl = ng < kMaxGrown ? ng : kMaxGrown;
-    for (int i = tid; i < ngl * n8n; i += kCompThreads) {
+    for (int i = tid; i < ngl * n8end; i += kCompThreads) {
       const int e = i % ngl, tok = i / ngl;
+      if (tok == dest) continue;
       const int pi = S.grown[e], kind = pi / per, hc = pi % per, hk = hc / D, ch = hc % D;
       const size_t u = (size_t)lb * dm.Hkv + hk;
       int8_t* p = (kind == 0 ? c.k8 + u * (size_t)dm.cap8 * D + k8_off(tok, ch, D)
@@ -452,7 +471,8 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dim
       const int kind = pi / per, hc = pi % per, hk = hc / D, ch = hc % D;
       int8_t* base = (kind == 0 ? c.k8 : c.v8) + ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap8 * D;
       const float s_new = amax_new[e] / 127.0f;
-      for (int tok = 0; tok < n8n; ++tok) {
+      for (int tok = 0; tok < n8end; ++tok) {
+        if (tok == dest) continue;
         int8_t* q = base + (kind == 0 ? k8_off(tok, ch, D) : v8_off(tok, ch, D));
         *q = quant_code((float)(*q) * s_old[e], s_new);
       }
@@ -467,7 +487,7 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dim
     pl[4] = jd;
     pl[5] = dest;
     if (jd >= 0 && dest < 0) atomicOr(c.status, (int)CONF_ST_INT8_FULL);
-    c.n8[lb] = n8n + (dest >= 0 ? 1 : 0);
+    c.n8[lb] = n8end;
     c.n16[lb] = n16n;
   }
 }
