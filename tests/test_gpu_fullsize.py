@@ -1,19 +1,20 @@
-"""Full-size parity on sampled (layer, sequence) pairs.
+"""Full-size parity on sampled (layer, sequence) pairs, for every workload shape.
 
-The Qwen-32B-shaped cache the benchmark runs: 64 layers, 40 query / 8 KV heads,
-head_dim 128, bf16, batch 8, a 32768-token prefill with the planted needle,
-budgets 2048 / 4096, P 256, W 512.  The library is driven exactly as the
-benchmark drives it: every layer and sequence in one launch per kernel, the
-benchmark's seed.  The oracle cannot run all 512 (layer, sequence) pairs, so it
-re-runs sampled pairs one by one from a snapshot of their device state
-(teacher forcing), at three kinds of step:
+Each workload runs at its full size, exactly as the benchmark drives the library:
+every layer and sequence in one launch per kernel.  The oracle cannot run every
+(layer, sequence) pair, so it re-runs sampled pairs one by one from a snapshot of
+their device state (teacher forcing) at chosen steps.  The steps of the
+Qwen-32B-shaped batch-8 cache (the benchmark's) are the three kinds a decode
+step can be:
   * step 0: the one-off cut of the prefilled 32769 tokens to the budget (the
     scores exceed the LDS, so the kernel takes its two-pass path);
   * step 1: a loose-budget step with 4097 tokens (also two-pass);
   * step 66: after the first confident phase, about 2050 tokens (single pass,
     scores in LDS), the steady state the benchmark times.
-Tolerances are those of the small-shape parity tests.  Confidence and budgets are
-checked for every sequence at every checked step.
+The caches that start empty are checked at their first demotion into INT8, at
+the first eviction and deep into their sawtooth.  Tolerances are those of the
+small-shape parity tests.  Confidence and budgets are checked for every sequence
+at every checked step.
 """
 import numpy as np
 import pytest
@@ -32,8 +33,15 @@ ATTN_TOL = 2e-3
 C_TOL = 1e-5
 EMA_RTOL = 1e-5
 SEED = 0                                   # the benchmark's seed
-SAMPLES = [(0, 0), (37, 5), (63, 7)]       # (layer, sequence)
-CHECKED = (0, 1, 66)
+# workload -> ((layer, sequence) samples, checked steps)
+CASES = {
+    "qwen32b_gqa_b8_32k": ([(0, 0), (37, 5), (63, 7)], (0, 1, 66)),
+    "qwen32b_gqa_b1_32k": ([(0, 0), (63, 0)], (0, 66)),
+    "qwen14b_gqa_b8_8k": ([(0, 3), (47, 6)], (0, 1, 66)),
+    "gptoss20b_gqa_b32_16k": ([(0, 0), (23, 31), (11, 17)], (0, 1, 40)),
+    "gpt2_1layer_b1": ([(0, 0)], (129, 600, 2047)),
+    "gpt2_12layer_b8_pyramid": ([(0, 0), (11, 7), (5, 3)], (129, 700, 1500)),
+}
 
 
 def _say(*a):
@@ -51,13 +59,15 @@ def _check_conf(c_gpu, budget_gpu, z, wl):
                                        for l in range(wl.n_layers)]
 
 
-def test_qwen32b_b8_32k_sampled_pairs():
-    wl = WORKLOADS["qwen32b_gqa_b8_32k"]
+@pytest.mark.parametrize("name", list(CASES))
+def test_full_size_sampled_pairs(name):
+    wl = WORKLOADS[name]
+    SAMPLES, CHECKED = CASES[name]
     prm = oracle_params(wl)
     dev = torch.device("cuda", 0)
     _say("full size: allocating and ingesting", wl.name)
     eng = Engine(wl, dev)
-    for l in range(wl.n_layers):
+    for l in range(wl.n_layers if wl.prefill else 0):
         k, v = synth.prefill_kv(wl, l, SEED, device=dev)
         eng.ingest(l, k, v)
         if l in {s[0] for s in SAMPLES}:
@@ -109,3 +119,5 @@ def test_qwen32b_b8_32k_sampled_pairs():
             _say(f"    {what}: n={len(new_pos)} attention rel err {err:.2e}")
     assert eng.status() == 0
     _say("  worst attention rel err", worst)
+    del eng, out, keep, q, k, v, z
+    torch.cuda.empty_cache()
