@@ -345,10 +345,10 @@ __device__ inline void softmax_item(const f4* acc, float scale, bool head_ok, co
 }
 
 template <int D, bool BF16, int MODE>
-__device__ inline void compute_item(const Item& I, const Buf<D>& K, const Buf<D>& V,
+__device__ inline void compute_item(const Item& I, Buf<D>& K, const Buf<D>& V,
                                     const QOps<D, BF16>& q, float scale8, float scale16,
                                     bool head_ok, WaveAcc<D>& wa, float* sc, int stride, float lse,
-                                    float* massp) {
+                                    float* massp, rsrc_t kr, uint32_t koff, int klane) {
   // Re-read the query operands from LDS for every item instead of letting the
   // compiler hoist 48 registers' worth of them out of the item loop.
   QOps<D, BF16> ql = q;
@@ -356,6 +356,7 @@ __device__ inline void compute_item(const Item& I, const Buf<D>& K, const Buf<D>
   if (I.i8) {
     f4 acc[4];
     scores_i8<D, BF16>(K, ql, acc);
+    load_run_rs<D>(kr, koff, klane, K);  // the keys are used: the next item's start loading
     float p[4][4];
     softmax_item<4, MODE, D>(acc, scale8, head_ok, I, wa, sc, stride, lse, massp, p);
     __builtin_amdgcn_sched_barrier(0);
@@ -363,6 +364,7 @@ __device__ inline void compute_item(const Item& I, const Buf<D>& K, const Buf<D>
   } else {
     f4 acc[2];
     scores_16<D, BF16>(K, ql, acc);
+    load_run_rs<D>(kr, koff, klane, K);
     float p[2][4];
     softmax_item<2, MODE, D>(acc, scale16, head_ok, I, wa, sc, stride, lse, massp, p);
     __builtin_amdgcn_sched_barrier(0);
@@ -379,8 +381,12 @@ __device__ inline void apply_vscale(WaveAcc<D>& wa, const float* sv) {
 }
 
 // One pass of a wavefront over its items (it = wave, wave + 4, ...), software
-// pipelined: while item i computes, its values and the keys of item i+1 load.
-// The key buffers alternate (two stages per loop trip, no register copies).
+// pipelined on one key and one value buffer: an item's values load from the
+// start of its stage, and the next item's keys as soon as this item's scores
+// are formed.  The key load is issued for every stage (an item past the end
+// reads at kNoItem), so no branch surrounds a load.  With non-temporal loads the
+// kernel runs as fast as a copy of it with the arithmetic removed, and a second
+// key buffer (a stage more of key prefetch) measured no faster.
 // `kb` holds (or is receiving) the keys of item `wave` if `preloaded`.
 struct UnitRs {
   rsrc_t k8, v8, k16, v16;  // the unit's four regions
@@ -400,33 +406,25 @@ __device__ inline void wave_pass(int nitems, int nb8, int n8, int nw, int cap8, 
   if (!preloaded)
     load_run_rs<D>(wave < nb8 ? rs.k8 : rs.k16, (uint32_t)(wave < nb8 ? wave : wave - nb8) * ib,
                    klane, kb);
-  Buf<D> V, kn;
+  Buf<D> V;
   int it = wave;
-#define CONFKV_STAGE(KC, KN)                                                                   \
-  {                                                                                            \
-    if constexpr (MODE != MODE_LSE)                                                            \
-      load_run_rs<D>(it < nb8 ? rs.v8 : rs.v16, (uint32_t)(it < nb8 ? it : it - nb8) * ib,     \
-                     vlane, V);                                                                \
-    const int nx = it + kWaves;                                                                \
-    load_run_rs<D>(nx < nb8 ? rs.k8 : rs.k16,                                                  \
-                   nx < nitems ? (uint32_t)(nx < nb8 ? nx : nx - nb8) * ib : kNoItem, klane,   \
-                   KN);                                                                        \
-    if constexpr (MODE != MODE_LSE) {                                                          \
-      if (it >= nb8 && !vscaled) {                                                             \
-        apply_vscale<D>(wa, sv);                                                               \
-        vscaled = true;                                                                        \
-      }                                                                                        \
-    }                                                                                          \
-    compute_item<D, BF16, MODE>(item_of(it, nb8, n8, nw, cap8), KC, V, q, scale8, scale16,     \
-                                head_ok, wa, sc, stride, lse, massp);                          \
-    it = nx;                                                                                   \
-    if (it >= nitems) break;                                                                   \
-  }
   for (;;) {
-    CONFKV_STAGE(kb, kn)
-    CONFKV_STAGE(kn, kb)
+    if constexpr (MODE != MODE_LSE)
+      load_run_rs<D>(it < nb8 ? rs.v8 : rs.v16, (uint32_t)(it < nb8 ? it : it - nb8) * ib, vlane, V);
+    const int nx = it + kWaves;
+    if constexpr (MODE != MODE_LSE) {
+      if (it >= nb8 && !vscaled) {
+        apply_vscale<D>(wa, sv);
+        vscaled = true;
+      }
+    }
+    compute_item<D, BF16, MODE>(item_of(it, nb8, n8, nw, cap8), kb, V, q, scale8, scale16,
+                                head_ok, wa, sc, stride, lse, massp, nx < nb8 ? rs.k8 : rs.k16,
+                                nx < nitems ? (uint32_t)(nx < nb8 ? nx : nx - nb8) * ib : kNoItem,
+                                klane);
+    it = nx;
+    if (it >= nitems) break;
   }
-#undef CONFKV_STAGE
 }
 
 // One workgroup per unit.  The unit of KV head 0 also records the (layer,
