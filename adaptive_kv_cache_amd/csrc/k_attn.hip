@@ -436,8 +436,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     const uint16_t* __restrict__ knew_all, const uint16_t* __restrict__ vnew_all,
     float* __restrict__ out_all, float* __restrict__ massp_all, int32_t* __restrict__ snap,
     int score_cap) {
-  // Dynamic LDS: the query operands, then one region reused as query staging
-  // [G + 1][D], scores [G][stride] and the O merge buffer [4][G][D].
+  // Dynamic LDS: the query operands, then one region reused as scores
+  // [G][stride] and the O merge buffer [4][G][D].
   extern __shared__ float dyn_lds[];
   u4* s_qops = (u4*)dyn_lds;
   float* smem = dyn_lds + 4 * qops_u4<D>(dm.G);
@@ -446,7 +446,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
   __shared__ float s_m[kWaves][kMaxGroup], s_l[kWaves][kMaxGroup];
   __shared__ float s_lse[kMaxGroup], s_pnew[kMaxGroup], s_f[kWaves][kMaxGroup];
   __shared__ float s_sv[D];
-  __shared__ float s_kn[D], s_vn[D];        // this step's key and value as fp32
+  __shared__ float s_vn[D];                 // this step's value as fp32
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, hl = lane & 15;
   const int unit_local = blockIdx.x;
@@ -468,21 +468,27 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
   const bool head_ok = hl < G;
 
 
-  // ---- set-up: every global load is issued before the first wait.  Each thread
-  // fetches at most one 16-byte chunk of the query group, of an absmax row and of
-  // the new key/value; then the keys of INT8 block `wave` start loading
-  // speculatively (they need no counter), and only then are the counters used.
-  const int nq4 = G * D / 8;  // 16-byte chunks of the query group (<= 256)
-  u4 rq = {0u, 0u, 0u, 0u}, ra = {0u, 0u, 0u, 0u}, rn = {0u, 0u, 0u, 0u};
-  if (tid < nq4) rq = ld16(qsrc + 8 * tid);
-  if (tid < D / 4)
-    ra = ld16(c.k_amax + u * D + 4 * tid);
-  else if (tid < D / 2)
-    ra = ld16(c.v_amax + u * D + 4 * (tid - D / 4));
-  if (tid < D / 8)
-    rn = ld16(knew + 8 * tid);
-  else if (tid < D / 4)
-    rn = ld16(vnew + 8 * (tid - D / 8));
+  // ---- set-up.  Every global load is issued before the first wait.  The query
+  // group is read as 16-byte chunks (8 channels of one head); the thread holding
+  // chunk k of head h also reads the same 8 channels of the key absmax row and of
+  // the new key.  The last D/4 threads read the value absmax row and the new
+  // value.  Then the keys of INT8 block `wave` start loading speculatively (they
+  // need no counter), and only then are the counters used.
+  const int nq = G * D / 8;                 // query chunks (<= 256)
+  const int qh_ = tid / (D / 8), qk = tid % (D / 8);
+  const int vt = tid - (kAttnThreads - D / 4);
+  const u4 z4 = {0u, 0u, 0u, 0u};
+  u4 rq = z4, rka0 = z4, rka1 = z4, rkn = z4, rva = z4, rvn = z4;
+  if (tid < nq) {
+    rq = ld16(qsrc + 8 * tid);
+    rka0 = ld16(c.k_amax + u * D + 8 * qk);
+    rka1 = ld16(c.k_amax + u * D + 8 * qk + 4);
+    rkn = ld16(knew + 8 * qk);
+  }
+  if (vt >= 0) {
+    rva = ld16(c.v_amax + u * D + 4 * vt);
+    if (vt < D / 8) rvn = ld16(vnew + 8 * vt);
+  }
   const UnitRs urs{make_rsrc(k8, (uint32_t)dm.cap8 * D), make_rsrc(v8, (uint32_t)dm.cap8 * D),
                    make_rsrc(k16, (uint32_t)dm.cap16 * D * 2),
                    make_rsrc(v16, (uint32_t)dm.cap16 * D * 2)};
@@ -505,97 +511,75 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     snap[3 * lb + 1] = nw;
     snap[3 * lb + 2] = t;
   }
-  float* s_q = smem;           // [G][D] query as fp32
-  float* s_ka = smem + G * D;  // [D] key scale amax_K / 127
-  if (tid < nq4) {
-    const uint32_t w[4] = {rq.x, rq.y, rq.z, rq.w};
+  if (!appended && tid == 0 && hk == 0) atomicOr(c.status, (int)CONF_ST_WINDOW_FULL);
+  // this step's row into window slot nw; the new value and the value scale into LDS
+  if (appended && qh_ == 0 && tid < nq)
+    *(u4*)(k16 + k16_off(nw, 8 * qk, D)) = rkn;  // 8 channels are contiguous in a key tile
+  if (vt >= 0) {
+    const uint32_t wa4[4] = {rva.x, rva.y, rva.z, rva.w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      s_q[8 * tid + e] = h16_to_f32((uint16_t)(w[e >> 1] >> (16 * (e & 1))), dm.bf16);
-  }
-  if (tid < D / 2) {
-    float* dst = tid < D / 4 ? s_ka + 4 * tid : s_sv + 4 * (tid - D / 4);
-    dst[0] = __uint_as_float(ra.x) / 127.0f;
-    dst[1] = __uint_as_float(ra.y) / 127.0f;
-    dst[2] = __uint_as_float(ra.z) / 127.0f;
-    dst[3] = __uint_as_float(ra.w) / 127.0f;
-  }
-  if (tid < D / 4) {
-    const bool isk = tid < D / 8;
-    const int c0 = 8 * (isk ? tid : tid - D / 8);
-    const uint32_t w[4] = {rn.x, rn.y, rn.z, rn.w};
-    float* dst = isk ? s_kn : s_vn;
+    for (int e = 0; e < 4; ++e) s_sv[4 * vt + e] = __uint_as_float(wa4[e]) / 127.0f;
+    if (vt < D / 8) {
+      const uint32_t w[4] = {rvn.x, rvn.y, rvn.z, rvn.w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      dst[c0 + e] = h16_to_f32((uint16_t)(w[e >> 1] >> (16 * (e & 1))), dm.bf16);
-    // append this step's row to window slot nw (channels c0 .. c0+7)
-    if (appended) {
-      if (isk) {
-        *(u4*)(k16 + k16_off(nw, c0, D)) = rn;  // 8 channels are contiguous in a key tile
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          v16[v16_off(nw, c0 + e, D)] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+      for (int e = 0; e < 8; ++e) {
+        const uint16_t b16 = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+        s_vn[8 * vt + e] = h16_to_f32(b16, dm.bf16);
+        if (appended) v16[v16_off(nw, 8 * vt + e, D)] = b16;
       }
     }
   }
-  if (!appended && tid == 0 && hk == 0) atomicOr(c.status, (int)CONF_ST_WINDOW_FULL);
-  __syncthreads();
-  float kn[D / 64];
-#pragma unroll
-  for (int y = 0; y < D / 64; ++y) kn[y] = s_kn[lane + 64 * y];
-  // per head: the new token's score and the power-of-two scale of q * amax_K / 127
-  for (int h = wave; h < G; h += kWaves) {
-    float s = 0.f, mx = 0.f;
-#pragma unroll
-    for (int y = 0; y < D / 64; ++y) {
-      const float qv = s_q[h * D + lane + 64 * y];
-      s = fmaf(qv, kn[y], s);
-      mx = fmaxf(mx, fabsf(qv * s_ka[lane + 64 * y]));
-    }
-    s = wave_sum(s);
-    mx = wave_max(mx);
-    if (lane == 0) {
-      s_snew[h] = s * rs;
-      s_qscale[h] = mx > 0.f ? ldexpf(1.0f, 14 - ilogbf(mx)) : 1.0f;
-    }
-  }
-  __syncthreads();
+  // Per head, from its D/8 chunk threads (consecutive lanes of one wavefront):
+  // the power-of-two scale that puts max |q * amax_K / 127| in [2^14, 2^15), the
+  // new token's score, and the query operands (each thread writes its own chunks).
   {
-    // every lane's operands; wavefront w writes the 32-channel steps w, w+4, ...
-    u4* dst = head_ok ? s_qops + (hl * 4 + g) * (D / 32) * 3 : s_qops + 4 * G * (D / 32) * 3;
-    const float al = head_ok ? s_qscale[hl] : 1.0f;
-    for (int s = wave; s < D / 32; s += kWaves) {
-      // 16-bit query for window keys: the fp32 staging value converts back exactly
-      uint16_t w16[8];
+    float qv[8], x8[8];
+    float mx = 0.f, sc = 0.f;
+    const uint32_t wq[4] = {rq.x, rq.y, rq.z, rq.w}, wn[4] = {rkn.x, rkn.y, rkn.z, rkn.w};
+    const uint32_t wk[8] = {rka0.x, rka0.y, rka0.z, rka0.w, rka1.x, rka1.y, rka1.z, rka1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qv[e] = h16_to_f32((uint16_t)(wq[e >> 1] >> (16 * (e & 1))), dm.bf16);
+      const float kn = h16_to_f32((uint16_t)(wn[e >> 1] >> (16 * (e & 1))), dm.bf16);
+      x8[e] = qv[e] * (__uint_as_float(wk[e]) / 127.0f);
+      mx = fmaxf(mx, fabsf(x8[e]));
+      sc = fmaf(qv[e], kn, sc);
+    }
+#pragma unroll
+    for (int off = 1; off < D / 8; off <<= 1) {
+      mx = fmaxf(mx, __shfl_xor(mx, off));
+      sc += __shfl_xor(sc, off);
+    }
+    const float al = mx > 0.f ? ldexpf(1.0f, 14 - ilogbf(mx)) : 1.0f;
+    if (tid < nq) {
+      if (qk == 0) {
+        s_snew[qh_] = sc * rs;
+        s_qscale[qh_] = al;
+      }
+      // INT8-key operands: channels 8k .. 8k+7 = 64*(s/2) + 16*g + 8*(s%2) + e
+      const int s8 = 2 * (qk / 8) + (qk & 1), g8 = (qk % 8) / 2;
       h8 hi8, lo8;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float xq = head_ok ? s_q[hl * D + 32 * s + 8 * g + e] : 0.f;
-        if constexpr (BF16)
-          w16[e] = (uint16_t)(__float_as_uint(xq) >> 16);
-        else
-          w16[e] = __builtin_bit_cast(uint16_t, (_Float16)xq);
-        // channel order of the INT8 key loads: 64*(s/2) + 16*g + 8*(s%2) + e
-        const int ch = 64 * (s >> 1) + 16 * g + 8 * (s & 1) + e;
-        const float x8 = head_ok ? (s_q[hl * D + ch] * s_ka[ch]) * al : 0.f;
-        const _Float16 hi = (_Float16)x8;
+        const float y = x8[e] * al;
+        const _Float16 hi = (_Float16)y;
         hi8[e] = hi;
-        lo8[e] = (_Float16)(x8 - (float)hi);
+        lo8[e] = (_Float16)(y - (float)hi);
       }
-      if (head_ok || g == 0) {
-        dst[3 * s] = (u4){w16[0] | ((uint32_t)w16[1] << 16), w16[2] | ((uint32_t)w16[3] << 16),
-                          w16[4] | ((uint32_t)w16[5] << 16), w16[6] | ((uint32_t)w16[7] << 16)};
-        dst[3 * s + 1] = __builtin_bit_cast(u4, hi8);
-        dst[3 * s + 2] = __builtin_bit_cast(u4, lo8);
-      }
+      u4* d8 = s_qops + (qh_ * 4 + g8) * (D / 32) * 3 + 3 * s8;
+      d8[1] = __builtin_bit_cast(u4, hi8);
+      d8[2] = __builtin_bit_cast(u4, lo8);
+      // window-key operands: the 16-bit query as stored, channels 32*s + 8*g + e
+      s_qops[(qh_ * 4 + qk % 4) * (D / 32) * 3 + 3 * (qk / 4)] = rq;
     }
+    // the all-zero operands that padding heads point at
+    if (tid < (D / 32) * 3) s_qops[4 * G * (D / 32) * 3 + tid] = z4;
   }
+  __syncthreads();  // operands, scales and the new token's values complete
   const QOps<D, BF16> q{(const lds_u4*)(head_ok ? s_qops + (hl * 4 + g) * (D / 32) * 3
                                                 : s_qops + 4 * G * (D / 32) * 3)};
   const float scale8 = head_ok ? rs / s_qscale[hl] : 0.f;
   const float scale16 = head_ok ? rs : 0.f;
-  __syncthreads();  // the staging area becomes the score store
 
   WaveAcc<D> wa;
   wa.m = -INFINITY;
