@@ -211,7 +211,7 @@ int conf_confidence(const conf_params* p, const float* logits, float* c, int32_t
   Dims d;
   int rc = make_dims(p, &d);
   if (rc) return rc;
-  if (!a16(logits) || !c || !budget || !ws) return CONF_E_INVALID;
+  if (!logits || !c || !budget || !ws) return CONF_E_INVALID;
   const WsMap w = make_ws(d);
   launch_confidence(d, logits, at<float>(ws, w.conf_part), c, budget, (hipStream_t)stream);
   return check_launch("conf_confidence");
@@ -265,7 +265,7 @@ int conf_step(const conf_params* p, conf_cache* c, const float* logits, const vo
   Dims d;
   int rc = make_dims(p, &d);
   if (rc) return rc;
-  if (!cache_ok(c) || !a16(logits) || !a16(q) || !a16(k_new) || !a16(v_new) || !out || !conf ||
+  if (!cache_ok(c) || !logits || !a16(q) || !a16(k_new) || !a16(v_new) || !out || !conf ||
       !budget || !ws)
     return CONF_E_INVALID;
   const WsMap w = make_ws(d);

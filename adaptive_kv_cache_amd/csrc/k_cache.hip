@@ -138,6 +138,7 @@ void launch_ingest(const Dims& dm, const conf_cache& c, int layer0, int nl, int 
 //       [4] demotee's window slot or -1 [5] its INT8 slot or -1  (kept in the
 //       workspace for inspection; the INT8 region ends at n8' + (demoted))
 constexpr int kCompThreads = 512;  // every (layer, sequence) workgroup resident at once
+typedef uint32_t cu4 __attribute__((ext_vector_type(4)));  // a 16-byte chunk
 constexpr int kCompWaves = kCompThreads / 64;
 constexpr int kMaxGrown = 512;    // grown channels requantised by the whole workgroup
 constexpr int kLdsFlags8 = 8192;  // INT8 keep flags cached in LDS (beyond: re-read)
@@ -330,11 +331,20 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dim
       pos8[dst] = pos8[src];
       ema8[dst] = ema8[src];
     }
-    for (int i = tid; i < nm8 * per; i += kCompThreads) {
-      const int k = i / per, r = i % per, hk = r / D, ch = r % D;
+    // Bulk moves: keys as 16-byte chunks (16 channels are contiguous in a key
+    // tile), values byte by byte; the move index varies fastest, so neighbouring
+    // threads read neighbouring slots of one channel (coalesced sources).
+    for (int i = tid; i < nm8 * dm.Hkv * (D / 16); i += kCompThreads) {
+      const int k = i % nm8, r = i / nm8, hk = r / (D / 16), cg = r % (D / 16);
       const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap8 * D;
       const int src = mv_at(S.mv8, mv8, 2 * k), dst = mv_at(S.mv8, mv8, 2 * k + 1);
-      c.k8[ub + k8_off(dst, ch, D)] = c.k8[ub + k8_off(src, ch, D)];
+      *(cu4*)(c.k8 + ub + k8_off(dst, 16 * cg, D)) =
+          *(const cu4*)(c.k8 + ub + k8_off(src, 16 * cg, D));
+    }
+    for (int i = tid; i < nm8 * per; i += kCompThreads) {
+      const int k = i % nm8, r = i / nm8, hk = r / D, ch = r % D;
+      const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap8 * D;
+      const int src = mv_at(S.mv8, mv8, 2 * k), dst = mv_at(S.mv8, mv8, 2 * k + 1);
       c.v8[ub + v8_off(dst, ch, D)] = c.v8[ub + v8_off(src, ch, D)];
     }
   }
@@ -440,13 +450,20 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dim
       pos16[dst] = pos16[src];
       ema16[dst] = ema16[src];
     }
-    for (int i = tid; i < nm16 * per; i += kCompThreads) {
-      const int k = i / per, r = i % per, hk = r / D, ch = r % D;
+    // bulk window moves: keys as 16-byte chunks (8 channels), values element by
+    // element, the move index fastest
+    for (int i = tid; i < nm16 * dm.Hkv * (D / 8); i += kCompThreads) {
+      const int k = i % nm16, r = i / nm16, hk = r / (D / 8), cg = r % (D / 8);
       const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap16 * D;
       const int src = mv_at(S.mv16, mv16, 2 * k), dst = mv_at(S.mv16, mv16, 2 * k + 1);
       uint16_t* k16 = (uint16_t*)c.k16 + ub;
+      *(cu4*)(k16 + k16_off(dst, 8 * cg, D)) = *(const cu4*)(k16 + k16_off(src, 8 * cg, D));
+    }
+    for (int i = tid; i < nm16 * per; i += kCompThreads) {
+      const int k = i % nm16, r = i / nm16, hk = r / D, ch = r % D;
+      const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap16 * D;
+      const int src = mv_at(S.mv16, mv16, 2 * k), dst = mv_at(S.mv16, mv16, 2 * k + 1);
       uint16_t* v16 = (uint16_t*)c.v16 + ub;
-      k16[k16_off(dst, ch, D)] = k16[k16_off(src, ch, D)];
       v16[v16_off(dst, ch, D)] = v16[v16_off(src, ch, D)];
     }
   }

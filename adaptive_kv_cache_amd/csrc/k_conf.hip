@@ -31,6 +31,9 @@ __device__ inline void top2_merge(float& a, float& b, float a2, float b2) {
   a = hi;
 }
 
+// VEC: every row starts 16-byte aligned (aligned base, V a multiple of 4), so a
+// thread reads its 16 elements as four 16-byte loads.
+template <bool VEC>
 __global__ __launch_bounds__(kConfThreads) void conf_partial_kernel(const float* __restrict__ logits,
                                                                    float* __restrict__ part,
                                                                    int V, int n_chunks) {
@@ -41,8 +44,8 @@ __global__ __launch_bounds__(kConfThreads) void conf_partial_kernel(const float*
   float z[kConfPer];
   float m = -INFINITY, a = -INFINITY, a2 = -INFINITY;
   int bad = 0;
-  if ((V & 3) == 0) {
-    // rows start 16-byte aligned: thread tid reads elements base + 4*(i*256 + tid) .. +3
+  if constexpr (VEC) {
+    // thread tid reads elements base + 4*(i*256 + tid) .. +3
 #pragma unroll
     for (int i = 0; i < kConfPer / 4; ++i) {
       const int idx = base + 4 * (i * kConfThreads + tid);
@@ -189,8 +192,13 @@ int conf_vchunks(int V) { return (V + kConfThreads * kConfPer - 1) / (kConfThrea
 void launch_confidence(const Dims& dm, const float* logits, float* part, float* c, int32_t* budget,
                        hipStream_t st) {
   const int nch = conf_vchunks(dm.V);
-  hipLaunchKernelGGL(conf_partial_kernel, dim3(nch, dm.B), dim3(kConfThreads), 0, st, logits, part,
-                     dm.V, nch);
+  const bool vec = ((uintptr_t)logits & 15u) == 0 && (dm.V & 3) == 0;
+  if (vec)
+    hipLaunchKernelGGL(conf_partial_kernel<true>, dim3(nch, dm.B), dim3(kConfThreads), 0, st,
+                       logits, part, dm.V, nch);
+  else
+    hipLaunchKernelGGL(conf_partial_kernel<false>, dim3(nch, dm.B), dim3(kConfThreads), 0, st,
+                       logits, part, dm.V, nch);
   hipLaunchKernelGGL(conf_final_kernel, dim3(dm.B), dim3(64), 0, st, part, nch, dm, c, budget);
 }
 
