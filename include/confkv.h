@@ -24,8 +24,8 @@
  *   - A call validates its arguments on the host, enqueues kernels on `stream`
  *     (a hipStream_t; NULL is the null stream) and returns without waiting for
  *     the device.  Results are valid once the stream has been synchronised.
- *   - logits, q, k_new, v_new and the cache's k8, v8, k16, v16, k_amax, v_amax
- *     must be 16-byte aligned (CONF_E_INVALID otherwise); PyTorch allocations are.
+ *   - q, k_new, v_new and the cache's k8, v8, k16, v16, k_amax, v_amax must be
+ *     16-byte aligned (CONF_E_INVALID otherwise); PyTorch allocations are.
  *   - Return value: CONF_OK (0) or a negative CONF_E_* code; nothing is
  *     enqueued when validation fails.  No C++ exception crosses the ABI.
  *   - `layer` = -1 processes every layer in one launch per kernel; then per-

@@ -134,8 +134,6 @@ def test_misaligned_pointers_rejected(lib):
         a[i] = odd
         assert lib.conf_decode_attn(ctypes.byref(p), ctypes.byref(cache), -1, *a[:3], fake, fake,
                                     ctypes.c_void_p(0)) == E_INVALID
-    assert lib.conf_confidence(ctypes.byref(p), odd, fake, fake, fake, ctypes.c_void_p(0)) == \
-        E_INVALID
     for field in ("k8", "v8", "k16", "v16", "k_amax", "v_amax"):
         bad = binding.ConfCache(*([0x1000] * 14))
         setattr(bad, field, 0x1004)
