@@ -38,14 +38,18 @@ struct WsMap {
 
 // Tiled layouts of one unit (layer, sequence, KV head).  Every region is cut
 // into 64-token tiles of 64*d elements; inside a tile the order is chosen so that
-// each 16-byte-per-lane load of a wavefront reads one contiguous 1 KB run and
-// lands in the lane that feeds it to the matrix cores.  Write a slot as
+// each 16-byte-per-lane load of a wavefront lands in the lane that feeds it to
+// the matrix cores and reads whole cache lines: a key load reads one contiguous
+// 1 KB run, a value load four contiguous 256-byte pieces.  The values are grouped
+// by g first so that one token's values (as compaction, demotion and the append
+// touch them) sit inside one 16*d-byte stretch, 16 bytes per channel, instead of
+// being spread over the whole tile.  Write a slot as
 // j = 64*tile + 32u + 16a + 4g + b = 64*tile + 16r + row  (u, a in {0,1}; g, b, r in 0..3).
 //
 //   k8  (INT8 keys):    [r][c / 64][(c / 16) % 4][row][c % 16]
-//   v8  (INT8 values):  [c][16g + 8u + 4a + b]
+//   v8  (INT8 values):  [g][c][8u + 4a + b]
 //   k16 (16-bit keys):  [u][r % 2][c / 32][(c / 8) % 4][row][c % 8]
-//   v16 (16-bit values):[u][c][8g + 4a + b]
+//   v16 (16-bit values):[u][g][c][4a + b]
 __host__ __device__ inline size_t k8_off(int slot, int c, int D) {
   const int jj = slot & 63, r = jj >> 4, row = jj & 15;
   return (size_t)(slot >> 6) * (size_t)(D * kTile) +
@@ -59,13 +63,13 @@ __host__ __device__ inline size_t k16_off(int slot, int c, int D) {
 __host__ __device__ inline size_t v8_off(int slot, int c, int D) {
   const int s = slot & 63;
   const int b = s & 3, g = (s >> 2) & 3, a = (s >> 4) & 1, u = (s >> 5) & 1;
-  return (size_t)(slot >> 6) * (size_t)(D * kTile) + (size_t)c * kTile +
-         (size_t)((g << 4) | (u << 3) | (a << 2) | b);
+  return (size_t)(slot >> 6) * (size_t)(D * kTile) + (size_t)(g * D + c) * 16 +
+         (size_t)((u << 3) | (a << 2) | b);
 }
 __host__ __device__ inline size_t v16_off(int slot, int c, int D) {
   const int s = slot & 31;
   const int b = s & 3, g = (s >> 2) & 3, a = (s >> 4) & 1;
-  return (size_t)(slot >> 5) * (size_t)(D * 32) + (size_t)c * 32 + (size_t)((g << 3) | (a << 2) | b);
+  return (size_t)(slot >> 5) * (size_t)(D * 32) + (size_t)(g * D + c) * 8 + (size_t)((a << 2) | b);
 }
 
 __device__ inline float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }

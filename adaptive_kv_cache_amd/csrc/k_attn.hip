@@ -139,11 +139,12 @@ __device__ inline Item item_of(int it, int nb8, int n8, int nw, int cap8) {
   return I;
 }
 
-// Every item's keys and values are D/16 runs of 1 KB: run i of an item starts
-// 1 KB * i after its base, and a lane reads 16 bytes at a fixed offset inside
-// each run (keys: 16 * lane; values: 64 * (lane % 16) + 16 * (lane / 16)).  That
-// holds for INT8 blocks and window halves alike (both are 64 * D bytes), so one
-// straight-line load sequence serves both.
+// Every item's keys and values are read as D/16 loads of 16 bytes per lane.
+// Keys: load i reads the 1 KB run at 1 KB * i, a lane at 16 * lane inside it.
+// Values: load i reads 16 channels (16i .. 16i+15) of the four token groups g,
+// a lane at 16*D*(lane / 16) + 16*(lane % 16) + 256*i: four 256-byte pieces.
+// That holds for INT8 blocks and window halves alike (both are 64 * D bytes), so
+// one straight-line load sequence serves both.
 //
 // The item loads go through buffer descriptors (one per region of the
 // unit: INT8 keys, INT8 values, window keys, window values).  A load whose offset
@@ -164,12 +165,12 @@ __device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 // default policy on the 32K, batch-8 cache).
 constexpr int kStreamPolicy = 2;
 
-template <int D>
+template <int D, int STEP = 1024>
 __device__ inline void load_run_rs(rsrc_t r, uint32_t off, int lane_off, Buf<D>& R) {
 #pragma unroll
   for (int i = 0; i < D / 16; ++i)
     R.x[i] = __builtin_bit_cast(
-        u4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + lane_off + i * 1024), 0,
+        u4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + lane_off + i * STEP), 0,
                                                   kStreamPolicy));
 }
 
@@ -401,7 +402,7 @@ __device__ inline void wave_pass(int nitems, int nb8, int n8, int nw, int cap8, 
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   if (wave >= nitems) return;
-  const int klane = 16 * lane, vlane = 64 * (lane & 15) + 16 * (lane >> 4);
+  const int klane = 16 * lane, vlane = 16 * D * (lane >> 4) + 16 * (lane & 15);
   const uint32_t ib = (uint32_t)kTile * D;  // bytes per item in every region
   if (!preloaded)
     load_run_rs<D>(wave < nb8 ? rs.k8 : rs.k16, (uint32_t)(wave < nb8 ? wave : wave - nb8) * ib,
@@ -410,7 +411,8 @@ __device__ inline void wave_pass(int nitems, int nb8, int n8, int nw, int cap8, 
   int it = wave;
   for (;;) {
     if constexpr (MODE != MODE_LSE)
-      load_run_rs<D>(it < nb8 ? rs.v8 : rs.v16, (uint32_t)(it < nb8 ? it : it - nb8) * ib, vlane, V);
+      load_run_rs<D, 256>(it < nb8 ? rs.v8 : rs.v16, (uint32_t)(it < nb8 ? it : it - nb8) * ib,
+                          vlane, V);
     const int nx = it + kWaves;
     if constexpr (MODE != MODE_LSE) {
       if (it >= nb8 && !vscaled) {

@@ -98,10 +98,12 @@ typedef struct conf_params {
  * Inside a tile, write a slot's index j (mod 64) as j = 32u + 16a + 4g + b =
  * 16r + row (u, a in {0,1}; g, b, r in 0..3; row in 0..15) and a channel c.
  * The element order of a tile is
- *   k8:  [r][c/64][(c/16)%4][row][c%16]         v8:  [c][16g + 8u + 4a + b]
- *   k16: [u][r%2][c/32][(c/8)%4][row][c%8]      v16: [u][c][8g + 4a + b]
- * so that every wavefront load of the attention kernel reads one contiguous
- * 1 KB run and lands in the lane that feeds it to the matrix cores.
+ *   k8:  [r][c/64][(c/16)%4][row][c%16]         v8:  [g][c][8u + 4a + b]
+ *   k16: [u][r%2][c/32][(c/8)%4][row][c%8]      v16: [u][g][c][4a + b]
+ * so that every wavefront load of the attention kernel reads whole cache lines
+ * (keys: one 1 KB run; values: four 256-byte pieces) and lands in the lane that
+ * feeds it to the matrix cores, while one token's values stay inside a 16*d-byte
+ * stretch of the tile.
  * conf_cache_export() returns plain row-major copies.
  * Slot order inside a region is arbitrary: compaction fills holes, so a token's
  * identity is its stored position.

@@ -116,4 +116,10 @@ def tiny_workloads() -> dict:
         name="gqa16_bf16_d64_long", n_layers=1, batch=2, n_q_heads=16, n_kv_heads=1, head_dim=64,
         vocab=500, dtype16="bf16", window=64, protect=8, n_high=100, n_low=300, prefill=2500,
         steps=8)
+    # every budget above what the LDS score rows hold, so that each step after the
+    # first also takes the two-pass path with the window's free slot masked
+    w["gqa16_bf16_d64_wide"] = Workload(
+        name="gqa16_bf16_d64_wide", n_layers=1, batch=2, n_q_heads=16, n_kv_heads=1,
+        head_dim=64, vocab=500, dtype16="bf16", window=64, protect=8, n_high=1300, n_low=1400,
+        prefill=2500, steps=6)
     return w
