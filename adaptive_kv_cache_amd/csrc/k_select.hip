@@ -12,14 +12,27 @@
 // exactly as (s desc, pos desc).  The K-th largest candidate key is found by an
 // MSB-first radix select over 8-bit digits: a 256-bin histogram in LDS per pass,
 // the bin holding the K-th key found by one wavefront's suffix scan, and an early
-// stop as soon as that bin's keys are all kept.  Keys live in LDS when the cache
-// fits (the steady state); otherwise each pass recomputes them from the cache.
+// stop as soon as that bin's keys are all kept.  When only a few candidates go
+// (the steady state evicts one token per step), the threshold is found instead by
+// that many rounds of a block-wide minimum over the candidate keys.  Keys live in
+// LDS when the cache fits (the steady state); otherwise each pass recomputes them
+// from the cache.
 #include "common.hpp"
 
 namespace confkv {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelLdsKeys = 6144;  // keys cached in LDS (48 KB)
+constexpr int kFewEvict = 8;       // evictions up to which minimum rounds replace the radix select
+
+__device__ inline uint64_t wave_min_u64(uint64_t x) {
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)x, off), hi = __shfl_xor((uint32_t)(x >> 32), off);
+    const uint64_t y = ((uint64_t)hi << 32) | lo;
+    x = y < x ? y : x;
+  }
+  return x;
+}
 
 __device__ inline uint64_t sel_key(float e, float emax, int pos, int t, float s_ema, float s_rec) {
 #pragma clang fp contract(off)
@@ -56,6 +69,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(conf_cache c, Dims 
   __shared__ float s_wmax[kSelThreads / 64];
   __shared__ int s_wprot[kSelThreads / 64];
   __shared__ unsigned long long s_prefix, s_mask;
+  __shared__ unsigned long long s_wmin[kSelThreads / 64];
   __shared__ int s_rem, s_done;
   const int prot_lo = t - dm.P;  // protected: pos > prot_lo
   const bool cached = n <= kSelLdsKeys;
@@ -106,6 +120,36 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(conf_cache c, Dims 
   };
   if (cached)
     for (int j = tid; j < n; j += kSelThreads) s_key[j] = key_of(j);
+  const int evict = (n - np) - K;  // candidates that go
+  if (K > 0 && evict <= kFewEvict) {
+    // the evict smallest candidate keys (keys are unique): after round e, thr is
+    // the (e+1)-th smallest; the candidates above the last thr stay
+    if (cached) __syncthreads();
+    uint64_t thr = 0ull;
+    for (int e = 0; e < evict; ++e) {
+      uint64_t m = ~0ull;
+      for (int j = tid; j < n; j += kSelThreads) {
+        const uint64_t key = cached ? s_key[j] : key_of(j);
+        if (key > thr && key < m) m = key;  // key 0 (protected) is never > thr
+      }
+      m = wave_min_u64(m);
+      if (lane == 0) s_wmin[wave] = m;
+      __syncthreads();
+      m = s_wmin[0];
+      for (int w = 1; w < kSelThreads / 64; ++w) m = s_wmin[w] < m ? s_wmin[w] : m;
+      thr = m;
+      __syncthreads();
+    }
+    for (int j = tid; j < n; j += kSelThreads) {
+      const uint64_t key = cached ? s_key[j] : key_of(j);
+      const int k = key == 0ull ? 1 : key > thr;
+      if (j < n8)
+        keep8[j] = (uint8_t)k;
+      else
+        keep16[j - n8] = (uint8_t)k;
+    }
+    return;
+  }
   if (tid == 0) {
     s_prefix = 0ull;
     s_mask = 0ull;

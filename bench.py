@@ -13,6 +13,12 @@ prefill with a planted needle, budgets 2048 / 4096, P 256, W 512).  The first
 128 steps (the one-off bulk eviction of the prefill and the first confident /
 unconfident phases) are warm-up; the timed steps are the steady state.
 
+The confidence reads only the step's logits, and the selection is the first call
+that needs its budgets, so it runs on a second stream (default priority) beside
+the attention; each step's second-stream work is ordered after the previous
+step, and the selection waits for it.  --one-stream issues every call in order
+on one stream.
+
 Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -158,16 +164,23 @@ def run(args):
     plan_off = _plan_offset(eng)
     hplan = torch.empty(args.steps, L, B, 16, dtype=torch.int32, device=dev)
     ws_plan = eng.ws[plan_off:plan_off + L * B * 16 * 4].view(torch.int32).view(L, B, 16)
+    main = torch.cuda.current_stream(dev)
+    side = main if args.one_stream else torch.cuda.Stream(device=dev)
     torch.cuda.synchronize()
     log("inputs resident; warm-up")
 
     def one_step(s, ev=None, i=None):
+        if side is not main:
+            side.wait_stream(main)
+        with torch.cuda.stream(side):
+            eng.confidence(logits[s], c=conf[s], budget=budget[s])
         if ev is not None:
-            ev[0].record()
+            ev[0].record(main)
         eng.decode_attn(-1, qs[s], ks[s], vs[s], out=out)
         if ev is not None:
-            ev[1].record()
-        eng.confidence(logits[s], c=conf[s], budget=budget[s])
+            ev[1].record(main)
+        if side is not main:
+            main.wait_stream(side)
         eng.rank_evict(-1, budget[s], keep=keep)
         eng.compact_demote(-1, keep)
         if i is not None:
@@ -224,7 +237,8 @@ def run(args):
                    "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "dtype16": wl.dtype16,
                    "prefill": wl.prefill, "n_high": wl.n_high, "n_low": wl.n_low,
                    "protect": wl.protect, "window": wl.window, "pyramid": wl.pyramid,
-                   "vocab": wl.vocab, "mean_tokens_attended": round(n_mean, 1)},
+                   "vocab": wl.vocab, "mean_tokens_attended": round(n_mean, 1),
+                   "streams": 1 if args.one_stream else 2},
         "roofline": {"bound": "hbm", "kernel": "conf_decode_attn (one launch)",
                      "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
@@ -343,6 +357,8 @@ def main():
     ap.add_argument("--workload", default="qwen32b_gqa_b8_32k")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--one-stream", action="store_true",
+                    help="run the confidence in order on the attention's stream")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--rocpd-summary", metavar="DB",
                     help="print per-kernel durations of a rocprofv3 database and exit")

@@ -189,6 +189,36 @@ def test_conf_step_equals_the_four_calls(name):
                     assert np.array_equal(np.asarray(ea[key]), np.asarray(eb[key])), (step, l, s, key)
 
 
+@pytest.mark.parametrize("name", ["gqa5_bf16_d128", "mha_f16_d64"])
+def test_rank_evict_budget_sweep(name):
+    """Selection alone against the oracle, bit-exact, for budgets that evict 1 .. 40
+    tokens (a few evictions take minimum rounds, more take the radix select)."""
+    wl = TINY[name]
+    prm = oracle_params(wl)
+    eng = Engine(wl)
+    if wl.prefill:
+        _ingest(eng, wl, SEED)
+    for step in range(wl.n_high + 5 if not wl.prefill else 4):
+        z, q = synth.logits(wl, step, SEED).cuda(), synth.q_new(wl, step, SEED).cuda()
+        k, v = (x.cuda() for x in synth.kv_new(wl, step, SEED))
+        eng.step(z, q, k, v)
+    S = _snap(eng, wl)
+    ntok = (eng.t_n8 + eng.t_n16).cpu().numpy()
+    cap8 = eng.cap8
+    for e in (1, 2, 3, 5, 8, 9, 17, 40):
+        budget = np.ascontiguousarray((ntok - e).T).astype(np.int32)
+        keep = eng.rank_evict(-1, torch.from_numpy(budget).cuda()).cpu().numpy()
+        for l in range(wl.n_layers):
+            for b in range(wl.batch):
+                st = to_oracle_state(S[l][b], wl.dtype16)
+                scores = O.composite_scores(st.ema.astype(np.float32), st.pos, st.t,
+                                            prm.s_ema, prm.s_rec)
+                kr = O.select_keep(scores, st.pos, st.t, prm.protect, int(budget[b, l]))
+                got = kept_positions(S[l][b], keep[l, b], cap8)
+                assert got == set(st.pos[kr].tolist()), (e, l, b)
+                assert len(got) == int(budget[b, l])
+
+
 def test_sawtooth_and_no_op_from_empty():
     wl = TINY["mha_f16_d64"]
     eng = Engine(wl)
