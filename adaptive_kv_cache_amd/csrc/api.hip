@@ -50,7 +50,7 @@ int make_dims(const conf_params* p, Dims* d) {
   if (p->dtype16 != CONF_F16 && p->dtype16 != CONF_BF16) return CONF_E_UNSUPPORTED;
   const int G = p->n_q_heads / p->n_kv_heads;
   if (G > kMaxGroup) return CONF_E_UNSUPPORTED;
-  // the demotion spreads (K|V, KV head, channel) over 1024 threads, four each
+  // the demotion spreads (K|V, KV head, channel) over 512 threads, eight each
   if (p->n_kv_heads * p->head_dim > 2048) return CONF_E_UNSUPPORTED;
   if (p->window < 1 || p->protect < 1 || p->protect > p->window) return CONF_E_INVALID;
   if (p->n_high < 1 || p->n_low < p->n_high) return CONF_E_INVALID;

@@ -289,11 +289,13 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dim
   // store, from registers.  Bulk steps (step 0 after a long prefill) loop.
   const int per = dm.Hkv * D;
   constexpr int kMv = 2;       // move elements per thread in the register path
-  constexpr int kDemPer = 4;   // (K|V, KV head, channel) triples per thread (<= 2048, host-checked)
+  constexpr int kDemPer = 8;   // (K|V, KV head, channel) triples per thread: 2*Hkv*d <= 4096 (host-checked)
   const bool fast = nm8 * per <= kMv * kCompThreads && nm16 * per <= kMv * kCompThreads &&
                     nm8 <= kCompThreads && nm16 <= kCompThreads;
-  int8_t mk[kMv], mvv[kMv];
-  uint16_t wk[kMv], wv[kMv];
+  // loaded values are held widened to 32 bits: packing 8- or 16-bit values into
+  // shared registers would make each load wait before the next one issues
+  int32_t mk[kMv], mvv[kMv];
+  uint32_t wk[kMv], wv[kMv];
   int32_t mp8 = 0, mp16 = 0;
   float me8 = 0.f, me16 = 0.f;
   if (fast) {
@@ -358,19 +360,28 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dim
       dpos = pos16[jd];
       dema = ema16[jd];
     }
+    // every load first (each thread's triples are clamped into range, so no
+    // branch separates them), then the arithmetic: one memory round trip
+    uint32_t xr[kDemPer];
+    float oldr[kDemPer];
+#pragma unroll
+    for (int e = 0; e < kDemPer; ++e) {
+      if (e * kCompThreads >= 2 * per) break;  // uniform
+      const int pi = min(tid + e * kCompThreads, 2 * per - 1);
+      const int kind = pi / per, hc = pi % per, hk = hc / D, ch = hc % D;
+      const size_t u = (size_t)lb * dm.Hkv + hk;
+      xr[e] = kind == 0 ? ((const uint16_t*)c.k16)[u * (size_t)dm.cap16 * D + k16_off(jd, ch, D)]
+                        : ((const uint16_t*)c.v16)[u * (size_t)dm.cap16 * D + v16_off(jd, ch, D)];
+      oldr[e] = (kind == 0 ? c.k_amax : c.v_amax)[u * D + ch];
+    }
 #pragma unroll
     for (int e = 0; e < kDemPer; ++e) {
       const int pi = tid + e * kCompThreads;
       grew[e] = false;
       listed[e] = false;
       if (pi < 2 * per) {
-        const int kind = pi / per, hc = pi % per, hk = hc / D, ch = hc % D;
-        const size_t u = (size_t)lb * dm.Hkv + hk;
-        const float x = h16_to_f32(
-            kind == 0 ? ((const uint16_t*)c.k16)[u * (size_t)dm.cap16 * D + k16_off(jd, ch, D)]
-                      : ((const uint16_t*)c.v16)[u * (size_t)dm.cap16 * D + v16_off(jd, ch, D)],
-            dm.bf16);
-        const float old = (kind == 0 ? c.k_amax : c.v_amax)[u * D + ch];
+        const float x = h16_to_f32((uint16_t)xr[e], dm.bf16);
+        const float old = oldr[e];
         const float a = fabsf(x);
         const float am = a > old ? a : old;
         amax_new[e] = am;
@@ -398,8 +409,8 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dim
         const int k = i / per, r = i % per, hk = r / D, ch = r % D;
         const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap8 * D;
         const int dst = mv_at(S.mv8, mv8, 2 * k + 1);
-        c.k8[ub + k8_off(dst, ch, D)] = mk[e];
-        c.v8[ub + v8_off(dst, ch, D)] = mvv[e];
+        c.k8[ub + k8_off(dst, ch, D)] = (int8_t)mk[e];
+        c.v8[ub + v8_off(dst, ch, D)] = (int8_t)mvv[e];
       }
     }
     if (tid < nm8) {
@@ -435,8 +446,8 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dim
         const int k = i / per, r = i % per, hk = r / D, ch = r % D;
         const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap16 * D;
         const int dst = mv_at(S.mv16, mv16, 2 * k + 1);
-        ((uint16_t*)c.k16)[ub + k16_off(dst, ch, D)] = wk[e];
-        ((uint16_t*)c.v16)[ub + v16_off(dst, ch, D)] = wv[e];
+        ((uint16_t*)c.k16)[ub + k16_off(dst, ch, D)] = (uint16_t)wk[e];
+        ((uint16_t*)c.v16)[ub + v16_off(dst, ch, D)] = (uint16_t)wv[e];
       }
     }
     if (tid < nm16) {

@@ -116,6 +116,12 @@ def tiny_workloads() -> dict:
         name="gqa16_bf16_d64_long", n_layers=1, batch=2, n_q_heads=16, n_kv_heads=1, head_dim=64,
         vocab=500, dtype16="bf16", window=64, protect=8, n_high=100, n_low=300, prefill=2500,
         steps=8)
+    # 16 KV heads of 128 channels: the largest Hkv * d the library takes (2048), so the
+    # demotion uses all eight (K|V, head, channel) triples per compaction thread
+    w["mha16_f16_d128"] = Workload(
+        name="mha16_f16_d128", n_layers=1, batch=2, n_q_heads=16, n_kv_heads=16, head_dim=128,
+        vocab=600, dtype16="f16", window=40, protect=8, n_high=60, n_low=100, prefill=150,
+        steps=12)
     # every budget above what the LDS score rows hold, so that each step after the
     # first also takes the two-pass path with the window's free slot masked
     w["gqa16_bf16_d64_wide"] = Workload(
