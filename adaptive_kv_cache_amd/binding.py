@@ -24,7 +24,8 @@ ST_WINDOW_FULL, ST_INT8_FULL = 1, 2
 
 EXPORTED = ("conf_cache_layout", "conf_workspace_bytes", "conf_cache_reset", "conf_cache_ingest",
             "conf_confidence", "conf_decode_attn", "conf_rank_evict", "conf_compact_demote",
-            "conf_step", "conf_cache_export", "conf_last_error", "conf_status_string")
+            "conf_evict_compact", "conf_step", "conf_cache_export", "conf_last_error",
+            "conf_status_string")
 
 
 class ConfParams(ctypes.Structure):
@@ -69,6 +70,7 @@ def load() -> ctypes.CDLL:
         "conf_decode_attn": [P, C, c_int32, vp, vp, vp, vp, vp, vp],
         "conf_rank_evict": [P, C, c_int32, vp, vp, vp, vp],
         "conf_compact_demote": [P, C, c_int32, vp, vp, vp],
+        "conf_evict_compact": [P, C, c_int32, vp, vp, vp],
         "conf_step": [P, C, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         "conf_cache_export": [P, C, c_int32, c_int32, vp, vp, vp, vp, vp],
     }
@@ -228,6 +230,13 @@ class Engine:
         _check(self.lib.conf_compact_demote(ctypes.byref(self.p), ctypes.byref(self.cache), layer,
                                             _ptr(keep), _ptr(self.ws), self._stream()),
                "conf_compact_demote")
+
+    def evict_compact(self, layer: int, budget):
+        wl = self.wl
+        self._expect(budget, (wl.batch, wl.n_layers), torch.int32, "budget")
+        _check(self.lib.conf_evict_compact(ctypes.byref(self.p), ctypes.byref(self.cache), layer,
+                                           _ptr(budget), _ptr(self.ws), self._stream()),
+               "conf_evict_compact")
 
     def step(self, logits, q, k_new, v_new, out=None, c=None, budget=None):
         wl = self.wl

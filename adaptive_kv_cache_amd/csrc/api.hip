@@ -19,6 +19,8 @@ void launch_ingest(const Dims&, const conf_cache&, int, int, int, const void*, c
 void launch_select(const Dims&, const conf_cache&, int, int, const int32_t*, uint8_t*, hipStream_t);
 void launch_compact(const Dims&, const conf_cache&, int, int, const uint8_t*, int32_t*, int32_t*,
                     int32_t*, uint8_t*, hipStream_t);
+void launch_evict(const Dims&, const conf_cache&, int, int, const int32_t*, uint8_t*, int32_t*,
+                  int32_t*, int32_t*, uint8_t*, hipStream_t);
 void launch_export(const Dims&, const conf_cache&, int, int8_t*, int8_t*, void*, void*, hipStream_t);
 }  // namespace confkv
 
@@ -259,6 +261,20 @@ int conf_compact_demote(const conf_params* p, conf_cache* c, int32_t layer, cons
   return check_launch("conf_compact_demote");
 }
 
+int conf_evict_compact(const conf_params* p, conf_cache* c, int32_t layer, const int32_t* budget,
+                       void* ws, conf_stream_t stream) {
+  Dims d;
+  int rc = make_dims(p, &d);
+  if (rc) return rc;
+  int l0, nl;
+  if (!cache_ok(c) || !budget || !ws || !layer_range(d, layer, &l0, &nl)) return CONF_E_INVALID;
+  const WsMap w = make_ws(d);
+  launch_evict(d, *c, l0, nl, budget, at<uint8_t>(ws, w.keep), at<int32_t>(ws, w.plan),
+               at<int32_t>(ws, w.mv8), at<int32_t>(ws, w.mv16), at<uint8_t>(ws, w.wkeep),
+               (hipStream_t)stream);
+  return check_launch("conf_evict_compact");
+}
+
 int conf_step(const conf_params* p, conf_cache* c, const float* logits, const void* q,
               const void* k_new, const void* v_new, float* out, float* conf, int32_t* budget,
               void* ws, conf_stream_t stream) {
@@ -273,10 +289,8 @@ int conf_step(const conf_params* p, conf_cache* c, const float* logits, const vo
   launch_attn(d, *c, 0, d.L, q, k_new, v_new, out, at<float>(ws, w.massp), at<int32_t>(ws, w.snap),
               st);
   launch_confidence(d, logits, at<float>(ws, w.conf_part), conf, budget, st);
-  uint8_t* keep = at<uint8_t>(ws, w.keep);
-  launch_select(d, *c, 0, d.L, budget, keep, st);
-  launch_compact(d, *c, 0, d.L, keep, at<int32_t>(ws, w.plan), at<int32_t>(ws, w.mv8),
-                 at<int32_t>(ws, w.mv16), at<uint8_t>(ws, w.wkeep), st);
+  launch_evict(d, *c, 0, d.L, budget, at<uint8_t>(ws, w.keep), at<int32_t>(ws, w.plan),
+               at<int32_t>(ws, w.mv8), at<int32_t>(ws, w.mv16), at<uint8_t>(ws, w.wkeep), st);
   return check_launch("conf_step");
 }
 

@@ -5,7 +5,7 @@
 // 16-bit, older kept tokens are INT8 per head and channel (mixed-precision
 // storage); contiguous compaction keeps a dense layout with no indirection
 // tables (implementation).  Token ranking and eviction: EMA attention mass.
-#include "common.hpp"
+#include "select.hpp"
 
 namespace confkv {
 
@@ -141,19 +141,23 @@ constexpr int kCompThreads = 512;  // every (layer, sequence) workgroup resident
 typedef uint32_t cu4 __attribute__((ext_vector_type(4)));  // a 16-byte chunk
 constexpr int kCompWaves = kCompThreads / 64;
 constexpr int kMaxGrown = 512;    // grown channels requantised by the whole workgroup
-constexpr int kLdsFlags8 = 8192;  // INT8 keep flags cached in LDS (beyond: re-read)
+constexpr int kLdsFlags8 = 4096;  // INT8 keep flags cached in LDS (beyond: global memory)
 constexpr int kLdsFlags16 = 2048; // window keep flags cached in LDS (beyond: workspace)
 constexpr int kLdsMoves = 2048;   // move-list pairs per region kept in LDS (beyond: workspace)
 
-struct CompLds {
+struct CompFlags {  // keep flags cached in LDS
   uint8_t k8[kLdsFlags8];
   uint8_t k16[kLdsFlags16];
+};
+struct CompScratch {  // move lists and the grown-channel list
   int mv8[2 * kLdsMoves];   // (source, destination) pairs
   int mv16[2 * kLdsMoves];
-  int wcnt[2][kCompWaves];
-  int c8[kCompWaves], c16[kCompWaves];
   int grown[kMaxGrown];
   float gold[kMaxGrown], gnew[kMaxGrown];
+};
+struct CompMisc {
+  int wcnt[2][kCompWaves];
+  int c8[kCompWaves], c16[kCompWaves];
   int jd, ngrown, first_hole;
 };
 
@@ -213,64 +217,24 @@ __device__ inline int mv_at(const int* lds_mv, const int32_t* gl_mv, int e) {
   return e < 2 * kLdsMoves ? lds_mv[e] : gl_mv[e];
 }
 
-__global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dims dm, int layer0,
-                                                               const uint8_t* __restrict__ keep_all,
-                                                               int32_t* __restrict__ plan_all,
-                                                               int32_t* __restrict__ mv8_all,
-                                                               int32_t* __restrict__ mv16_all,
-                                                               uint8_t* __restrict__ wkeep_all) {
+// Steps 2-4 of the compaction for one (layer, sequence), once the keep flags are
+// known: F holds those of slots below kLdsFlags8 / kLdsFlags16, keep8 / wkeep (in
+// global memory) the others; the window flag of the demotee (window slot jd, or
+// -1) is already cleared, and n8n / n16n count the kept INT8 / window tokens.
+// M.ngrown must be 0.  All kCompThreads threads call it.
+__device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8, int n16, int t,
+                             int n8n, int n16n, int jd, const uint8_t* keep8, const uint8_t* wkeep,
+                             CompFlags& F, CompScratch& X, CompMisc& M, int32_t* plan_all,
+                             int32_t* mv8_all, int32_t* mv16_all) {
 #pragma clang fp contract(off)
-  __shared__ CompLds S;
-  const int lb = layer0 * dm.B + blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n8 = c.n8[lb], n16 = c.n16[lb], t = c.t[lb];
+  const int tid = threadIdx.x;
   const int D = dm.D;
-  const uint8_t* keep8 = keep_all + (size_t)lb * dm.capt;
-  const uint8_t* keep16 = keep8 + dm.cap8;
-  uint8_t* wkeep = wkeep_all + (size_t)lb * dm.cap16;
   int32_t* pos8 = c.pos8 + (size_t)lb * dm.cap8;
   float* ema8 = c.ema8 + (size_t)lb * dm.cap8;
   int32_t* pos16 = c.pos16 + (size_t)lb * dm.cap16;
   float* ema16 = c.ema16 + (size_t)lb * dm.cap16;
   int32_t* mv8 = mv8_all + (size_t)lb * dm.cap8;
   int32_t* mv16 = mv16_all + (size_t)lb * dm.cap16;
-  if (tid == 0) {
-    S.jd = -1;
-    S.ngrown = 0;
-  }
-  __syncthreads();
-  // ---- 1. keep flags (one read), counts, the demotee
-  const int target = t - dm.W;
-  int c8 = 0, c16 = 0;
-  for (int i = tid; i < n8; i += kCompThreads) {
-    const uint8_t k = keep8[i] ? 1 : 0;
-    if (i < kLdsFlags8) S.k8[i] = k;
-    c8 += k;
-  }
-  for (int w = tid; w < n16; w += kCompThreads) {
-    uint8_t k = keep16[w] ? 1 : 0;
-    if (k && target >= 0 && pos16[w] == target) {
-      S.jd = w;  // at most one slot holds this position
-      k = 0;
-    }
-    if (w < kLdsFlags16) S.k16[w] = k; else wkeep[w] = k;
-    c16 += k;
-  }
-  for (int off = 32; off > 0; off >>= 1) {
-    c8 += __shfl_xor(c8, off);
-    c16 += __shfl_xor(c16, off);
-  }
-  if (lane == 0) {
-    S.c8[wave] = c8;
-    S.c16[wave] = c16;
-  }
-  __syncthreads();
-  int n8n = 0, n16n = 0;
-  for (int w = 0; w < kCompWaves; ++w) {
-    n8n += S.c8[w];
-    n16n += S.c16[w];
-  }
-  const int jd = S.jd;
   // ---- 2. move lists.  With a demotee, the INT8 region grows to n8' + 1 and the
   // demotee takes its first hole (in the steady state: the slot of the evicted
   // INT8 token, so nothing moves); without one it ends at n8'.
@@ -278,12 +242,12 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dim
   const int n8end = n8n + (demote ? 1 : 0);
   const int nm8 = build_moves(
       n8, n8end, demote ? 1 : 0,
-      [&](int i) { return i < kLdsFlags8 ? S.k8[i] != 0 : keep8[i] != 0; }, S.mv8, mv8, S.wcnt,
-      &S.first_hole);
+      [&](int i) { return i < kLdsFlags8 ? F.k8[i] != 0 : keep8[i] != 0; }, X.mv8, mv8, M.wcnt,
+      &M.first_hole);
   const int nm16 = build_moves(
-      n16, n16n, 0, [&](int w) { return w < kLdsFlags16 ? S.k16[w] != 0 : wkeep[w] != 0; },
-      S.mv16, mv16, S.wcnt, &S.first_hole);
-  const int dest = demote ? S.first_hole : -1;  // written by build_moves before its last barrier
+      n16, n16n, 0, [&](int w) { return w < kLdsFlags16 ? F.k16[w] != 0 : wkeep[w] != 0; },
+      X.mv16, mv16, M.wcnt, &M.first_hole);
+  const int dest = demote ? M.first_hole : -1;  // written by build_moves before its last barrier
   // ---- 3. INT8 moves; the demotion's reads and arithmetic; window-move reads.
   // Steady state (a move or so per region): every load is issued before any
   // store, from registers.  Bulk steps (step 0 after a long prefill) loop.
@@ -305,31 +269,31 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dim
       if (i < nm8 * per) {
         const int k = i / per, r = i % per, hk = r / D, ch = r % D;
         const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap8 * D;
-        const int src = mv_at(S.mv8, mv8, 2 * k);
+        const int src = mv_at(X.mv8, mv8, 2 * k);
         mk[e] = c.k8[ub + k8_off(src, ch, D)];
         mvv[e] = c.v8[ub + v8_off(src, ch, D)];
       }
       if (i < nm16 * per) {
         const int k = i / per, r = i % per, hk = r / D, ch = r % D;
         const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap16 * D;
-        const int src = mv_at(S.mv16, mv16, 2 * k);
+        const int src = mv_at(X.mv16, mv16, 2 * k);
         wk[e] = ((const uint16_t*)c.k16)[ub + k16_off(src, ch, D)];
         wv[e] = ((const uint16_t*)c.v16)[ub + v16_off(src, ch, D)];
       }
     }
     if (tid < nm8) {
-      const int src = mv_at(S.mv8, mv8, 2 * tid);
+      const int src = mv_at(X.mv8, mv8, 2 * tid);
       mp8 = pos8[src];
       me8 = ema8[src];
     }
     if (tid < nm16) {
-      const int src = mv_at(S.mv16, mv16, 2 * tid);
+      const int src = mv_at(X.mv16, mv16, 2 * tid);
       mp16 = pos16[src];
       me16 = ema16[src];
     }
   } else {
     for (int k = tid; k < nm8; k += kCompThreads) {
-      const int src = mv_at(S.mv8, mv8, 2 * k), dst = mv_at(S.mv8, mv8, 2 * k + 1);
+      const int src = mv_at(X.mv8, mv8, 2 * k), dst = mv_at(X.mv8, mv8, 2 * k + 1);
       pos8[dst] = pos8[src];
       ema8[dst] = ema8[src];
     }
@@ -339,14 +303,14 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dim
     for (int i = tid; i < nm8 * dm.Hkv * (D / 16); i += kCompThreads) {
       const int k = i % nm8, r = i / nm8, hk = r / (D / 16), cg = r % (D / 16);
       const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap8 * D;
-      const int src = mv_at(S.mv8, mv8, 2 * k), dst = mv_at(S.mv8, mv8, 2 * k + 1);
+      const int src = mv_at(X.mv8, mv8, 2 * k), dst = mv_at(X.mv8, mv8, 2 * k + 1);
       *(cu4*)(c.k8 + ub + k8_off(dst, 16 * cg, D)) =
           *(const cu4*)(c.k8 + ub + k8_off(src, 16 * cg, D));
     }
     for (int i = tid; i < nm8 * per; i += kCompThreads) {
       const int k = i % nm8, r = i / nm8, hk = r / D, ch = r % D;
       const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap8 * D;
-      const int src = mv_at(S.mv8, mv8, 2 * k), dst = mv_at(S.mv8, mv8, 2 * k + 1);
+      const int src = mv_at(X.mv8, mv8, 2 * k), dst = mv_at(X.mv8, mv8, 2 * k + 1);
       c.v8[ub + v8_off(dst, ch, D)] = c.v8[ub + v8_off(src, ch, D)];
     }
   }
@@ -389,12 +353,12 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dim
         s_old[e] = old / 127.0f;
         if (a > old) {
           grew[e] = true;
-          const int slot = atomicAdd(&S.ngrown, 1);
+          const int slot = atomicAdd(&M.ngrown, 1);
           if (slot < kMaxGrown) {
             listed[e] = true;
-            S.grown[slot] = pi;
-            S.gold[slot] = s_old[e];
-            S.gnew[slot] = am / 127.0f;
+            X.grown[slot] = pi;
+            X.gold[slot] = s_old[e];
+            X.gnew[slot] = am / 127.0f;
           }
         }
       }
@@ -408,13 +372,13 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dim
       if (i < nm8 * per) {
         const int k = i / per, r = i % per, hk = r / D, ch = r % D;
         const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap8 * D;
-        const int dst = mv_at(S.mv8, mv8, 2 * k + 1);
+        const int dst = mv_at(X.mv8, mv8, 2 * k + 1);
         c.k8[ub + k8_off(dst, ch, D)] = (int8_t)mk[e];
         c.v8[ub + v8_off(dst, ch, D)] = (int8_t)mvv[e];
       }
     }
     if (tid < nm8) {
-      const int dst = mv_at(S.mv8, mv8, 2 * tid + 1);
+      const int dst = mv_at(X.mv8, mv8, 2 * tid + 1);
       pos8[dst] = mp8;
       ema8[dst] = me8;
     }
@@ -445,19 +409,19 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dim
       if (i < nm16 * per) {
         const int k = i / per, r = i % per, hk = r / D, ch = r % D;
         const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap16 * D;
-        const int dst = mv_at(S.mv16, mv16, 2 * k + 1);
+        const int dst = mv_at(X.mv16, mv16, 2 * k + 1);
         ((uint16_t*)c.k16)[ub + k16_off(dst, ch, D)] = (uint16_t)wk[e];
         ((uint16_t*)c.v16)[ub + v16_off(dst, ch, D)] = (uint16_t)wv[e];
       }
     }
     if (tid < nm16) {
-      const int dst = mv_at(S.mv16, mv16, 2 * tid + 1);
+      const int dst = mv_at(X.mv16, mv16, 2 * tid + 1);
       pos16[dst] = mp16;
       ema16[dst] = me16;
     }
   } else {
     for (int k = tid; k < nm16; k += kCompThreads) {
-      const int src = mv_at(S.mv16, mv16, 2 * k), dst = mv_at(S.mv16, mv16, 2 * k + 1);
+      const int src = mv_at(X.mv16, mv16, 2 * k), dst = mv_at(X.mv16, mv16, 2 * k + 1);
       pos16[dst] = pos16[src];
       ema16[dst] = ema16[src];
     }
@@ -466,30 +430,30 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dim
     for (int i = tid; i < nm16 * dm.Hkv * (D / 8); i += kCompThreads) {
       const int k = i % nm16, r = i / nm16, hk = r / (D / 8), cg = r % (D / 8);
       const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap16 * D;
-      const int src = mv_at(S.mv16, mv16, 2 * k), dst = mv_at(S.mv16, mv16, 2 * k + 1);
+      const int src = mv_at(X.mv16, mv16, 2 * k), dst = mv_at(X.mv16, mv16, 2 * k + 1);
       uint16_t* k16 = (uint16_t*)c.k16 + ub;
       *(cu4*)(k16 + k16_off(dst, 8 * cg, D)) = *(const cu4*)(k16 + k16_off(src, 8 * cg, D));
     }
     for (int i = tid; i < nm16 * per; i += kCompThreads) {
       const int k = i % nm16, r = i / nm16, hk = r / D, ch = r % D;
       const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap16 * D;
-      const int src = mv_at(S.mv16, mv16, 2 * k), dst = mv_at(S.mv16, mv16, 2 * k + 1);
+      const int src = mv_at(X.mv16, mv16, 2 * k), dst = mv_at(X.mv16, mv16, 2 * k + 1);
       uint16_t* v16 = (uint16_t*)c.v16 + ub;
       v16[v16_off(dst, ch, D)] = v16[v16_off(src, ch, D)];
     }
   }
   if (dest >= 0) {
     // codes of every other INT8 slot of each grown channel: c = clamp(rne((c * s_old) / s_new))
-    const int ng = S.ngrown;
+    const int ng = M.ngrown;
     const int ngl = ng < kMaxGrown ? ng : kMaxGrown;
     for (int i = tid; i < ngl * n8end; i += kCompThreads) {
       const int e = i % ngl, tok = i / ngl;
       if (tok == dest) continue;
-      const int pi = S.grown[e], kind = pi / per, hc = pi % per, hk = hc / D, ch = hc % D;
+      const int pi = X.grown[e], kind = pi / per, hc = pi % per, hk = hc / D, ch = hc % D;
       const size_t u = (size_t)lb * dm.Hkv + hk;
       int8_t* p = (kind == 0 ? c.k8 + u * (size_t)dm.cap8 * D + k8_off(tok, ch, D)
                              : c.v8 + u * (size_t)dm.cap8 * D + v8_off(tok, ch, D));
-      *p = quant_code((float)(*p) * S.gold[e], S.gnew[e]);
+      *p = quant_code((float)(*p) * X.gold[e], X.gnew[e]);
     }
     // a list overflow (very many channels grew at once): the owner requantises
 #pragma unroll
@@ -520,10 +484,141 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dim
   }
 }
 
+// Sums per-thread counts of kept INT8 and window tokens over the workgroup.
+__device__ inline void count_kept(int c8, int c16, CompMisc& M, int& n8n, int& n16n) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int off = 32; off > 0; off >>= 1) {
+    c8 += __shfl_xor(c8, off);
+    c16 += __shfl_xor(c16, off);
+  }
+  if (lane == 0) {
+    M.c8[wave] = c8;
+    M.c16[wave] = c16;
+  }
+  __syncthreads();
+  n8n = 0;
+  n16n = 0;
+  for (int w = 0; w < kCompWaves; ++w) {
+    n8n += M.c8[w];
+    n16n += M.c16[w];
+  }
+}
+
+__global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dims dm, int layer0,
+                                                               const uint8_t* __restrict__ keep_all,
+                                                               int32_t* __restrict__ plan_all,
+                                                               int32_t* __restrict__ mv8_all,
+                                                               int32_t* __restrict__ mv16_all,
+                                                               uint8_t* __restrict__ wkeep_all) {
+  __shared__ CompFlags F;
+  __shared__ CompScratch X;
+  __shared__ CompMisc M;
+  const int lb = layer0 * dm.B + blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n8 = c.n8[lb], n16 = c.n16[lb], t = c.t[lb];
+  const uint8_t* keep8 = keep_all + (size_t)lb * dm.capt;
+  const uint8_t* keep16 = keep8 + dm.cap8;
+  uint8_t* wkeep = wkeep_all + (size_t)lb * dm.cap16;
+  const int32_t* pos16 = c.pos16 + (size_t)lb * dm.cap16;
+  if (tid == 0) {
+    M.jd = -1;
+    M.ngrown = 0;
+  }
+  __syncthreads();
+  // ---- 1. keep flags (one read), counts, the demotee
+  const int target = t - dm.W;
+  int c8 = 0, c16 = 0;
+  for (int i = tid; i < n8; i += kCompThreads) {
+    const uint8_t k = keep8[i] ? 1 : 0;
+    if (i < kLdsFlags8) F.k8[i] = k;
+    c8 += k;
+  }
+  for (int w = tid; w < n16; w += kCompThreads) {
+    uint8_t k = keep16[w] ? 1 : 0;
+    if (k && target >= 0 && pos16[w] == target) {
+      M.jd = w;  // at most one slot holds this position
+      k = 0;
+    }
+    if (w < kLdsFlags16) F.k16[w] = k; else wkeep[w] = k;
+    c16 += k;
+  }
+  int n8n, n16n;
+  count_kept(c8, c16, M, n8n, n16n);
+  compact_core(c, dm, lb, n8, n16, t, n8n, n16n, M.jd, keep8, wkeep, F, X, M, plan_all, mv8_all,
+               mv16_all);
+}
+
+// (d)+(e) in one launch: the selection's keep flags go straight into the LDS
+// flag cache (INT8 flags beyond it into keep_all, window flags beyond it into
+// the window flag spill), the demotee is recognised from its ranking key (whose
+// low bits hold the position), and the compaction follows in the same
+// workgroup.  The selection's key cache and the compaction's move lists share
+// LDS.  Results are those of select_kernel followed by compact_kernel.
+__global__ __launch_bounds__(kCompThreads) void evict_kernel(conf_cache c, Dims dm, int layer0,
+                                                             const int32_t* __restrict__ budget,
+                                                             uint8_t* __restrict__ keep_all,
+                                                             int32_t* __restrict__ plan_all,
+                                                             int32_t* __restrict__ mv8_all,
+                                                             int32_t* __restrict__ mv16_all,
+                                                             uint8_t* __restrict__ wkeep_all) {
+  // 52 KB of LDS in all, so that three workgroups fit on a CU
+  __shared__ CompFlags F;
+  __shared__ union {
+    SelScratch sel;
+    CompScratch comp;
+  } U;
+  __shared__ SelMisc SM;
+  __shared__ CompMisc M;
+  const int lb = layer0 * dm.B + blockIdx.x;
+  const int l = lb / dm.B, b = lb % dm.B;
+  const int tid = threadIdx.x;
+  const int n8 = c.n8[lb], n16 = c.n16[lb], t = c.t[lb];
+  const int N = budget[(size_t)b * dm.L + l];
+  uint8_t* keep8 = keep_all + (size_t)lb * dm.capt;
+  uint8_t* wkeep = wkeep_all + (size_t)lb * dm.cap16;
+  const int32_t* pos16 = c.pos16 + (size_t)lb * dm.cap16;
+  if (tid == 0) {
+    M.jd = -1;
+    M.ngrown = 0;
+  }
+  __syncthreads();
+  const int target = t - dm.W;
+  int c8 = 0, c16 = 0;
+  select_core<kCompThreads>(c, dm, lb, n8, n16, t, N, U.sel, SM, [&](int j, int k, uint64_t key) {
+    if (j < n8) {
+      if (j < kLdsFlags8) F.k8[j] = (uint8_t)k; else keep8[j] = (uint8_t)k;
+      c8 += k;
+    } else {
+      const int w = j - n8;
+      if (k && target >= 0) {
+        // a protected token (key 0) is newer than t - W
+        const int p = key == kAllKept ? pos16[w] : key ? (int)(uint32_t)(key - 1ull) : -1;
+        if (p == target) {
+          M.jd = w;  // at most one slot holds this position
+          k = 0;
+        }
+      }
+      if (w < kLdsFlags16) F.k16[w] = (uint8_t)k; else wkeep[w] = (uint8_t)k;
+      c16 += k;
+    }
+  });
+  int n8n, n16n;
+  count_kept(c8, c16, M, n8n, n16n);  // its barrier also ends the key cache's use
+  compact_core(c, dm, lb, n8, n16, t, n8n, n16n, M.jd, keep8, wkeep, F, U.comp, M, plan_all,
+               mv8_all, mv16_all);
+}
+
 void launch_compact(const Dims& dm, const conf_cache& c, int layer0, int nl, const uint8_t* keep,
                     int32_t* plan, int32_t* mv8, int32_t* mv16, uint8_t* wkeep, hipStream_t st) {
   hipLaunchKernelGGL(compact_kernel, dim3(nl * dm.B), dim3(kCompThreads), 0, st, c, dm, layer0,
                      keep, plan, mv8, mv16, wkeep);
+}
+
+void launch_evict(const Dims& dm, const conf_cache& c, int layer0, int nl, const int32_t* budget,
+                  uint8_t* keep, int32_t* plan, int32_t* mv8, int32_t* mv16, uint8_t* wkeep,
+                  hipStream_t st) {
+  hipLaunchKernelGGL(evict_kernel, dim3(nl * dm.B), dim3(kCompThreads), 0, st, c, dm, layer0,
+                     budget, keep, plan, mv8, mv16, wkeep);
 }
 
 // ---------------------------------------------------------------- export

@@ -3,9 +3,9 @@
     python bench.py [--gpus 1] [--steps 384] [--warmup 128] [--workload NAME]
 
 A step is one pass of the whole path over one batch: decode attention with
-append and EMA (conf_decode_attn), confidence + budgets (conf_confidence),
-rank + select (conf_rank_evict) and compaction + demotion (conf_compact_demote),
-for every layer and sequence.  Inputs (logits, q, k, v of every step) are
+append and EMA (conf_decode_attn), confidence + budgets (conf_confidence), and
+rank + select with compaction + demotion in one launch (conf_evict_compact), for
+every layer and sequence.  Inputs (logits, q, k, v of every step) are
 generated on the device before the timed region; the prefilled context is
 ingested during set-up.  Default workload: the Qwen-32B-shaped GQA cache
 (64 layers, 40 query / 8 KV heads, head_dim 128, bf16, batch 8, 32768-token
@@ -64,14 +64,14 @@ def attn_bytes(wl, n8, nw):
 
 
 def step_bytes(wl, n8, nw, plan):
-    """Algorithmic bytes of one whole step: attention, logits, selection reads and
-    keep flags, hole-fill moves and the demotion (requantisation not counted)."""
+    """Algorithmic bytes of one whole step: attention, logits, the selection's reads,
+    hole-fill moves and the demotion (requantisation not counted; the keep flags
+    stay on chip in the fused selection + compaction launch)."""
     H, d, e = wl.n_kv_heads, wl.head_dim, 2
     n = n8 + nw + 1
     b = attn_bytes(wl, n8, nw)
     b += wl.batch * wl.vocab * 4
-    b += int((9 * n).sum())                                     # EMA + pos read, keep written
-    b += int(n.sum())                                           # keep read by the compaction
+    b += int((8 * n).sum())                                     # EMA + pos read
     moves8, moves16, dest = plan[..., 1], plan[..., 3], plan[..., 5]
     b += int((moves8 * (2 * 2 * H * d + 16)).sum())
     b += int((moves16 * (2 * 2 * H * d * e + 16)).sum())
@@ -158,7 +158,6 @@ def run(args):
     out = torch.empty(L, B, wl.n_q_heads, wl.head_dim, dtype=torch.float32, device=dev)
     conf = torch.empty(total, B, dtype=torch.float32, device=dev)
     budget = torch.empty(total, B, L, dtype=torch.int32, device=dev)
-    keep = torch.zeros(L, B, eng.cap8 + eng.cap16, dtype=torch.uint8, device=dev)
     n8_first = torch.empty(L, B, dtype=torch.int32, device=dev)
     n16_first = torch.empty_like(n8_first)
     plan_off = _plan_offset(eng)
@@ -181,8 +180,7 @@ def run(args):
             ev[1].record(main)
         if side is not main:
             main.wait_stream(side)
-        eng.rank_evict(-1, budget[s], keep=keep)
-        eng.compact_demote(-1, keep)
+        eng.evict_compact(-1, budget[s])
         if i is not None:
             hplan[i].copy_(ws_plan)
 

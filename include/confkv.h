@@ -202,9 +202,18 @@ int conf_compact_demote(const conf_params* p, conf_cache* c, int32_t layer, cons
                         void* ws, conf_stream_t stream);
 
 /*
+ * (d)+(e) in one launch [ranking][impl][storage]: the same result as
+ * conf_rank_evict followed by conf_compact_demote on the same layer selector,
+ * without a keep array (the flags stay on chip; those of caches larger than the
+ * on-chip flag cache go to ws).  budget: int32 [B][L].
+ */
+int conf_evict_compact(const conf_params* p, conf_cache* c, int32_t layer, const int32_t* budget,
+                       void* ws, conf_stream_t stream);
+
+/*
  * One full decode step of every layer and sequence: conf_decode_attn(-1),
- * conf_confidence, conf_rank_evict(-1), conf_compact_demote(-1).  c: fp32 [B]
- * and budget: int32 [B][L] receive (a)'s results; the keep flags live in ws.
+ * conf_confidence and conf_evict_compact(-1).  c: fp32 [B] and budget: int32
+ * [B][L] receive (a)'s results.
  */
 int conf_step(const conf_params* p, conf_cache* c, const float* logits, const void* q,
               const void* k_new, const void* v_new, float* out, float* conf, int32_t* budget,

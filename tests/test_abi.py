@@ -103,6 +103,8 @@ def test_null_pointers_rejected_before_launch(lib):
                                null) == E_INVALID
     assert lib.conf_compact_demote(ctypes.byref(p), ctypes.byref(cache), 0, null, null,
                                    null) == E_INVALID
+    assert lib.conf_evict_compact(ctypes.byref(p), ctypes.byref(cache), 0, null, null,
+                                  null) == E_INVALID
     assert lib.conf_step(ctypes.byref(p), ctypes.byref(cache), *([null] * 9)) == E_INVALID
     assert lib.conf_cache_reset(ctypes.byref(p), ctypes.byref(cache), null) == E_INVALID
     assert lib.conf_status_string(E_CAPACITY) == b"capacity too small"
@@ -114,6 +116,8 @@ def test_bad_layer_rejected(lib):
     cache = binding.ConfCache(*([0x1000] * 14))
     assert lib.conf_rank_evict(ctypes.byref(p), ctypes.byref(cache), 64, fake, fake, fake,
                                null := ctypes.c_void_p(0)) == E_INVALID
+    assert lib.conf_evict_compact(ctypes.byref(p), ctypes.byref(cache), -2, fake, fake,
+                                  null) == E_INVALID
     assert lib.conf_cache_export(ctypes.byref(p), ctypes.byref(cache), 0, 8, fake, fake, fake,
                                  fake, null) == E_INVALID
     assert lib.conf_cache_ingest(ctypes.byref(p), ctypes.byref(cache), 0, fake, fake, 40000,

@@ -163,10 +163,44 @@ def test_teacher_forced_steps(name):
     _say("  worst attention rel err", worst)
 
 
+@pytest.mark.parametrize("name", list(TINY))
+def test_evict_compact_equals_rank_then_compact(name):
+    """The fused selection + compaction launch leaves exactly the cache that
+    conf_rank_evict followed by conf_compact_demote leaves (every exported array,
+    bit for bit), for all layers at once and layer by layer."""
+    wl = TINY[name]
+    _say("evict_compact", name)
+    a, b = Engine(wl), Engine(wl)
+    if wl.prefill:
+        _ingest(a, wl, SEED)
+        _ingest(b, wl, SEED)
+    steps = min(wl.steps, 40) if wl.prefill else 200
+    for step in range(steps):
+        z = synth.logits(wl, step, SEED).cuda()
+        q = synth.q_new(wl, step, SEED).cuda()
+        k, v = (x.cuda() for x in synth.kv_new(wl, step, SEED))
+        for e in (a, b):
+            e.decode_attn(-1, q, k, v)
+        _, bud = a.confidence(z)
+        layers = [-1] if step % 2 == 0 else list(range(wl.n_layers))
+        for l in layers:
+            a.compact_demote(l, a.rank_evict(l, bud))
+            b.evict_compact(l, bud)
+        if step % 10 == 9 or step == steps - 1:
+            for l in range(wl.n_layers):
+                for s_ in range(wl.batch):
+                    ea, eb = a.export(l, s_), b.export(l, s_)
+                    for key in ea:
+                        assert np.array_equal(np.asarray(ea[key]), np.asarray(eb[key])), \
+                            (step, l, s_, key)
+    assert a.status() == 0 and b.status() == 0
+
+
 @pytest.mark.parametrize("name", ["gqa5_bf16_d128", "mha_f16_d64"])
 def test_conf_step_equals_the_four_calls(name):
-    """conf_step must be exactly decode_attn + confidence + rank_evict + compact_demote,
-    which the teacher-forced test holds to the oracle."""
+    """conf_step (attention, confidence and the fused selection + compaction) must
+    be exactly decode_attn + confidence + rank_evict + compact_demote, which the
+    teacher-forced test holds to the oracle."""
     wl = TINY[name]
     _say("conf_step", name)
     a, b = Engine(wl), Engine(wl)
