@@ -14,10 +14,12 @@ prefill with a planted needle, budgets 2048 / 4096, P 256, W 512).  The first
 unconfident phases) are warm-up; the timed steps are the steady state.
 
 The confidence reads only the step's logits, and the selection is the first call
-that needs its budgets, so it runs on a second stream (default priority) beside
-the attention; each step's second-stream work is ordered after the previous
-step, and the selection waits for it.  --one-stream issues every call in order
-on one stream.
+that needs its budgets, so on caches whose attention launch is long it runs on a
+second stream (default priority) beside the attention; each step's second-stream
+work is ordered after the previous step, and the selection waits for it.  On small
+caches the two cross-stream waits per step cost more than they hide (measured:
+the GPT-2-shaped caches ran 33-46% slower), so every call goes in order on one
+stream.  --streams 1|2 overrides the choice.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -164,7 +166,12 @@ def run(args):
     hplan = torch.empty(args.steps, L, B, 16, dtype=torch.int32, device=dev)
     ws_plan = eng.ws[plan_off:plan_off + L * B * 16 * 4].view(torch.int32).view(L, B, 16)
     main = torch.cuda.current_stream(dev)
-    side = main if args.one_stream else torch.cuda.Stream(device=dev)
+    streams = args.streams
+    if streams == "auto":
+        # K/V bytes one attention launch streams at the tight budget
+        kv = L * B * wl.n_kv_heads * wl.head_dim * (wl.n_high + wl.window) * 2
+        streams = "2" if kv >= 1 << 28 else "1"
+    side = main if streams == "1" else torch.cuda.Stream(device=dev)
     torch.cuda.synchronize()
     log("inputs resident; warm-up")
 
@@ -240,7 +247,7 @@ def run(args):
                    "prefill": wl.prefill, "n_high": wl.n_high, "n_low": wl.n_low,
                    "protect": wl.protect, "window": wl.window, "pyramid": wl.pyramid,
                    "vocab": wl.vocab, "mean_tokens_attended": round(n_mean, 1),
-                   "streams": 1 if args.one_stream else 2},
+                   "streams": int(streams)},
         "roofline": {"bound": "hbm", "kernel": "conf_decode_attn (one launch)",
                      "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
@@ -359,8 +366,9 @@ def main():
     ap.add_argument("--workload", default="qwen32b_gqa_b8_32k")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--one-stream", action="store_true",
-                    help="run the confidence in order on the attention's stream")
+    ap.add_argument("--streams", choices=("auto", "1", "2"), default="auto",
+                    help="2: confidence on a second stream beside the attention; auto: 2 when "
+                         "the attention streams at least 256 MB per launch")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--rocpd-summary", metavar="DB",
                     help="print per-kernel durations of a rocprofv3 database and exit")
