@@ -373,6 +373,21 @@ __device__ inline void compute_item(const Item& I, Buf<D>& K, const Buf<D>& V,
   }
 }
 
+// This wavefront's O tile into the merge buffer ob [4][G][D]: lane (g, hl) holds
+// heads 4g .. 4g+3 of channels 16*cb + hl.
+template <int D>
+__device__ inline void store_o(const WaveAcc<D>& wa, float* ob, int G) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, hl = lane & 15;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hh = 4 * g + i;
+    if (hh < G) {
+#pragma unroll
+      for (int cb = 0; cb < D / 16; ++cb) ob[(wave * G + hh) * D + 16 * cb + hl] = wa.o[cb][i];
+    }
+  }
+}
+
 // value scale of the INT8 part: the lane's O channels are 16*cb + lane%16
 template <int D>
 __device__ inline void apply_vscale(WaveAcc<D>& wa, const float* sv) {
@@ -438,11 +453,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     const uint16_t* __restrict__ knew_all, const uint16_t* __restrict__ vnew_all,
     float* __restrict__ out_all, float* __restrict__ massp_all, int32_t* __restrict__ snap,
     int score_cap) {
-  // Dynamic LDS: the query operands, then one region reused as scores
-  // [G][stride] and the O merge buffer [4][G][D].
+  // Dynamic LDS: the query operands, the O merge buffer [4][G][D], and the
+  // scores [G][stride] (apart, so that the O merge runs beside the mass pass).
   extern __shared__ float dyn_lds[];
   u4* s_qops = (u4*)dyn_lds;
-  float* smem = dyn_lds + 4 * qops_u4<D>(dm.G);
+  float* ob = dyn_lds + 4 * qops_u4<D>(dm.G);
+  float* smem = ob + kWaves * dm.G * D;
   __shared__ float s_qscale[kMaxGroup];    // power-of-two scale of the INT8 query
   __shared__ float s_snew[kMaxGroup];      // score of this step's token
   __shared__ float s_m[kWaves][kMaxGroup], s_l[kWaves][kMaxGroup];
@@ -600,10 +616,16 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
                                   scale16, head_ok, wa, vscaled, s_sv, nullptr, 0, 0.f, nullptr,
                                   cur, true);
   }
-  // ---- merge the waves' running (max, sum) and add this step's token
+  // ---- merge the waves' running (max, sum) and add this step's token.  On the
+  // single-pass path each wavefront's O (value scale applied, not yet normalised)
+  // goes to LDS before the barrier, and the O merge shares a phase with the mass.
   if (lane < 16) {
     s_m[wave][lane] = wa.m;
     s_l[wave][lane] = wa.l;
+  }
+  if (in_lds) {
+    if (!vscaled) apply_vscale<D>(wa, s_sv);
+    store_o<D>(wa, ob, G);
   }
   __syncthreads();
   if (tid < G) {
@@ -622,6 +644,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
   }
   __syncthreads();
 
+  float* out = out_all + ((size_t)lbl * dm.Hq + (size_t)hk * G) * D;
   if (in_lds) {
     // per-token mass of this query group from the stored scores
     for (int j0 = tid; j0 < n; j0 += 4 * kAttnThreads) {
@@ -641,7 +664,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
         if (j < n) massp[j < n8 ? j : dm.cap8 + (j - n8)] = s[k];
       }
     }
-    __syncthreads();
+    // O = sum over wavefronts of O_w * exp(m_w - lse), plus this step's token
+    for (int i = tid; i < G * D; i += kAttnThreads) {
+      const int hh = i / D, ch = i % D;
+      float s = 0.f;
+      for (int w = 0; w < kWaves; ++w) s += ob[(w * G + hh) * D + ch] * s_f[w][hh];
+      out[i] = fmaf(s_pnew[hh], s_vn[ch], s);
+    }
   } else {
     // second pass: probabilities with the final normaliser, mass and values
     const float lse = head_ok ? s_lse[hl] : 0.f;
@@ -653,27 +682,15 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
       for (int h = 0; h < G; ++h) s += s_pnew[h];
       massp[dm.cap8 + nw] = s;
     }
-  }
-  if (!vscaled) apply_vscale<D>(wa, s_sv);
-
-  // ---- merge the waves' O tiles in LDS (the score region is free again)
-  float* ob = smem;  // [kWaves][G][D]
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int hh = 4 * g + i;
-    if (hh < G) {
-      const float f = in_lds ? s_f[wave][hh] : 1.0f;
-#pragma unroll
-      for (int cb = 0; cb < D / 16; ++cb) ob[(wave * G + hh) * D + 16 * cb + hl] = wa.o[cb][i] * f;
+    if (!vscaled) apply_vscale<D>(wa, s_sv);
+    store_o<D>(wa, ob, G);
+    __syncthreads();
+    for (int i = tid; i < G * D; i += kAttnThreads) {
+      const int hh = i / D, ch = i % D;
+      float s = 0.f;
+      for (int w = 0; w < kWaves; ++w) s += ob[(w * G + hh) * D + ch];
+      out[i] = fmaf(s_pnew[hh], s_vn[ch], s);
     }
-  }
-  __syncthreads();
-  float* out = out_all + ((size_t)lbl * dm.Hq + (size_t)hk * G) * D;
-  for (int i = tid; i < G * D; i += kAttnThreads) {
-    const int hh = i / D, ch = i % D;
-    float s = 0.f;
-    for (int w = 0; w < kWaves; ++w) s += ob[(w * G + hh) * D + ch];
-    out[i] = fmaf(s_pnew[hh], s_vn[ch], s);
   }
 }
 
@@ -721,21 +738,22 @@ __global__ __launch_bounds__(kEmaThreads) void ema_kernel(conf_cache c, Dims dm,
 }
 
 // Scores one workgroup keeps in LDS (G rows of stride cap | 1, odd so that the
-// 16 heads of a store spread over banks), next to the query operands.
+// 16 heads of a store spread over banks), after the query operands and the O
+// merge buffer.
 static int qops_bytes(const Dims& dm) {
   return 16 * (dm.D == 64 ? qops_u4<64>(dm.G) : qops_u4<128>(dm.G));
 }
 
 int attn_score_cap(const Dims& dm) {
-  int cap = (kLdsDynBytes - qops_bytes(dm)) / (4 * dm.G) - 1;
+  int cap = (kLdsDynBytes - qops_bytes(dm) - 4 * kWaves * dm.G * dm.D) / (4 * dm.G) - 1;
   cap &= ~1;
   return cap < dm.capt + 2 ? cap : dm.capt + 2;
 }
 
 size_t attn_dyn_lds(const Dims& dm) {
   const size_t sc = (size_t)dm.G * (attn_score_cap(dm) | 1);
-  const size_t ob = (size_t)kWaves * dm.G * dm.D;  // also covers the [G + 1][D] staging
-  return (size_t)qops_bytes(dm) + 4 * (sc > ob ? sc : ob);
+  const size_t ob = (size_t)kWaves * dm.G * dm.D;
+  return (size_t)qops_bytes(dm) + 4 * (ob + sc);
 }
 
 template <int D, bool BF16>
