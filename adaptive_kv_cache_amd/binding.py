@@ -24,8 +24,8 @@ ST_WINDOW_FULL, ST_INT8_FULL = 1, 2
 
 EXPORTED = ("conf_cache_layout", "conf_workspace_bytes", "conf_cache_reset", "conf_cache_ingest",
             "conf_confidence", "conf_decode_attn", "conf_rank_evict", "conf_compact_demote",
-            "conf_evict_compact", "conf_step", "conf_cache_export", "conf_last_error",
-            "conf_status_string")
+            "conf_evict_compact", "conf_attend", "conf_ema_evict_compact", "conf_step",
+            "conf_cache_export", "conf_last_error", "conf_status_string")
 
 
 class ConfParams(ctypes.Structure):
@@ -71,6 +71,8 @@ def load() -> ctypes.CDLL:
         "conf_rank_evict": [P, C, c_int32, vp, vp, vp, vp],
         "conf_compact_demote": [P, C, c_int32, vp, vp, vp],
         "conf_evict_compact": [P, C, c_int32, vp, vp, vp],
+        "conf_attend": [P, C, c_int32, vp, vp, vp, vp, vp, vp],
+        "conf_ema_evict_compact": [P, C, c_int32, vp, vp, vp],
         "conf_step": [P, C, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         "conf_cache_export": [P, C, c_int32, c_int32, vp, vp, vp, vp, vp],
     }
@@ -197,7 +199,7 @@ class Engine:
                                         _ptr(self.ws), self._stream()), "conf_confidence")
         return c, budget
 
-    def decode_attn(self, layer: int, q, k_new, v_new, out=None):
+    def _attention(self, layer, q, k_new, v_new, out, fn, name):
         wl = self.wl
         self._expect(q, self._layer_shape(layer, wl.batch, wl.n_q_heads, wl.head_dim),
                      self.dtype16, "q")
@@ -207,10 +209,25 @@ class Engine:
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=self.device)
         self._expect(out, q.shape, torch.float32, "out")
-        _check(self.lib.conf_decode_attn(ctypes.byref(self.p), ctypes.byref(self.cache), layer,
-                                         _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out),
-                                         _ptr(self.ws), self._stream()), "conf_decode_attn")
+        _check(fn(ctypes.byref(self.p), ctypes.byref(self.cache), layer, _ptr(q), _ptr(k_new),
+                  _ptr(v_new), _ptr(out), _ptr(self.ws), self._stream()), name)
         return out
+
+    def decode_attn(self, layer: int, q, k_new, v_new, out=None):
+        return self._attention(layer, q, k_new, v_new, out, self.lib.conf_decode_attn,
+                               "conf_decode_attn")
+
+    def attend(self, layer: int, q, k_new, v_new, out=None):
+        """conf_attend: the attention without its EMA update, which the next
+        ema_evict_compact on the same layers applies."""
+        return self._attention(layer, q, k_new, v_new, out, self.lib.conf_attend, "conf_attend")
+
+    def ema_evict_compact(self, layer: int, budget):
+        wl = self.wl
+        self._expect(budget, (wl.batch, wl.n_layers), torch.int32, "budget")
+        _check(self.lib.conf_ema_evict_compact(ctypes.byref(self.p), ctypes.byref(self.cache),
+                                               layer, _ptr(budget), _ptr(self.ws), self._stream()),
+               "conf_ema_evict_compact")
 
     def rank_evict(self, layer: int, budget, keep=None):
         wl = self.wl

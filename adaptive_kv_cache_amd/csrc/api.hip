@@ -13,14 +13,14 @@ int conf_vchunks(int V);
 void launch_confidence(const Dims&, const float*, float*, float*, int32_t*, hipStream_t);
 void launch_reset(const Dims&, const conf_cache&, hipStream_t);
 void launch_attn(const Dims&, const conf_cache&, int, int, const void*, const void*, const void*,
-                 float*, float*, int32_t*, hipStream_t);
+                 float*, float*, int32_t*, bool, hipStream_t);
 void launch_ingest(const Dims&, const conf_cache&, int, int, int, const void*, const void*,
                    hipStream_t);
 void launch_select(const Dims&, const conf_cache&, int, int, const int32_t*, uint8_t*, hipStream_t);
 void launch_compact(const Dims&, const conf_cache&, int, int, const uint8_t*, int32_t*, int32_t*,
                     int32_t*, uint8_t*, hipStream_t);
 void launch_evict(const Dims&, const conf_cache&, int, int, const int32_t*, uint8_t*, int32_t*,
-                  int32_t*, int32_t*, uint8_t*, hipStream_t);
+                  int32_t*, int32_t*, uint8_t*, const float*, const int32_t*, bool, hipStream_t);
 void launch_export(const Dims&, const conf_cache&, int, int8_t*, int8_t*, void*, void*, hipStream_t);
 }  // namespace confkv
 
@@ -219,9 +219,9 @@ int conf_confidence(const conf_params* p, const float* logits, float* c, int32_t
   return check_launch("conf_confidence");
 }
 
-int conf_decode_attn(const conf_params* p, conf_cache* c, int32_t layer, const void* q,
-                     const void* k_new, const void* v_new, float* out, void* ws,
-                     conf_stream_t stream) {
+static int decode_attn(const conf_params* p, conf_cache* c, int32_t layer, const void* q,
+                       const void* k_new, const void* v_new, float* out, void* ws,
+                       conf_stream_t stream, bool with_ema, const char* name) {
   Dims d;
   int rc = make_dims(p, &d);
   if (rc) return rc;
@@ -230,10 +230,20 @@ int conf_decode_attn(const conf_params* p, conf_cache* c, int32_t layer, const v
       !layer_range(d, layer, &l0, &nl))
     return CONF_E_INVALID;
   const WsMap w = make_ws(d);
-  hipStream_t st = (hipStream_t)stream;
   launch_attn(d, *c, l0, nl, q, k_new, v_new, out, at<float>(ws, w.massp), at<int32_t>(ws, w.snap),
-              st);
-  return check_launch("conf_decode_attn");
+              with_ema, (hipStream_t)stream);
+  return check_launch(name);
+}
+
+int conf_decode_attn(const conf_params* p, conf_cache* c, int32_t layer, const void* q,
+                     const void* k_new, const void* v_new, float* out, void* ws,
+                     conf_stream_t stream) {
+  return decode_attn(p, c, layer, q, k_new, v_new, out, ws, stream, true, "conf_decode_attn");
+}
+
+int conf_attend(const conf_params* p, conf_cache* c, int32_t layer, const void* q,
+                const void* k_new, const void* v_new, float* out, void* ws, conf_stream_t stream) {
+  return decode_attn(p, c, layer, q, k_new, v_new, out, ws, stream, false, "conf_attend");
 }
 
 int conf_rank_evict(const conf_params* p, conf_cache* c, int32_t layer, const int32_t* budget,
@@ -261,8 +271,8 @@ int conf_compact_demote(const conf_params* p, conf_cache* c, int32_t layer, cons
   return check_launch("conf_compact_demote");
 }
 
-int conf_evict_compact(const conf_params* p, conf_cache* c, int32_t layer, const int32_t* budget,
-                       void* ws, conf_stream_t stream) {
+static int evict(const conf_params* p, conf_cache* c, int32_t layer, const int32_t* budget,
+                 void* ws, conf_stream_t stream, bool with_ema, const char* name) {
   Dims d;
   int rc = make_dims(p, &d);
   if (rc) return rc;
@@ -271,8 +281,18 @@ int conf_evict_compact(const conf_params* p, conf_cache* c, int32_t layer, const
   const WsMap w = make_ws(d);
   launch_evict(d, *c, l0, nl, budget, at<uint8_t>(ws, w.keep), at<int32_t>(ws, w.plan),
                at<int32_t>(ws, w.mv8), at<int32_t>(ws, w.mv16), at<uint8_t>(ws, w.wkeep),
-               (hipStream_t)stream);
-  return check_launch("conf_evict_compact");
+               at<float>(ws, w.massp), at<int32_t>(ws, w.snap), with_ema, (hipStream_t)stream);
+  return check_launch(name);
+}
+
+int conf_evict_compact(const conf_params* p, conf_cache* c, int32_t layer, const int32_t* budget,
+                       void* ws, conf_stream_t stream) {
+  return evict(p, c, layer, budget, ws, stream, false, "conf_evict_compact");
+}
+
+int conf_ema_evict_compact(const conf_params* p, conf_cache* c, int32_t layer,
+                           const int32_t* budget, void* ws, conf_stream_t stream) {
+  return evict(p, c, layer, budget, ws, stream, true, "conf_ema_evict_compact");
 }
 
 int conf_step(const conf_params* p, conf_cache* c, const float* logits, const void* q,
@@ -287,10 +307,11 @@ int conf_step(const conf_params* p, conf_cache* c, const float* logits, const vo
   const WsMap w = make_ws(d);
   hipStream_t st = (hipStream_t)stream;
   launch_attn(d, *c, 0, d.L, q, k_new, v_new, out, at<float>(ws, w.massp), at<int32_t>(ws, w.snap),
-              st);
+              false, st);
   launch_confidence(d, logits, at<float>(ws, w.conf_part), conf, budget, st);
   launch_evict(d, *c, 0, d.L, budget, at<uint8_t>(ws, w.keep), at<int32_t>(ws, w.plan),
-               at<int32_t>(ws, w.mv8), at<int32_t>(ws, w.mv16), at<uint8_t>(ws, w.wkeep), st);
+               at<int32_t>(ws, w.mv8), at<int32_t>(ws, w.mv16), at<uint8_t>(ws, w.wkeep),
+               at<float>(ws, w.massp), at<int32_t>(ws, w.snap), true, st);
   return check_launch("conf_step");
 }
 

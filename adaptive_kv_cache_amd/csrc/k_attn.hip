@@ -38,7 +38,7 @@
 // mass is formed once the softmax normaliser is final.  Otherwise (the first step
 // after a long prefill) the kernel makes two passes over the keys: the first
 // finds each head's log-sum-exp, the second forms probabilities, mass and values.
-#include "common.hpp"
+#include "ema.hpp"
 
 namespace confkv {
 
@@ -694,45 +694,20 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
   }
 }
 
-// EMA of every token once all KV heads' mass rows exist (kernel boundary).
-// mass_j = (sum of the KV heads' rows, in index order) / Hq;
-// e <- decay*e + (1-decay)*mass; the appended token starts from e = 0 and takes
-// position t+1.  Each (layer, sequence) is spread over gridDim.y workgroups that
-// read the sizes from the attention kernel's snapshot; workgroup y = 0 then
-// advances n16 and t.
+// EMA of every token once all KV heads' mass rows exist (kernel boundary).  Each
+// (layer, sequence) is spread over gridDim.y workgroups that read the sizes from
+// the attention kernel's snapshot; workgroup y = 0 then advances n16 and t.
 constexpr int kEmaThreads = 256;
 
 __global__ __launch_bounds__(kEmaThreads) void ema_kernel(conf_cache c, Dims dm, int layer0,
                                                           const float* __restrict__ massp_all,
                                                           const int32_t* __restrict__ snap) {
-#pragma clang fp contract(off)
   const int lb = layer0 * dm.B + blockIdx.x;
   const int n8 = snap[3 * lb], nw = snap[3 * lb + 1], t = snap[3 * lb + 2];
-  const int appended = nw < dm.cap16;
-  const float* rows = massp_all + (size_t)lb * dm.Hkv * dm.capt;
-  const float hq = (float)dm.Hq;
-  for (int j = blockIdx.y * kEmaThreads + threadIdx.x; j < n8 + nw + appended;
-       j += gridDim.y * kEmaThreads) {
-    const int idx = j < n8 ? j : dm.cap8 + (j - n8);
-    float a = 0.f;
-    for (int hk = 0; hk < dm.Hkv; ++hk) a += rows[(size_t)hk * dm.capt + idx];
-    a = a / hq;
-    if (j < n8) {
-      float* e = c.ema8 + (size_t)lb * dm.cap8 + j;
-      *e = dm.decay * (*e) + dm.one_minus_decay * a;
-    } else {
-      const int w = j - n8;
-      float* e = c.ema16 + (size_t)lb * dm.cap16 + w;
-      if (w == nw) {
-        *e = dm.one_minus_decay * a;  // decay * 0 + (1 - decay) * mass
-        c.pos16[(size_t)lb * dm.cap16 + w] = t + 1;
-      } else {
-        *e = dm.decay * (*e) + dm.one_minus_decay * a;
-      }
-    }
-  }
+  ema_tokens(c, dm, lb, massp_all, n8, nw, t, blockIdx.y * kEmaThreads + threadIdx.x,
+             gridDim.y * kEmaThreads);
   if (blockIdx.y == 0 && threadIdx.x == 0) {
-    c.n16[lb] = nw + appended;
+    c.n16[lb] = nw + (nw < dm.cap16);
     c.t[lb] = t + 1;
   }
 }
@@ -759,7 +734,7 @@ size_t attn_dyn_lds(const Dims& dm) {
 template <int D, bool BF16>
 static void launch_t(const Dims& dm, const conf_cache& c, int layer0, int nl, const void* q,
                      const void* k_new, const void* v_new, float* out, float* massp,
-                     int32_t* snap, hipStream_t st) {
+                     int32_t* snap, bool with_ema, hipStream_t st) {
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute((const void*)attn_kernel<D, BF16>,
@@ -770,6 +745,7 @@ static void launch_t(const Dims& dm, const conf_cache& c, int layer0, int nl, co
                      attn_dyn_lds(dm), st, c, dm, layer0, (const uint16_t*)q,
                      (const uint16_t*)k_new, (const uint16_t*)v_new, out, massp, snap,
                      attn_score_cap(dm));
+  if (!with_ema) return;  // a fused EMA + selection + compaction launch follows
   // token chunks per (layer, sequence): enough for the largest budget plus the
   // window growth of one phase; larger caches loop inside the workgroups
   const int typical = (dm.n_low > dm.n_high ? dm.n_low : dm.n_high) + dm.W + 1;
@@ -779,15 +755,24 @@ static void launch_t(const Dims& dm, const conf_cache& c, int layer0, int nl, co
                      massp, snap);
 }
 
+template <int D_, bool BF16_>
+struct Variant {
+  static constexpr int D = D_;
+  static constexpr bool BF16 = BF16_;
+};
+
 void launch_attn(const Dims& dm, const conf_cache& c, int layer0, int nl, const void* q,
                  const void* k_new, const void* v_new, float* out, float* massp, int32_t* snap,
-                 hipStream_t st) {
+                 bool with_ema, hipStream_t st) {
+  auto go = [&](auto kernel_tag) {
+    constexpr int D = decltype(kernel_tag)::D;
+    constexpr bool BF16 = decltype(kernel_tag)::BF16;
+    launch_t<D, BF16>(dm, c, layer0, nl, q, k_new, v_new, out, massp, snap, with_ema, st);
+  };
   if (dm.D == 64) {
-    if (dm.bf16) launch_t<64, true>(dm, c, layer0, nl, q, k_new, v_new, out, massp, snap, st);
-    else launch_t<64, false>(dm, c, layer0, nl, q, k_new, v_new, out, massp, snap, st);
+    if (dm.bf16) go(Variant<64, true>{}); else go(Variant<64, false>{});
   } else {
-    if (dm.bf16) launch_t<128, true>(dm, c, layer0, nl, q, k_new, v_new, out, massp, snap, st);
-    else launch_t<128, false>(dm, c, layer0, nl, q, k_new, v_new, out, massp, snap, st);
+    if (dm.bf16) go(Variant<128, true>{}); else go(Variant<128, false>{});
   }
 }
 

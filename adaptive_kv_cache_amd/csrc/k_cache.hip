@@ -5,6 +5,7 @@
 // 16-bit, older kept tokens are INT8 per head and channel (mixed-precision
 // storage); contiguous compaction keeps a dense layout with no indirection
 // tables (implementation).  Token ranking and eviction: EMA attention mass.
+#include "ema.hpp"
 #include "select.hpp"
 
 namespace confkv {
@@ -548,19 +549,88 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dim
                mv16_all);
 }
 
+// The EMA update of (layer, sequence) lb, as ema_tokens computes it (same
+// arithmetic, same order over the KV heads), by a kCompThreads workgroup whose
+// thread tid takes tokens tid, tid + kCompThreads, ...  Each round issues the loads
+// of five tokens (EMA, position, then the mass rows two heads at a time) before
+// the arithmetic.  With the
+// selection's keys in LDS, each token's new (bits(e) << 32 | pos) is left in
+// X.key[j] for select_core, which then reads no memory in its first pass.
+__device__ inline void ema_pairs(const conf_cache& c, const Dims& dm, int lb,
+                                 const float* __restrict__ massp_all, int n8, int nw, int t,
+                                 SelScratch& X) {
+#pragma clang fp contract(off)
+  const int appended = nw < dm.cap16;
+  const int end = n8 + nw + appended;
+  const bool cached = end <= kSelLdsKeys;
+  const float* rows = massp_all + (size_t)lb * dm.Hkv * dm.capt;
+  float* ema8 = c.ema8 + (size_t)lb * dm.cap8;
+  float* ema16 = c.ema16 + (size_t)lb * dm.cap16;
+  const int32_t* pos8 = c.pos8 + (size_t)lb * dm.cap8;
+  int32_t* pos16 = c.pos16 + (size_t)lb * dm.cap16;
+  const float hq = (float)dm.Hq;
+  constexpr int kT = 5;  // one round up to 2560 tokens, within 80 VGPRs (6 waves/SIMD)
+  for (int jb = threadIdx.x; jb < end; jb += kT * kCompThreads) {
+    int idx[kT], po[kT];
+    float a[kT], eo[kT];
+#pragma unroll
+    for (int k = 0; k < kT; ++k) {
+      const int j = jb + k * kCompThreads;
+      idx[k] = j >= end ? 0 : j < n8 ? j : dm.cap8 + (j - n8);
+      const int w = j >= end ? 0 : j - n8;
+      eo[k] = j < n8 ? ema8[idx[k]] : ema16[w];
+      po[k] = j < n8 ? pos8[idx[k]] : pos16[w];
+      a[k] = 0.f;
+    }
+#pragma unroll 2
+    for (int hk = 0; hk < dm.Hkv; ++hk)
+#pragma unroll
+      for (int k = 0; k < kT; ++k) a[k] += rows[(size_t)hk * dm.capt + idx[k]];
+#pragma unroll
+    for (int k = 0; k < kT; ++k) {
+      const int j = jb + k * kCompThreads;
+      if (j >= end) continue;
+      const float m = a[k] / hq;
+      float e;
+      int p = po[k];
+      if (j < n8) {
+        e = dm.decay * eo[k] + dm.one_minus_decay * m;
+        ema8[j] = e;
+      } else if (j - n8 == nw) {
+        e = dm.one_minus_decay * m;  // decay * 0 + (1 - decay) * mass
+        p = t + 1;
+        ema16[nw] = e;
+        pos16[nw] = p;
+      } else {
+        e = dm.decay * eo[k] + dm.one_minus_decay * m;
+        ema16[j - n8] = e;
+      }
+      if (cached) X.key[j] = ((uint64_t)__float_as_uint(e) << 32) | (uint32_t)p;
+    }
+  }
+}
+
 // (d)+(e) in one launch: the selection's keep flags go straight into the LDS
 // flag cache (INT8 flags beyond it into keep_all, window flags beyond it into
 // the window flag spill), the demotee is recognised from its ranking key (whose
 // low bits hold the position), and the compaction follows in the same
 // workgroup.  The selection's key cache and the compaction's move lists share
 // LDS.  Results are those of select_kernel followed by compact_kernel.
-__global__ __launch_bounds__(kCompThreads) void evict_kernel(conf_cache c, Dims dm, int layer0,
+// With EMA, (c) comes first, in place of the EMA kernel after an attention launch
+// that left it pending: the sizes before the step's append come from the
+// attention's snapshot, every token's EMA is updated (and the appended token's
+// position written), and n16 and t advance.
+template <bool EMA>
+// (six wavefronts per SIMD: three workgroups per CU, which the LDS allows too)
+__global__ __launch_bounds__(kCompThreads, 6) void evict_kernel(conf_cache c, Dims dm, int layer0,
                                                              const int32_t* __restrict__ budget,
                                                              uint8_t* __restrict__ keep_all,
                                                              int32_t* __restrict__ plan_all,
                                                              int32_t* __restrict__ mv8_all,
                                                              int32_t* __restrict__ mv16_all,
-                                                             uint8_t* __restrict__ wkeep_all) {
+                                                             uint8_t* __restrict__ wkeep_all,
+                                                             const float* __restrict__ massp_all,
+                                                             const int32_t* __restrict__ snap) {
   // 52 KB of LDS in all, so that three workgroups fit on a CU
   __shared__ CompFlags F;
   __shared__ union {
@@ -572,7 +642,20 @@ __global__ __launch_bounds__(kCompThreads) void evict_kernel(conf_cache c, Dims 
   const int lb = layer0 * dm.B + blockIdx.x;
   const int l = lb / dm.B, b = lb % dm.B;
   const int tid = threadIdx.x;
-  const int n8 = c.n8[lb], n16 = c.n16[lb], t = c.t[lb];
+  int n8, n16, t;
+  if constexpr (EMA) {
+    n8 = snap[3 * lb];
+    const int nw = snap[3 * lb + 1], t0 = snap[3 * lb + 2];
+    n16 = nw + (nw < dm.cap16);
+    t = t0 + 1;
+    ema_pairs(c, dm, lb, massp_all, n8, nw, t0, U.sel);
+    if (tid == 0) c.t[lb] = t;  // n16 is written by the compaction
+    __syncthreads();  // the EMA and the appended position are in memory for the selection
+  } else {
+    n8 = c.n8[lb];
+    n16 = c.n16[lb];
+    t = c.t[lb];
+  }
   const int N = budget[(size_t)b * dm.L + l];
   uint8_t* keep8 = keep_all + (size_t)lb * dm.capt;
   uint8_t* wkeep = wkeep_all + (size_t)lb * dm.cap16;
@@ -584,7 +667,7 @@ __global__ __launch_bounds__(kCompThreads) void evict_kernel(conf_cache c, Dims 
   __syncthreads();
   const int target = t - dm.W;
   int c8 = 0, c16 = 0;
-  select_core<kCompThreads>(c, dm, lb, n8, n16, t, N, U.sel, SM, [&](int j, int k, uint64_t key) {
+  select_core<kCompThreads, EMA>(c, dm, lb, n8, n16, t, N, U.sel, SM, [&](int j, int k, uint64_t key) {
     if (j < n8) {
       if (j < kLdsFlags8) F.k8[j] = (uint8_t)k; else keep8[j] = (uint8_t)k;
       c8 += k;
@@ -616,9 +699,13 @@ void launch_compact(const Dims& dm, const conf_cache& c, int layer0, int nl, con
 
 void launch_evict(const Dims& dm, const conf_cache& c, int layer0, int nl, const int32_t* budget,
                   uint8_t* keep, int32_t* plan, int32_t* mv8, int32_t* mv16, uint8_t* wkeep,
-                  hipStream_t st) {
-  hipLaunchKernelGGL(evict_kernel, dim3(nl * dm.B), dim3(kCompThreads), 0, st, c, dm, layer0,
-                     budget, keep, plan, mv8, mv16, wkeep);
+                  const float* massp, const int32_t* snap, bool with_ema, hipStream_t st) {
+  if (with_ema)
+    hipLaunchKernelGGL(evict_kernel<true>, dim3(nl * dm.B), dim3(kCompThreads), 0, st, c, dm,
+                       layer0, budget, keep, plan, mv8, mv16, wkeep, massp, snap);
+  else
+    hipLaunchKernelGGL(evict_kernel<false>, dim3(nl * dm.B), dim3(kCompThreads), 0, st, c, dm,
+                       layer0, budget, keep, plan, mv8, mv16, wkeep, massp, snap);
 }
 
 // ---------------------------------------------------------------- export

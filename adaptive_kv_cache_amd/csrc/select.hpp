@@ -64,7 +64,10 @@ __device__ inline uint64_t sel_key(float e, float emax, int pos, int t, float s_
 // key + 1 (so a candidate's is never 0), 0 for a protected token, or kAllKept
 // when n <= N and nothing is ranked.  All NT threads of the workgroup must call
 // it; the sink calls are the last thing it does (no barrier follows them).
-template <int NT, typename Sink>
+// With PAIRS, the caller has left each token's (bits(e) << 32 | pos) in X.key[j]
+// whenever n8 + n16 <= kSelLdsKeys, written by the thread that owns j here
+// (j mod NT), so the first pass reads no memory.
+template <int NT, bool PAIRS = false, typename Sink>
 __device__ void select_core(const conf_cache& c, const Dims& dm, int lb, int n8, int n16, int t,
                             int N, SelScratch& X, SelMisc& M, Sink sink) {
   constexpr int kWaves = NT / 64;
@@ -97,8 +100,14 @@ __device__ void select_core(const conf_cache& c, const Dims& dm, int lb, int n8,
   for (int j = tid; j < n; j += NT) {
     float e;
     int p;
-    tok(j, e, p);
-    if (cached) X.key[j] = ((uint64_t)__float_as_uint(e) << 32) | (uint32_t)p;
+    if (PAIRS && cached) {
+      const uint64_t v = X.key[j];
+      e = __uint_as_float((uint32_t)(v >> 32));
+      p = (int)(uint32_t)v;
+    } else {
+      tok(j, e, p);
+      if (cached) X.key[j] = ((uint64_t)__float_as_uint(e) << 32) | (uint32_t)p;
+    }
     emax = fmaxf(emax, e);
     nprot += p > prot_lo;
   }

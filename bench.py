@@ -2,10 +2,11 @@
 
     python bench.py [--gpus 1] [--steps 384] [--warmup 128] [--workload NAME]
 
-A step is one pass of the whole path over one batch: decode attention with
-append and EMA (conf_decode_attn), confidence + budgets (conf_confidence), and
-rank + select with compaction + demotion in one launch (conf_evict_compact), for
-every layer and sequence.  Inputs (logits, q, k, v of every step) are
+A step is one pass of the whole path over one batch: append + decode attention
+(conf_attend), confidence + budgets (conf_confidence), and the EMA update, rank +
+select and compaction + demotion in one launch (conf_ema_evict_compact), for
+every layer and sequence.  HIP events around conf_attend time the attention
+kernel alone.  Inputs (logits, q, k, v of every step) are
 generated on the device before the timed region; the prefilled context is
 ingested during set-up.  Default workload: the Qwen-32B-shaped GQA cache
 (64 layers, 40 query / 8 KV heads, head_dim 128, bf16, batch 8, 32768-token
@@ -51,29 +52,32 @@ def log(*a):
 
 # ---------------------------------------------------------------- byte model
 def attn_bytes(wl, n8, nw):
-    """Algorithmic bytes of one attention launch (every layer and sequence).
+    """Algorithmic bytes of one attention launch (conf_attend: every layer and
+    sequence; the EMA update is counted with the step).
 
     n8, nw: int64 tensors [L][B] of INT8 and window tokens before the append.
     Per (layer, sequence): cached K and V (1 byte per INT8 element, e per 16-bit
-    element), this step's k and v read and appended, both absmax rows, q in and
-    o out (fp32), and every token's EMA read and written plus the new position.
+    element), this step's k and v read and appended, both absmax rows, and q in
+    and o out (fp32).
     """
     e = 2
     H, d, Hq = wl.n_kv_heads, wl.head_dim, wl.n_q_heads
     kv = 2 * H * d * (n8 + e * nw)
-    per_lb = kv + 2 * H * d * e * 2 + 2 * H * d * 4 + Hq * d * (e + 4) + 8 * (n8 + nw + 1) + 4
+    per_lb = kv + 2 * H * d * e * 2 + 2 * H * d * 4 + Hq * d * (e + 4)
     return int(per_lb.sum())
 
 
 def step_bytes(wl, n8, nw, plan):
-    """Algorithmic bytes of one whole step: attention, logits, the selection's reads,
-    hole-fill moves and the demotion (requantisation not counted; the keep flags
-    stay on chip in the fused selection + compaction launch)."""
+    """Algorithmic bytes of one whole step: attention, logits, the EMA update, the
+    selection's position reads, hole-fill moves and the demotion (requantisation
+    not counted; the selection takes the EMA it has just written, and the keep
+    flags stay on chip in the fused EMA + selection + compaction launch)."""
     H, d, e = wl.n_kv_heads, wl.head_dim, 2
     n = n8 + nw + 1
     b = attn_bytes(wl, n8, nw)
     b += wl.batch * wl.vocab * 4
-    b += int((8 * n).sum())                                     # EMA + pos read
+    b += int((8 * n + 4).sum())                                 # EMA read and written, new pos
+    b += int((4 * n).sum())                                     # positions read by the selection
     moves8, moves16, dest = plan[..., 1], plan[..., 3], plan[..., 5]
     b += int((moves8 * (2 * 2 * H * d + 16)).sum())
     b += int((moves16 * (2 * 2 * H * d * e + 16)).sum())
@@ -187,12 +191,12 @@ def run(args):
             eng.confidence(logits[s], c=conf[s], budget=budget[s])
         if ev is not None:
             ev[0].record(main)
-        eng.decode_attn(-1, qs[s], ks[s], vs[s], out=out)
+        eng.attend(-1, qs[s], ks[s], vs[s], out=out)
         if ev is not None:
             ev[1].record(main)
         if side is not main:
             main.wait_stream(side)
-        eng.evict_compact(-1, budget[s])
+        eng.ema_evict_compact(-1, budget[s])
 
     for s in range(args.warmup):
         one_step(s)
@@ -248,7 +252,7 @@ def run(args):
                    "protect": wl.protect, "window": wl.window, "pyramid": wl.pyramid,
                    "vocab": wl.vocab, "mean_tokens_attended": round(n_mean, 1),
                    "streams": int(streams)},
-        "roofline": {"bound": "hbm", "kernel": "conf_decode_attn (one launch)",
+        "roofline": {"bound": "hbm", "kernel": "attn_kernel (conf_attend, one launch)",
                      "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                      "traffic": stored_traffic(wl.name),
@@ -311,7 +315,7 @@ def attn_source_hash():
 
 
 def stored_traffic(workload):
-    """HBM bytes per conf_decode_attn launch from the committed counter summary, or
+    """HBM bytes per attention launch from the committed counter summary, or
     None when it is missing, for another workload, or taken on other kernel source."""
     try:
         text = open(TRAFFIC_FILE).read()

@@ -177,6 +177,17 @@ int conf_decode_attn(const conf_params* p, conf_cache* c, int32_t layer, const v
                      conf_stream_t stream);
 
 /*
+ * (b) alone: conf_decode_attn without its EMA update.  The new row is stored in
+ * the window and `out` is written, but each token's attention mass stays in ws
+ * and n16 and t do not advance yet: conf_ema_evict_compact on the same layer
+ * selector and ws must follow before any other call touches those layers.
+ * Together the two calls give exactly the results of conf_decode_attn followed
+ * by conf_evict_compact, with one launch fewer.
+ */
+int conf_attend(const conf_params* p, conf_cache* c, int32_t layer, const void* q,
+                const void* k_new, const void* v_new, float* out, void* ws, conf_stream_t stream);
+
+/*
  * (d) Rank and select [ranking].  budget: int32 [B][L] (conf_confidence).
  * keep: uint8 [L][B][cap8 + cap16]; entry i < cap8 flags INT8 slot i, entry
  * cap8 + w flags window slot w; only occupied slots are written.  If a
@@ -211,9 +222,18 @@ int conf_evict_compact(const conf_params* p, conf_cache* c, int32_t layer, const
                        void* ws, conf_stream_t stream);
 
 /*
- * One full decode step of every layer and sequence: conf_decode_attn(-1),
- * conf_confidence and conf_evict_compact(-1).  c: fp32 [B] and budget: int32
- * [B][L] receive (a)'s results.
+ * (c)+(d)+(e) in one launch, after conf_attend: the pending EMA update (as in
+ * conf_decode_attn), then conf_evict_compact.  budget: int32 [B][L].
+ */
+int conf_ema_evict_compact(const conf_params* p, conf_cache* c, int32_t layer,
+                           const int32_t* budget, void* ws, conf_stream_t stream);
+
+/*
+ * One full decode step of every layer and sequence: conf_attend(-1),
+ * conf_confidence and conf_ema_evict_compact(-1), the same results as
+ * conf_decode_attn(-1), conf_confidence, conf_rank_evict(-1) and
+ * conf_compact_demote(-1).  c: fp32 [B] and budget: int32 [B][L] receive (a)'s
+ * results.
  */
 int conf_step(const conf_params* p, conf_cache* c, const float* logits, const void* q,
               const void* k_new, const void* v_new, float* out, float* conf, int32_t* budget,

@@ -105,6 +105,10 @@ def test_null_pointers_rejected_before_launch(lib):
                                    null) == E_INVALID
     assert lib.conf_evict_compact(ctypes.byref(p), ctypes.byref(cache), 0, null, null,
                                   null) == E_INVALID
+    assert lib.conf_ema_evict_compact(ctypes.byref(p), ctypes.byref(cache), 0, null, null,
+                                      null) == E_INVALID
+    assert lib.conf_attend(ctypes.byref(p), ctypes.byref(cache), -1, null, null, null, null,
+                           null, null) == E_INVALID
     assert lib.conf_step(ctypes.byref(p), ctypes.byref(cache), *([null] * 9)) == E_INVALID
     assert lib.conf_cache_reset(ctypes.byref(p), ctypes.byref(cache), null) == E_INVALID
     assert lib.conf_status_string(E_CAPACITY) == b"capacity too small"
@@ -118,6 +122,8 @@ def test_bad_layer_rejected(lib):
                                null := ctypes.c_void_p(0)) == E_INVALID
     assert lib.conf_evict_compact(ctypes.byref(p), ctypes.byref(cache), -2, fake, fake,
                                   null) == E_INVALID
+    assert lib.conf_ema_evict_compact(ctypes.byref(p), ctypes.byref(cache), 64, fake, fake,
+                                      null) == E_INVALID
     assert lib.conf_cache_export(ctypes.byref(p), ctypes.byref(cache), 0, 8, fake, fake, fake,
                                  fake, null) == E_INVALID
     assert lib.conf_cache_ingest(ctypes.byref(p), ctypes.byref(cache), 0, fake, fake, 40000,

@@ -14,9 +14,12 @@ step can be:
 The caches that start empty are checked at their first demotion into INT8, at
 the first eviction and deep into their sawtooth.  Tolerances are those of the
 small-shape parity tests.  Confidence and budgets are checked for every sequence
-at every checked step.  Even steps run the fused selection + compaction launch
-(the benchmark's), odd steps the two separate ones; on a fused step the kept set
-is read off the cache after compaction.
+at every checked step.  The steps between checked ones run the benchmark's
+launches (conf_attend, then the EMA fused into the selection + compaction).  A
+checked step runs conf_decode_attn, so that the EMA can be read before the
+selection, and then on even steps the fused selection + compaction, on odd steps
+the two separate ones; on a fused step the kept set is read off the cache after
+compaction.
 """
 import numpy as np
 import pytest
@@ -87,9 +90,14 @@ def test_full_size_sampled_pairs(name):
         z = synth.logits(wl, step, SEED, device=dev)
         q = synth.q_new(wl, step, SEED, device=dev)
         k, v = synth.kv_new(wl, step, SEED, device=dev)
-        S0 = {s: eng.export(*s) for s in SAMPLES} if check else None
+        if not check:
+            eng.attend(-1, q, k, v)
+            _, budget = eng.confidence(z)
+            eng.ema_evict_compact(-1, budget)
+            continue
+        S0 = {s: eng.export(*s) for s in SAMPLES}
         out = eng.decode_attn(-1, q, k, v)
-        S1 = {s: eng.export(*s) for s in SAMPLES} if check else None
+        S1 = {s: eng.export(*s) for s in SAMPLES}
         c, budget = eng.confidence(z)
         fused = step % 2 == 0
         if fused:
@@ -97,8 +105,6 @@ def test_full_size_sampled_pairs(name):
         else:
             keep = eng.rank_evict(-1, budget)
             eng.compact_demote(-1, keep)
-        if not check:
-            continue
         _say("  checking step", step)
         S2 = {s: eng.export(*s) for s in SAMPLES}
         budget_h = budget.cpu().numpy()

@@ -164,36 +164,46 @@ def test_teacher_forced_steps(name):
 
 
 @pytest.mark.parametrize("name", list(TINY))
-def test_evict_compact_equals_rank_then_compact(name):
-    """The fused selection + compaction launch leaves exactly the cache that
-    conf_rank_evict followed by conf_compact_demote leaves (every exported array,
-    bit for bit), for all layers at once and layer by layer."""
+def test_fused_launches_equal_the_separate_ones(name):
+    """Three engines on the same inputs: (a) decode_attn, rank_evict, compact_demote;
+    (b) decode_attn, evict_compact; (c) attend, ema_evict_compact.  All leave the
+    same cache (every exported array, bit for bit) and the same attention output,
+    for all layers at once and layer by layer."""
     wl = TINY[name]
-    _say("evict_compact", name)
-    a, b = Engine(wl), Engine(wl)
+    _say("fused launches", name)
+    a, b, c = Engine(wl), Engine(wl), Engine(wl)
     if wl.prefill:
-        _ingest(a, wl, SEED)
-        _ingest(b, wl, SEED)
+        for e in (a, b, c):
+            _ingest(e, wl, SEED)
     steps = min(wl.steps, 40) if wl.prefill else 200
     for step in range(steps):
         z = synth.logits(wl, step, SEED).cuda()
         q = synth.q_new(wl, step, SEED).cuda()
         k, v = (x.cuda() for x in synth.kv_new(wl, step, SEED))
-        for e in (a, b):
-            e.decode_attn(-1, q, k, v)
         _, bud = a.confidence(z)
         layers = [-1] if step % 2 == 0 else list(range(wl.n_layers))
+        outs = []
         for l in layers:
+            ql, kl, vl = (x if l < 0 else x[l].contiguous() for x in (q, k, v))
+            oa = a.decode_attn(l, ql, kl, vl)
+            ob = b.decode_attn(l, ql, kl, vl)
+            oc = c.attend(l, ql, kl, vl)
+            outs.append((oa, ob, oc))
             a.compact_demote(l, a.rank_evict(l, bud))
             b.evict_compact(l, bud)
+            c.ema_evict_compact(l, bud)
+        for oa, ob, oc in outs:
+            assert torch.equal(oa, ob) and torch.equal(oa, oc), step
         if step % 10 == 9 or step == steps - 1:
             for l in range(wl.n_layers):
                 for s_ in range(wl.batch):
-                    ea, eb = a.export(l, s_), b.export(l, s_)
+                    ea, eb, ec = a.export(l, s_), b.export(l, s_), c.export(l, s_)
                     for key in ea:
                         assert np.array_equal(np.asarray(ea[key]), np.asarray(eb[key])), \
-                            (step, l, s_, key)
-    assert a.status() == 0 and b.status() == 0
+                            ("evict_compact", step, l, s_, key)
+                        assert np.array_equal(np.asarray(ea[key]), np.asarray(ec[key])), \
+                            ("ema_evict_compact", step, l, s_, key)
+    assert a.status() == 0 and b.status() == 0 and c.status() == 0
 
 
 @pytest.mark.parametrize("name", ["gqa5_bf16_d128", "mha_f16_d64"])
