@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libc
 CONF_F16, CONF_BF16 = 1, 2
 DTYPE16 = {"f16": (CONF_F16, torch.float16), "bf16": (CONF_BF16, torch.bfloat16)}
 ST_WINDOW_FULL, ST_INT8_FULL = 1, 2
+POLICY = {"confkv": 0, "full": 1, "window": 2}
 
 EXPORTED = ("conf_cache_layout", "conf_workspace_bytes", "conf_cache_reset", "conf_cache_ingest",
             "conf_confidence", "conf_decode_attn", "conf_rank_evict", "conf_compact_demote",
@@ -32,7 +33,8 @@ class ConfParams(ctypes.Structure):
     _fields_ = [(n, c_int32) for n in ("n_layers", "batch", "n_q_heads", "n_kv_heads", "head_dim",
                                         "vocab", "dtype16", "window", "protect", "n_high", "n_low",
                                         "cap8", "pyramid")] + \
-               [(n, c_float) for n in ("tau", "w_H", "w_m", "w_p", "ema_decay", "s_ema", "s_rec")]
+               [(n, c_float) for n in ("tau", "w_H", "w_m", "w_p", "ema_decay", "s_ema", "s_rec")] + \
+               [("policy", c_int32)]
 
 
 _CACHE_FIELDS = ("k8", "v8", "k16", "v16", "k_amax", "v_amax", "pos8", "ema8", "pos16", "ema16",
@@ -106,7 +108,8 @@ def params_from_workload(wl: Workload, cap8: int | None = None, **over) -> ConfP
              dtype16=DTYPE16[wl.dtype16][0], window=wl.window, protect=wl.protect,
              n_high=wl.n_high, n_low=wl.n_low, cap8=wl.cap8 if cap8 is None else cap8,
              pyramid=int(wl.pyramid), tau=wl.tau, w_H=wl.w_H, w_m=wl.w_m, w_p=wl.w_p,
-             ema_decay=wl.ema_decay, s_ema=wl.s_ema, s_rec=wl.s_rec)
+             ema_decay=wl.ema_decay, s_ema=wl.s_ema, s_rec=wl.s_rec,
+             policy=POLICY[wl.policy])
     d.update(over)
     return ConfParams(**d)
 

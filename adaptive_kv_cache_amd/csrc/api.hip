@@ -66,6 +66,9 @@ int make_dims(const conf_params* p, Dims* d) {
   if (!(p->ema_decay >= 0.f && p->ema_decay <= 1.f)) return CONF_E_INVALID;
   if (!(p->s_ema >= 0.f && p->s_rec >= 0.f)) return CONF_E_INVALID;
   if (p->pyramid != 0 && p->pyramid != 1) return CONF_E_INVALID;
+  if (p->policy != CONF_POLICY_CONFKV && p->policy != CONF_POLICY_FULL &&
+      p->policy != CONF_POLICY_WINDOW)
+    return CONF_E_INVALID;
   d->L = p->n_layers;
   d->B = p->batch;
   d->Hq = p->n_q_heads;
@@ -82,6 +85,7 @@ int make_dims(const conf_params* p, Dims* d) {
   d->capt = d->cap8 + d->cap16;
   d->bf16 = p->dtype16 == CONF_BF16;
   d->pyramid = p->pyramid;
+  d->policy = p->policy;
   d->tau = p->tau;
   d->w_H = p->w_H;
   d->w_m = p->w_m;
@@ -202,7 +206,8 @@ int conf_cache_ingest(const conf_params* p, conf_cache* c, int32_t layer, const 
   if (!cache_ok(c) || !k_pre || !v_pre || prefill_len < 0 || !layer_range(d, layer, &l0, &nl))
     return CONF_E_INVALID;
   (void)ws;
-  if (prefill_len - d.W > d.cap8) return CONF_E_CAPACITY;
+  if (d.policy != CONF_POLICY_WINDOW && prefill_len - d.W > d.cap8) return CONF_E_CAPACITY;
+  if (d.policy == CONF_POLICY_FULL && prefill_len > d.W) return CONF_E_CAPACITY;
   if (prefill_len == 0) return CONF_OK;
   launch_ingest(d, *c, l0, nl, prefill_len, k_pre, v_pre, (hipStream_t)stream);
   return check_launch("conf_cache_ingest");

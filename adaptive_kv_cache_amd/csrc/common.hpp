@@ -18,6 +18,7 @@ struct Dims {
   int W, P, n_high, n_low, cap8, cap16, capt;  // capt = cap8 + cap16
   int bf16;                                    // 1: bfloat16, 0: IEEE half
   int pyramid;
+  int policy;                                  // CONF_POLICY_*
   float tau, w_H, w_m, w_p, decay, one_minus_decay, s_ema, s_rec;
 };
 

@@ -15,11 +15,20 @@ namespace confkv {
 // e <- decay*e + (1-decay)*mass; the appended token (window slot nw, if the
 // window had room) starts from e = 0 and takes position t+1.  (n8, nw, t) are
 // the sizes before this step's append.  A thread takes tokens j0, j0 + jstep, ...
+// The baseline policies keep no EMA: only the appended token's slot is set (EMA 0,
+// position t+1), by the thread with j0 = 0.
 __device__ inline void ema_tokens(const conf_cache& c, const Dims& dm, int lb,
                                   const float* __restrict__ massp_all, int n8, int nw, int t,
                                   int j0, int jstep) {
 #pragma clang fp contract(off)
   const int appended = nw < dm.cap16;
+  if (dm.policy != CONF_POLICY_CONFKV) {  // no EMA: the appended token's slot only
+    if (j0 == 0 && appended) {
+      c.ema16[(size_t)lb * dm.cap16 + nw] = 0.f;
+      c.pos16[(size_t)lb * dm.cap16 + nw] = t + 1;
+    }
+    return;
+  }
   const int end = n8 + nw + appended;
   const float* rows = massp_all + (size_t)lb * dm.Hkv * dm.capt;
   float* ema8 = c.ema8 + (size_t)lb * dm.cap8;

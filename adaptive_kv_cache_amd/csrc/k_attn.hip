@@ -52,7 +52,9 @@ constexpr int kWaves = 4;
 constexpr int kAttnThreads = kWaves * 64;
 constexpr int kLdsDynBytes = 76 * 1024;  // dynamic LDS of one workgroup (two fit a CU)
 
-enum { MODE_ONLINE = 0, MODE_LSE = 1, MODE_FINAL = 2 };
+// ONLINE: one pass, scores kept in LDS for the mass; LSE + FINAL: two passes when
+// they do not fit; PLAIN: one pass for a policy that needs no mass.
+enum { MODE_ONLINE = 0, MODE_LSE = 1, MODE_FINAL = 2, MODE_PLAIN = 3 };
 
 __device__ inline f4 mma_f16(h8 a, h8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -325,8 +327,8 @@ __device__ inline void softmax_item(const f4* acc, float scale, bool head_ok, co
       }
     wa.l = wa.l * corr + head_sum(lsum);
     wa.m = mnew;
-    if constexpr (MODE == MODE_ONLINE) {
-      if (head_ok) {
+    if constexpr (MODE == MODE_ONLINE || MODE == MODE_PLAIN) {
+      if (MODE == MODE_ONLINE && head_ok) {
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -519,7 +521,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
   const int n = n8 + nw + appended;
   const int nb8 = (n8 + kTile - 1) / kTile;
   const int nitems = nb8 + (nw + 31) / 32;
-  const bool in_lds = n <= score_cap;
+  // CONF-KV needs each token's attention mass; the baseline policies do not
+  const bool mass = dm.policy == CONF_POLICY_CONFKV;
+  const bool in_lds = mass && n <= score_cap;
+  const bool one_pass = in_lds || !mass;
   // the speculative keys are this wavefront's first item unless the INT8 part is short
   if (wave < nitems && wave >= nb8)
     load_run_rs<D>(urs.k16, (uint32_t)(wave - nb8) * ib, 16 * lane, cur);
@@ -611,6 +616,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
                                      scale16, head_ok, wa, vscaled, s_sv, smem, stride, 0.f, nullptr,
                                      cur, true);
     if (appended && tid < G) smem[tid * stride + n - 1] = s_snew[tid];
+  } else if (!mass) {
+    wave_pass<D, BF16, MODE_PLAIN>(nitems, nb8, n8, nw, dm.cap8, urs, q, scale8,
+                                    scale16, head_ok, wa, vscaled, s_sv, nullptr, 0, 0.f, nullptr,
+                                    cur, true);
   } else {
     wave_pass<D, BF16, MODE_LSE>(nitems, nb8, n8, nw, dm.cap8, urs, q, scale8,
                                   scale16, head_ok, wa, vscaled, s_sv, nullptr, 0, 0.f, nullptr,
@@ -623,7 +632,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     s_m[wave][lane] = wa.m;
     s_l[wave][lane] = wa.l;
   }
-  if (in_lds) {
+  if (one_pass) {
     if (!vscaled) apply_vscale<D>(wa, s_sv);
     store_o<D>(wa, ob, G);
   }
@@ -645,9 +654,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
   __syncthreads();
 
   float* out = out_all + ((size_t)lbl * dm.Hq + (size_t)hk * G) * D;
-  if (in_lds) {
+  if (one_pass) {
     // per-token mass of this query group from the stored scores
-    for (int j0 = tid; j0 < n; j0 += 4 * kAttnThreads) {
+    for (int j0 = tid; in_lds && j0 < n; j0 += 4 * kAttnThreads) {
       float s[4] = {0.f, 0.f, 0.f, 0.f};
       for (int h = 0; h < G; ++h) {
         const float l = s_lse[h];

@@ -38,7 +38,8 @@ void launch_reset(const Dims& dm, const conf_cache& c, hipStream_t st) {
 
 // ---------------------------------------------------------------- ingest
 // Prefill of L0 tokens for one unit: positions < L0 - W become INT8 with the
-// absmax over exactly those tokens; the rest go to the window.
+// absmax over exactly those tokens (a sliding window drops them); the rest go to
+// the window.
 __global__ __launch_bounds__(256) void ingest_kernel(conf_cache c, Dims dm, int layer0, int L0,
                                                      const uint16_t* __restrict__ kp,
                                                      const uint16_t* __restrict__ vp) {
@@ -49,8 +50,9 @@ __global__ __launch_bounds__(256) void ingest_kernel(conf_cache c, Dims dm, int 
   const int lb = layer0 * dm.B + lbl;
   const size_t u = unit_of(dm, lb, hk);
   const int D = dm.D;
-  const int n8 = L0 > dm.W ? L0 - dm.W : 0;
-  const int nw = L0 - n8;
+  const int old = L0 > dm.W ? L0 - dm.W : 0;  // positions older than the window
+  const int n8 = dm.policy == CONF_POLICY_WINDOW ? 0 : old;
+  const int nw = L0 - old;
   const uint16_t* ksrc = kp + (size_t)unit_local * L0 * D;
   const uint16_t* vsrc = vp + (size_t)unit_local * L0 * D;
   __shared__ float amk[256], amv[256];
@@ -91,7 +93,7 @@ __global__ __launch_bounds__(256) void ingest_kernel(conf_cache c, Dims dm, int 
   uint16_t* v16 = (uint16_t*)c.v16 + u * (size_t)dm.cap16 * D;
   for (size_t i = threadIdx.x; i < (size_t)nw * D; i += blockDim.x) {
     const int w = (int)(i / D), cc = (int)(i % D);
-    const size_t s = (size_t)(n8 + w) * D + cc;
+    const size_t s = (size_t)(old + w) * D + cc;
     k16[k16_off(w, cc, D)] = ksrc[s];
     v16[v16_off(w, cc, D)] = vsrc[s];
   }
@@ -101,7 +103,7 @@ __global__ __launch_bounds__(256) void ingest_kernel(conf_cache c, Dims dm, int 
       c.ema8[(size_t)lb * dm.cap8 + i] = 0.f;
     }
     for (int w = threadIdx.x; w < nw; w += blockDim.x) {
-      c.pos16[(size_t)lb * dm.cap16 + w] = n8 + w;
+      c.pos16[(size_t)lb * dm.cap16 + w] = old + w;
       c.ema16[(size_t)lb * dm.cap16 + w] = 0.f;
     }
     if (threadIdx.x == 0) {
@@ -527,7 +529,8 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dim
   }
   __syncthreads();
   // ---- 1. keep flags (one read), counts, the demotee
-  const int target = t - dm.W;
+  // the token that leaves the window (full KV demotes nothing)
+  const int target = dm.policy == CONF_POLICY_FULL ? -1 : t - dm.W;
   int c8 = 0, c16 = 0;
   for (int i = tid; i < n8; i += kCompThreads) {
     const uint8_t k = keep8[i] ? 1 : 0;
@@ -561,6 +564,13 @@ __device__ inline void ema_pairs(const conf_cache& c, const Dims& dm, int lb,
                                  SelScratch& X) {
 #pragma clang fp contract(off)
   const int appended = nw < dm.cap16;
+  if (dm.policy != CONF_POLICY_CONFKV) {  // no EMA: the appended token's slot only
+    if (threadIdx.x == 0 && appended) {
+      c.ema16[(size_t)lb * dm.cap16 + nw] = 0.f;
+      c.pos16[(size_t)lb * dm.cap16 + nw] = t + 1;
+    }
+    return;
+  }
   const int end = n8 + nw + appended;
   const bool cached = end <= kSelLdsKeys;
   const float* rows = massp_all + (size_t)lb * dm.Hkv * dm.capt;
@@ -665,7 +675,8 @@ __global__ __launch_bounds__(kCompThreads, 6) void evict_kernel(conf_cache c, Di
     M.ngrown = 0;
   }
   __syncthreads();
-  const int target = t - dm.W;
+  // the token that leaves the window (full KV demotes nothing)
+  const int target = dm.policy == CONF_POLICY_FULL ? -1 : t - dm.W;
   int c8 = 0, c16 = 0;
   select_core<kCompThreads, EMA>(c, dm, lb, n8, n16, t, N, U.sel, SM, [&](int j, int k, uint64_t key) {
     if (j < n8) {

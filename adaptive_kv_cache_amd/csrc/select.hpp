@@ -74,7 +74,8 @@ __device__ void select_core(const conf_cache& c, const Dims& dm, int lb, int n8,
   static_assert(kWaves <= 16, "SelMisc holds 16 wavefronts");
   const int n = n8 + n16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (n <= N) {
+  // full KV keeps everything, as CONF-KV does under its budget
+  if (n <= N || dm.policy == CONF_POLICY_FULL) {
     for (int j = tid; j < n; j += NT) sink(j, 1, kAllKept);
     return;
   }
@@ -82,6 +83,11 @@ __device__ void select_core(const conf_cache& c, const Dims& dm, int lb, int n8,
   const float* ema8 = c.ema8 + (size_t)lb * dm.cap8;
   const int32_t* pos16 = c.pos16 + (size_t)lb * dm.cap16;
   const float* ema16 = c.ema16 + (size_t)lb * dm.cap16;
+  if (dm.policy == CONF_POLICY_WINDOW) {  // the newest W positions, (t-W, t]
+    for (int j = tid; j < n; j += NT)
+      sink(j, (j < n8 ? pos8[j] : pos16[j - n8]) > t - dm.W, kAllKept);
+    return;
+  }
   const int prot_lo = t - dm.P;  // protected: pos > prot_lo
   const bool cached = n <= kSelLdsKeys;
   auto tok = [&](int j, float& e, int& p) {

@@ -51,6 +51,7 @@ class Workload:
     s_rec: float = 0.3
     temp_schedule: str = "alt"   # "alt": 0.5 / 8 in 64-step runs; "uniform": U[1.5, 3]
     needle: bool = False
+    policy: str = "confkv"       # "confkv", or a baseline: "full" (full KV), "window" (sliding)
 
     @property
     def group(self) -> int:
@@ -59,11 +60,31 @@ class Workload:
     @property
     def cap8(self) -> int:
         """INT8-region capacity in tokens per (layer, sequence), a multiple of 64."""
-        need = max(self.prefill - self.window, self.n_low + 1, 64)
+        old = 0 if self.policy == "window" else self.prefill - self.window  # a window drops them
+        need = max(old, self.n_low + 1, 64)
         return (need + 63) // 64 * 64
 
     def scaled(self, **kw) -> "Workload":
         return replace(self, **kw)
+
+    def baseline(self, policy: str, horizon: int) -> "Workload":
+        """The same shape under a baseline policy, for `horizon` decode steps.
+
+        full: the window holds the prefill and every decoded token (rounded up to
+        64); budgets and P at their smallest valid values, since nothing is evicted.
+        window: a W-token sliding window; P = N_high = N_low = W and no pyramid, so
+        the ranking keeps exactly the protected newest W.
+        """
+        if policy == "confkv":
+            return self
+        if policy == "full":
+            w = (self.prefill + horizon + 1 + 63) // 64 * 64
+            return replace(self, name=f"{self.name}_full", policy="full", window=w, protect=1,
+                           n_high=64, n_low=64, pyramid=False)
+        if policy == "window":
+            return replace(self, name=f"{self.name}_window", policy="window", protect=self.window,
+                           n_high=self.window, n_low=self.window, pyramid=False)
+        raise ValueError(policy)
 
 
 def _mk() -> dict:

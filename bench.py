@@ -22,6 +22,10 @@ caches the two cross-stream waits per step cost more than they hide (measured:
 the GPT-2-shaped caches ran 33-46% slower), so every call goes in order on one
 stream.  --streams 1|2 overrides the choice.
 
+--policy full | window runs the same step under the full-KV or the sliding-window
+baseline (the pages' comparison policies) on the same kernels and shape: full KV
+keeps every prefill and decoded token in 16 bits, the window the newest W.
+
 Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -136,7 +140,7 @@ def cpu_baseline(wl, seed, budget_s=20.0):
 
 # ---------------------------------------------------------------- GPU run
 def run(args):
-    wl = WORKLOADS[args.workload]
+    wl = WORKLOADS[args.workload].baseline(args.policy, args.warmup + args.steps)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     total = args.warmup + args.steps
@@ -246,7 +250,8 @@ def run(args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": f"int8+{wl.dtype16} operands, f32 accumulate",
         "data": "synthetic",
-        "config": {"workload": wl.name, "layers": L, "batch": B, "q_heads": wl.n_q_heads,
+        "config": {"workload": wl.name, "policy": wl.policy, "layers": L, "batch": B,
+                   "q_heads": wl.n_q_heads,
                    "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "dtype16": wl.dtype16,
                    "prefill": wl.prefill, "n_high": wl.n_high, "n_low": wl.n_low,
                    "protect": wl.protect, "window": wl.window, "pyramid": wl.pyramid,
@@ -370,6 +375,9 @@ def main():
     ap.add_argument("--workload", default="qwen32b_gqa_b8_32k")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--policy", choices=("confkv", "full", "window"), default="confkv",
+                    help="cache policy: CONF-KV, or the full-KV / sliding-window baseline on the "
+                         "same kernels")
     ap.add_argument("--streams", choices=("auto", "1", "2"), default="auto",
                     help="2: confidence on a second stream beside the attention; auto: 2 when "
                          "the attention streams at least 256 MB per launch")
@@ -395,7 +403,7 @@ def main():
               "(sharding is described in the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     res, wl = run(args)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.policy == "confkv":
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(wl, args.seed, args.cpu_seconds)
     print(json.dumps(res), flush=True)

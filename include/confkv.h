@@ -14,6 +14,8 @@
  *   [pyramid]     Methodology, system integration, pyramidal budgets (CONF-KV-L)
  *   [impl]        Methodology, system integration, implementation
  *   [online]      Key contributions, system design (block-wise online softmax)
+ *   [problem]     Problem statement (sliding-window eviction as a prior policy)
+ *   [results]     Experimental results (full-KV latency and throughput comparison)
  *
  * Conventions shared by every call
  *   - Every pointer argument is a DEVICE pointer owned by the caller, except
@@ -59,6 +61,23 @@ enum {
 
 enum { CONF_F16 = 1, CONF_BF16 = 2 };
 
+/* Cache policy (conf_params.policy).  CONF-KV itself, and two baselines that the
+ * pages compare it with, run on the same kernels and layout:
+ *   CONF_POLICY_CONFKV  the method: confidence-chosen budgets, EMA ranking,
+ *                       INT8 demotion of tokens older than the window.
+ *   CONF_POLICY_FULL    full KV [results]: every token stays, in 16 bits.  The
+ *                       window W must hold the prefill and every decoded token
+ *                       (conf_cache_ingest returns CONF_E_CAPACITY for a longer
+ *                       prefill; an append that finds it full sets
+ *                       CONF_ST_WINDOW_FULL).  Budgets do not evict, nothing is
+ *                       demoted.
+ *   CONF_POLICY_WINDOW  sliding window [problem]: after each step only positions
+ *                       (t-W, t] stay, in 16 bits; older prefill tokens leave at
+ *                       the first step.  Budgets and ranking play no part.
+ * The baselines need no per-token attention mass: their attention is a single
+ * online pass whatever the cache length, and they keep no EMA (it stays 0). */
+enum { CONF_POLICY_CONFKV = 0, CONF_POLICY_FULL = 1, CONF_POLICY_WINDOW = 2 };
+
 /* Device status word bits (conf_cache.status), set by kernels, never cleared
  * except by conf_cache_reset(). */
 enum {
@@ -79,6 +98,7 @@ typedef struct conf_params {
   float w_H, w_m, w_p;      /* confidence weights; the pages use 0.4, 0.3, 0.3 [confidence] */
   float ema_decay;          /* e <- decay*e + (1-decay)*mass [ranking] */
   float s_ema, s_rec;       /* score = s_ema*(e/e_max) + s_rec*(pos/t) [ranking] */
+  int32_t policy;           /* CONF_POLICY_*; 0 is CONF-KV */
 } conf_params;
 
 /*
@@ -144,9 +164,10 @@ int conf_cache_reset(const conf_params* p, conf_cache* c, conf_stream_t stream);
  * Load a prefilled context of `prefill_len` tokens, positions 0..prefill_len-1.
  * k_pre, v_pre: 16-bit [L][B][Hkv][prefill_len][d] (layer = -1) or
  * [B][Hkv][prefill_len][d] (layer = l).  Positions < prefill_len - W become
- * INT8 with absmax over exactly those tokens; the rest fill the window; every
- * EMA is 0 and t = prefill_len - 1 [storage].  The layer must be empty.
- * CONF_E_CAPACITY if prefill_len - W > cap8.
+ * INT8 with absmax over exactly those tokens (CONF_POLICY_WINDOW drops them
+ * instead); the rest fill the window; every EMA is 0 and t = prefill_len - 1
+ * [storage].  The layer must be empty.  CONF_E_CAPACITY if prefill_len - W >
+ * cap8 (CONF-KV), or prefill_len > W (CONF_POLICY_FULL).
  */
 int conf_cache_ingest(const conf_params* p, conf_cache* c, int32_t layer, const void* k_pre,
                       const void* v_pre, int32_t prefill_len, void* ws, conf_stream_t stream);

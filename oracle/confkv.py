@@ -51,6 +51,15 @@ function):
   * pyramid: N_l = floor(N * (2(L-1) - l) / (2(L-1))), i.e. 1.0x at layer 0 and
     0.5x at the last layer; applies to both budgets.
   * attention scale 1/sqrt(d); the new token attends to itself; no mask.
+
+Baseline policies the pages compare CONF-KV with ([Problem] sliding windows,
+[Results] full KV) are the same step under other parameters:
+  * full KV: no token is ever evicted or demoted, i.e. step_layer with a budget
+    no cache reaches and a window no position leaves (W > t);
+  * sliding window: P = W = N, so the protected newest W positions are exactly
+    what stays, all 16-bit; a window cache never holds an older token, so its
+    ingest drops the prefill before position L0 - W (`ingest(..., drop_old=True)`).
+The baselines need no EMA; the oracle still computes one, which tests ignore.
 """
 from __future__ import annotations
 
@@ -416,15 +425,21 @@ class LayerSeqState:
         self.is8[j] = True
 
 
-def ingest(k_bits, v_bits, W: int, dtype16: str) -> LayerSeqState:
+def ingest(k_bits, v_bits, W: int, dtype16: str, drop_old: bool = False) -> LayerSeqState:
     """Prefilled context [Hkv, L0, d] (16-bit patterns) -> cache state.
 
     Positions 0 .. L0-W-1 go to INT8 with the absmax taken over exactly those
-    tokens; positions L0-W .. L0-1 stay 16-bit; every EMA is 0; t = L0 - 1.
+    tokens (with drop_old, the sliding-window baseline, they are not kept at
+    all); positions L0-W .. L0-1 stay 16-bit; every EMA is 0; t = L0 - 1.
     """
     k_bits = np.asarray(k_bits, np.uint16)
     v_bits = np.asarray(v_bits, np.uint16)
     H, L0, d = k_bits.shape
+    if drop_old and L0 > W:
+        st = ingest(k_bits[:, L0 - W:], v_bits[:, L0 - W:], W, dtype16)
+        st.pos = st.pos + (L0 - W)
+        st.t = L0 - 1
+        return st
     st = LayerSeqState(H, d, dtype16)
     st.pos = np.arange(L0, dtype=np.int64)
     st.is8 = st.pos < (L0 - W)

@@ -263,6 +263,57 @@ def test_rank_evict_budget_sweep(name):
                 assert len(got) == int(budget[b, l])
 
 
+@pytest.mark.parametrize("policy", ["full", "window"])
+@pytest.mark.parametrize("name", ["gqa5_bf16_d128", "mha_f16_d64", "gqa16_bf16_d64_long"])
+def test_baseline_policies(policy, name):
+    """Full KV and the sliding window on the same kernels (conf_step), teacher-
+    forced against the oracle run with the same policy's parameters: the ingest
+    and every step's cache (positions, 16-bit bits) bit-exact, attention within
+    tolerance.  The baselines keep no EMA, so it is not compared."""
+    import dataclasses
+    base = TINY[name]
+    steps = 24 if base.prefill else 120
+    wl = base.baseline(policy, steps)
+    prm = oracle_params(wl)
+    N = wl.window if policy == "window" else 10 ** 9
+    if policy == "full":
+        prm = dataclasses.replace(prm, n_high=N, n_low=N)
+    _say("baseline", policy, name)
+    eng = Engine(wl)
+    if wl.prefill:
+        pre = _ingest(eng, wl, SEED)
+        for l in range(wl.n_layers):
+            for b in range(wl.batch):
+                ref = O.ingest(pre[l][0][b], pre[l][1][b], wl.window, wl.dtype16,
+                               drop_old=policy == "window")
+                assert_same_state(to_oracle_state(eng.export(l, b), wl.dtype16), ref,
+                                  what=("ingest", l, b))
+    worst = 0.0
+    for step in range(steps):
+        S0 = _snap(eng, wl)
+        z = synth.logits(wl, step, SEED)
+        q = synth.q_new(wl, step, SEED)
+        k, v = synth.kv_new(wl, step, SEED)
+        out, _, _ = eng.step(z.cuda(), q.cuda(), k.cuda(), v.cuda())
+        out = out.cpu().numpy()
+        S2 = _snap(eng, wl)
+        qb, kb, vb = bits16(q), bits16(k), bits16(v)
+        for l in range(wl.n_layers):
+            for b in range(wl.batch):
+                st = to_oracle_state(S0[l][b], wl.dtype16)
+                r = O.step_layer(st, qb[l, b], kb[l, b], vb[l, b], N, prm)
+                err = attn_rel_err(out[l, b], r["o"])
+                worst = max(worst, err)
+                assert err <= ATTN_TOL, (policy, name, step, l, b, err)
+                assert_same_state(to_oracle_state(S2[l][b], wl.dtype16), st,
+                                  what=(policy, step, l, b))
+                assert not st.is8.any()                     # the baselines stay 16-bit
+                if policy == "window":
+                    assert st.pos.tolist() == list(range(max(0, st.t - wl.window + 1), st.t + 1))
+    assert eng.status() == 0
+    _say("  worst attention rel err", worst)
+
+
 def test_sawtooth_and_no_op_from_empty():
     wl = TINY["mha_f16_d64"]
     eng = Engine(wl)
