@@ -655,17 +655,33 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
 
   float* out = out_all + ((size_t)lbl * dm.Hq + (size_t)hk * G) * D;
   if (one_pass) {
-    // per-token mass of this query group from the stored scores
+    // per-token mass of this query group from the stored scores: four tokens per
+    // thread, the scores of four heads read from LDS together (an index past the
+    // end reads the last token and is not stored)
     for (int j0 = tid; in_lds && j0 < n; j0 += 4 * kAttnThreads) {
       float s[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int h = 0; h < G; ++h) {
+      int jj[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) jj[k] = min(j0 + k * kAttnThreads, n - 1);
+      int h = 0;
+      for (; h + 4 <= G; h += 4) {
+        float x[4][4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) x[e][k] = smem[(h + e) * stride + jj[k]];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float l = s_lse[h + e];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) s[k] += __expf(x[e][k] - l);
+        }
+      }
+      for (; h < G; ++h) {
         const float l = s_lse[h];
         const float* row = smem + h * stride;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int j = j0 + k * kAttnThreads;
-          if (j < n) s[k] += __expf(row[j] - l);
-        }
+        for (int k = 0; k < 4; ++k) s[k] += __expf(row[jj[k]] - l);
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
