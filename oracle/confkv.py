@@ -60,6 +60,20 @@ Baseline policies the pages compare CONF-KV with ([Problem] sliding windows,
     what stays, all 16-bit; a window cache never holds an older token, so its
     ingest drops the prefill before position L0 - W (`ingest(..., drop_old=True)`).
 The baselines need no EMA; the oracle still computes one, which tests ignore.
+
+Retention eviction (the TRIM-KV page, Methodology: retention gate, inference and
+eviction): each token carries a retention score beta in [0, 1] fixed when it is
+created; its current score at step t is beta^(t - i); once the cache is at its
+limit M the lowest current score leaves.  Readings:
+  * beta is supplied per token and (layer, sequence), as its logarithm
+    l = ln beta <= 0 in float32 (the gate that predicts it is training, not part
+    of the decode step); tokens are ranked by ln(beta^(t-i)) = (t - i) * l, one
+    float32 product, 0 for the newest token (beta^0 = 1) -- the same order as
+    beta^(t-i) in exact arithmetic;
+  * ties go to the newer position, as in CONF-KV's ranking; one keep set per
+    (layer, sequence); the cache holds at most M tokens after each step, all
+    16-bit (the page names no quantisation), and no window is protected beyond
+    the newest token.
 """
 from __future__ import annotations
 
@@ -76,6 +90,7 @@ __all__ = [
     "layer_budget", "dequantize", "attention", "attention_online", "token_mass",
     "ema_update", "composite_scores", "select_keep", "quant_codes", "requant_codes",
     "demote_token", "ingest", "step_layer", "decode_step",
+    "retention_scores", "trim_step",
 ]
 
 
@@ -292,6 +307,17 @@ def select_keep(scores, pos, t: int, P: int, N: int) -> np.ndarray:
     return keep
 
 
+def retention_scores(log_beta32, pos, t: int) -> np.ndarray:
+    """Current retention log-score (t - i) * ln(beta_i) of each token, float32,
+    one rounding; 0 for the newest token.  [TRIM-KV: inference and eviction]"""
+    lb = np.asarray(log_beta32, F32)
+    age = (t - np.asarray(pos, np.int64)).astype(F32)
+    with np.errstate(invalid="ignore"):
+        s = (age * lb).astype(F32)
+    s[age == 0] = F32(0)
+    return s
+
+
 # --------------------------------------------------------------------------
 # (e) INT8 quantiser, per (KV head, channel)                    [Method/storage]
 # --------------------------------------------------------------------------
@@ -490,6 +516,24 @@ def step_layer(st: LayerSeqState, q_bits, k_bits, v_bits, N: int, prm: OraclePar
     st.evict(keep)
     st.demote(prm.window)
     return dict(o=o, p=p, mass=mass, ema=ema64, scores=scores, keep=keep, pos_before=pos_before)
+
+
+def trim_step(st: LayerSeqState, q_bits, k_bits, v_bits, log_beta_new: float, M: int,
+              prm: OracleParams) -> dict:
+    """One step of retention eviction for one (layer, sequence); `st.ema` holds
+    each token's ln(beta) (float32 values).  Append (with this step's ln beta),
+    attention over the cache (float64), then keep the M tokens with the highest
+    current retention score (ties: newer first).  No token is quantised.
+    [TRIM-KV: retention gate; inference and eviction]"""
+    st.append(k_bits, v_bits)
+    st.ema[-1] = float(np.float32(log_beta_new))
+    q = decode16(q_bits, prm.dtype16).astype(F64)
+    K, V = st.kv_values()
+    o, p = attention(q, K, V, prm.group)
+    scores = retention_scores(st.ema.astype(F32), st.pos, st.t)
+    keep = select_keep(scores, st.pos, st.t, 1, M)
+    st.evict(keep)
+    return dict(o=o, p=p, scores=scores, keep=keep)
 
 
 def decode_step(states, logits, q_bits, k_bits, v_bits, prm: OracleParams,

@@ -83,3 +83,65 @@ def test_full_kv_attention_is_plain_softmax_attention():
         p = np.exp(s - s.max())
         p /= p.sum()
         np.testing.assert_allclose(r["o"][h], p @ V[h // g], rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# Retention eviction (TRIM-KV page, Methodology: retention gate; inference and
+# eviction): the current score is beta^(t - i); at the limit M the lowest goes.
+# ----------------------------------------------------------------------------
+from oracle import retention_scores, trim_step  # noqa: E402
+
+
+def _trim_run(rng, prm, M, betas, steps):
+    """From an empty cache; returns the state and every token's beta by position."""
+    from oracle import LayerSeqState
+    st = LayerSeqState(prm.n_kv_heads, prm.head_dim, prm.dtype16)
+    for i in range(steps):
+        q = encode16(rng.standard_normal((prm.n_q_heads, prm.head_dim)), prm.dtype16)
+        k, v = _kv(rng, prm, 1)
+        trim_step(st, q, k[:, 0], v[:, 0], np.log(np.float32(betas[i])), M, prm)
+    return st
+
+
+def test_retention_keeps_the_m_largest_beta_powers_float64():
+    """Brute force: after every step the kept set is the M tokens with the largest
+    beta_i^(t-i) computed in float64 (betas spread so that no two are close)."""
+    rng = np.random.default_rng(7)
+    prm = _prm()
+    M, steps = 12, 60
+    betas = rng.permutation(np.linspace(0.05, 0.999, steps)).astype(np.float32)
+    from oracle import LayerSeqState
+    st = LayerSeqState(prm.n_kv_heads, prm.head_dim, prm.dtype16)
+    for t in range(steps):
+        q = encode16(rng.standard_normal((prm.n_q_heads, prm.head_dim)), prm.dtype16)
+        k, v = _kv(rng, prm, 1)
+        trim_step(st, q, k[:, 0], v[:, 0], np.log(betas[t]), M, prm)
+        if t + 1 <= M:
+            assert st.pos.tolist() == list(range(t + 1))
+            prev = st.pos.tolist()
+            continue
+        # the survivors of the previous step plus the new token, best M of them
+        cand = set(prev) | {t}
+        val = {i: np.float64(betas[i]) ** (t - i) for i in cand}
+        want = sorted(cand, key=lambda i: (-val[i], -i))[:M]
+        assert sorted(st.pos.tolist()) == sorted(want), t
+        prev = st.pos.tolist()
+    assert st.n == M and not st.is8.any()
+
+
+def test_retention_with_beta_one_is_a_sliding_window():
+    """beta = 1 for every token: all scores are 0, the newer wins every tie, so the
+    cache is the newest M positions."""
+    rng = np.random.default_rng(8)
+    prm = _prm()
+    st = _trim_run(rng, prm, 9, np.ones(40, np.float32), 40)
+    assert st.pos.tolist() == list(range(31, 40))
+
+
+def test_retention_scores_closed_form():
+    with np.errstate(divide="ignore"):
+        lb = np.log(np.array([0.5, 0.25, 1.0, 0.0], np.float32))   # ln 0 = -inf
+    s = retention_scores(lb, np.array([3, 4, 0, 5]), 5)
+    assert s[0] == np.float32(2) * np.float32(np.log(np.float32(0.5)))
+    assert s[1] == np.float32(np.log(np.float32(0.25)))
+    assert s[2] == 0 and s[3] == 0            # beta = 1 never decays; the newest scores 0
