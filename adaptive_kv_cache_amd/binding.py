@@ -21,11 +21,12 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libc
 CONF_F16, CONF_BF16 = 1, 2
 DTYPE16 = {"f16": (CONF_F16, torch.float16), "bf16": (CONF_BF16, torch.bfloat16)}
 ST_WINDOW_FULL, ST_INT8_FULL = 1, 2
-POLICY = {"confkv": 0, "full": 1, "window": 2}
+POLICY = {"confkv": 0, "full": 1, "window": 2, "trim": 3}
 
 EXPORTED = ("conf_cache_layout", "conf_workspace_bytes", "conf_cache_reset", "conf_cache_ingest",
             "conf_confidence", "conf_decode_attn", "conf_rank_evict", "conf_compact_demote",
-            "conf_evict_compact", "conf_attend", "conf_ema_evict_compact", "conf_step",
+            "conf_evict_compact", "conf_attend", "conf_ema_evict_compact",
+            "conf_trim_evict_compact", "conf_cache_set_retention", "conf_step",
             "conf_cache_export", "conf_last_error", "conf_status_string")
 
 
@@ -75,6 +76,8 @@ def load() -> ctypes.CDLL:
         "conf_evict_compact": [P, C, c_int32, vp, vp, vp],
         "conf_attend": [P, C, c_int32, vp, vp, vp, vp, vp, vp],
         "conf_ema_evict_compact": [P, C, c_int32, vp, vp, vp],
+        "conf_trim_evict_compact": [P, C, c_int32, vp, vp, vp, vp],
+        "conf_cache_set_retention": [P, C, c_int32, vp, c_int32, vp],
         "conf_step": [P, C, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         "conf_cache_export": [P, C, c_int32, c_int32, vp, vp, vp, vp, vp],
     }
@@ -231,6 +234,28 @@ class Engine:
         _check(self.lib.conf_ema_evict_compact(ctypes.byref(self.p), ctypes.byref(self.cache),
                                                layer, _ptr(budget), _ptr(self.ws), self._stream()),
                "conf_ema_evict_compact")
+
+    def trim_evict_compact(self, layer: int, budget, log_beta):
+        """conf_trim_evict_compact: after attend, the new token takes ln(beta)
+        (fp32 [L][B], or [B] for one layer) and each (layer, sequence) keeps its
+        budget[b][l] tokens of largest (t - pos) * ln(beta)."""
+        wl = self.wl
+        self._expect(budget, (wl.batch, wl.n_layers), torch.int32, "budget")
+        self._expect(log_beta, self._layer_shape(layer, wl.batch), torch.float32, "log_beta")
+        _check(self.lib.conf_trim_evict_compact(ctypes.byref(self.p), ctypes.byref(self.cache),
+                                                layer, _ptr(budget), _ptr(log_beta),
+                                                _ptr(self.ws), self._stream()),
+               "conf_trim_evict_compact")
+
+    def set_retention(self, layer: int, log_beta):
+        """conf_cache_set_retention: ln(beta) of the prefill, fp32 [L][B][L0] or
+        [B][L0] for one layer, right after ingest."""
+        wl = self.wl
+        L0 = int(log_beta.shape[-1])
+        self._expect(log_beta, self._layer_shape(layer, wl.batch, L0), torch.float32, "log_beta")
+        _check(self.lib.conf_cache_set_retention(ctypes.byref(self.p), ctypes.byref(self.cache),
+                                                 layer, _ptr(log_beta), L0, self._stream()),
+               "conf_cache_set_retention")
 
     def rank_evict(self, layer: int, budget, keep=None):
         wl = self.wl

@@ -20,7 +20,9 @@ void launch_select(const Dims&, const conf_cache&, int, int, const int32_t*, uin
 void launch_compact(const Dims&, const conf_cache&, int, int, const uint8_t*, int32_t*, int32_t*,
                     int32_t*, uint8_t*, hipStream_t);
 void launch_evict(const Dims&, const conf_cache&, int, int, const int32_t*, uint8_t*, int32_t*,
-                  int32_t*, int32_t*, uint8_t*, const float*, const int32_t*, bool, hipStream_t);
+                  int32_t*, int32_t*, uint8_t*, const float*, const int32_t*, const float*, bool,
+                  hipStream_t);
+void launch_set_retention(const Dims&, const conf_cache&, int, int, const float*, int, hipStream_t);
 void launch_export(const Dims&, const conf_cache&, int, int8_t*, int8_t*, void*, void*, hipStream_t);
 }  // namespace confkv
 
@@ -66,9 +68,7 @@ int make_dims(const conf_params* p, Dims* d) {
   if (!(p->ema_decay >= 0.f && p->ema_decay <= 1.f)) return CONF_E_INVALID;
   if (!(p->s_ema >= 0.f && p->s_rec >= 0.f)) return CONF_E_INVALID;
   if (p->pyramid != 0 && p->pyramid != 1) return CONF_E_INVALID;
-  if (p->policy != CONF_POLICY_CONFKV && p->policy != CONF_POLICY_FULL &&
-      p->policy != CONF_POLICY_WINDOW)
-    return CONF_E_INVALID;
+  if (p->policy < CONF_POLICY_CONFKV || p->policy > CONF_POLICY_TRIM) return CONF_E_INVALID;
   d->L = p->n_layers;
   d->B = p->batch;
   d->Hq = p->n_q_heads;
@@ -207,7 +207,8 @@ int conf_cache_ingest(const conf_params* p, conf_cache* c, int32_t layer, const 
     return CONF_E_INVALID;
   (void)ws;
   if (d.policy != CONF_POLICY_WINDOW && prefill_len - d.W > d.cap8) return CONF_E_CAPACITY;
-  if (d.policy == CONF_POLICY_FULL && prefill_len > d.W) return CONF_E_CAPACITY;
+  if ((d.policy == CONF_POLICY_FULL || d.policy == CONF_POLICY_TRIM) && prefill_len > d.W)
+    return CONF_E_CAPACITY;
   if (prefill_len == 0) return CONF_OK;
   launch_ingest(d, *c, l0, nl, prefill_len, k_pre, v_pre, (hipStream_t)stream);
   return check_launch("conf_cache_ingest");
@@ -243,6 +244,7 @@ static int decode_attn(const conf_params* p, conf_cache* c, int32_t layer, const
 int conf_decode_attn(const conf_params* p, conf_cache* c, int32_t layer, const void* q,
                      const void* k_new, const void* v_new, float* out, void* ws,
                      conf_stream_t stream) {
+  if (p && p->policy == CONF_POLICY_TRIM) return CONF_E_INVALID;
   return decode_attn(p, c, layer, q, k_new, v_new, out, ws, stream, true, "conf_decode_attn");
 }
 
@@ -277,27 +279,52 @@ int conf_compact_demote(const conf_params* p, conf_cache* c, int32_t layer, cons
 }
 
 static int evict(const conf_params* p, conf_cache* c, int32_t layer, const int32_t* budget,
-                 void* ws, conf_stream_t stream, bool with_ema, const char* name) {
+                 const float* log_beta, void* ws, conf_stream_t stream, bool with_ema,
+                 const char* name) {
   Dims d;
   int rc = make_dims(p, &d);
   if (rc) return rc;
   int l0, nl;
   if (!cache_ok(c) || !budget || !ws || !layer_range(d, layer, &l0, &nl)) return CONF_E_INVALID;
+  // the retention policy's appended token needs its ln(beta); nothing else takes one
+  if (with_ema && (d.policy == CONF_POLICY_TRIM) != (log_beta != nullptr)) return CONF_E_INVALID;
   const WsMap w = make_ws(d);
   launch_evict(d, *c, l0, nl, budget, at<uint8_t>(ws, w.keep), at<int32_t>(ws, w.plan),
                at<int32_t>(ws, w.mv8), at<int32_t>(ws, w.mv16), at<uint8_t>(ws, w.wkeep),
-               at<float>(ws, w.massp), at<int32_t>(ws, w.snap), with_ema, (hipStream_t)stream);
+               at<float>(ws, w.massp), at<int32_t>(ws, w.snap), log_beta, with_ema,
+               (hipStream_t)stream);
   return check_launch(name);
 }
 
 int conf_evict_compact(const conf_params* p, conf_cache* c, int32_t layer, const int32_t* budget,
                        void* ws, conf_stream_t stream) {
-  return evict(p, c, layer, budget, ws, stream, false, "conf_evict_compact");
+  return evict(p, c, layer, budget, nullptr, ws, stream, false, "conf_evict_compact");
 }
 
 int conf_ema_evict_compact(const conf_params* p, conf_cache* c, int32_t layer,
                            const int32_t* budget, void* ws, conf_stream_t stream) {
-  return evict(p, c, layer, budget, ws, stream, true, "conf_ema_evict_compact");
+  return evict(p, c, layer, budget, nullptr, ws, stream, true, "conf_ema_evict_compact");
+}
+
+int conf_trim_evict_compact(const conf_params* p, conf_cache* c, int32_t layer,
+                            const int32_t* budget, const float* log_beta, void* ws,
+                            conf_stream_t stream) {
+  if (!log_beta) return CONF_E_INVALID;
+  return evict(p, c, layer, budget, log_beta, ws, stream, true, "conf_trim_evict_compact");
+}
+
+int conf_cache_set_retention(const conf_params* p, conf_cache* c, int32_t layer,
+                             const float* log_beta, int32_t prefill_len, conf_stream_t stream) {
+  Dims d;
+  int rc = make_dims(p, &d);
+  if (rc) return rc;
+  int l0, nl;
+  if (!cache_ok(c) || !log_beta || prefill_len < 0 || prefill_len > d.W ||
+      d.policy != CONF_POLICY_TRIM || !layer_range(d, layer, &l0, &nl))
+    return CONF_E_INVALID;
+  if (prefill_len == 0) return CONF_OK;
+  launch_set_retention(d, *c, l0, nl, log_beta, prefill_len, (hipStream_t)stream);
+  return check_launch("conf_cache_set_retention");
 }
 
 int conf_step(const conf_params* p, conf_cache* c, const float* logits, const void* q,
@@ -307,7 +334,7 @@ int conf_step(const conf_params* p, conf_cache* c, const float* logits, const vo
   int rc = make_dims(p, &d);
   if (rc) return rc;
   if (!cache_ok(c) || !logits || !a16(q) || !a16(k_new) || !a16(v_new) || !out || !conf ||
-      !budget || !ws)
+      !budget || !ws || d.policy == CONF_POLICY_TRIM)
     return CONF_E_INVALID;
   const WsMap w = make_ws(d);
   hipStream_t st = (hipStream_t)stream;
@@ -316,7 +343,7 @@ int conf_step(const conf_params* p, conf_cache* c, const float* logits, const vo
   launch_confidence(d, logits, at<float>(ws, w.conf_part), conf, budget, st);
   launch_evict(d, *c, 0, d.L, budget, at<uint8_t>(ws, w.keep), at<int32_t>(ws, w.plan),
                at<int32_t>(ws, w.mv8), at<int32_t>(ws, w.mv16), at<uint8_t>(ws, w.wkeep),
-               at<float>(ws, w.massp), at<int32_t>(ws, w.snap), true, st);
+               at<float>(ws, w.massp), at<int32_t>(ws, w.snap), nullptr, true, st);
   return check_launch("conf_step");
 }
 

@@ -529,8 +529,9 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dim
   }
   __syncthreads();
   // ---- 1. keep flags (one read), counts, the demotee
-  // the token that leaves the window (full KV demotes nothing)
-  const int target = dm.policy == CONF_POLICY_FULL ? -1 : t - dm.W;
+  // the token that leaves the window (full KV and retention eviction demote nothing)
+  const int target =
+      dm.policy == CONF_POLICY_FULL || dm.policy == CONF_POLICY_TRIM ? -1 : t - dm.W;
   int c8 = 0, c16 = 0;
   for (int i = tid; i < n8; i += kCompThreads) {
     const uint8_t k = keep8[i] ? 1 : 0;
@@ -561,12 +562,12 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dim
 // X.key[j] for select_core, which then reads no memory in its first pass.
 __device__ inline void ema_pairs(const conf_cache& c, const Dims& dm, int lb,
                                  const float* __restrict__ massp_all, int n8, int nw, int t,
-                                 SelScratch& X) {
+                                 float log_beta, SelScratch& X) {
 #pragma clang fp contract(off)
   const int appended = nw < dm.cap16;
   if (dm.policy != CONF_POLICY_CONFKV) {  // no EMA: the appended token's slot only
-    if (threadIdx.x == 0 && appended) {
-      c.ema16[(size_t)lb * dm.cap16 + nw] = 0.f;
+    if (threadIdx.x == 0 && appended) {   // (retention eviction keeps its ln(beta) there)
+      c.ema16[(size_t)lb * dm.cap16 + nw] = dm.policy == CONF_POLICY_TRIM ? log_beta : 0.f;
       c.pos16[(size_t)lb * dm.cap16 + nw] = t + 1;
     }
     return;
@@ -640,7 +641,8 @@ __global__ __launch_bounds__(kCompThreads, 6) void evict_kernel(conf_cache c, Di
                                                              int32_t* __restrict__ mv16_all,
                                                              uint8_t* __restrict__ wkeep_all,
                                                              const float* __restrict__ massp_all,
-                                                             const int32_t* __restrict__ snap) {
+                                                             const int32_t* __restrict__ snap,
+                                                             const float* __restrict__ log_beta) {
   // 52 KB of LDS in all, so that three workgroups fit on a CU
   __shared__ CompFlags F;
   __shared__ union {
@@ -658,7 +660,7 @@ __global__ __launch_bounds__(kCompThreads, 6) void evict_kernel(conf_cache c, Di
     const int nw = snap[3 * lb + 1], t0 = snap[3 * lb + 2];
     n16 = nw + (nw < dm.cap16);
     t = t0 + 1;
-    ema_pairs(c, dm, lb, massp_all, n8, nw, t0, U.sel);
+    ema_pairs(c, dm, lb, massp_all, n8, nw, t0, log_beta ? log_beta[blockIdx.x] : 0.f, U.sel);
     if (tid == 0) c.t[lb] = t;  // n16 is written by the compaction
     __syncthreads();  // the EMA and the appended position are in memory for the selection
   } else {
@@ -675,8 +677,9 @@ __global__ __launch_bounds__(kCompThreads, 6) void evict_kernel(conf_cache c, Di
     M.ngrown = 0;
   }
   __syncthreads();
-  // the token that leaves the window (full KV demotes nothing)
-  const int target = dm.policy == CONF_POLICY_FULL ? -1 : t - dm.W;
+  // the token that leaves the window (full KV and retention eviction demote nothing)
+  const int target =
+      dm.policy == CONF_POLICY_FULL || dm.policy == CONF_POLICY_TRIM ? -1 : t - dm.W;
   int c8 = 0, c16 = 0;
   select_core<kCompThreads, EMA>(c, dm, lb, n8, n16, t, N, U.sel, SM, [&](int j, int k, uint64_t key) {
     if (j < n8) {
@@ -710,13 +713,29 @@ void launch_compact(const Dims& dm, const conf_cache& c, int layer0, int nl, con
 
 void launch_evict(const Dims& dm, const conf_cache& c, int layer0, int nl, const int32_t* budget,
                   uint8_t* keep, int32_t* plan, int32_t* mv8, int32_t* mv16, uint8_t* wkeep,
-                  const float* massp, const int32_t* snap, bool with_ema, hipStream_t st) {
+                  const float* massp, const int32_t* snap, const float* log_beta, bool with_ema,
+                  hipStream_t st) {
   if (with_ema)
     hipLaunchKernelGGL(evict_kernel<true>, dim3(nl * dm.B), dim3(kCompThreads), 0, st, c, dm,
-                       layer0, budget, keep, plan, mv8, mv16, wkeep, massp, snap);
+                       layer0, budget, keep, plan, mv8, mv16, wkeep, massp, snap, log_beta);
   else
     hipLaunchKernelGGL(evict_kernel<false>, dim3(nl * dm.B), dim3(kCompThreads), 0, st, c, dm,
-                       layer0, budget, keep, plan, mv8, mv16, wkeep, massp, snap);
+                       layer0, budget, keep, plan, mv8, mv16, wkeep, massp, snap, log_beta);
+}
+
+// ln(beta) of an ingested prefill (retention eviction): window slot w holds
+// position w, since the prefill fits the window.  log_beta [nl*B][L0].
+__global__ void set_retention_kernel(conf_cache c, Dims dm, int layer0, const float* log_beta,
+                                     int L0) {
+  const int lb = layer0 * dm.B + blockIdx.x;
+  for (int w = threadIdx.x; w < L0; w += blockDim.x)
+    c.ema16[(size_t)lb * dm.cap16 + w] = log_beta[(size_t)blockIdx.x * L0 + w];
+}
+
+void launch_set_retention(const Dims& dm, const conf_cache& c, int layer0, int nl,
+                          const float* log_beta, int L0, hipStream_t st) {
+  hipLaunchKernelGGL(set_retention_kernel, dim3(nl * dm.B), dim3(256), 0, st, c, dm, layer0,
+                     log_beta, L0);
 }
 
 // ---------------------------------------------------------------- export

@@ -48,6 +48,18 @@ __device__ inline uint64_t wave_min_u64(uint64_t x) {
   return x;
 }
 
+// Retention key (CONF_POLICY_TRIM): s = (t - pos) * ln(beta) <= 0, one float32
+// product, 0 for the newest token.  For m = -s >= 0 (with -0 made +0) the bits of
+// m order like m, so ~bits(m) orders like s; with the position below it the key
+// orders as (s desc, pos desc).
+__device__ inline uint64_t retention_key(float log_beta, int pos, int t) {
+#pragma clang fp contract(off)
+  float m = 0.f;
+  if (t != pos) m = -((float)(t - pos) * log_beta);
+  const uint32_t bits = m == 0.f ? 0u : __float_as_uint(m);
+  return ((uint64_t)~bits << 32) | (uint32_t)pos;
+}
+
 __device__ inline uint64_t sel_key(float e, float emax, int pos, int t, float s_ema, float s_rec) {
 #pragma clang fp contract(off)
   const float ehat = emax > 0.f ? e / emax : 0.f;
@@ -106,7 +118,7 @@ __device__ void select_core(const conf_cache& c, const Dims& dm, int lb, int n8,
   for (int j = tid; j < n; j += NT) {
     float e;
     int p;
-    if (PAIRS && cached) {
+    if (PAIRS && cached && dm.policy == CONF_POLICY_CONFKV) {
       const uint64_t v = X.key[j];
       e = __uint_as_float((uint32_t)(v >> 32));
       p = (int)(uint32_t)v;
@@ -137,6 +149,7 @@ __device__ void select_core(const conf_cache& c, const Dims& dm, int lb, int n8,
   // candidate keys; protected tokens get key 0, which no candidate can have
   auto key_from = [&](float e, int p) -> uint64_t {
     if (p > prot_lo) return 0ull;
+    if (dm.policy == CONF_POLICY_TRIM) return retention_key(e, p, t) + 1ull;
     return sel_key(e, em, p, t, dm.s_ema, dm.s_rec) + 1ull;
   };
   auto key_of = [&](int j) -> uint64_t {

@@ -19,7 +19,8 @@ import torch
 
 from .workloads import Workload
 
-_TAG_LOGITS, _TAG_TEMP, _TAG_Q, _TAG_K, _TAG_V, _TAG_PRE_K, _TAG_PRE_V, _TAG_NEEDLE = range(8)
+(_TAG_LOGITS, _TAG_TEMP, _TAG_Q, _TAG_K, _TAG_V, _TAG_PRE_K, _TAG_PRE_V, _TAG_NEEDLE,
+ _TAG_BETA, _TAG_PRE_BETA) = range(10)
 
 TORCH_DTYPE = {"f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -102,3 +103,27 @@ def prefill_kv(wl: Workload, layer: int, seed: int, device="cpu", length=None):
         k[:, :, pos, :] = 4.0 * math.sqrt(wl.head_dim) * qhat
     dt = TORCH_DTYPE[wl.dtype16]
     return k.to(dt), v.to(dt)
+
+
+def _log_gate(z: torch.Tensor) -> torch.Tensor:
+    # a retention gate's output: beta = sigmoid(z), given as ln(beta) <= 0
+    return torch.nn.functional.logsigmoid(z)
+
+
+def log_beta_new(wl: Workload, step: int, seed: int, device="cpu", layers=None) -> torch.Tensor:
+    """ln(beta) of each new token, fp32 [L][B]: beta = sigmoid(z), z ~ N(4, 2),
+    so most tokens decay slowly (beta near 0.98) and a tail decays fast.  Stands
+    in for a trained retention gate's output."""
+    nl = wl.n_layers if layers is None else layers
+    g = _gen(seed, _TAG_BETA, step, device)
+    z = 4.0 + 2.0 * torch.randn(nl, wl.batch, generator=g, device=device, dtype=torch.float32)
+    return _log_gate(z)
+
+
+def log_beta_prefill(wl: Workload, layer: int, seed: int, device="cpu", length=None):
+    """ln(beta) of the prefilled tokens of one layer, fp32 [B][L0], drawn as in
+    log_beta_new."""
+    L0 = wl.prefill if length is None else length
+    g = _gen(seed, _TAG_PRE_BETA, layer, device)
+    z = 4.0 + 2.0 * torch.randn(wl.batch, L0, generator=g, device=device, dtype=torch.float32)
+    return _log_gate(z)

@@ -51,7 +51,8 @@ class Workload:
     s_rec: float = 0.3
     temp_schedule: str = "alt"   # "alt": 0.5 / 8 in 64-step runs; "uniform": U[1.5, 3]
     needle: bool = False
-    policy: str = "confkv"       # "confkv", or a baseline: "full" (full KV), "window" (sliding)
+    policy: str = "confkv"       # "confkv", or a baseline: "full" (full KV), "window" (sliding),
+                                 # "trim" (retention eviction)
 
     @property
     def group(self) -> int:
@@ -74,6 +75,10 @@ class Workload:
         64); budgets and P at their smallest valid values, since nothing is evicted.
         window: a W-token sliding window; P = N_high = N_low = W and no pyramid, so
         the ranking keeps exactly the protected newest W.
+        trim: retention eviction with memory budget M = N_high, held entirely in the
+        16-bit window (W = M); P = 1 protects the token being appended; the prefill
+        is cut to M tokens, which is the cache that retention eviction holds once it
+        has run over a longer one.
         """
         if policy == "confkv":
             return self
@@ -84,6 +89,11 @@ class Workload:
         if policy == "window":
             return replace(self, name=f"{self.name}_window", policy="window", protect=self.window,
                            n_high=self.window, n_low=self.window, pyramid=False)
+        if policy == "trim":
+            m = self.n_high
+            return replace(self, name=f"{self.name}_trim", policy="trim", window=m, protect=1,
+                           n_high=m, n_low=m, pyramid=False, prefill=min(self.prefill, m),
+                           needle=False)
         raise ValueError(policy)
 
 

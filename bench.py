@@ -25,6 +25,9 @@ stream.  --streams 1|2 overrides the choice.
 --policy full | window runs the same step under the full-KV or the sliding-window
 baseline (the pages' comparison policies) on the same kernels and shape: full KV
 keeps every prefill and decoded token in 16 bits, the window the newest W.
+--policy trim runs retention eviction: a step is the attention and one launch that
+stores the new token's ln(beta), ranks by (t - pos) * ln(beta) and compacts, with a
+16-bit cache of M = N_high tokens (the prefill cut to M) and no confidence.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -75,13 +78,23 @@ def step_bytes(wl, n8, nw, plan):
     """Algorithmic bytes of one whole step: attention, logits, the EMA update, the
     selection's position reads, hole-fill moves and the demotion (requantisation
     not counted; the selection takes the EMA it has just written, and the keep
-    flags stay on chip in the fused EMA + selection + compaction launch)."""
+    flags stay on chip in the fused EMA + selection + compaction launch).  The
+    baselines read what their policy needs: full KV ranks nothing, the window
+    reads positions, retention eviction reads ln(beta) and positions and has no
+    confidence."""
     H, d, e = wl.n_kv_heads, wl.head_dim, 2
     n = n8 + nw + 1
     b = attn_bytes(wl, n8, nw)
-    b += wl.batch * wl.vocab * 4
-    b += int((8 * n + 4).sum())                                 # EMA read and written, new pos
-    b += int((4 * n).sum())                                     # positions read by the selection
+    if wl.policy != "trim":
+        b += wl.batch * wl.vocab * 4                            # logits (confidence)
+    if wl.policy == "confkv":
+        b += int((8 * n + 4).sum())                             # EMA read and written, new pos
+    else:
+        b += 8 * n.numel()                                      # the new token's EMA slot and pos
+    if wl.policy == "trim":
+        b += int((4 * n).sum())                                 # ln(beta) read by the ranking
+    if wl.policy != "full":
+        b += int((4 * n).sum())                                 # positions read by the selection
     moves8, moves16, dest = plan[..., 1], plan[..., 3], plan[..., 5]
     b += int((moves8 * (2 * 2 * H * d + 16)).sum())
     b += int((moves16 * (2 * 2 * H * d * e + 16)).sum())
@@ -148,11 +161,14 @@ def run(args):
         log(f"note: {total} steps exceed the workload's {wl.steps}; inputs are generated anyway")
     log(f"set-up {wl.name}: cap8={wl.cap8} prefill={wl.prefill}")
     eng = Engine(wl, dev)
+    trim = wl.policy == "trim"
     t0 = time.perf_counter()
     if wl.prefill:
         for l in range(wl.n_layers):
             k, v = synth.prefill_kv(wl, l, args.seed, device=dev)
             eng.ingest(l, k, v)
+            if trim:
+                eng.set_retention(l, synth.log_beta_prefill(wl, l, args.seed, device=dev))
             del k, v
     torch.cuda.synchronize()
     log(f"ingest done in {time.perf_counter() - t0:.1f} s")
@@ -165,9 +181,15 @@ def run(args):
         logits[s] = synth.logits(wl, s, args.seed, device=dev)
         qs[s] = synth.q_new(wl, s, args.seed, device=dev)
         ks[s], vs[s] = synth.kv_new(wl, s, args.seed, device=dev)
+    if trim:
+        # retention eviction: ln(beta) of each new token, and the memory budget M
+        lbetas = torch.stack([synth.log_beta_new(wl, s, args.seed, device=dev)
+                              for s in range(total)])
     out = torch.empty(L, B, wl.n_q_heads, wl.head_dim, dtype=torch.float32, device=dev)
     conf = torch.empty(total, B, dtype=torch.float32, device=dev)
     budget = torch.empty(total, B, L, dtype=torch.int32, device=dev)
+    if trim:
+        budget.fill_(wl.n_high)
     n8_first = torch.empty(L, B, dtype=torch.int32, device=dev)
     n16_first = torch.empty_like(n8_first)
     plan_off = _plan_offset(eng)
@@ -178,7 +200,7 @@ def run(args):
     if streams == "auto":
         # K/V bytes one attention launch streams at the tight budget
         kv = L * B * wl.n_kv_heads * wl.head_dim * (wl.n_high + wl.window) * 2
-        streams = "2" if kv >= 1 << 28 else "1"
+        streams = "2" if kv >= 1 << 28 and not trim else "1"  # trim has no confidence
     side = main if streams == "1" else torch.cuda.Stream(device=dev)
     torch.cuda.synchronize()
     log("inputs resident; warm-up")
@@ -192,7 +214,8 @@ def run(args):
             # it waits for this stream)
             if i:
                 hplan[i - 1].copy_(ws_plan)
-            eng.confidence(logits[s], c=conf[s], budget=budget[s])
+            if not trim:
+                eng.confidence(logits[s], c=conf[s], budget=budget[s])
         if ev is not None:
             ev[0].record(main)
         eng.attend(-1, qs[s], ks[s], vs[s], out=out)
@@ -200,7 +223,10 @@ def run(args):
             ev[1].record(main)
         if side is not main:
             main.wait_stream(side)
-        eng.ema_evict_compact(-1, budget[s])
+        if trim:
+            eng.trim_evict_compact(-1, budget[s], lbetas[s])
+        else:
+            eng.ema_evict_compact(-1, budget[s])
 
     for s in range(args.warmup):
         one_step(s)
@@ -248,7 +274,8 @@ def run(args):
         "metric": METRIC, "value": round(sps, 3), "unit": "steps/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms / args.steps, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": f"int8+{wl.dtype16} operands, f32 accumulate",
+        "dtype": (f"int8+{wl.dtype16}" if wl.policy == "confkv" else wl.dtype16)
+                 + " operands, f32 accumulate",
         "data": "synthetic",
         "config": {"workload": wl.name, "policy": wl.policy, "layers": L, "batch": B,
                    "q_heads": wl.n_q_heads,
@@ -375,9 +402,9 @@ def main():
     ap.add_argument("--workload", default="qwen32b_gqa_b8_32k")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--policy", choices=("confkv", "full", "window"), default="confkv",
-                    help="cache policy: CONF-KV, or the full-KV / sliding-window baseline on the "
-                         "same kernels")
+    ap.add_argument("--policy", choices=("confkv", "full", "window", "trim"), default="confkv",
+                    help="cache policy: CONF-KV, or the full-KV / sliding-window / retention-"
+                         "eviction baseline on the same kernels")
     ap.add_argument("--streams", choices=("auto", "1", "2"), default="auto",
                     help="2: confidence on a second stream beside the attention; auto: 2 when "
                          "the attention streams at least 256 MB per launch")

@@ -16,6 +16,8 @@
  *   [online]      Key contributions, system design (block-wise online softmax)
  *   [problem]     Problem statement (sliding-window eviction as a prior policy)
  *   [results]     Experimental results (full-KV latency and throughput comparison)
+ *   [trim]        the TRIM-KV page, Methodology: retention gate; inference and
+ *                 eviction (a related method in the same bundle)
  *
  * Conventions shared by every call
  *   - Every pointer argument is a DEVICE pointer owned by the caller, except
@@ -74,9 +76,21 @@ enum { CONF_F16 = 1, CONF_BF16 = 2 };
  *   CONF_POLICY_WINDOW  sliding window [problem]: after each step only positions
  *                       (t-W, t] stay, in 16 bits; older prefill tokens leave at
  *                       the first step.  Budgets and ranking play no part.
- * The baselines need no per-token attention mass: their attention is a single
- * online pass whatever the cache length, and they keep no EMA (it stays 0). */
-enum { CONF_POLICY_CONFKV = 0, CONF_POLICY_FULL = 1, CONF_POLICY_WINDOW = 2 };
+ *   CONF_POLICY_TRIM    retention eviction [trim]: each token carries ln(beta),
+ *                       beta in [0, 1], fixed at its creation and supplied by the
+ *                       caller; its current score is (t - pos) * ln(beta), the
+ *                       logarithm of beta^(t - pos) (0 for the newest token),
+ *                       one float32 product.  After each step the budget's best
+ *                       tokens stay (ties: newer first), all in 16 bits; nothing
+ *                       is demoted and only the newest token is protected.  The
+ *                       ema arrays hold ln(beta).  A step is conf_attend, then
+ *                       conf_trim_evict_compact; the prefill's ln(beta) is set
+ *                       by conf_cache_set_retention after conf_cache_ingest.
+ * The baselines and TRIM need no per-token attention mass: their attention is a
+ * single online pass whatever the cache length, and they keep no EMA (it stays
+ * 0 for FULL and WINDOW). */
+enum { CONF_POLICY_CONFKV = 0, CONF_POLICY_FULL = 1, CONF_POLICY_WINDOW = 2,
+       CONF_POLICY_TRIM = 3 };
 
 /* Device status word bits (conf_cache.status), set by kernels, never cleared
  * except by conf_cache_reset(). */
@@ -167,7 +181,7 @@ int conf_cache_reset(const conf_params* p, conf_cache* c, conf_stream_t stream);
  * INT8 with absmax over exactly those tokens (CONF_POLICY_WINDOW drops them
  * instead); the rest fill the window; every EMA is 0 and t = prefill_len - 1
  * [storage].  The layer must be empty.  CONF_E_CAPACITY if prefill_len - W >
- * cap8 (CONF-KV), or prefill_len > W (CONF_POLICY_FULL).
+ * cap8 (CONF-KV), or prefill_len > W (CONF_POLICY_FULL, CONF_POLICY_TRIM).
  */
 int conf_cache_ingest(const conf_params* p, conf_cache* c, int32_t layer, const void* k_pre,
                       const void* v_pre, int32_t prefill_len, void* ws, conf_stream_t stream);
@@ -191,7 +205,9 @@ int conf_confidence(const conf_params* p, const float* logits, float* c, int32_t
  * cached tokens of KV head h / (Hq/Hkv), INT8 tokens dequantised as code*amax/127
  * inside the block reads.  out: fp32 [L][B][Hq][d].  Then every token's EMA
  * becomes decay*e + (1-decay)*mass_j, mass_j = mean over the Hq heads of its
- * softmax probability; the new token starts from e = 0.
+ * softmax probability; the new token starts from e = 0.  CONF_E_INVALID under
+ * CONF_POLICY_TRIM (whose step is conf_attend + conf_trim_evict_compact);
+ * conf_ema_evict_compact and conf_step likewise.
  */
 int conf_decode_attn(const conf_params* p, conf_cache* c, int32_t layer, const void* q,
                      const void* k_new, const void* v_new, float* out, void* ws,
@@ -200,8 +216,9 @@ int conf_decode_attn(const conf_params* p, conf_cache* c, int32_t layer, const v
 /*
  * (b) alone: conf_decode_attn without its EMA update.  The new row is stored in
  * the window and `out` is written, but each token's attention mass stays in ws
- * and n16 and t do not advance yet: conf_ema_evict_compact on the same layer
- * selector and ws must follow before any other call touches those layers.
+ * and n16 and t do not advance yet: conf_ema_evict_compact (under
+ * CONF_POLICY_TRIM, conf_trim_evict_compact) on the same layer selector and ws
+ * must follow before any other call touches those layers.
  * Together the two calls give exactly the results of conf_decode_attn followed
  * by conf_evict_compact, with one launch fewer.
  */
@@ -248,6 +265,26 @@ int conf_evict_compact(const conf_params* p, conf_cache* c, int32_t layer, const
  */
 int conf_ema_evict_compact(const conf_params* p, conf_cache* c, int32_t layer,
                            const int32_t* budget, void* ws, conf_stream_t stream);
+
+/*
+ * Retention eviction after conf_attend (CONF_POLICY_TRIM only) [trim]: this
+ * step's token takes log_beta (fp32 [L][B] for layer = -1, [B] otherwise; each
+ * <= 0, -INFINITY for beta = 0, no NaN), n16 and t advance, and each (layer,
+ * sequence) keeps its budget[b][l] best tokens by (t - pos) * ln(beta), then
+ * compacts.  CONF_E_INVALID under any other policy.
+ */
+int conf_trim_evict_compact(const conf_params* p, conf_cache* c, int32_t layer,
+                            const int32_t* budget, const float* log_beta, void* ws,
+                            conf_stream_t stream);
+
+/*
+ * The prefill's retention (CONF_POLICY_TRIM only), right after
+ * conf_cache_ingest of `prefill_len` tokens: log_beta fp32 [L][B][prefill_len]
+ * (layer = -1) or [B][prefill_len] gives ln(beta) of positions 0 ..
+ * prefill_len-1.
+ */
+int conf_cache_set_retention(const conf_params* p, conf_cache* c, int32_t layer,
+                             const float* log_beta, int32_t prefill_len, conf_stream_t stream);
 
 /*
  * One full decode step of every layer and sequence: conf_attend(-1),

@@ -130,6 +130,37 @@ def test_bad_layer_rejected(lib):
                                  fake, null) == E_CAPACITY
 
 
+def test_policy_gated_entries(lib):
+    """Calls that do not belong to the cache's policy fail on the host: retention
+    eviction needs CONF_POLICY_TRIM and its ln(beta), the EMA paths refuse TRIM."""
+    fake = ctypes.c_void_p(0x1000)           # never dereferenced: validation fails first
+    null = ctypes.c_void_p(0)
+    cache = binding.ConfCache(*([0x1000] * 14))
+    conf, trim = _p(), _p(policy=binding.POLICY["trim"])
+    assert lib.conf_trim_evict_compact(ctypes.byref(conf), ctypes.byref(cache), -1, fake, fake,
+                                       fake, null) == E_INVALID
+    assert lib.conf_trim_evict_compact(ctypes.byref(trim), ctypes.byref(cache), -1, fake, null,
+                                       fake, null) == E_INVALID
+    assert lib.conf_trim_evict_compact(ctypes.byref(trim), ctypes.byref(cache), 64, fake, fake,
+                                       fake, null) == E_INVALID
+    assert lib.conf_ema_evict_compact(ctypes.byref(trim), ctypes.byref(cache), -1, fake, fake,
+                                      null) == E_INVALID
+    assert lib.conf_decode_attn(ctypes.byref(trim), ctypes.byref(cache), -1, fake, fake, fake,
+                                fake, fake, null) == E_INVALID
+    assert lib.conf_step(ctypes.byref(trim), ctypes.byref(cache), *([fake] * 8), null) == E_INVALID
+    W = trim.window
+    assert lib.conf_cache_set_retention(ctypes.byref(conf), ctypes.byref(cache), -1, fake, 4,
+                                        null) == E_INVALID
+    assert lib.conf_cache_set_retention(ctypes.byref(trim), ctypes.byref(cache), -1, fake, W + 1,
+                                        null) == E_INVALID
+    assert lib.conf_cache_set_retention(ctypes.byref(trim), ctypes.byref(cache), -1, null, 4,
+                                        null) == E_INVALID
+    assert lib.conf_cache_set_retention(ctypes.byref(trim), ctypes.byref(cache), 0, fake, 0,
+                                        null) == 0          # nothing to set: no launch
+    rc, _ = _layout(lib, _p(policy=4))
+    assert rc == E_INVALID
+
+
 @pytest.mark.skipif(torch.cuda.is_available(),
                     reason="passes fake device pointers: run where no GPU could receive a launch")
 def test_misaligned_pointers_rejected(lib):

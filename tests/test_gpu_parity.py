@@ -337,3 +337,82 @@ def test_sawtooth_and_no_op_from_empty():
     assert saw == {wl.n_high, wl.n_low}
     assert int((eng.t_n16).max()) <= wl.window
     assert eng.status() == 0
+
+
+def _trim_cases():
+    long = TINY["gqa16_bf16_d64_long"].scaled(name="gqa16_bf16_d64_trim6k", prefill=6100,
+                                             n_high=6000, n_low=6000, steps=5)
+    return {"mha_f16_d64": (TINY["mha_f16_d64"], 190), "gqa5_bf16_d128": (TINY["gqa5_bf16_d128"], 30),
+            "gqa8_bf16_d64": (TINY["gqa8_bf16_d64"], 30), "trim6k": (long, 5)}
+
+
+def _trim_betas(shape, step, special):
+    """ln(beta) of the new tokens: the seeded gate draws, or a small set of values
+    (0, -0.5, -1, -2, -inf) that gives tied retention scores."""
+    if not special:
+        return None
+    g = torch.Generator().manual_seed(999 + step)
+    vals = torch.tensor([0.0, -0.5, -1.0, -2.0, float("-inf")])
+    return vals[torch.randint(0, 5, shape, generator=g)]
+
+
+@pytest.mark.parametrize("special", [False, True])
+@pytest.mark.parametrize("case", ["mha_f16_d64", "gqa5_bf16_d128", "gqa8_bf16_d64", "trim6k"])
+def test_retention_eviction(case, special):
+    """Retention eviction (conf_attend + conf_trim_evict_compact) teacher-forced
+    against the oracle's trim_step: attention within tolerance, kept positions,
+    window bits and each token's ln(beta) bit-exact.  Budgets are M, with some
+    steps cutting 9 to 40 tokens at once (the radix path) and the cache then
+    growing back under its budget (no-op steps)."""
+    base, steps = _trim_cases()[case]
+    wl = base.baseline("trim", steps)
+    M = wl.n_high
+    prm = oracle_params(wl)
+    _say("trim", case, "special" if special else "gate", "M", M, "prefill", wl.prefill)
+    eng = Engine(wl)
+    if wl.prefill:
+        pre = _ingest(eng, wl, SEED)
+        for l in range(wl.n_layers):
+            lb_pre = synth.log_beta_prefill(wl, l, SEED)
+            if special:
+                lb_pre = _trim_betas(lb_pre.shape, -1 - l, True)
+            eng.set_retention(l, lb_pre.cuda())
+            for b in range(wl.batch):
+                ref = O.ingest(pre[l][0][b], pre[l][1][b], wl.window, wl.dtype16)
+                ref.ema = lb_pre[b].numpy().astype(np.float32).astype(np.float64)
+                got = to_oracle_state(eng.export(l, b), wl.dtype16)
+                assert_same_state(got, ref, what=("ingest", l, b))
+                assert np.array_equal(got.ema, ref.ema)
+    worst = 0.0
+    L, B = wl.n_layers, wl.batch
+    for step in range(steps):
+        S0 = _snap(eng, wl)
+        q = synth.q_new(wl, step, SEED)
+        k, v = synth.kv_new(wl, step, SEED)
+        lbn = _trim_betas((L, B), step, special) if special else synth.log_beta_new(wl, step, SEED)
+        budget = torch.full((B, L), M, dtype=torch.int32)
+        if step % 7 == 3:
+            for b in range(B):
+                for l in range(L):
+                    budget[b, l] = M - (9 + 11 * b + 5 * l) % 32
+        out = eng.attend(-1, q.cuda(), k.cuda(), v.cuda())
+        eng.trim_evict_compact(-1, budget.cuda(), lbn.cuda())
+        out = out.cpu().numpy()
+        S2 = _snap(eng, wl)
+        qb, kb, vb = bits16(q), bits16(k), bits16(v)
+        for l in range(L):
+            for b in range(B):
+                st = to_oracle_state(S0[l][b], wl.dtype16)
+                n_before = st.n
+                r = O.trim_step(st, qb[l, b], kb[l, b], vb[l, b], float(lbn[l, b]),
+                                int(budget[b, l]), prm)
+                err = attn_rel_err(out[l, b], r["o"])
+                worst = max(worst, err)
+                assert err <= ATTN_TOL, (case, step, l, b, err)
+                got = to_oracle_state(S2[l][b], wl.dtype16)
+                assert_same_state(got, st, what=("trim", step, l, b))
+                assert np.array_equal(got.ema, st.ema), ("ln(beta)", step, l, b)
+                assert not st.is8.any()
+                assert st.n == min(n_before + 1, int(budget[b, l]))
+    assert eng.status() == 0
+    _say("  worst attention rel err", worst)
