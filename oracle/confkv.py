@@ -74,6 +74,16 @@ limit M the lowest current score leaves.  Readings:
     (layer, sequence); the cache holds at most M tokens after each step, all
     16-bit (the page names no quantisation), and no window is protected beyond
     the newest token.
+
+Head-wise budgets (the CONF-KV page, Significance and claims: the method composes
+with head-wise allocation).  Readings:
+  * each KV head of a (layer, sequence) keeps its own tokens, so the heads'
+    caches have their own lengths, windows and INT8 splits;
+  * the layer's budget for the sequence is Hkv * N_l (token, head) pairs, spent
+    jointly: a head's own newest P positions are protected, and the other pairs
+    compete on the composite score with e_max over every head of the layer;
+  * a token's mass in head h is the mean over that head's G query heads;
+  * ties: score desc, then position desc, then head index desc.
 """
 from __future__ import annotations
 
@@ -90,7 +100,7 @@ __all__ = [
     "layer_budget", "dequantize", "attention", "attention_online", "token_mass",
     "ema_update", "composite_scores", "select_keep", "quant_codes", "requant_codes",
     "demote_token", "ingest", "step_layer", "decode_step",
-    "retention_scores", "trim_step",
+    "retention_scores", "trim_step", "joint_keep", "headwise_step",
 ]
 
 
@@ -534,6 +544,63 @@ def trim_step(st: LayerSeqState, q_bits, k_bits, v_bits, log_beta_new: float, M:
     keep = select_keep(scores, st.pos, st.t, 1, M)
     st.evict(keep)
     return dict(o=o, p=p, scores=scores, keep=keep)
+
+
+def joint_keep(e32_heads, pos_heads, t: int, P: int, N_total: int, s_ema: float,
+               s_rec: float):
+    """Keep masks of the KV heads of one (layer, sequence) under a shared budget of
+    N_total (token, head) pairs.  [Significance: head-wise allocation]
+
+    Scores are composite_scores over every head's tokens together, so e_max is the
+    largest EMA of the layer.  Below the budget everything stays.  Otherwise each
+    head's positions (t - P, t] stay, and the best N_total - |protected| other
+    pairs in the order (score desc, position desc, head desc).
+    """
+    H = len(e32_heads)
+    sizes = [np.asarray(p).size for p in pos_heads]
+    e_all = np.concatenate([np.asarray(e, F32) for e in e32_heads]) if H else np.zeros(0, F32)
+    pos_all = np.concatenate([np.asarray(p, np.int64) for p in pos_heads])
+    head_all = np.concatenate([np.full(n, h, np.int64) for h, n in enumerate(sizes)])
+    keep = np.ones(pos_all.size, bool)
+    if pos_all.size > N_total:
+        scores = composite_scores(e_all, pos_all, t, s_ema, s_rec)
+        prot = pos_all > (t - P)
+        K = N_total - int(prot.sum())
+        if K < 0:
+            raise ValueError("protected windows larger than the budget")
+        cand = np.flatnonzero(~prot)
+        order = np.lexsort((-head_all[cand], -pos_all[cand], -scores[cand]))
+        keep[:] = prot
+        keep[cand[order[:K]]] = True
+    return np.split(keep, np.cumsum(sizes)[:-1])
+
+
+def headwise_step(heads, q_bits, k_bits, v_bits, N: int, prm: OracleParams) -> dict:
+    """One decode step of one (layer, sequence) with head-wise keep sets.
+
+    heads[h] is the LayerSeqState of KV head h alone (one KV head each); q_bits
+    [Hq][d], k_bits and v_bits [Hkv][d].  Per head: append, attention of its G
+    query heads (float64), mass (mean over those G) and EMA.  Then joint_keep with
+    Hkv * N pairs, and per head eviction and the demotion of position t - W.
+    [Method/ranking] [Method/storage] [Significance: head-wise allocation]
+    """
+    G = prm.group
+    H = len(heads)
+    q = decode16(q_bits, prm.dtype16).astype(F64)
+    outs = []
+    for h, st in enumerate(heads):
+        st.append(np.asarray(k_bits)[h:h + 1], np.asarray(v_bits)[h:h + 1])
+        K, V = st.kv_values()
+        o, p = attention(q[h * G:(h + 1) * G], K, V, G)
+        st.ema = ema_update(st.ema, token_mass(p), prm.ema_decay)
+        outs.append(o)
+    t = heads[0].t
+    keeps = joint_keep([st.ema.astype(F32) for st in heads], [st.pos for st in heads], t,
+                       prm.protect, H * N, prm.s_ema, prm.s_rec)
+    for st, kp in zip(heads, keeps):
+        st.evict(kp)
+        st.demote(prm.window)
+    return dict(o=np.concatenate(outs), keeps=keeps)
 
 
 def decode_step(states, logits, q_bits, k_bits, v_bits, prm: OracleParams,
