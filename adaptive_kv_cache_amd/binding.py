@@ -35,7 +35,7 @@ class ConfParams(ctypes.Structure):
                                         "vocab", "dtype16", "window", "protect", "n_high", "n_low",
                                         "cap8", "pyramid")] + \
                [(n, c_float) for n in ("tau", "w_H", "w_m", "w_p", "ema_decay", "s_ema", "s_rec")] + \
-               [("policy", c_int32)]
+               [("policy", c_int32), ("headwise", c_int32)]
 
 
 _CACHE_FIELDS = ("k8", "v8", "k16", "v16", "k_amax", "v_amax", "pos8", "ema8", "pos16", "ema16",
@@ -112,7 +112,7 @@ def params_from_workload(wl: Workload, cap8: int | None = None, **over) -> ConfP
              n_high=wl.n_high, n_low=wl.n_low, cap8=wl.cap8 if cap8 is None else cap8,
              pyramid=int(wl.pyramid), tau=wl.tau, w_H=wl.w_H, w_m=wl.w_m, w_p=wl.w_p,
              ema_decay=wl.ema_decay, s_ema=wl.s_ema, s_rec=wl.s_rec,
-             policy=POLICY[wl.policy])
+             policy=POLICY[wl.policy], headwise=int(wl.headwise))
     d.update(over)
     return ConfParams(**d)
 
@@ -144,17 +144,19 @@ class Engine:
         L, B, Hkv, D = wl.n_layers, wl.batch, wl.n_kv_heads, wl.head_dim
         dev = self.device
         U = L * B * Hkv
+        S = wl.n_sub      # caches per layer: sequences, or (sequence, KV head) head-wise
+        self.n_sub = S
         self.t_k8 = torch.zeros(U * self.cap8 * D, dtype=torch.int8, device=dev)
         self.t_v8 = torch.zeros_like(self.t_k8)
         self.t_k16 = torch.zeros(U * self.cap16 * D, dtype=torch.int16, device=dev)
         self.t_v16 = torch.zeros_like(self.t_k16)
         self.t_k_amax = torch.zeros(L, B, Hkv, D, dtype=torch.float32, device=dev)
         self.t_v_amax = torch.zeros_like(self.t_k_amax)
-        self.t_pos8 = torch.zeros(L, B, self.cap8, dtype=torch.int32, device=dev)
-        self.t_ema8 = torch.zeros(L, B, self.cap8, dtype=torch.float32, device=dev)
-        self.t_pos16 = torch.zeros(L, B, self.cap16, dtype=torch.int32, device=dev)
-        self.t_ema16 = torch.zeros(L, B, self.cap16, dtype=torch.float32, device=dev)
-        self.t_n8 = torch.zeros(L, B, dtype=torch.int32, device=dev)
+        self.t_pos8 = torch.zeros(L, S, self.cap8, dtype=torch.int32, device=dev)
+        self.t_ema8 = torch.zeros(L, S, self.cap8, dtype=torch.float32, device=dev)
+        self.t_pos16 = torch.zeros(L, S, self.cap16, dtype=torch.int32, device=dev)
+        self.t_ema16 = torch.zeros(L, S, self.cap16, dtype=torch.float32, device=dev)
+        self.t_n8 = torch.zeros(L, S, dtype=torch.int32, device=dev)
         self.t_n16 = torch.zeros_like(self.t_n8)
         self.t_t = torch.zeros_like(self.t_n8)
         self.t_status = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -261,9 +263,9 @@ class Engine:
         wl = self.wl
         self._expect(budget, (wl.batch, wl.n_layers), torch.int32, "budget")
         if keep is None:
-            keep = torch.zeros(wl.n_layers, wl.batch, self.cap8 + self.cap16, dtype=torch.uint8,
+            keep = torch.zeros(wl.n_layers, self.n_sub, self.cap8 + self.cap16, dtype=torch.uint8,
                                device=self.device)
-        self._expect(keep, (wl.n_layers, wl.batch, self.cap8 + self.cap16), torch.uint8, "keep")
+        self._expect(keep, (wl.n_layers, self.n_sub, self.cap8 + self.cap16), torch.uint8, "keep")
         _check(self.lib.conf_rank_evict(ctypes.byref(self.p), ctypes.byref(self.cache), layer,
                                         _ptr(budget), _ptr(keep), _ptr(self.ws), self._stream()),
                "conf_rank_evict")
@@ -271,7 +273,7 @@ class Engine:
 
     def compact_demote(self, layer: int, keep):
         wl = self.wl
-        self._expect(keep, (wl.n_layers, wl.batch, self.cap8 + self.cap16), torch.uint8, "keep")
+        self._expect(keep, (wl.n_layers, self.n_sub, self.cap8 + self.cap16), torch.uint8, "keep")
         _check(self.lib.conf_compact_demote(ctypes.byref(self.p), ctypes.byref(self.cache), layer,
                                             _ptr(keep), _ptr(self.ws), self._stream()),
                "conf_compact_demote")
@@ -305,9 +307,11 @@ class Engine:
         return out, c, budget
 
     def export(self, layer: int, seq: int) -> dict:
-        """One (layer, sequence) as host numpy arrays, slot order, occupied slots only."""
+        """One (layer, sequence) as host numpy arrays, slot order, occupied slots only.
+        Head-wise, `seq` is the (sequence, KV head) pair b * Hkv + h and the
+        arrays hold that one head."""
         wl = self.wl
-        H, D = wl.n_kv_heads, wl.head_dim
+        H, D = (1 if wl.headwise else wl.n_kv_heads), wl.head_dim
         k8 = torch.empty(self.cap8, H, D, dtype=torch.int8, device=self.device)
         v8 = torch.empty_like(k8)
         k16 = torch.empty(self.cap16, H, D, dtype=torch.int16, device=self.device)
@@ -326,8 +330,8 @@ class Engine:
             ema8=self.t_ema8[layer, seq, :n8].cpu().numpy(),
             pos16=self.t_pos16[layer, seq, :n16].cpu().numpy(),
             ema16=self.t_ema16[layer, seq, :n16].cpu().numpy(),
-            k_amax=self.t_k_amax[layer, seq].cpu().numpy(),
-            v_amax=self.t_v_amax[layer, seq].cpu().numpy(),
+            k_amax=self.t_k_amax.view(wl.n_layers, self.n_sub, H, D)[layer, seq].cpu().numpy(),
+            v_amax=self.t_v_amax.view(wl.n_layers, self.n_sub, H, D)[layer, seq].cpu().numpy(),
         )
 
     def status(self) -> int:

@@ -16,7 +16,11 @@ void launch_attn(const Dims&, const conf_cache&, int, int, const void*, const vo
                  float*, float*, int32_t*, bool, hipStream_t);
 void launch_ingest(const Dims&, const conf_cache&, int, int, int, const void*, const void*,
                    hipStream_t);
+void launch_ema(const Dims&, const conf_cache&, int, int, const float*, const int32_t*,
+                hipStream_t);
 void launch_select(const Dims&, const conf_cache&, int, int, const int32_t*, uint8_t*, hipStream_t);
+void launch_joint_select(const Dims&, const conf_cache&, int, int, const int32_t*, uint8_t*,
+                         hipStream_t);
 void launch_compact(const Dims&, const conf_cache&, int, int, const uint8_t*, int32_t*, int32_t*,
                     int32_t*, uint8_t*, hipStream_t);
 void launch_evict(const Dims&, const conf_cache&, int, int, const int32_t*, uint8_t*, int32_t*,
@@ -69,10 +73,21 @@ int make_dims(const conf_params* p, Dims* d) {
   if (!(p->s_ema >= 0.f && p->s_rec >= 0.f)) return CONF_E_INVALID;
   if (p->pyramid != 0 && p->pyramid != 1) return CONF_E_INVALID;
   if (p->policy < CONF_POLICY_CONFKV || p->policy > CONF_POLICY_TRIM) return CONF_E_INVALID;
+  if (p->headwise != 0 && p->headwise != 1) return CONF_E_INVALID;
+  if (p->headwise) {
+    // the baselines keep every head's tokens alike: head-wise sets are CONF-KV's
+    if (p->policy != CONF_POLICY_CONFKV) return CONF_E_INVALID;
+    // one head may hold every pair the others leave it
+    if ((int64_t)p->cap8 <= (int64_t)p->n_kv_heads * p->n_low) return CONF_E_CAPACITY;
+    if ((int64_t)p->batch * p->n_kv_heads > (1 << 30)) return CONF_E_INVALID;
+  }
   d->L = p->n_layers;
-  d->B = p->batch;
-  d->Hq = p->n_q_heads;
-  d->Hkv = p->n_kv_heads;
+  d->headwise = p->headwise;
+  d->nseq = p->batch;
+  d->hw = p->headwise ? p->n_kv_heads : 1;
+  d->B = p->batch * d->hw;
+  d->Hq = p->headwise ? G : p->n_q_heads;
+  d->Hkv = p->headwise ? 1 : p->n_kv_heads;
   d->G = G;
   d->D = p->head_dim;
   d->V = p->vocab;
@@ -127,6 +142,25 @@ WsMap make_ws(const Dims& d) {
 template <typename T>
 T* at(void* ws, size_t off) {
   return (T*)((char*)ws + off);
+}
+
+// The per-sequence dimensions (logits, confidence and budgets are per sequence
+// also when the cache is kept per KV head).
+Dims seq_dims(const Dims& d) {
+  Dims s = d;
+  s.B = d.nseq;
+  return s;
+}
+
+// Rank + select (+ compaction) of a head-wise cache: the joint selection per
+// (layer, sequence) writes every head's keep flags to the workspace, then each
+// head is compacted on its own.
+void headwise_evict(const Dims& d, const conf_cache& c, int l0, int nl, const int32_t* budget,
+                    void* ws, const WsMap& w, bool with_ema, hipStream_t st) {
+  if (with_ema) launch_ema(d, c, l0, nl, at<float>(ws, w.massp), at<int32_t>(ws, w.snap), st);
+  launch_joint_select(d, c, l0, nl, budget, at<uint8_t>(ws, w.keep), st);
+  launch_compact(d, c, l0, nl, at<uint8_t>(ws, w.keep), at<int32_t>(ws, w.plan),
+                 at<int32_t>(ws, w.mv8), at<int32_t>(ws, w.mv16), at<uint8_t>(ws, w.wkeep), st);
 }
 
 // non-null and 16-byte aligned (the kernels read these with 16-byte loads)
@@ -221,7 +255,8 @@ int conf_confidence(const conf_params* p, const float* logits, float* c, int32_t
   if (rc) return rc;
   if (!logits || !c || !budget || !ws) return CONF_E_INVALID;
   const WsMap w = make_ws(d);
-  launch_confidence(d, logits, at<float>(ws, w.conf_part), c, budget, (hipStream_t)stream);
+  launch_confidence(seq_dims(d), logits, at<float>(ws, w.conf_part), c, budget,
+                    (hipStream_t)stream);
   return check_launch("conf_confidence");
 }
 
@@ -261,7 +296,10 @@ int conf_rank_evict(const conf_params* p, conf_cache* c, int32_t layer, const in
   int l0, nl;
   if (!cache_ok(c) || !budget || !keep || !layer_range(d, layer, &l0, &nl)) return CONF_E_INVALID;
   (void)ws;
-  launch_select(d, *c, l0, nl, budget, keep, (hipStream_t)stream);
+  if (d.headwise)
+    launch_joint_select(d, *c, l0, nl, budget, keep, (hipStream_t)stream);
+  else
+    launch_select(d, *c, l0, nl, budget, keep, (hipStream_t)stream);
   return check_launch("conf_rank_evict");
 }
 
@@ -289,6 +327,10 @@ static int evict(const conf_params* p, conf_cache* c, int32_t layer, const int32
   // the retention policy's appended token needs its ln(beta); nothing else takes one
   if (with_ema && (d.policy == CONF_POLICY_TRIM) != (log_beta != nullptr)) return CONF_E_INVALID;
   const WsMap w = make_ws(d);
+  if (d.headwise) {
+    headwise_evict(d, *c, l0, nl, budget, ws, w, with_ema, (hipStream_t)stream);
+    return check_launch(name);
+  }
   launch_evict(d, *c, l0, nl, budget, at<uint8_t>(ws, w.keep), at<int32_t>(ws, w.plan),
                at<int32_t>(ws, w.mv8), at<int32_t>(ws, w.mv16), at<uint8_t>(ws, w.wkeep),
                at<float>(ws, w.massp), at<int32_t>(ws, w.snap), log_beta, with_ema,
@@ -338,6 +380,13 @@ int conf_step(const conf_params* p, conf_cache* c, const float* logits, const vo
     return CONF_E_INVALID;
   const WsMap w = make_ws(d);
   hipStream_t st = (hipStream_t)stream;
+  if (d.headwise) {
+    launch_attn(d, *c, 0, d.L, q, k_new, v_new, out, at<float>(ws, w.massp),
+                at<int32_t>(ws, w.snap), true, st);
+    launch_confidence(seq_dims(d), logits, at<float>(ws, w.conf_part), conf, budget, st);
+    headwise_evict(d, *c, 0, d.L, budget, ws, w, false, st);
+    return check_launch("conf_step");
+  }
   launch_attn(d, *c, 0, d.L, q, k_new, v_new, out, at<float>(ws, w.massp), at<int32_t>(ws, w.snap),
               false, st);
   launch_confidence(d, logits, at<float>(ws, w.conf_part), conf, budget, st);

@@ -19,6 +19,11 @@ struct Dims {
   int bf16;                                    // 1: bfloat16, 0: IEEE half
   int pyramid;
   int policy;                                  // CONF_POLICY_*
+  // Head-wise keep sets view each KV head of a sequence as a cache of its own:
+  // then B counts (sequence, KV head) pairs, Hkv = 1 and Hq = G, while nseq is
+  // the number of sequences and hw = KV heads per sequence.  Otherwise nseq = B
+  // and hw = 1.
+  int headwise, nseq, hw;
   float tau, w_H, w_m, w_p, decay, one_minus_decay, s_ema, s_rec;
 };
 

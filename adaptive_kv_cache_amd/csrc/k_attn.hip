@@ -737,6 +737,20 @@ __global__ __launch_bounds__(kEmaThreads) void ema_kernel(conf_cache c, Dims dm,
   }
 }
 
+// The EMA launch that follows an attention launch whose EMA is pending.
+void launch_ema(const Dims& dm, const conf_cache& c, int layer0, int nl, const float* massp,
+                const int32_t* snap, hipStream_t st) {
+  // token chunks per (layer, sequence): enough for the largest budget plus the
+  // window growth of one phase (a head-wise head typically holds up to twice the
+  // per-head budget); larger caches loop inside the workgroups
+  const int typical = (dm.n_low > dm.n_high ? dm.n_low : dm.n_high) * (dm.headwise ? 2 : 1) +
+                      dm.W + 1;
+  const int cap = dm.capt < typical ? dm.capt : typical;
+  const int chunks = (cap + kEmaThreads - 1) / kEmaThreads;
+  hipLaunchKernelGGL(ema_kernel, dim3(nl * dm.B, chunks), dim3(kEmaThreads), 0, st, c, dm, layer0,
+                     massp, snap);
+}
+
 // Scores one workgroup keeps in LDS (G rows of stride cap | 1, odd so that the
 // 16 heads of a store spread over banks), after the query operands and the O
 // merge buffer.
@@ -770,14 +784,8 @@ static void launch_t(const Dims& dm, const conf_cache& c, int layer0, int nl, co
                      attn_dyn_lds(dm), st, c, dm, layer0, (const uint16_t*)q,
                      (const uint16_t*)k_new, (const uint16_t*)v_new, out, massp, snap,
                      attn_score_cap(dm));
-  if (!with_ema) return;  // a fused EMA + selection + compaction launch follows
-  // token chunks per (layer, sequence): enough for the largest budget plus the
-  // window growth of one phase; larger caches loop inside the workgroups
-  const int typical = (dm.n_low > dm.n_high ? dm.n_low : dm.n_high) + dm.W + 1;
-  const int cap = dm.capt < typical ? dm.capt : typical;
-  const int chunks = (cap + kEmaThreads - 1) / kEmaThreads;
-  hipLaunchKernelGGL(ema_kernel, dim3(nl * dm.B, chunks), dim3(kEmaThreads), 0, st, c, dm, layer0,
-                     massp, snap);
+  if (with_ema) launch_ema(dm, c, layer0, nl, massp, snap, st);
+  // otherwise a launch that applies the EMA itself follows
 }
 
 template <int D_, bool BF16_>

@@ -60,74 +60,57 @@ __device__ inline uint64_t retention_key(float log_beta, int pos, int t) {
   return ((uint64_t)~bits << 32) | (uint32_t)pos;
 }
 
-__device__ inline uint64_t sel_key(float e, float emax, int pos, int t, float s_ema, float s_rec) {
+__device__ inline uint64_t sel_key(float e, float emax, int pos, int t, float s_ema, float s_rec,
+                                   uint32_t tag) {
 #pragma clang fp contract(off)
   const float ehat = emax > 0.f ? e / emax : 0.f;
   const float r = t > 0 ? (float)pos / (float)t : 1.0f;
   const float a = s_ema * ehat;
   const float b = s_rec * r;
   const float s = a + b;
-  return ((uint64_t)__float_as_uint(s) << 32) | (uint32_t)pos;
+  return ((uint64_t)__float_as_uint(s) << 32) | tag;
 }
 
-// Keep flags of one (layer, sequence) with n8 INT8 and n16 window tokens and
-// budget N, over the index space j < n8 (INT8 slot j), j >= n8 (window slot
-// j - n8).  Calls sink(j, keep, key) exactly once per index; key is the token's
-// key + 1 (so a candidate's is never 0), 0 for a protected token, or kAllKept
-// when n <= N and nothing is ranked.  All NT threads of the workgroup must call
-// it; the sink calls are the last thing it does (no barrier follows them).
-// With PAIRS, the caller has left each token's (bits(e) << 32 | pos) in X.key[j]
-// whenever n8 + n16 <= kSelLdsKeys, written by the thread that owns j here
-// (j mod NT), so the first pass reads no memory.
-template <int NT, bool PAIRS = false, typename Sink>
-__device__ void select_core(const conf_cache& c, const Dims& dm, int lb, int n8, int n16, int t,
-                            int N, SelScratch& X, SelMisc& M, Sink sink) {
+// The ranking shared by the per-sequence and the head-wise selection.  Tokens
+// j < n each have (e, tag) from tok(j, e, tag); tag is the token's position, or
+// in the head-wise (JOINT) form position * hw + head, so that the low key word
+// is unique among the n tokens.  A token is protected when its position is
+// above prot_lo.  keyf(e, e_max, tag) gives a candidate's 64-bit key; larger
+// keys are kept first.  Keeps the protected tokens and the N - |protected|
+// candidates with the largest keys, and calls sink(j, keep, key) once per j
+// with key = the candidate's key + 1, 0 for a protected token (or kAllKept when
+// n <= N and nothing is ranked).  With PAIRS and use_pairs, X.key[j] already
+// holds (bits(e) << 32 | tag) for every j, written by thread j mod NT, whenever
+// n <= kSelLdsKeys.
+template <int NT, bool PAIRS, bool JOINT, typename Tok, typename KeyFn, typename Sink>
+__device__ void rank_core(int n, int N, int prot_lo, int hw, bool use_pairs, Tok tok, KeyFn keyf,
+                          SelScratch& X, SelMisc& M, Sink sink) {
   constexpr int kWaves = NT / 64;
   static_assert(kWaves <= 16, "SelMisc holds 16 wavefronts");
-  const int n = n8 + n16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // full KV keeps everything, as CONF-KV does under its budget
-  if (n <= N || dm.policy == CONF_POLICY_FULL) {
+  if (n <= N) {
     for (int j = tid; j < n; j += NT) sink(j, 1, kAllKept);
     return;
   }
-  const int32_t* pos8 = c.pos8 + (size_t)lb * dm.cap8;
-  const float* ema8 = c.ema8 + (size_t)lb * dm.cap8;
-  const int32_t* pos16 = c.pos16 + (size_t)lb * dm.cap16;
-  const float* ema16 = c.ema16 + (size_t)lb * dm.cap16;
-  if (dm.policy == CONF_POLICY_WINDOW) {  // the newest W positions, (t-W, t]
-    for (int j = tid; j < n; j += NT)
-      sink(j, (j < n8 ? pos8[j] : pos16[j - n8]) > t - dm.W, kAllKept);
-    return;
-  }
-  const int prot_lo = t - dm.P;  // protected: pos > prot_lo
+  auto pos_of = [&](uint32_t tag) -> int { return JOINT ? (int)(tag / (uint32_t)hw) : (int)tag; };
   const bool cached = n <= kSelLdsKeys;
-  auto tok = [&](int j, float& e, int& p) {
-    if (j < n8) {
-      e = ema8[j];
-      p = pos8[j];
-    } else {
-      e = ema16[j - n8];
-      p = pos16[j - n8];
-    }
-  };
-  // e_max over every cached token and the protected count; with the keys in LDS
-  // the (e, pos) pairs wait there for the key pass (same thread, same index)
+  // e_max over every token and the protected count; with the keys in LDS the
+  // (e, tag) pairs wait there for the key pass (same thread, same index)
   float emax = 0.f;
   int nprot = 0;
   for (int j = tid; j < n; j += NT) {
     float e;
-    int p;
-    if (PAIRS && cached && dm.policy == CONF_POLICY_CONFKV) {
+    uint32_t tag;
+    if (PAIRS && cached && use_pairs) {
       const uint64_t v = X.key[j];
       e = __uint_as_float((uint32_t)(v >> 32));
-      p = (int)(uint32_t)v;
+      tag = (uint32_t)v;
     } else {
-      tok(j, e, p);
-      if (cached) X.key[j] = ((uint64_t)__float_as_uint(e) << 32) | (uint32_t)p;
+      tok(j, e, tag);
+      if (cached) X.key[j] = ((uint64_t)__float_as_uint(e) << 32) | tag;
     }
     emax = fmaxf(emax, e);
-    nprot += p > prot_lo;
+    nprot += pos_of(tag) > prot_lo;
   }
   for (int off = 32; off > 0; off >>= 1) {
     emax = fmaxf(emax, __shfl_xor(emax, off));
@@ -147,21 +130,20 @@ __device__ void select_core(const conf_cache& c, const Dims& dm, int lb, int n8,
   int K = N - np;
   if (K < 0) K = 0;
   // candidate keys; protected tokens get key 0, which no candidate can have
-  auto key_from = [&](float e, int p) -> uint64_t {
-    if (p > prot_lo) return 0ull;
-    if (dm.policy == CONF_POLICY_TRIM) return retention_key(e, p, t) + 1ull;
-    return sel_key(e, em, p, t, dm.s_ema, dm.s_rec) + 1ull;
+  auto key_from = [&](float e, uint32_t tag) -> uint64_t {
+    if (pos_of(tag) > prot_lo) return 0ull;
+    return keyf(e, em, tag) + 1ull;
   };
   auto key_of = [&](int j) -> uint64_t {
     float e;
-    int p;
-    tok(j, e, p);
-    return key_from(e, p);
+    uint32_t tag;
+    tok(j, e, tag);
+    return key_from(e, tag);
   };
   if (cached)
     for (int j = tid; j < n; j += NT) {
       const uint64_t v = X.key[j];
-      X.key[j] = key_from(__uint_as_float((uint32_t)(v >> 32)), (int)(uint32_t)v);
+      X.key[j] = key_from(__uint_as_float((uint32_t)(v >> 32)), (uint32_t)v);
     }
   const int evict = (n - np) - K;  // candidates that go
   if (K > 0 && evict <= kFewEvict) {
@@ -249,6 +231,51 @@ __device__ void select_core(const conf_cache& c, const Dims& dm, int lb, int n8,
     const uint64_t key = cached ? X.key[j] : key_of(j);
     sink(j, key == 0ull ? 1 : (K > 0 && key >= kth), key);
   }
+}
+
+// Keep flags of one (layer, sequence) with n8 INT8 and n16 window tokens and
+// budget N, over the index space j < n8 (INT8 slot j), j >= n8 (window slot
+// j - n8).  Calls sink(j, keep, key) exactly once per index; key is the token's
+// key + 1 (so a candidate's is never 0), 0 for a protected token, or kAllKept
+// when n <= N and nothing is ranked.  All NT threads of the workgroup must call
+// it; the sink calls are the last thing it does (no barrier follows them).
+// With PAIRS, the caller has left each token's (bits(e) << 32 | pos) in X.key[j]
+// whenever n8 + n16 <= kSelLdsKeys, written by the thread that owns j here
+// (j mod NT), so the first pass reads no memory.
+template <int NT, bool PAIRS = false, typename Sink>
+__device__ void select_core(const conf_cache& c, const Dims& dm, int lb, int n8, int n16, int t,
+                            int N, SelScratch& X, SelMisc& M, Sink sink) {
+  const int n = n8 + n16;
+  const int tid = threadIdx.x;
+  // full KV keeps everything, as CONF-KV does under its budget
+  if (n <= N || dm.policy == CONF_POLICY_FULL) {
+    for (int j = tid; j < n; j += NT) sink(j, 1, kAllKept);
+    return;
+  }
+  const int32_t* pos8 = c.pos8 + (size_t)lb * dm.cap8;
+  const float* ema8 = c.ema8 + (size_t)lb * dm.cap8;
+  const int32_t* pos16 = c.pos16 + (size_t)lb * dm.cap16;
+  const float* ema16 = c.ema16 + (size_t)lb * dm.cap16;
+  if (dm.policy == CONF_POLICY_WINDOW) {  // the newest W positions, (t-W, t]
+    for (int j = tid; j < n; j += NT)
+      sink(j, (j < n8 ? pos8[j] : pos16[j - n8]) > t - dm.W, kAllKept);
+    return;
+  }
+  auto tok = [&](int j, float& e, uint32_t& tag) {
+    if (j < n8) {
+      e = ema8[j];
+      tag = (uint32_t)pos8[j];
+    } else {
+      e = ema16[j - n8];
+      tag = (uint32_t)pos16[j - n8];
+    }
+  };
+  const bool trim = dm.policy == CONF_POLICY_TRIM;
+  auto keyf = [&](float e, float em, uint32_t tag) -> uint64_t {
+    if (trim) return retention_key(e, (int)tag, t);
+    return sel_key(e, em, (int)tag, t, dm.s_ema, dm.s_rec, tag);
+  };
+  rank_core<NT, PAIRS, false>(n, N, t - dm.P, 1, !trim, tok, keyf, X, M, sink);
 }
 
 }  // namespace confkv

@@ -53,6 +53,7 @@ class Workload:
     needle: bool = False
     policy: str = "confkv"       # "confkv", or a baseline: "full" (full KV), "window" (sliding),
                                  # "trim" (retention eviction)
+    headwise: bool = False       # per-KV-head keep sets sharing Hkv * N pairs per layer
 
     @property
     def group(self) -> int:
@@ -62,11 +63,21 @@ class Workload:
     def cap8(self) -> int:
         """INT8-region capacity in tokens per (layer, sequence), a multiple of 64."""
         old = 0 if self.policy == "window" else self.prefill - self.window  # a window drops them
-        need = max(old, self.n_low + 1, 64)
+        per_budget = self.n_low * (self.n_kv_heads if self.headwise else 1)
+        need = max(old, per_budget + 1, 64)
         return (need + 63) // 64 * 64
 
     def scaled(self, **kw) -> "Workload":
         return replace(self, **kw)
+
+    @property
+    def n_sub(self) -> int:
+        """Caches per layer: sequences, or (sequence, KV head) pairs head-wise."""
+        return self.batch * (self.n_kv_heads if self.headwise else 1)
+
+    def headwise_variant(self) -> "Workload":
+        """The same shape with head-wise keep sets."""
+        return replace(self, name=f"{self.name}_hw", headwise=True)
 
     def baseline(self, policy: str, horizon: int) -> "Workload":
         """The same shape under a baseline policy, for `horizon` decode steps.

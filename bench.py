@@ -58,17 +58,27 @@ def log(*a):
 
 
 # ---------------------------------------------------------------- byte model
+def _heads(wl):
+    """KV heads per cache: one when each head keeps its own tokens."""
+    return 1 if wl.headwise else wl.n_kv_heads
+
+
+def _qheads(wl):
+    return wl.group if wl.headwise else wl.n_q_heads
+
+
 def attn_bytes(wl, n8, nw):
     """Algorithmic bytes of one attention launch (conf_attend: every layer and
     sequence; the EMA update is counted with the step).
 
-    n8, nw: int64 tensors [L][B] of INT8 and window tokens before the append.
+    n8, nw: int64 tensors [L][B] of INT8 and window tokens before the append
+    ([L][B*Hkv] head-wise, each cache then holding one KV head).
     Per (layer, sequence): cached K and V (1 byte per INT8 element, e per 16-bit
     element), this step's k and v read and appended, both absmax rows, and q in
     and o out (fp32).
     """
     e = 2
-    H, d, Hq = wl.n_kv_heads, wl.head_dim, wl.n_q_heads
+    H, d, Hq = _heads(wl), wl.head_dim, _qheads(wl)
     kv = 2 * H * d * (n8 + e * nw)
     per_lb = kv + 2 * H * d * e * 2 + 2 * H * d * 4 + Hq * d * (e + 4)
     return int(per_lb.sum())
@@ -82,7 +92,7 @@ def step_bytes(wl, n8, nw, plan):
     baselines read what their policy needs: full KV ranks nothing, the window
     reads positions, retention eviction reads ln(beta) and positions and has no
     confidence."""
-    H, d, e = wl.n_kv_heads, wl.head_dim, 2
+    H, d, e = _heads(wl), wl.head_dim, 2
     n = n8 + nw + 1
     b = attn_bytes(wl, n8, nw)
     if wl.policy != "trim":
@@ -154,6 +164,8 @@ def cpu_baseline(wl, seed, budget_s=20.0):
 # ---------------------------------------------------------------- GPU run
 def run(args):
     wl = WORKLOADS[args.workload].baseline(args.policy, args.warmup + args.steps)
+    if args.headwise:
+        wl = wl.headwise_variant()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     total = args.warmup + args.steps
@@ -190,11 +202,12 @@ def run(args):
     budget = torch.empty(total, B, L, dtype=torch.int32, device=dev)
     if trim:
         budget.fill_(wl.n_high)
-    n8_first = torch.empty(L, B, dtype=torch.int32, device=dev)
+    S = wl.n_sub
+    n8_first = torch.empty(L, S, dtype=torch.int32, device=dev)
     n16_first = torch.empty_like(n8_first)
     plan_off = _plan_offset(eng)
-    hplan = torch.empty(args.steps, L, B, 16, dtype=torch.int32, device=dev)
-    ws_plan = eng.ws[plan_off:plan_off + L * B * 16 * 4].view(torch.int32).view(L, B, 16)
+    hplan = torch.empty(args.steps, L, S, 16, dtype=torch.int32, device=dev)
+    ws_plan = eng.ws[plan_off:plan_off + L * S * 16 * 4].view(torch.int32).view(L, S, 16)
     main = torch.cuda.current_stream(dev)
     streams = args.streams
     if streams == "auto":
@@ -277,7 +290,8 @@ def run(args):
         "dtype": (f"int8+{wl.dtype16}" if wl.policy == "confkv" else wl.dtype16)
                  + " operands, f32 accumulate",
         "data": "synthetic",
-        "config": {"workload": wl.name, "policy": wl.policy, "layers": L, "batch": B,
+        "config": {"workload": wl.name, "policy": wl.policy, "headwise": wl.headwise,
+                   "layers": L, "batch": B,
                    "q_heads": wl.n_q_heads,
                    "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "dtype16": wl.dtype16,
                    "prefill": wl.prefill, "n_high": wl.n_high, "n_low": wl.n_low,
@@ -301,12 +315,12 @@ def _plan_offset(eng):
     """Byte offset of the compaction plan inside the workspace (same arithmetic
     as the library's workspace map: 256-byte aligned regions in a fixed order)."""
     wl = eng.wl
-    LB = wl.n_layers * wl.batch
+    LB = wl.n_layers * wl.n_sub
     a = lambda x: (x + 255) & ~255  # noqa: E731
     nch = -(-wl.vocab // (256 * 16))
-    off = a(wl.batch * nch * 8 * 4)
-    off = a(off + LB * wl.n_kv_heads * (eng.cap8 + eng.cap16) * 4)
-    off = a(off + LB * wl.n_q_heads * 4)
+    off = a(wl.n_sub * nch * 8 * 4)
+    off = a(off + LB * _heads(wl) * (eng.cap8 + eng.cap16) * 4)
+    off = a(off + LB * _qheads(wl) * 4)
     off = a(off + LB * (eng.cap8 + eng.cap16))
     return off
 
@@ -405,6 +419,9 @@ def main():
     ap.add_argument("--policy", choices=("confkv", "full", "window", "trim"), default="confkv",
                     help="cache policy: CONF-KV, or the full-KV / sliding-window / retention-"
                          "eviction baseline on the same kernels")
+    ap.add_argument("--headwise", action="store_true",
+                    help="head-wise keep sets: each KV head keeps its own tokens, the layer's "
+                         "Hkv * N pairs shared by the heads")
     ap.add_argument("--streams", choices=("auto", "1", "2"), default="auto",
                     help="2: confidence on a second stream beside the attention; auto: 2 when "
                          "the attention streams at least 256 MB per launch")
@@ -430,7 +447,7 @@ def main():
               "(sharding is described in the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     res, wl = run(args)
-    if not args.no_cpu_baseline and args.policy == "confkv":
+    if not args.no_cpu_baseline and args.policy == "confkv" and not args.headwise:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(wl, args.seed, args.cpu_seconds)
     print(json.dumps(res), flush=True)

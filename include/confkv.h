@@ -18,6 +18,8 @@
  *   [results]     Experimental results (full-KV latency and throughput comparison)
  *   [trim]        the TRIM-KV page, Methodology: retention gate; inference and
  *                 eviction (a related method in the same bundle)
+ *   [heads]       Significance and claims (the method composes with head-wise
+ *                 allocation)
  *
  * Conventions shared by every call
  *   - Every pointer argument is a DEVICE pointer owned by the caller, except
@@ -113,7 +115,28 @@ typedef struct conf_params {
   float ema_decay;          /* e <- decay*e + (1-decay)*mass [ranking] */
   float s_ema, s_rec;       /* score = s_ema*(e/e_max) + s_rec*(pos/t) [ranking] */
   int32_t policy;           /* CONF_POLICY_*; 0 is CONF-KV */
+  int32_t headwise;         /* 1: head-wise keep sets (CONF_POLICY_CONFKV only), below */
 } conf_params;
+
+/*
+ * Head-wise keep sets [heads] (conf_params.headwise = 1).  Each KV head h of
+ * sequence b is a cache of its own, sub-sequence s = b*Hkv + h, with its own
+ * tokens, window and INT8 split:
+ *   - pos8, ema8, pos16, ema16, n8, n16 and t are [L][B*Hkv][...] in place of
+ *     [L][B][...]; conf_cache_layout() reports those sizes; conf_cache_export's
+ *     `seq` is s and its outputs have one KV head;
+ *   - q, k_new, v_new, out, k_pre, v_pre, logits, c and budget keep their shapes;
+ *   - a token's mass in head h is the mean over h's Hq/Hkv query heads;
+ *   - the selection of (layer l, sequence b) spends Hkv * budget[b][l]
+ *     (token, head) pairs jointly: each head's positions (t-P, t] stay, the
+ *     other pairs are ranked by the composite score with e_max over every head
+ *     of the layer, ties by position desc, then head desc; each head then
+ *     demotes its own position t-W;
+ *   - the steps that apply the EMA and select run as separate launches (EMA,
+ *     joint selection, per-head compaction).
+ * CONF_E_CAPACITY unless cap8 > Hkv * n_low (one head may hold all the pairs
+ * the others leave it).  Positions must stay below 2^32 / Hkv.
+ */
 
 /*
  * The dense mixed-precision cache [storage][impl].  All arrays are caller-

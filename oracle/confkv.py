@@ -575,32 +575,39 @@ def joint_keep(e32_heads, pos_heads, t: int, P: int, N_total: int, s_ema: float,
     return np.split(keep, np.cumsum(sizes)[:-1])
 
 
-def headwise_step(heads, q_bits, k_bits, v_bits, N: int, prm: OracleParams) -> dict:
+def headwise_step(heads, q_bits, k_bits, v_bits, N: int, prm: OracleParams,
+                  ema32_override=None) -> dict:
     """One decode step of one (layer, sequence) with head-wise keep sets.
 
     heads[h] is the LayerSeqState of KV head h alone (one KV head each); q_bits
     [Hq][d], k_bits and v_bits [Hkv][d].  Per head: append, attention of its G
     query heads (float64), mass (mean over those G) and EMA.  Then joint_keep with
     Hkv * N pairs, and per head eviction and the demotion of position t - W.
+    The selection reads the float32 rounding of each head's EMA, or
+    ema32_override[h] (one value per token after the append), as step_layer does.
     [Method/ranking] [Method/storage] [Significance: head-wise allocation]
     """
     G = prm.group
     H = len(heads)
     q = decode16(q_bits, prm.dtype16).astype(F64)
-    outs = []
+    outs, emas = [], []
     for h, st in enumerate(heads):
         st.append(np.asarray(k_bits)[h:h + 1], np.asarray(v_bits)[h:h + 1])
         K, V = st.kv_values()
         o, p = attention(q[h * G:(h + 1) * G], K, V, G)
         st.ema = ema_update(st.ema, token_mass(p), prm.ema_decay)
+        emas.append(st.ema.copy())
         outs.append(o)
+        if ema32_override is not None:
+            st.ema = np.asarray(ema32_override[h], F32).astype(F64)
     t = heads[0].t
     keeps = joint_keep([st.ema.astype(F32) for st in heads], [st.pos for st in heads], t,
                        prm.protect, H * N, prm.s_ema, prm.s_rec)
+    pos_before = [st.pos.copy() for st in heads]
     for st, kp in zip(heads, keeps):
         st.evict(kp)
         st.demote(prm.window)
-    return dict(o=np.concatenate(outs), keeps=keeps)
+    return dict(o=np.concatenate(outs), keeps=keeps, ema=emas, pos_before=pos_before)
 
 
 def decode_step(states, logits, q_bits, k_bits, v_bits, prm: OracleParams,

@@ -92,6 +92,25 @@ def test_invalid_params(lib, over, code):
     assert rc == code
 
 
+def test_headwise_layout_and_checks(lib):
+    """Head-wise caches keep their per-token arrays per (sequence, KV head)."""
+    wl = WORKLOADS["qwen32b_gqa_b8_32k"].headwise_variant()
+    p = binding.params_from_workload(wl)
+    rc, out = _layout(lib, p)
+    assert rc == 0
+    S = wl.batch * wl.n_kv_heads
+    assert out.n8 == wl.n_layers * S * 4
+    assert out.pos8 == wl.n_layers * S * wl.cap8 * 4
+    assert out.k8 == wl.n_layers * S * wl.cap8 * wl.head_dim
+    assert out.k_amax == wl.n_layers * S * wl.head_dim * 4
+    assert wl.cap8 > wl.n_kv_heads * wl.n_low
+    assert _layout(lib, binding.params_from_workload(wl, cap8=wl.n_kv_heads * wl.n_low))[0] \
+        == E_CAPACITY
+    assert _layout(lib, binding.params_from_workload(wl, headwise=2))[0] == E_INVALID
+    assert _layout(lib, binding.params_from_workload(wl, policy=binding.POLICY["trim"]))[0] \
+        == E_INVALID
+
+
 def test_null_pointers_rejected_before_launch(lib):
     p = _p()
     cache = binding.ConfCache()

@@ -416,3 +416,129 @@ def test_retention_eviction(case, special):
                 assert st.n == min(n_before + 1, int(budget[b, l]))
     assert eng.status() == 0
     _say("  worst attention rel err", worst)
+
+
+def _headwise_cases():
+    wide = Workload(name="hw_wide_f16_d64", n_layers=1, batch=1, n_q_heads=8, n_kv_heads=8,
+                    head_dim=64, vocab=500, dtype16="f16", window=40, protect=6, n_high=700,
+                    n_low=760, prefill=1000, steps=6)
+    return {"mha_f16_d64": (TINY["mha_f16_d64"], 170), "gqa5_bf16_d128": (TINY["gqa5_bf16_d128"], 14),
+            "gqa8_bf16_d64": (TINY["gqa8_bf16_d64"], 14), "mha16_f16_d128": (TINY["mha16_f16_d128"], 10),
+            "hw_wide_f16_d64": (wide, 6)}
+
+
+@pytest.mark.parametrize("case", list(_headwise_cases()))
+def test_headwise_teacher_forced(case):
+    """Head-wise keep sets through the C ABI (decode_attn, confidence, the joint
+    rank_evict, compact_demote), teacher-forced against the oracle's
+    headwise_step on every (layer, sequence): attention within tolerance, each
+    head's EMA within 1e-5, the joint keep sets and every head's cache bit-exact.
+    hw_wide holds 8000 tokens over its 8 heads at the first step, more than the
+    selection's LDS key cache, and cuts them to 5600 pairs."""
+    base, steps = _headwise_cases()[case]
+    wl = base.headwise_variant()
+    H, S = wl.n_kv_heads, wl.n_sub
+    prm = oracle_params(wl)
+    _say("headwise", case, "heads", H, "steps", steps)
+    eng = Engine(wl)
+    cap8 = eng.cap8
+    if wl.prefill:
+        pre = _ingest(eng, wl, SEED)
+        for l in range(wl.n_layers):
+            for b in range(wl.batch):
+                for h in range(H):
+                    ref = O.ingest(pre[l][0][b][h:h + 1], pre[l][1][b][h:h + 1], wl.window,
+                                   wl.dtype16)
+                    got = to_oracle_state(eng.export(l, b * H + h), wl.dtype16)
+                    assert_same_state(got, ref, ema_rtol=0, what=("ingest", l, b, h))
+    worst = 0.0
+    sizes_seen = set()
+    for step in range(steps):
+        S0 = _snap_sub(eng, wl)
+        z = synth.logits(wl, step, SEED)
+        q = synth.q_new(wl, step, SEED)
+        k, v = synth.kv_new(wl, step, SEED)
+        out = eng.decode_attn(-1, q.cuda(), k.cuda(), v.cuda())
+        S1 = _snap_sub(eng, wl)
+        c, budget = eng.confidence(z.cuda())
+        keep = eng.rank_evict(-1, budget)
+        eng.compact_demote(-1, keep)
+        keep = keep.cpu().numpy()
+        S2 = _snap_sub(eng, wl)
+        out = out.cpu().numpy()
+        budget = budget.cpu().numpy()
+        _check_conf(c.cpu().numpy(), budget, z.numpy().astype(np.float64), wl)
+        qb, kb, vb = bits16(q), bits16(k), bits16(v)
+        for l in range(wl.n_layers):
+            for b in range(wl.batch):
+                subs = [b * H + h for h in range(H)]
+                heads = [to_oracle_state(S0[l][s], wl.dtype16) for s in subs]
+                override = []
+                for s, st in zip(subs, heads):
+                    e_gpu = ema_by_pos(S1[l][s])
+                    override.append(np.array([e_gpu[p] for p in np.append(st.pos, st.t + 1)],
+                                             np.float32))
+                n_before = sum(st.n for st in heads)
+                r = O.headwise_step(heads, qb[l, b], kb[l, b], vb[l, b], int(budget[b, l]), prm,
+                                    ema32_override=override)
+                what = (case, step, l, b)
+                err = attn_rel_err(out[l, b], r["o"])
+                worst = max(worst, err)
+                assert err <= ATTN_TOL, (what, err)
+                for h, s in enumerate(subs):
+                    np.testing.assert_allclose(override[h], r["ema"][h], rtol=EMA_RTOL,
+                                               atol=1e-12, err_msg=str((what, h)))
+                    got = kept_positions(S1[l][s], keep[l, s], cap8)
+                    assert got == set(r["pos_before"][h][r["keeps"][h]].tolist()), (what, h)
+                    assert_same_state(to_oracle_state(S2[l][s], wl.dtype16), heads[h],
+                                      ema_rtol=0, what=(what, h))
+                n_heads = [heads[h].n for h in range(H)]
+                sizes_seen.add(tuple(n_heads))
+                assert sum(n_heads) == min(n_before + H, H * int(budget[b, l])), what
+    assert eng.status() == 0
+    # the keep sets are ragged: heads of one (layer, sequence) end with different sizes
+    assert any(len(set(sz)) > 1 for sz in sizes_seen) or H == 1
+    _say("  worst attention rel err", worst)
+
+
+def _snap_sub(eng, wl):
+    return [[eng.export(l, s) for s in range(wl.n_sub)] for l in range(wl.n_layers)]
+
+
+@pytest.mark.parametrize("case", ["mha_f16_d64", "gqa5_bf16_d128", "hw_wide_f16_d64"])
+def test_headwise_entry_points_agree(case):
+    """Head-wise: conf_step, attend + ema_evict_compact, and decode_attn +
+    evict_compact leave bit-identical caches and outputs, for all layers at once
+    and layer by layer."""
+    base, steps = _headwise_cases()[case]
+    wl = base.headwise_variant()
+    _say("headwise entry points", case)
+    a, b, c = Engine(wl), Engine(wl), Engine(wl)
+    if wl.prefill:
+        for e in (a, b, c):
+            _ingest(e, wl, SEED)
+    steps = min(steps, 60)
+    for step in range(steps):
+        z = synth.logits(wl, step, SEED).cuda()
+        q = synth.q_new(wl, step, SEED).cuda()
+        k, v = (x.cuda() for x in synth.kv_new(wl, step, SEED))
+        oa, ca, bud = a.step(z, q, k, v)
+        layers = [-1] if step % 2 == 0 else list(range(wl.n_layers))
+        for l in layers:
+            ql, kl, vl = (x if l < 0 else x[l].contiguous() for x in (q, k, v))
+            ob = b.attend(l, ql, kl, vl)
+            b.ema_evict_compact(l, bud)
+            oc = c.decode_attn(l, ql, kl, vl)
+            c.evict_compact(l, bud)
+            ref = oa if l < 0 else oa[l]
+            assert torch.equal(ref, ob) and torch.equal(ref, oc), (step, l)
+        if step % 5 == 4 or step == steps - 1:
+            for l in range(wl.n_layers):
+                for s_ in range(wl.n_sub):
+                    ea, eb, ec = a.export(l, s_), b.export(l, s_), c.export(l, s_)
+                    for key in ea:
+                        assert np.array_equal(np.asarray(ea[key]), np.asarray(eb[key])), \
+                            ("ema_evict_compact", step, l, s_, key)
+                        assert np.array_equal(np.asarray(ea[key]), np.asarray(ec[key])), \
+                            ("evict_compact", step, l, s_, key)
+    assert a.status() == 0 and b.status() == 0 and c.status() == 0
