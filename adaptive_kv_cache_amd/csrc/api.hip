@@ -16,11 +16,9 @@ void launch_attn(const Dims&, const conf_cache&, int, int, const void*, const vo
                  float*, float*, int32_t*, bool, hipStream_t);
 void launch_ingest(const Dims&, const conf_cache&, int, int, int, const void*, const void*,
                    hipStream_t);
-void launch_ema(const Dims&, const conf_cache&, int, int, const float*, const int32_t*,
-                hipStream_t);
 void launch_select(const Dims&, const conf_cache&, int, int, const int32_t*, uint8_t*, hipStream_t);
 void launch_joint_select(const Dims&, const conf_cache&, int, int, const int32_t*, uint8_t*,
-                         hipStream_t);
+                         const float*, const int32_t*, bool, hipStream_t);
 void launch_compact(const Dims&, const conf_cache&, int, int, const uint8_t*, int32_t*, int32_t*,
                     int32_t*, uint8_t*, hipStream_t);
 void launch_evict(const Dims&, const conf_cache&, int, int, const int32_t*, uint8_t*, int32_t*,
@@ -153,12 +151,13 @@ Dims seq_dims(const Dims& d) {
 }
 
 // Rank + select (+ compaction) of a head-wise cache: the joint selection per
-// (layer, sequence) writes every head's keep flags to the workspace, then each
-// head is compacted on its own.
+// (layer, sequence), with the pending EMA update first when with_ema, writes
+// every head's keep flags to the workspace, then each head is compacted on its
+// own.
 void headwise_evict(const Dims& d, const conf_cache& c, int l0, int nl, const int32_t* budget,
                     void* ws, const WsMap& w, bool with_ema, hipStream_t st) {
-  if (with_ema) launch_ema(d, c, l0, nl, at<float>(ws, w.massp), at<int32_t>(ws, w.snap), st);
-  launch_joint_select(d, c, l0, nl, budget, at<uint8_t>(ws, w.keep), st);
+  launch_joint_select(d, c, l0, nl, budget, at<uint8_t>(ws, w.keep), at<float>(ws, w.massp),
+                      at<int32_t>(ws, w.snap), with_ema, st);
   launch_compact(d, c, l0, nl, at<uint8_t>(ws, w.keep), at<int32_t>(ws, w.plan),
                  at<int32_t>(ws, w.mv8), at<int32_t>(ws, w.mv16), at<uint8_t>(ws, w.wkeep), st);
 }
@@ -297,7 +296,8 @@ int conf_rank_evict(const conf_params* p, conf_cache* c, int32_t layer, const in
   if (!cache_ok(c) || !budget || !keep || !layer_range(d, layer, &l0, &nl)) return CONF_E_INVALID;
   (void)ws;
   if (d.headwise)
-    launch_joint_select(d, *c, l0, nl, budget, keep, (hipStream_t)stream);
+    launch_joint_select(d, *c, l0, nl, budget, keep, nullptr, nullptr, false,
+                        (hipStream_t)stream);
   else
     launch_select(d, *c, l0, nl, budget, keep, (hipStream_t)stream);
   return check_launch("conf_rank_evict");

@@ -79,12 +79,13 @@ __device__ inline uint64_t sel_key(float e, float emax, int pos, int t, float s_
 // keys are kept first.  Keeps the protected tokens and the N - |protected|
 // candidates with the largest keys, and calls sink(j, keep, key) once per j
 // with key = the candidate's key + 1, 0 for a protected token (or kAllKept when
-// n <= N and nothing is ranked).  With PAIRS and use_pairs, X.key[j] already
-// holds (bits(e) << 32 | tag) for every j, written by thread j mod NT, whenever
-// n <= kSelLdsKeys.
+// n <= N and nothing is ranked).  The keys live in LDS (keys[key_cap], beside
+// a 256-bin histogram) when n <= key_cap; otherwise each pass recomputes them.
+// With PAIRS and use_pairs, keys[j] already holds (bits(e) << 32 | tag) for
+// every j, written by thread j mod NT, whenever n <= key_cap.
 template <int NT, bool PAIRS, bool JOINT, typename Tok, typename KeyFn, typename Sink>
 __device__ void rank_core(int n, int N, int prot_lo, int hw, bool use_pairs, Tok tok, KeyFn keyf,
-                          SelScratch& X, SelMisc& M, Sink sink) {
+                          uint64_t* keys, unsigned* hist, int key_cap, SelMisc& M, Sink sink) {
   constexpr int kWaves = NT / 64;
   static_assert(kWaves <= 16, "SelMisc holds 16 wavefronts");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -93,7 +94,7 @@ __device__ void rank_core(int n, int N, int prot_lo, int hw, bool use_pairs, Tok
     return;
   }
   auto pos_of = [&](uint32_t tag) -> int { return JOINT ? (int)(tag / (uint32_t)hw) : (int)tag; };
-  const bool cached = n <= kSelLdsKeys;
+  const bool cached = n <= key_cap;
   // e_max over every token and the protected count; with the keys in LDS the
   // (e, tag) pairs wait there for the key pass (same thread, same index)
   float emax = 0.f;
@@ -102,12 +103,12 @@ __device__ void rank_core(int n, int N, int prot_lo, int hw, bool use_pairs, Tok
     float e;
     uint32_t tag;
     if (PAIRS && cached && use_pairs) {
-      const uint64_t v = X.key[j];
+      const uint64_t v = keys[j];
       e = __uint_as_float((uint32_t)(v >> 32));
       tag = (uint32_t)v;
     } else {
       tok(j, e, tag);
-      if (cached) X.key[j] = ((uint64_t)__float_as_uint(e) << 32) | tag;
+      if (cached) keys[j] = ((uint64_t)__float_as_uint(e) << 32) | tag;
     }
     emax = fmaxf(emax, e);
     nprot += pos_of(tag) > prot_lo;
@@ -142,8 +143,8 @@ __device__ void rank_core(int n, int N, int prot_lo, int hw, bool use_pairs, Tok
   };
   if (cached)
     for (int j = tid; j < n; j += NT) {
-      const uint64_t v = X.key[j];
-      X.key[j] = key_from(__uint_as_float((uint32_t)(v >> 32)), (uint32_t)v);
+      const uint64_t v = keys[j];
+      keys[j] = key_from(__uint_as_float((uint32_t)(v >> 32)), (uint32_t)v);
     }
   const int evict = (n - np) - K;  // candidates that go
   if (K > 0 && evict <= kFewEvict) {
@@ -154,7 +155,7 @@ __device__ void rank_core(int n, int N, int prot_lo, int hw, bool use_pairs, Tok
     for (int e = 0; e < evict; ++e) {
       uint64_t m = ~0ull;
       for (int j = tid; j < n; j += NT) {
-        const uint64_t key = cached ? X.key[j] : key_of(j);
+        const uint64_t key = cached ? keys[j] : key_of(j);
         if (key > thr && key < m) m = key;  // key 0 (protected) is never > thr
       }
       m = wave_min_u64(m);
@@ -166,7 +167,7 @@ __device__ void rank_core(int n, int N, int prot_lo, int hw, bool use_pairs, Tok
       __syncthreads();
     }
     for (int j = tid; j < n; j += NT) {
-      const uint64_t key = cached ? X.key[j] : key_of(j);
+      const uint64_t key = cached ? keys[j] : key_of(j);
       sink(j, key == 0ull ? 1 : key > thr, key);
     }
     return;
@@ -179,12 +180,12 @@ __device__ void rank_core(int n, int N, int prot_lo, int hw, bool use_pairs, Tok
   }
   __syncthreads();
   for (int shift = 56; shift >= 0 && !M.done; shift -= 8) {
-    if (tid < 256) X.hist[tid] = 0u;
+    if (tid < 256) hist[tid] = 0u;
     __syncthreads();
     const unsigned long long pre = M.prefix, msk = M.mask;
     for (int j = tid; j < n; j += NT) {
-      const uint64_t key = cached ? X.key[j] : key_of(j);
-      if (key != 0ull && (key & msk) == pre) atomicAdd(&X.hist[(key >> shift) & 255u], 1u);
+      const uint64_t key = cached ? keys[j] : key_of(j);
+      if (key != 0ull && (key & msk) == pre) atomicAdd(&hist[(key >> shift) & 255u], 1u);
     }
     __syncthreads();
     if (wave == 0) {
@@ -192,7 +193,7 @@ __device__ void rank_core(int n, int N, int prot_lo, int hw, bool use_pairs, Tok
       unsigned hb[4], sum = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        hb[i] = X.hist[255 - 4 * lane - i];
+        hb[i] = hist[255 - 4 * lane - i];
         sum += hb[i];
       }
       unsigned incl = sum;
@@ -228,7 +229,7 @@ __device__ void rank_core(int n, int N, int prot_lo, int hw, bool use_pairs, Tok
   // bits at zero); when K = 0 no candidate is kept
   const unsigned long long kth = M.prefix;
   for (int j = tid; j < n; j += NT) {
-    const uint64_t key = cached ? X.key[j] : key_of(j);
+    const uint64_t key = cached ? keys[j] : key_of(j);
     sink(j, key == 0ull ? 1 : (K > 0 && key >= kth), key);
   }
 }
@@ -275,7 +276,8 @@ __device__ void select_core(const conf_cache& c, const Dims& dm, int lb, int n8,
     if (trim) return retention_key(e, (int)tag, t);
     return sel_key(e, em, (int)tag, t, dm.s_ema, dm.s_rec, tag);
   };
-  rank_core<NT, PAIRS, false>(n, N, t - dm.P, 1, !trim, tok, keyf, X, M, sink);
+  rank_core<NT, PAIRS, false>(n, N, t - dm.P, 1, !trim, tok, keyf, X.key, X.hist, kSelLdsKeys, M,
+                              sink);
 }
 
 }  // namespace confkv
