@@ -84,6 +84,22 @@ with head-wise allocation).  Readings:
     compete on the composite score with e_max over every head of the layer;
   * a token's mass in head h is the mean over that head's G query heads;
   * ties: score desc, then position desc, then head index desc.
+
+ARKV (the ARKV page, Methodology: three-state assignment, decoding-phase token
+ranking, prefill-phase layer-wise budgets).  Readings:
+  * states: Original (16-bit), Quantized (FP8 e4m3, the OCP "fn" form: bias 7,
+    three mantissa bits, largest finite 448, subnormals down to 2^-9), Evicted;
+    per (KV head, channel) a running absmax, scale = absmax / 448, codes by
+    round-to-nearest-even of x / scale clamped to +-448, requantised on a new
+    maximum as for INT8;
+  * heavy-hitter score of a token this step: over the KV heads, the mean plus
+    the population variance of m_k = its attention averaged over head k's query
+    heads; ranked on its EMA (decay as for CONF-KV), ties to the newer position;
+  * budgets per (layer, sequence): N kept tokens and N_O Original ones (the
+    layer's OQ ratio, computed at prefill, is an input); the newest P positions
+    are protected and stay Original;
+  * a step appends the token as Original, evicts below the top N, then while more
+    than N_O tokens are Original, quantises the lowest-ranked unprotected one.
 """
 from __future__ import annotations
 
@@ -101,6 +117,8 @@ __all__ = [
     "ema_update", "composite_scores", "select_keep", "quant_codes", "requant_codes",
     "demote_token", "ingest", "step_layer", "decode_step",
     "retention_scores", "trim_step", "joint_keep", "headwise_step",
+    "FP8_MAX", "fp8_decode", "fp8_encode", "quant_codes_fp8", "requant_codes_fp8",
+    "arkv_stat", "Fp8State", "ingest_fp8", "arkv_step",
 ]
 
 
@@ -608,6 +626,187 @@ def headwise_step(heads, q_bits, k_bits, v_bits, N: int, prm: OracleParams,
         st.evict(kp)
         st.demote(prm.window)
     return dict(o=np.concatenate(outs), keeps=keeps, ema=emas, pos_before=pos_before)
+
+
+# --------------------------------------------------------------------------
+# ARKV: FP8 e4m3 codes, heavy-hitter score, three states        [ARKV]
+# --------------------------------------------------------------------------
+FP8_MAX = 448.0
+
+
+def fp8_decode(codes) -> np.ndarray:
+    """Value of each e4m3 bit pattern (uint8 or int8 bits), float64: sign, four
+    exponent bits (bias 7), three mantissa bits; exponent 0 is subnormal
+    (m * 2^-9).  0x7f / 0xff (NaN) are never produced here."""
+    c = np.asarray(codes).astype(np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(F64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(F64) - 7.0))
+    return sign * mag
+
+
+_FP8_POS = fp8_decode(np.arange(0x7F))          # codes 0x00 .. 0x7e, increasing
+
+
+def fp8_encode(x32) -> np.ndarray:
+    """Nearest e4m3 code (int8 bit pattern) of each value with |x| <= 448, ties to
+    the even code; the sign bit follows x (so -0 gives 0x80)."""
+    x = np.asarray(x32, F32).astype(F64)
+    a = np.abs(x)
+    if (a > FP8_MAX).any() or np.isnan(a).any():
+        raise ValueError("fp8_encode takes |x| <= 448")
+    hi = np.searchsorted(_FP8_POS, a, side="left")          # first value >= a
+    hi = np.minimum(hi, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    dlo = a - _FP8_POS[lo]
+    dhi = _FP8_POS[hi] - a
+    pick = np.where(dhi < dlo, hi, np.where(dlo < dhi, lo, np.where(hi % 2 == 0, hi, lo)))
+    code = pick | np.where(np.signbit(x), 0x80, 0)
+    return code.astype(np.uint8).view(np.int8)
+
+
+def quant_codes_fp8(x32, s32) -> np.ndarray:
+    """code = e4m3(clamp(x / s, -448, 448)) with the division in fp32; a zero
+    scale gives code 0."""
+    x32 = np.asarray(x32, F32)
+    s32 = np.broadcast_to(np.asarray(s32, F32), x32.shape)
+    r = np.zeros(x32.shape, F32)
+    nz = s32 > 0
+    r[nz] = x32[nz] / s32[nz]
+    r = np.clip(r, F32(-FP8_MAX), F32(FP8_MAX)).astype(F32)
+    return fp8_encode(r)
+
+
+def requant_codes_fp8(codes, s_old, s_new) -> np.ndarray:
+    """Re-express e4m3 codes under a larger scale: e4m3((value * s_old) / s_new),
+    fp32 arithmetic (the decoded value is exact in fp32)."""
+    v = fp8_decode(codes).astype(F32)
+    prod = (v * np.asarray(s_old, F32)).astype(F32)
+    return quant_codes_fp8(prod, s_new)
+
+
+def dequantize_fp8(codes, amax) -> np.ndarray:
+    """Code value * scale in float64, scale = fp32(amax / 448)."""
+    s = (np.asarray(amax, F32) / F32(FP8_MAX)).astype(F32)
+    return fp8_decode(codes) * s.astype(F64)
+
+
+def arkv_stat(p, group: int) -> np.ndarray:
+    """Heavy-hitter score of each token this step (float64) from p [Hq, n]:
+    m_k = mean of p over KV head k's query heads; mean_k m_k + var_k m_k
+    (population variance over the KV heads).  [ARKV: decoding-phase ranking]"""
+    p = np.asarray(p, F64)
+    Hq, n = p.shape
+    m = p.reshape(Hq // group, group, n).mean(axis=1)
+    mu = m.mean(axis=0)
+    return mu + ((m - mu) ** 2).mean(axis=0)
+
+
+class Fp8State(LayerSeqState):
+    """A cache whose 8-bit tokens hold e4m3 codes (the ARKV Quantized state)."""
+
+    def copy(self) -> "Fp8State":
+        c = Fp8State(self.k16.shape[1], self.k16.shape[2], self.dtype16)
+        for f in ("pos", "is8", "k16", "v16", "k8", "v8", "ema", "amax_k", "amax_v"):
+            setattr(c, f, getattr(self, f).copy())
+        c.t = self.t
+        return c
+
+    def kv_values(self):
+        K = np.where(self.is8[:, None, None], dequantize_fp8(self.k8, self.amax_k),
+                     decode16(self.k16, self.dtype16).astype(F64))
+        V = np.where(self.is8[:, None, None], dequantize_fp8(self.v8, self.amax_v),
+                     decode16(self.v16, self.dtype16).astype(F64))
+        return K, V
+
+    def quantise(self, j: int):
+        """Token j (Original) becomes Quantized: per (KV head, channel) a larger |x|
+        first requantises the stored codes of that channel and becomes the absmax;
+        then code = e4m3(x / (absmax / 448))."""
+        assert not self.is8[j]
+        old8 = np.flatnonzero(self.is8)
+        for key, amax_name, c8 in (("k16", "amax_k", "k8"), ("v16", "amax_v", "v8")):
+            x = decode16(getattr(self, key)[j], self.dtype16).astype(F32)
+            amax = getattr(self, amax_name).astype(F32)
+            a = np.abs(x)
+            grow = a > amax
+            codes = getattr(self, c8)
+            if grow.any() and old8.size:
+                s_old = (amax / F32(FP8_MAX)).astype(F32)
+                s_new = (np.where(grow, a, amax) / F32(FP8_MAX)).astype(F32)
+                hh, cc = np.nonzero(grow)
+                rows = old8[:, None]
+                codes[rows, hh[None, :], cc[None, :]] = requant_codes_fp8(
+                    codes[rows, hh[None, :], cc[None, :]], s_old[hh, cc], s_new[hh, cc])
+            amax = np.where(grow, a, amax).astype(F32)
+            setattr(self, amax_name, amax)
+            codes[j] = quant_codes_fp8(x, (amax / F32(FP8_MAX)).astype(F32))
+            getattr(self, key)[j] = 0
+        self.is8[j] = True
+
+
+def ingest_fp8(k_bits, v_bits, W: int, dtype16: str) -> Fp8State:
+    """ARKV prefill: positions 0 .. L0-W-1 Quantized (absmax over exactly those
+    tokens), the newest W Original, every score 0, t = L0 - 1."""
+    k_bits = np.asarray(k_bits, np.uint16)
+    v_bits = np.asarray(v_bits, np.uint16)
+    H, L0, d = k_bits.shape
+    st = Fp8State(H, d, dtype16)
+    st.pos = np.arange(L0, dtype=np.int64)
+    st.is8 = st.pos < (L0 - W)
+    st.k16 = np.ascontiguousarray(k_bits.transpose(1, 0, 2))
+    st.v16 = np.ascontiguousarray(v_bits.transpose(1, 0, 2))
+    st.k8 = np.zeros((L0, H, d), np.int8)
+    st.v8 = np.zeros((L0, H, d), np.int8)
+    st.ema = np.zeros(L0, F64)
+    st.t = L0 - 1
+    old = st.is8
+    if old.any():
+        for name, src, dst in (("amax_k", st.k16, st.k8), ("amax_v", st.v16, st.v8)):
+            x = decode16(src[old], dtype16).astype(F32)
+            amax = np.abs(x).max(axis=0).astype(F32)
+            dst[old] = quant_codes_fp8(x, (amax / F32(FP8_MAX)).astype(F32))
+            setattr(st, name, amax)
+        st.k16[old] = 0
+        st.v16[old] = 0
+    return st
+
+
+def arkv_step(st: Fp8State, q_bits, k_bits, v_bits, N: int, N_O: int, prm: OracleParams,
+              ema32_override=None) -> dict:
+    """One ARKV decode step of one (layer, sequence).  [ARKV: three-state
+    assignment; decoding-phase ranking]
+
+    Append as Original; attention (float64) over Original values and dequantised
+    Quantized ones; heavy-hitter score and its EMA; keep the protected newest P
+    and the best N - |protected| others by (EMA desc, position desc); then, while
+    more than N_O kept tokens are Original, the lowest-ranked unprotected one is
+    quantised (lowest first).  The ranking reads the fp32 rounding of the EMA, or
+    `ema32_override` (one value per token after the append).
+    """
+    st.append(k_bits, v_bits)
+    q = decode16(q_bits, prm.dtype16).astype(F64)
+    K, V = st.kv_values()
+    o, p = attention(q, K, V, prm.group)
+    st.ema = ema_update(st.ema, arkv_stat(p, prm.group), prm.ema_decay)
+    ema64 = st.ema.copy()
+    e32 = st.ema.astype(F32) if ema32_override is None else np.asarray(ema32_override, F32)
+    if ema32_override is not None:
+        st.ema = e32.astype(F64)
+    keep = select_keep(e32, st.pos, st.t, prm.protect, N)
+    pos_before = st.pos.copy()
+    st.evict(keep)
+    e32 = e32[keep]
+    demoted = []
+    while int((~st.is8).sum()) > N_O:
+        cand = np.flatnonzero(~st.is8 & (st.pos <= st.t - prm.protect))
+        if cand.size == 0:
+            break
+        j = cand[np.lexsort((st.pos[cand], e32[cand]))[0]]   # lowest (score, position)
+        demoted.append(int(st.pos[j]))
+        st.quantise(int(j))
+    return dict(o=o, p=p, ema=ema64, keep=keep, pos_before=pos_before, demoted=demoted)
 
 
 def decode_step(states, logits, q_bits, k_bits, v_bits, prm: OracleParams,
