@@ -21,12 +21,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libc
 CONF_F16, CONF_BF16 = 1, 2
 DTYPE16 = {"f16": (CONF_F16, torch.float16), "bf16": (CONF_BF16, torch.bfloat16)}
 ST_WINDOW_FULL, ST_INT8_FULL = 1, 2
-POLICY = {"confkv": 0, "full": 1, "window": 2, "trim": 3}
+POLICY = {"confkv": 0, "full": 1, "window": 2, "trim": 3, "arkv": 4}
 
 EXPORTED = ("conf_cache_layout", "conf_workspace_bytes", "conf_cache_reset", "conf_cache_ingest",
             "conf_confidence", "conf_decode_attn", "conf_rank_evict", "conf_compact_demote",
             "conf_evict_compact", "conf_attend", "conf_ema_evict_compact",
-            "conf_trim_evict_compact", "conf_cache_set_retention", "conf_step",
+            "conf_trim_evict_compact", "conf_cache_set_retention", "conf_arkv_evict_compact",
+            "conf_arkv_ema_evict_compact", "conf_step",
             "conf_cache_export", "conf_last_error", "conf_status_string")
 
 
@@ -78,6 +79,8 @@ def load() -> ctypes.CDLL:
         "conf_ema_evict_compact": [P, C, c_int32, vp, vp, vp],
         "conf_trim_evict_compact": [P, C, c_int32, vp, vp, vp, vp],
         "conf_cache_set_retention": [P, C, c_int32, vp, c_int32, vp],
+        "conf_arkv_evict_compact": [P, C, c_int32, vp, vp, vp, vp],
+        "conf_arkv_ema_evict_compact": [P, C, c_int32, vp, vp, vp, vp],
         "conf_step": [P, C, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         "conf_cache_export": [P, C, c_int32, c_int32, vp, vp, vp, vp, vp],
     }
@@ -248,6 +251,24 @@ class Engine:
                                                 layer, _ptr(budget), _ptr(log_beta),
                                                 _ptr(self.ws), self._stream()),
                "conf_trim_evict_compact")
+
+    def _arkv(self, fn, name, layer, budget, n_orig):
+        wl = self.wl
+        self._expect(budget, (wl.batch, wl.n_layers), torch.int32, "budget")
+        self._expect(n_orig, (wl.batch, wl.n_layers), torch.int32, "n_orig")
+        _check(fn(ctypes.byref(self.p), ctypes.byref(self.cache), layer, _ptr(budget),
+                  _ptr(n_orig), _ptr(self.ws), self._stream()), name)
+
+    def arkv_evict_compact(self, layer: int, budget, n_orig):
+        """conf_arkv_evict_compact (after decode_attn): keep budget[b][l] tokens by the
+        heavy-hitter EMA, then quantise the lowest-ranked Originals beyond n_orig."""
+        self._arkv(self.lib.conf_arkv_evict_compact, "conf_arkv_evict_compact", layer, budget,
+                   n_orig)
+
+    def arkv_ema_evict_compact(self, layer: int, budget, n_orig):
+        """conf_arkv_ema_evict_compact (after attend): the score EMA, then the same."""
+        self._arkv(self.lib.conf_arkv_ema_evict_compact, "conf_arkv_ema_evict_compact", layer,
+                   budget, n_orig)
 
     def set_retention(self, layer: int, log_beta):
         """conf_cache_set_retention: ln(beta) of the prefill, fp32 [L][B][L0] or

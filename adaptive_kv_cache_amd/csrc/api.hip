@@ -24,6 +24,9 @@ void launch_compact(const Dims&, const conf_cache&, int, int, const uint8_t*, in
 void launch_evict(const Dims&, const conf_cache&, int, int, const int32_t*, uint8_t*, int32_t*,
                   int32_t*, int32_t*, uint8_t*, const float*, const int32_t*, const float*, bool,
                   hipStream_t);
+void launch_arkv(const Dims&, const conf_cache&, int, int, const int32_t*, const int32_t*,
+                 uint8_t*, int32_t*, int32_t*, int32_t*, uint8_t*, const float*, const int32_t*,
+                 bool, hipStream_t);
 void launch_set_retention(const Dims&, const conf_cache&, int, int, const float*, int, hipStream_t);
 void launch_export(const Dims&, const conf_cache&, int, int8_t*, int8_t*, void*, void*, hipStream_t);
 }  // namespace confkv
@@ -70,7 +73,7 @@ int make_dims(const conf_params* p, Dims* d) {
   if (!(p->ema_decay >= 0.f && p->ema_decay <= 1.f)) return CONF_E_INVALID;
   if (!(p->s_ema >= 0.f && p->s_rec >= 0.f)) return CONF_E_INVALID;
   if (p->pyramid != 0 && p->pyramid != 1) return CONF_E_INVALID;
-  if (p->policy < CONF_POLICY_CONFKV || p->policy > CONF_POLICY_TRIM) return CONF_E_INVALID;
+  if (p->policy < CONF_POLICY_CONFKV || p->policy > CONF_POLICY_ARKV) return CONF_E_INVALID;
   if (p->headwise != 0 && p->headwise != 1) return CONF_E_INVALID;
   if (p->headwise) {
     // the baselines keep every head's tokens alike: head-wise sets are CONF-KV's
@@ -278,6 +281,7 @@ static int decode_attn(const conf_params* p, conf_cache* c, int32_t layer, const
 int conf_decode_attn(const conf_params* p, conf_cache* c, int32_t layer, const void* q,
                      const void* k_new, const void* v_new, float* out, void* ws,
                      conf_stream_t stream) {
+  // retention eviction keeps no EMA: its step is conf_attend + conf_trim_evict_compact
   if (p && p->policy == CONF_POLICY_TRIM) return CONF_E_INVALID;
   return decode_attn(p, c, layer, q, k_new, v_new, out, ws, stream, true, "conf_decode_attn");
 }
@@ -310,6 +314,7 @@ int conf_compact_demote(const conf_params* p, conf_cache* c, int32_t layer, cons
   if (rc) return rc;
   int l0, nl;
   if (!cache_ok(c) || !keep || !ws || !layer_range(d, layer, &l0, &nl)) return CONF_E_INVALID;
+  if (d.policy == CONF_POLICY_ARKV) return CONF_E_INVALID;  // ARKV demotes by rank, not position
   const WsMap w = make_ws(d);
   launch_compact(d, *c, l0, nl, keep, at<int32_t>(ws, w.plan), at<int32_t>(ws, w.mv8),
                  at<int32_t>(ws, w.mv16), at<uint8_t>(ws, w.wkeep), (hipStream_t)stream);
@@ -326,6 +331,7 @@ static int evict(const conf_params* p, conf_cache* c, int32_t layer, const int32
   if (!cache_ok(c) || !budget || !ws || !layer_range(d, layer, &l0, &nl)) return CONF_E_INVALID;
   // the retention policy's appended token needs its ln(beta); nothing else takes one
   if (with_ema && (d.policy == CONF_POLICY_TRIM) != (log_beta != nullptr)) return CONF_E_INVALID;
+  if (d.policy == CONF_POLICY_ARKV) return CONF_E_INVALID;  // conf_arkv_evict_compact
   const WsMap w = make_ws(d);
   if (d.headwise) {
     headwise_evict(d, *c, l0, nl, budget, ws, w, with_ema, (hipStream_t)stream);
@@ -355,6 +361,35 @@ int conf_trim_evict_compact(const conf_params* p, conf_cache* c, int32_t layer,
   return evict(p, c, layer, budget, log_beta, ws, stream, true, "conf_trim_evict_compact");
 }
 
+static int arkv(const conf_params* p, conf_cache* c, int32_t layer, const int32_t* budget,
+                const int32_t* n_orig, void* ws, conf_stream_t stream, bool with_ema,
+                const char* name) {
+  Dims d;
+  int rc = make_dims(p, &d);
+  if (rc) return rc;
+  int l0, nl;
+  if (!cache_ok(c) || !budget || !n_orig || !ws || d.policy != CONF_POLICY_ARKV ||
+      !layer_range(d, layer, &l0, &nl))
+    return CONF_E_INVALID;
+  const WsMap w = make_ws(d);
+  launch_arkv(d, *c, l0, nl, budget, n_orig, at<uint8_t>(ws, w.keep), at<int32_t>(ws, w.plan),
+              at<int32_t>(ws, w.mv8), at<int32_t>(ws, w.mv16), at<uint8_t>(ws, w.wkeep),
+              at<float>(ws, w.massp), at<int32_t>(ws, w.snap), with_ema, (hipStream_t)stream);
+  return check_launch(name);
+}
+
+int conf_arkv_evict_compact(const conf_params* p, conf_cache* c, int32_t layer,
+                            const int32_t* budget, const int32_t* n_orig, void* ws,
+                            conf_stream_t stream) {
+  return arkv(p, c, layer, budget, n_orig, ws, stream, false, "conf_arkv_evict_compact");
+}
+
+int conf_arkv_ema_evict_compact(const conf_params* p, conf_cache* c, int32_t layer,
+                                const int32_t* budget, const int32_t* n_orig, void* ws,
+                                conf_stream_t stream) {
+  return arkv(p, c, layer, budget, n_orig, ws, stream, true, "conf_arkv_ema_evict_compact");
+}
+
 int conf_cache_set_retention(const conf_params* p, conf_cache* c, int32_t layer,
                              const float* log_beta, int32_t prefill_len, conf_stream_t stream) {
   Dims d;
@@ -376,7 +411,7 @@ int conf_step(const conf_params* p, conf_cache* c, const float* logits, const vo
   int rc = make_dims(p, &d);
   if (rc) return rc;
   if (!cache_ok(c) || !logits || !a16(q) || !a16(k_new) || !a16(v_new) || !out || !conf ||
-      !budget || !ws || d.policy == CONF_POLICY_TRIM)
+      !budget || !ws || d.policy == CONF_POLICY_TRIM || d.policy == CONF_POLICY_ARKV)
     return CONF_E_INVALID;
   const WsMap w = make_ws(d);
   hipStream_t st = (hipStream_t)stream;

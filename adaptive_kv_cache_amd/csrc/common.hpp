@@ -102,4 +102,48 @@ __device__ inline int8_t quant_code(float x, float s) {
   return (int8_t)(int)r;
 }
 
+// e4m3 code (OCP "fn" form: sign, four exponent bits with bias 7, three mantissa
+// bits, largest finite 448) of y, |y| <= 448, by round-to-nearest-even; the sign
+// bit follows y.  ARKV's Quantized state [the ARKV page, Methodology: three-state
+// assignment].
+__device__ inline int8_t fp8_code(float y) {
+  const uint32_t b = __float_as_uint(y);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const uint32_t a = b & 0x7FFFFFFFu;  // |y|
+  uint32_t code;
+  if (a < 0x3C800000u) {  // |y| < 2^-6: subnormal codes, steps of 2^-9
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);  // 0 .. 8 (8: 2^-6)
+  } else {
+    const int e = (int)(a >> 23) - 127;  // -6 .. 8
+    uint32_t m = (a >> 20) & 7u;         // the three mantissa bits kept
+    const uint32_t rest = a & 0xFFFFFu;  // the twenty below them
+    if (rest > 0x80000u || (rest == 0x80000u && (m & 1u))) ++m;
+    code = ((uint32_t)(e + 7) << 3) + m;  // a carry out of m raises the exponent
+    if (code > 0x7Eu) code = 0x7Eu;
+  }
+  return (int8_t)(sign | code);
+}
+
+// Value of an e4m3 code (exact in fp32).
+__device__ inline float fp8_value(int8_t code) {
+  const uint32_t b = (uint8_t)code;
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  const float v = e == 0 ? (float)m * 0.001953125f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (b & 0x80u) ? -v : v;
+}
+
+// The 8-bit quantiser of a cache: INT8 (CONF-KV) or e4m3 (ARKV), both with
+// scale = absmax / code_max and a zero scale giving code 0.
+__host__ __device__ inline float code_max(bool fp8) { return fp8 ? 448.0f : 127.0f; }
+
+__device__ inline int8_t quant8(float x, float s, bool fp8) {
+#pragma clang fp contract(off)
+  if (!fp8) return quant_code(x, s);
+  if (!(s > 0.0f)) return 0;
+  const float r = fminf(fmaxf(x / s, -448.0f), 448.0f);
+  return fp8_code(r);
+}
+
+__device__ inline float code_value(int8_t c, bool fp8) { return fp8 ? fp8_value(c) : (float)c; }
+
 }  // namespace confkv

@@ -10,6 +10,50 @@
 
 namespace confkv {
 
+// ARKV's heavy-hitter score of a token [the ARKV page, Methodology: decoding-phase
+// token ranking] from a = sum over the KV heads of its mass rows (each the sum of
+// the head's G query heads' probabilities) and a2 = the sum of their squares,
+// both in KV-head order: with m_k = row_k / G,
+//   mean_k m_k + max(mean_k m_k^2 - (mean_k m_k)^2, 0),
+// fp32, one rounding per operation.
+__device__ inline float arkv_h(float a, float a2, const Dims& dm) {
+#pragma clang fp contract(off)
+  const float mean = a / (float)dm.Hq;
+  const float gg_h = (float)dm.G * (float)dm.G * (float)dm.Hkv;
+  const float var = fmaxf(a2 / gg_h - mean * mean, 0.f);
+  return mean + var;
+}
+
+// ARKV's score EMA in the layout of ema_tokens below (same threads and tokens).
+__device__ inline void arkv_tokens(const conf_cache& c, const Dims& dm, int lb,
+                                   const float* __restrict__ massp_all, int n8, int nw, int t,
+                                   int j0, int jstep) {
+#pragma clang fp contract(off)
+  const int appended = nw < dm.cap16;
+  const int end = n8 + nw + appended;
+  const float* rows = massp_all + (size_t)lb * dm.Hkv * dm.capt;
+  float* ema8 = c.ema8 + (size_t)lb * dm.cap8;
+  float* ema16 = c.ema16 + (size_t)lb * dm.cap16;
+  for (int j = j0; j < end; j += jstep) {
+    const int idx = j < n8 ? j : dm.cap8 + (j - n8);
+    float a = 0.f, a2 = 0.f;
+    for (int hk = 0; hk < dm.Hkv; ++hk) {
+      const float r = rows[(size_t)hk * dm.capt + idx];
+      a += r;
+      a2 += r * r;
+    }
+    const float h = arkv_h(a, a2, dm);
+    if (j < n8) {
+      ema8[j] = dm.decay * ema8[j] + dm.one_minus_decay * h;
+    } else if (j - n8 == nw) {
+      ema16[nw] = dm.one_minus_decay * h;  // decay * 0 + (1 - decay) * h
+      c.pos16[(size_t)lb * dm.cap16 + nw] = t + 1;
+    } else {
+      ema16[j - n8] = dm.decay * ema16[j - n8] + dm.one_minus_decay * h;
+    }
+  }
+}
+
 // EMA of the tokens of (layer, sequence) lb once every KV head's mass row is in
 // massp: mass_j = (sum of the KV heads' rows, in index order) / Hq and
 // e <- decay*e + (1-decay)*mass; the appended token (window slot nw, if the
@@ -22,6 +66,10 @@ __device__ inline void ema_tokens(const conf_cache& c, const Dims& dm, int lb,
                                   int j0, int jstep) {
 #pragma clang fp contract(off)
   const int appended = nw < dm.cap16;
+  if (dm.policy == CONF_POLICY_ARKV) {
+    arkv_tokens(c, dm, lb, massp_all, n8, nw, t, j0, jstep);
+    return;
+  }
   if (dm.policy != CONF_POLICY_CONFKV) {  // no EMA: the appended token's slot only
     if (j0 == 0 && appended) {
       c.ema16[(size_t)lb * dm.cap16 + nw] = 0.f;

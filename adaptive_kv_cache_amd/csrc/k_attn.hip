@@ -26,7 +26,8 @@
 // so P never leaves registers, and the tiled value layout hands each lane its
 // tokens of one channel in one 16-byte load.  Heads beyond g are zero padding.
 //
-// Precision.  INT8 codes become fp16 exactly.  The key scale folds into the
+// Precision.  INT8 codes become fp16 exactly, and so do e4m3 codes (ARKV's
+// Quantized state), scaled by 2^-8.  The key scale folds into the
 // query: q' = q * amax_K/127, times a power of two per head that puts its largest
 // entry in [2^14, 2^15), split into fp16 hi + lo parts (two MFMAs, ~22 bits).
 // Window keys meet the 16-bit query as stored (exact products).  P is rounded to
@@ -70,7 +71,29 @@ __device__ inline h2 bias_pair(uint32_t w, uint32_t sel) {
   const uint32_t v = __builtin_amdgcn_perm(0x64646464u, w, sel);
   return __builtin_bit_cast(h2, v) - (h2){(_Float16)1152.0f, (_Float16)1152.0f};
 }
+// 16 e4m3 codes -> two groups of 8 exact fp16 values, each the code's value / 256:
+// a code b placed in the high byte of a 16-bit half keeps its sign bit where fp16
+// has it, and one right shift puts its four exponent and three mantissa bits on
+// fp16's (exponent bias 15 against e4m3's 7: a factor 2^-8; e4m3 subnormals land
+// on fp16 subnormals with the same factor).
+__device__ inline uint32_t fp8_pair(uint32_t w, uint32_t sel) {
+  const uint32_t x = __builtin_amdgcn_perm(0u, w, sel);
+  return (x & 0x80008000u) | ((x >> 1) & 0x3F803F80u);
+}
+
+template <bool FP8>
 __device__ inline void codes_to_f16(u4 raw, h8& a0, h8& a1) {
+  if constexpr (FP8) {
+    // selector 0x0c gives a zero byte: halves (byte 0 | byte 1 ...) << 8
+    const uint32_t lo = 0x010C000Cu, hi = 0x030C020Cu;
+    const uint32_t r0 = fp8_pair(raw.x, lo), r1 = fp8_pair(raw.x, hi);
+    const uint32_t r2 = fp8_pair(raw.y, lo), r3 = fp8_pair(raw.y, hi);
+    const uint32_t r4 = fp8_pair(raw.z, lo), r5 = fp8_pair(raw.z, hi);
+    const uint32_t r6 = fp8_pair(raw.w, lo), r7 = fp8_pair(raw.w, hi);
+    a0 = __builtin_bit_cast(h8, (u4){r0, r1, r2, r3});
+    a1 = __builtin_bit_cast(h8, (u4){r4, r5, r6, r7});
+    return;
+  }
   const uint32_t w0 = raw.x ^ 0x80808080u, w1 = raw.y ^ 0x80808080u;
   const uint32_t w2 = raw.z ^ 0x80808080u, w3 = raw.w ^ 0x80808080u;
   const h2 p0 = bias_pair(w0, 0x04010400u), p1 = bias_pair(w0, 0x04030402u);
@@ -79,6 +102,15 @@ __device__ inline void codes_to_f16(u4 raw, h8& a0, h8& a1) {
   const h2 p6 = bias_pair(w3, 0x04010400u), p7 = bias_pair(w3, 0x04030402u);
   a0 = (h8){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
   a1 = (h8){p4.x, p4.y, p5.x, p5.y, p6.x, p6.y, p7.x, p7.y};
+}
+
+// The factor that turns a converted 8-bit code into its value: the INT8 scale
+// amax/127, or for e4m3 the scale amax/448 times the 2^8 the conversion took off.
+template <bool FP8>
+__device__ inline float code_scale(float amax) {
+#pragma clang fp contract(off)
+  if constexpr (FP8) return (amax / 448.0f) * 256.0f;
+  return amax / 127.0f;
 }
 
 __device__ inline u4 ld16(const void* p) { return *(const u4*)p; }
@@ -177,7 +209,7 @@ __device__ inline void load_run_rs(rsrc_t r, uint32_t off, int lane_off, Buf<D>&
 }
 
 // Raw S^T: acc[r][i] is the score of item token 16r + 4*(lane/16) + i for head lane%16.
-template <int D, bool BF16>
+template <int D, bool BF16, bool FP8>
 __device__ inline void scores_i8(const Buf<D>& R, const QOps<D, BF16>& q, f4 acc[4]) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -185,7 +217,7 @@ __device__ inline void scores_i8(const Buf<D>& R, const QOps<D, BF16>& q, f4 acc
 #pragma unroll
     for (int hh = 0; hh < D / 64; ++hh) {
       h8 k0, k1;
-      codes_to_f16(R.x[r * (D / 64) + hh], k0, k1);
+      codes_to_f16<FP8>(R.x[r * (D / 64) + hh], k0, k1);
       a = mma_f16(k0, q.qh(2 * hh), a);
       a = mma_f16(k0, q.ql(2 * hh), a);
       a = mma_f16(k1, q.qh(2 * hh + 1), a);
@@ -216,7 +248,7 @@ __device__ inline void scores_16(const Buf<D>& R, const QOps<D, BF16>& q, f4 acc
 }
 
 // O += P . V.  p[r][i]: probability of item token 16r + 4g + i for head lane%16.
-template <int D>
+template <int D, bool FP8>
 __device__ inline void pv_i8(const Buf<D>& R, const float p[4][4], f4* o) {
   h8 pa[2];
 #pragma unroll
@@ -226,7 +258,7 @@ __device__ inline void pv_i8(const Buf<D>& R, const float p[4][4], f4* o) {
 #pragma unroll
   for (int cb = 0; cb < D / 16; ++cb) {
     h8 v0, v1;
-    codes_to_f16(R.x[cb], v0, v1);
+    codes_to_f16<FP8>(R.x[cb], v0, v1);
     o[cb] = mma_f16(pa[0], v0, o[cb]);
     o[cb] = mma_f16(pa[1], v1, o[cb]);
     __builtin_amdgcn_sched_barrier(0);
@@ -347,7 +379,7 @@ __device__ inline void softmax_item(const f4* acc, float scale, bool head_ok, co
   }
 }
 
-template <int D, bool BF16, int MODE>
+template <int D, bool BF16, int MODE, bool FP8>
 __device__ inline void compute_item(const Item& I, Buf<D>& K, const Buf<D>& V,
                                     const QOps<D, BF16>& q, float scale8, float scale16,
                                     bool head_ok, WaveAcc<D>& wa, float* sc, int stride, float lse,
@@ -358,12 +390,12 @@ __device__ inline void compute_item(const Item& I, Buf<D>& K, const Buf<D>& V,
   __asm__ volatile("" : "+v"(ql.p));
   if (I.i8) {
     f4 acc[4];
-    scores_i8<D, BF16>(K, ql, acc);
+    scores_i8<D, BF16, FP8>(K, ql, acc);
     load_run_rs<D>(kr, koff, klane, K);  // the keys are used: the next item's start loading
     float p[4][4];
     softmax_item<4, MODE, D>(acc, scale8, head_ok, I, wa, sc, stride, lse, massp, p);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (MODE != MODE_LSE) pv_i8<D>(V, p, wa.o);
+    if constexpr (MODE != MODE_LSE) pv_i8<D, FP8>(V, p, wa.o);
   } else {
     f4 acc[2];
     scores_16<D, BF16>(K, ql, acc);
@@ -410,7 +442,7 @@ struct UnitRs {
   rsrc_t k8, v8, k16, v16;  // the unit's four regions
 };
 
-template <int D, bool BF16, int MODE>
+template <int D, bool BF16, int MODE, bool FP8>
 __device__ inline void wave_pass(int nitems, int nb8, int n8, int nw, int cap8, const UnitRs& rs,
                                  const QOps<D, BF16>& q, float scale8, float scale16, bool head_ok,
                                  WaveAcc<D>& wa, bool& vscaled, const float* sv, float* sc,
@@ -437,7 +469,7 @@ __device__ inline void wave_pass(int nitems, int nb8, int n8, int nw, int cap8, 
         vscaled = true;
       }
     }
-    compute_item<D, BF16, MODE>(item_of(it, nb8, n8, nw, cap8), kb, V, q, scale8, scale16,
+    compute_item<D, BF16, MODE, FP8>(item_of(it, nb8, n8, nw, cap8), kb, V, q, scale8, scale16,
                                 head_ok, wa, sc, stride, lse, massp, nx < nb8 ? rs.k8 : rs.k16,
                                 nx < nitems ? (uint32_t)(nx < nb8 ? nx : nx - nb8) * ib : kNoItem,
                                 klane);
@@ -449,7 +481,7 @@ __device__ inline void wave_pass(int nitems, int nb8, int n8, int nw, int cap8, 
 // One workgroup per unit.  The unit of KV head 0 also records the (layer,
 // sequence)'s sizes before this step in `snap` [L][B][3] = (n8, n16, t) for the
 // EMA kernel, which must not read the counters it advances.
-template <int D, bool BF16>
+template <int D, bool BF16, bool FP8>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     conf_cache c, Dims dm, int layer0, const uint16_t* __restrict__ q_all,
     const uint16_t* __restrict__ knew_all, const uint16_t* __restrict__ vnew_all,
@@ -521,8 +553,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
   const int n = n8 + nw + appended;
   const int nb8 = (n8 + kTile - 1) / kTile;
   const int nitems = nb8 + (nw + 31) / 32;
-  // CONF-KV needs each token's attention mass; the baseline policies do not
-  const bool mass = dm.policy == CONF_POLICY_CONFKV;
+  // CONF-KV and ARKV rank on each token's attention mass; the baselines do not
+  const bool mass = dm.policy == CONF_POLICY_CONFKV || dm.policy == CONF_POLICY_ARKV;
   const bool in_lds = mass && n <= score_cap;
   const bool one_pass = in_lds || !mass;
   // the speculative keys are this wavefront's first item unless the INT8 part is short
@@ -541,7 +573,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
   if (vt >= 0) {
     const uint32_t wa4[4] = {rva.x, rva.y, rva.z, rva.w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) s_sv[4 * vt + e] = __uint_as_float(wa4[e]) / 127.0f;
+    for (int e = 0; e < 4; ++e) s_sv[4 * vt + e] = code_scale<FP8>(__uint_as_float(wa4[e]));
     if (vt < D / 8) {
       const uint32_t w[4] = {rvn.x, rvn.y, rvn.z, rvn.w};
 #pragma unroll
@@ -564,7 +596,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     for (int e = 0; e < 8; ++e) {
       qv[e] = h16_to_f32((uint16_t)(wq[e >> 1] >> (16 * (e & 1))), dm.bf16);
       const float kn = h16_to_f32((uint16_t)(wn[e >> 1] >> (16 * (e & 1))), dm.bf16);
-      x8[e] = qv[e] * (__uint_as_float(wk[e]) / 127.0f);
+      x8[e] = qv[e] * code_scale<FP8>(__uint_as_float(wk[e]));
       mx = fmaxf(mx, fabsf(x8[e]));
       sc = fmaf(qv[e], kn, sc);
     }
@@ -612,16 +644,16 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
   bool vscaled = false;
 
   if (in_lds) {
-    wave_pass<D, BF16, MODE_ONLINE>(nitems, nb8, n8, nw, dm.cap8, urs, q, scale8,
+    wave_pass<D, BF16, MODE_ONLINE, FP8>(nitems, nb8, n8, nw, dm.cap8, urs, q, scale8,
                                      scale16, head_ok, wa, vscaled, s_sv, smem, stride, 0.f, nullptr,
                                      cur, true);
     if (appended && tid < G) smem[tid * stride + n - 1] = s_snew[tid];
   } else if (!mass) {
-    wave_pass<D, BF16, MODE_PLAIN>(nitems, nb8, n8, nw, dm.cap8, urs, q, scale8,
+    wave_pass<D, BF16, MODE_PLAIN, FP8>(nitems, nb8, n8, nw, dm.cap8, urs, q, scale8,
                                     scale16, head_ok, wa, vscaled, s_sv, nullptr, 0, 0.f, nullptr,
                                     cur, true);
   } else {
-    wave_pass<D, BF16, MODE_LSE>(nitems, nb8, n8, nw, dm.cap8, urs, q, scale8,
+    wave_pass<D, BF16, MODE_LSE, FP8>(nitems, nb8, n8, nw, dm.cap8, urs, q, scale8,
                                   scale16, head_ok, wa, vscaled, s_sv, nullptr, 0, 0.f, nullptr,
                                   cur, true);
   }
@@ -699,7 +731,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
   } else {
     // second pass: probabilities with the final normaliser, mass and values
     const float lse = head_ok ? s_lse[hl] : 0.f;
-    wave_pass<D, BF16, MODE_FINAL>(nitems, nb8, n8, nw, dm.cap8, urs, q, scale8,
+    wave_pass<D, BF16, MODE_FINAL, FP8>(nitems, nb8, n8, nw, dm.cap8, urs, q, scale8,
                                     scale16, head_ok, wa, vscaled, s_sv, nullptr, 0, lse, massp,
                                     cur, false);
     if (appended && tid == 0) {
@@ -770,17 +802,17 @@ size_t attn_dyn_lds(const Dims& dm) {
   return (size_t)qops_bytes(dm) + 4 * (ob + sc);
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool FP8>
 static void launch_t(const Dims& dm, const conf_cache& c, int layer0, int nl, const void* q,
                      const void* k_new, const void* v_new, float* out, float* massp,
                      int32_t* snap, bool with_ema, hipStream_t st) {
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)attn_kernel<D, BF16>,
+    (void)hipFuncSetAttribute((const void*)attn_kernel<D, BF16, FP8>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, kLdsDynBytes);
     attr_set = true;
   }
-  hipLaunchKernelGGL((attn_kernel<D, BF16>), dim3(nl * dm.B * dm.Hkv), dim3(kAttnThreads),
+  hipLaunchKernelGGL((attn_kernel<D, BF16, FP8>), dim3(nl * dm.B * dm.Hkv), dim3(kAttnThreads),
                      attn_dyn_lds(dm), st, c, dm, layer0, (const uint16_t*)q,
                      (const uint16_t*)k_new, (const uint16_t*)v_new, out, massp, snap,
                      attn_score_cap(dm));
@@ -788,10 +820,11 @@ static void launch_t(const Dims& dm, const conf_cache& c, int layer0, int nl, co
   // otherwise a launch that applies the EMA itself follows
 }
 
-template <int D_, bool BF16_>
+template <int D_, bool BF16_, bool FP8_>
 struct Variant {
   static constexpr int D = D_;
   static constexpr bool BF16 = BF16_;
+  static constexpr bool FP8 = FP8_;
 };
 
 void launch_attn(const Dims& dm, const conf_cache& c, int layer0, int nl, const void* q,
@@ -800,12 +833,23 @@ void launch_attn(const Dims& dm, const conf_cache& c, int layer0, int nl, const 
   auto go = [&](auto kernel_tag) {
     constexpr int D = decltype(kernel_tag)::D;
     constexpr bool BF16 = decltype(kernel_tag)::BF16;
-    launch_t<D, BF16>(dm, c, layer0, nl, q, k_new, v_new, out, massp, snap, with_ema, st);
+    constexpr bool FP8 = decltype(kernel_tag)::FP8;
+    launch_t<D, BF16, FP8>(dm, c, layer0, nl, q, k_new, v_new, out, massp, snap, with_ema, st);
   };
+  // the 8-bit region holds e4m3 codes under ARKV, INT8 codes otherwise
+  const bool fp8 = dm.policy == CONF_POLICY_ARKV;
   if (dm.D == 64) {
-    if (dm.bf16) go(Variant<64, true>{}); else go(Variant<64, false>{});
+    if (dm.bf16) {
+      if (fp8) go(Variant<64, true, true>{}); else go(Variant<64, true, false>{});
+    } else {
+      if (fp8) go(Variant<64, false, true>{}); else go(Variant<64, false, false>{});
+    }
   } else {
-    if (dm.bf16) go(Variant<128, true>{}); else go(Variant<128, false>{});
+    if (dm.bf16) {
+      if (fp8) go(Variant<128, true, true>{}); else go(Variant<128, true, false>{});
+    } else {
+      if (fp8) go(Variant<128, false, true>{}); else go(Variant<128, false, false>{});
+    }
   }
 }
 

@@ -52,6 +52,7 @@ __global__ __launch_bounds__(256) void ingest_kernel(conf_cache c, Dims dm, int 
   const int D = dm.D;
   const int old = L0 > dm.W ? L0 - dm.W : 0;  // positions older than the window
   const int n8 = dm.policy == CONF_POLICY_WINDOW ? 0 : old;
+  const bool fp8 = dm.policy == CONF_POLICY_ARKV;  // ARKV quantises to e4m3
   const int nw = L0 - old;
   const uint16_t* ksrc = kp + (size_t)unit_local * L0 * D;
   const uint16_t* vsrc = vp + (size_t)unit_local * L0 * D;
@@ -78,16 +79,16 @@ __global__ __launch_bounds__(256) void ingest_kernel(conf_cache c, Dims dm, int 
     }
     c.k_amax[u * D + threadIdx.x] = a;
     c.v_amax[u * D + threadIdx.x] = b;
-    sk[threadIdx.x] = a / 127.0f;
-    sv[threadIdx.x] = b / 127.0f;
+    sk[threadIdx.x] = a / code_max(fp8);
+    sv[threadIdx.x] = b / code_max(fp8);
   }
   __syncthreads();
   int8_t* k8 = c.k8 + u * (size_t)dm.cap8 * D;
   int8_t* v8 = c.v8 + u * (size_t)dm.cap8 * D;
   for (size_t i = threadIdx.x; i < (size_t)n8 * D; i += blockDim.x) {
     const int tok = (int)(i / D), cc = (int)(i % D);
-    k8[k8_off(tok, cc, D)] = quant_code(h16_to_f32(ksrc[i], dm.bf16), sk[cc]);
-    v8[v8_off(tok, cc, D)] = quant_code(h16_to_f32(vsrc[i], dm.bf16), sv[cc]);
+    k8[k8_off(tok, cc, D)] = quant8(h16_to_f32(ksrc[i], dm.bf16), sk[cc], fp8);
+    v8[v8_off(tok, cc, D)] = quant8(h16_to_f32(vsrc[i], dm.bf16), sv[cc], fp8);
   }
   uint16_t* k16 = (uint16_t*)c.k16 + u * (size_t)dm.cap16 * D;
   uint16_t* v16 = (uint16_t*)c.v16 + u * (size_t)dm.cap16 * D;
@@ -232,6 +233,8 @@ __device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8
 #pragma clang fp contract(off)
   const int tid = threadIdx.x;
   const int D = dm.D;
+  const bool fp8 = dm.policy == CONF_POLICY_ARKV;  // e4m3 codes in place of INT8
+  const float cmax = code_max(fp8);
   int32_t* pos8 = c.pos8 + (size_t)lb * dm.cap8;
   float* ema8 = c.ema8 + (size_t)lb * dm.cap8;
   int32_t* pos16 = c.pos16 + (size_t)lb * dm.cap16;
@@ -352,8 +355,8 @@ __device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8
         const float a = fabsf(x);
         const float am = a > old ? a : old;
         amax_new[e] = am;
-        code[e] = quant_code(x, am / 127.0f);
-        s_old[e] = old / 127.0f;
+        code[e] = quant8(x, am / cmax, fp8);
+        s_old[e] = old / cmax;
         if (a > old) {
           grew[e] = true;
           const int slot = atomicAdd(&M.ngrown, 1);
@@ -361,7 +364,7 @@ __device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8
             listed[e] = true;
             X.grown[slot] = pi;
             X.gold[slot] = s_old[e];
-            X.gnew[slot] = am / 127.0f;
+            X.gnew[slot] = am / cmax;
           }
         }
       }
@@ -456,7 +459,7 @@ __device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8
       const size_t u = (size_t)lb * dm.Hkv + hk;
       int8_t* p = (kind == 0 ? c.k8 + u * (size_t)dm.cap8 * D + k8_off(tok, ch, D)
                              : c.v8 + u * (size_t)dm.cap8 * D + v8_off(tok, ch, D));
-      *p = quant_code((float)(*p) * X.gold[e], X.gnew[e]);
+      *p = quant8(code_value(*p, fp8) * X.gold[e], X.gnew[e], fp8);
     }
     // a list overflow (very many channels grew at once): the owner requantises
 #pragma unroll
@@ -465,11 +468,11 @@ __device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8
       const int pi = tid + e * kCompThreads;
       const int kind = pi / per, hc = pi % per, hk = hc / D, ch = hc % D;
       int8_t* base = (kind == 0 ? c.k8 : c.v8) + ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap8 * D;
-      const float s_new = amax_new[e] / 127.0f;
+      const float s_new = amax_new[e] / cmax;
       for (int tok = 0; tok < n8end; ++tok) {
         if (tok == dest) continue;
         int8_t* q = base + (kind == 0 ? k8_off(tok, ch, D) : v8_off(tok, ch, D));
-        *q = quant_code((float)(*q) * s_old[e], s_new);
+        *q = quant8(code_value(*q, fp8) * s_old[e], s_new, fp8);
       }
     }
   }
@@ -703,6 +706,250 @@ __global__ __launch_bounds__(kCompThreads, 6) void evict_kernel(conf_cache c, Di
   count_kept(c8, c16, M, n8n, n16n);  // its barrier also ends the key cache's use
   compact_core(c, dm, lb, n8, n16, t, n8n, n16n, M.jd, keep8, wkeep, F, U.comp, M, plan_all,
                mv8_all, mv16_all);
+}
+
+// ARKV's pending score update (the ARKV page, Methodology: decoding-phase token
+// ranking) for (layer, sequence) lb: over the KV heads k, with m_k = row_k / G
+// the token's attention averaged over head k's query heads,
+//   h = mean_k m_k + (mean_k m_k^2 - (mean_k m_k)^2, at least 0),
+//   e <- decay*e + (1-decay)*h   (the appended token from e = 0 at position t+1),
+// fp32, one rounding per operation.  Each token's (bits(e) << 32 | pos) is left in
+// X.key[j] for select_core when the keys fit in LDS.
+__device__ inline void arkv_pairs(const conf_cache& c, const Dims& dm, int lb,
+                                  const float* __restrict__ massp_all, int n8, int nw, int t,
+                                  SelScratch& X) {
+#pragma clang fp contract(off)
+  const int appended = nw < dm.cap16;
+  const int end = n8 + nw + appended;
+  const bool cached = end <= kSelLdsKeys;
+  const float* rows = massp_all + (size_t)lb * dm.Hkv * dm.capt;
+  float* ema8 = c.ema8 + (size_t)lb * dm.cap8;
+  float* ema16 = c.ema16 + (size_t)lb * dm.cap16;
+  const int32_t* pos8 = c.pos8 + (size_t)lb * dm.cap8;
+  int32_t* pos16 = c.pos16 + (size_t)lb * dm.cap16;
+  constexpr int kT = 4;
+  for (int jb = threadIdx.x; jb < end; jb += kT * kCompThreads) {
+    int idx[kT], po[kT];
+    float a[kT], a2[kT], eo[kT];
+#pragma unroll
+    for (int k = 0; k < kT; ++k) {
+      const int j = jb + k * kCompThreads;
+      idx[k] = j >= end ? 0 : j < n8 ? j : dm.cap8 + (j - n8);
+      const int w = j >= end ? 0 : j - n8;
+      eo[k] = j < n8 ? ema8[idx[k]] : ema16[w];
+      po[k] = j < n8 ? pos8[idx[k]] : pos16[w];
+      a[k] = 0.f;
+      a2[k] = 0.f;
+    }
+    for (int hk = 0; hk < dm.Hkv; ++hk)
+#pragma unroll
+      for (int k = 0; k < kT; ++k) {
+        const float r = rows[(size_t)hk * dm.capt + idx[k]];
+        a[k] += r;
+        a2[k] += r * r;
+      }
+#pragma unroll
+    for (int k = 0; k < kT; ++k) {
+      const int j = jb + k * kCompThreads;
+      if (j >= end) continue;
+      const float h = arkv_h(a[k], a2[k], dm);
+      float e;
+      int p = po[k];
+      if (j < n8) {
+        e = dm.decay * eo[k] + dm.one_minus_decay * h;
+        ema8[j] = e;
+      } else if (j - n8 == nw) {
+        e = dm.one_minus_decay * h;  // decay * 0 + (1 - decay) * h
+        p = t + 1;
+        ema16[nw] = e;
+        pos16[nw] = p;
+      } else {
+        e = dm.decay * eo[k] + dm.one_minus_decay * h;
+        ema16[j - n8] = e;
+      }
+      if (cached) X.key[j] = ((uint64_t)__float_as_uint(e) << 32) | (uint32_t)p;
+    }
+  }
+}
+
+// One ARKV step's cache update, one workgroup per (layer, sequence) [the ARKV
+// page, Methodology: three-state assignment]:
+//  1. with EMA (after conf_attend), the score update above (sizes from the
+//     attention's snapshot; t advances); without, the EMA kernel has applied it;
+//  2. keep the newest P positions and the budget's best others by (EMA desc,
+//     position desc) (select_core);
+//  3. with more than N_O kept tokens Original (16-bit), the lowest-ranked
+//     unprotected one becomes Quantized: compact_core's demotion, with e4m3
+//     codes, together with the eviction.  Any further demotion the step needs
+//     is arkv_rounds_kernel's.
+template <bool EMA>
+__global__ __launch_bounds__(kCompThreads) void arkv_kernel(
+    conf_cache c, Dims dm, int layer0, const int32_t* __restrict__ budget,
+    const int32_t* __restrict__ n_orig, uint8_t* __restrict__ keep_all,
+    int32_t* __restrict__ plan_all, int32_t* __restrict__ mv8_all, int32_t* __restrict__ mv16_all,
+    uint8_t* __restrict__ wkeep_all, const float* __restrict__ massp_all,
+    const int32_t* __restrict__ snap) {
+  __shared__ CompFlags F;
+  __shared__ union {
+    SelScratch sel;
+    CompScratch comp;
+  } U;
+  __shared__ SelMisc SM;
+  __shared__ CompMisc M;
+  const int lb = layer0 * dm.B + blockIdx.x;
+  const int l = lb / dm.B, b = lb % dm.B;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int n8, n16, t;
+  if constexpr (EMA) {
+    n8 = snap[3 * lb];
+    const int nw = snap[3 * lb + 1], t0 = snap[3 * lb + 2];
+    n16 = nw + (nw < dm.cap16);
+    t = t0 + 1;
+    arkv_pairs(c, dm, lb, massp_all, n8, nw, t0, U.sel);
+    if (tid == 0) c.t[lb] = t;  // n8 and n16 are written by the compaction
+  } else {
+    n8 = c.n8[lb];
+    n16 = c.n16[lb];
+    t = c.t[lb];
+  }
+  if (tid == 0) {
+    M.jd = -1;
+    M.ngrown = 0;
+  }
+  __syncthreads();  // scores and the appended position are in memory for the selection
+  const int N = budget[(size_t)b * dm.L + l];
+  const int NO = n_orig[(size_t)b * dm.L + l];
+  const int prot_lo = t - dm.P;
+  uint8_t* keep8 = keep_all + (size_t)lb * dm.capt;
+  uint8_t* wkeep = wkeep_all + (size_t)lb * dm.cap16;
+  const int32_t* pos16 = c.pos16 + (size_t)lb * dm.cap16;
+  const float* ema16 = c.ema16 + (size_t)lb * dm.cap16;
+  // ranking key + 1 of window slot w, or 0 when it is protected
+  auto win_key = [&](int w) -> uint64_t {
+    const int p = pos16[w];
+    if (p > prot_lo) return 0ull;
+    return (((uint64_t)__float_as_uint(ema16[w]) << 32) | (uint32_t)p) + 1ull;
+  };
+  // the kept unprotected Original with the smallest key: (key, slot) per thread
+  uint64_t mn = ~0ull;
+  int ms = -1;
+  int c8 = 0, c16 = 0;
+  select_core<kCompThreads, EMA>(c, dm, lb, n8, n16, t, N, U.sel, SM, [&](int j, int k, uint64_t key) {
+    if (j < n8) {
+      if (j < kLdsFlags8) F.k8[j] = (uint8_t)k; else keep8[j] = (uint8_t)k;
+      c8 += k;
+    } else {
+      const int w = j - n8;
+      if (k) {
+        const uint64_t kk = key == kAllKept ? win_key(w) : key;
+        if (kk != 0ull && kk < mn) {
+          mn = kk;
+          ms = w;
+        }
+      }
+      if (w < kLdsFlags16) F.k16[w] = (uint8_t)k; else wkeep[w] = (uint8_t)k;
+      c16 += k;
+    }
+  });
+  int n8n, n16n;
+  count_kept(c8, c16, M, n8n, n16n);  // its barrier also ends the key cache's use
+  // the demotee, if more than N_O Original tokens remain
+  int jd = -1;
+  if (n16n > NO) {
+    const uint64_t wm = wave_min_u64(mn);
+    if (lane == 0) SM.wmin[wave] = wm;
+    __syncthreads();
+    uint64_t gm = SM.wmin[0];
+    for (int w = 1; w < kCompWaves; ++w) gm = SM.wmin[w] < gm ? SM.wmin[w] : gm;
+    if (gm != ~0ull && mn == gm) {  // keys are unique: one thread
+      M.jd = ms;
+      if (ms < kLdsFlags16) F.k16[ms] = 0; else wkeep[ms] = 0;
+    }
+    __syncthreads();
+    jd = M.jd;
+    if (jd >= 0) --n16n;
+  }
+  compact_core(c, dm, lb, n8, n16, t, n8n, n16n, jd, keep8, wkeep, F, U.comp, M, plan_all,
+               mv8_all, mv16_all);
+}
+
+// Further ARKV demotions of a step whose N_O fell by more than one token (or the
+// first step after a prefill whose window holds more than N_O): one round per
+// token, each the lowest-ranked unprotected Original of the cache as it stands,
+// moved by compact_core with every other token kept.  A workgroup whose cache is
+// within N_O returns at once, so in the steady state this launch does nothing.
+__global__ __launch_bounds__(kCompThreads) void arkv_rounds_kernel(
+    conf_cache c, Dims dm, int layer0, const int32_t* __restrict__ n_orig,
+    uint8_t* __restrict__ keep_all, int32_t* __restrict__ plan_all, int32_t* __restrict__ mv8_all,
+    int32_t* __restrict__ mv16_all, uint8_t* __restrict__ wkeep_all) {
+  __shared__ CompFlags F;
+  __shared__ CompScratch X;
+  __shared__ CompMisc M;
+  __shared__ unsigned long long wmin[kCompWaves];
+  const int lb = layer0 * dm.B + blockIdx.x;
+  const int l = lb / dm.B, b = lb % dm.B;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int NO = n_orig[(size_t)b * dm.L + l];
+  int n8 = c.n8[lb], n16 = c.n16[lb];
+  const int t = c.t[lb];
+  if (n16 <= NO) return;  // uniform over the workgroup
+  const int prot_lo = t - dm.P;
+  uint8_t* keep8 = keep_all + (size_t)lb * dm.capt;
+  uint8_t* wkeep = wkeep_all + (size_t)lb * dm.cap16;
+  const int32_t* pos16 = c.pos16 + (size_t)lb * dm.cap16;
+  const float* ema16 = c.ema16 + (size_t)lb * dm.cap16;
+  while (n16 > NO) {
+    uint64_t mn = ~0ull;
+    int ms = -1;
+    for (int i = tid; i < n8; i += kCompThreads)
+      if (i < kLdsFlags8) F.k8[i] = 1; else keep8[i] = 1;
+    for (int w = tid; w < n16; w += kCompThreads) {
+      if (w < kLdsFlags16) F.k16[w] = 1; else wkeep[w] = 1;
+      const int p = pos16[w];
+      if (p > prot_lo) continue;
+      const uint64_t kk = ((uint64_t)__float_as_uint(ema16[w]) << 32) | (uint32_t)p;
+      if (kk < mn) {
+        mn = kk;
+        ms = w;
+      }
+    }
+    if (tid == 0) {
+      M.jd = -1;
+      M.ngrown = 0;
+    }
+    const uint64_t wm = wave_min_u64(mn);
+    if (lane == 0) wmin[wave] = wm;
+    __syncthreads();
+    uint64_t gm = wmin[0];
+    for (int w = 1; w < kCompWaves; ++w) gm = wmin[w] < gm ? wmin[w] : gm;
+    if (gm != ~0ull && mn == gm) {
+      M.jd = ms;
+      if (ms < kLdsFlags16) F.k16[ms] = 0; else wkeep[ms] = 0;
+    }
+    __syncthreads();
+    const int jd = M.jd;
+    if (jd < 0) break;  // every Original token is protected
+    compact_core(c, dm, lb, n8, n16, t, n8, n16 - 1, jd, keep8, wkeep, F, X, M, plan_all,
+                 mv8_all, mv16_all);
+    // the demotee took the INT8 region's first free slot (or was dropped when it was full)
+    n8 += n8 < dm.cap8 ? 1 : 0;
+    n16 -= 1;
+    __syncthreads();  // this round's moves are in memory
+  }
+}
+
+void launch_arkv(const Dims& dm, const conf_cache& c, int layer0, int nl, const int32_t* budget,
+                 const int32_t* n_orig, uint8_t* keep, int32_t* plan, int32_t* mv8, int32_t* mv16,
+                 uint8_t* wkeep, const float* massp, const int32_t* snap, bool with_ema,
+                 hipStream_t st) {
+  if (with_ema)
+    hipLaunchKernelGGL(arkv_kernel<true>, dim3(nl * dm.B), dim3(kCompThreads), 0, st, c, dm,
+                       layer0, budget, n_orig, keep, plan, mv8, mv16, wkeep, massp, snap);
+  else
+    hipLaunchKernelGGL(arkv_kernel<false>, dim3(nl * dm.B), dim3(kCompThreads), 0, st, c, dm,
+                       layer0, budget, n_orig, keep, plan, mv8, mv16, wkeep, massp, snap);
+  hipLaunchKernelGGL(arkv_rounds_kernel, dim3(nl * dm.B), dim3(kCompThreads), 0, st, c, dm,
+                     layer0, n_orig, keep, plan, mv8, mv16, wkeep);
 }
 
 void launch_compact(const Dims& dm, const conf_cache& c, int layer0, int nl, const uint8_t* keep,

@@ -272,8 +272,11 @@ __device__ void select_core(const conf_cache& c, const Dims& dm, int lb, int n8,
     }
   };
   const bool trim = dm.policy == CONF_POLICY_TRIM;
+  const bool arkv = dm.policy == CONF_POLICY_ARKV;
   auto keyf = [&](float e, float em, uint32_t tag) -> uint64_t {
     if (trim) return retention_key(e, (int)tag, t);
+    // ARKV ranks on its heavy-hitter EMA itself (e >= 0 orders like its bits)
+    if (arkv) return ((uint64_t)__float_as_uint(e) << 32) | tag;
     return sel_key(e, em, (int)tag, t, dm.s_ema, dm.s_rec, tag);
   };
   rank_core<NT, PAIRS, false>(n, N, t - dm.P, 1, !trim, tok, keyf, X.key, X.hist, kSelLdsKeys, M,

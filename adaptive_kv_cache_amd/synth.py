@@ -20,7 +20,7 @@ import torch
 from .workloads import Workload
 
 (_TAG_LOGITS, _TAG_TEMP, _TAG_Q, _TAG_K, _TAG_V, _TAG_PRE_K, _TAG_PRE_V, _TAG_NEEDLE,
- _TAG_BETA, _TAG_PRE_BETA) = range(10)
+ _TAG_BETA, _TAG_PRE_BETA, _TAG_OQ) = range(11)
 
 TORCH_DTYPE = {"f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -127,3 +127,13 @@ def log_beta_prefill(wl: Workload, layer: int, seed: int, device="cpu", length=N
     g = _gen(seed, _TAG_PRE_BETA, layer, device)
     z = 4.0 + 2.0 * torch.randn(wl.batch, L0, generator=g, device=device, dtype=torch.float32)
     return _log_gate(z)
+
+
+def arkv_n_orig(wl: Workload, seed: int) -> torch.Tensor:
+    """Original-token budget of each layer, int32 [L]: ceil(r_l * N_high) with the
+    layer's OQ ratio r_l ~ U[0.75, 0.95], at least P.  Stands in for the ratios
+    that ARKV derives from prefill attention statistics."""
+    g = _gen(seed, _TAG_OQ, 0, "cpu")
+    r = 0.75 + 0.2 * torch.rand(wl.n_layers, generator=g, dtype=torch.float64)
+    n = torch.ceil(r * wl.n_high).to(torch.int32)
+    return torch.clamp(n, min=wl.protect)

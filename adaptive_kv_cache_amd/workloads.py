@@ -52,7 +52,7 @@ class Workload:
     temp_schedule: str = "alt"   # "alt": 0.5 / 8 in 64-step runs; "uniform": U[1.5, 3]
     needle: bool = False
     policy: str = "confkv"       # "confkv", or a baseline: "full" (full KV), "window" (sliding),
-                                 # "trim" (retention eviction)
+                                 # "trim" (retention eviction), "arkv" (ARKV's three states)
     headwise: bool = False       # per-KV-head keep sets sharing Hkv * N pairs per layer
 
     @property
@@ -86,6 +86,11 @@ class Workload:
         64); budgets and P at their smallest valid values, since nothing is evicted.
         window: a W-token sliding window; P = N_high = N_low = W and no pyramid, so
         the ranking keeps exactly the protected newest W.
+        arkv: ARKV's three states with N = N_high kept tokens, up to 95% of them
+        Original (W = ceil(0.95 N) sizes the 16-bit arrays), P = 32; the prefill is
+        cut to W tokens, all Original, so that after a few steps the cache is in
+        ARKV's steady state (N tokens, N_O of them Original) rather than a
+        positional split that Original tokens could never win back.
         trim: retention eviction with memory budget M = N_high, held entirely in the
         16-bit window (W = M); P = 1 protects the token being appended; the prefill
         is cut to M tokens, which is the cache that retention eviction holds once it
@@ -105,6 +110,15 @@ class Workload:
             return replace(self, name=f"{self.name}_trim", policy="trim", window=m, protect=1,
                            n_high=m, n_low=m, pyramid=False, prefill=min(self.prefill, m),
                            needle=False)
+        if policy == "arkv":
+            # N = N_high kept tokens, at most 95% of them Original (the OQ ratios are
+            # drawn per layer in [0.75, 0.95]); the window arrays hold the Original
+            # ones; the page's example protects the newest 32
+            n = self.n_high
+            w = -(-95 * n // 100)
+            return replace(self, name=f"{self.name}_arkv", policy="arkv", window=w,
+                           protect=min(32, w), n_high=n, n_low=n, pyramid=False,
+                           prefill=min(self.prefill, w), needle=False)
         raise ValueError(policy)
 
 

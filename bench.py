@@ -25,6 +25,9 @@ stream.  --streams 1|2 overrides the choice.
 --policy full | window runs the same step under the full-KV or the sliding-window
 baseline (the pages' comparison policies) on the same kernels and shape: full KV
 keeps every prefill and decoded token in 16 bits, the window the newest W.
+--policy arkv runs ARKV's three-state cache: a step is the attention and the ARKV
+launches (score EMA, eviction to N = N_high, quantisation to e4m3 of the lowest-
+ranked Original tokens beyond the layer's N_O), with no confidence.
 --policy trim runs retention eviction: a step is the attention and one launch that
 stores the new token's ln(beta), ranks by (t - pos) * ln(beta) and compacts, with a
 16-bit cache of M = N_high tokens (the prefill cut to M) and no confidence.
@@ -95,9 +98,9 @@ def step_bytes(wl, n8, nw, plan):
     H, d, e = _heads(wl), wl.head_dim, 2
     n = n8 + nw + 1
     b = attn_bytes(wl, n8, nw)
-    if wl.policy != "trim":
+    if wl.policy not in ("trim", "arkv"):
         b += wl.batch * wl.vocab * 4                            # logits (confidence)
-    if wl.policy == "confkv":
+    if wl.policy in ("confkv", "arkv"):
         b += int((8 * n + 4).sum())                             # EMA read and written, new pos
     else:
         b += 8 * n.numel()                                      # the new token's EMA slot and pos
@@ -174,6 +177,8 @@ def run(args):
     log(f"set-up {wl.name}: cap8={wl.cap8} prefill={wl.prefill}")
     eng = Engine(wl, dev)
     trim = wl.policy == "trim"
+    arkv = wl.policy == "arkv"
+    no_conf = trim or arkv  # these policies take no confidence-chosen budget
     t0 = time.perf_counter()
     if wl.prefill:
         for l in range(wl.n_layers):
@@ -200,8 +205,11 @@ def run(args):
     out = torch.empty(L, B, wl.n_q_heads, wl.head_dim, dtype=torch.float32, device=dev)
     conf = torch.empty(total, B, dtype=torch.float32, device=dev)
     budget = torch.empty(total, B, L, dtype=torch.int32, device=dev)
-    if trim:
+    if no_conf:
         budget.fill_(wl.n_high)
+    if arkv:
+        # ARKV: N = N_high kept tokens, N_O of them Original per the layer's OQ ratio
+        n_orig = synth.arkv_n_orig(wl, args.seed).to(dev)[None, :].repeat(B, 1).contiguous()
     S = wl.n_sub
     n8_first = torch.empty(L, S, dtype=torch.int32, device=dev)
     n16_first = torch.empty_like(n8_first)
@@ -213,7 +221,7 @@ def run(args):
     if streams == "auto":
         # K/V bytes one attention launch streams at the tight budget
         kv = L * B * wl.n_kv_heads * wl.head_dim * (wl.n_high + wl.window) * 2
-        streams = "2" if kv >= 1 << 28 and not trim else "1"  # trim has no confidence
+        streams = "2" if kv >= 1 << 28 and not no_conf else "1"  # nothing to overlap otherwise
     side = main if streams == "1" else torch.cuda.Stream(device=dev)
     torch.cuda.synchronize()
     log("inputs resident; warm-up")
@@ -227,7 +235,7 @@ def run(args):
             # it waits for this stream)
             if i:
                 hplan[i - 1].copy_(ws_plan)
-            if not trim:
+            if not no_conf:
                 eng.confidence(logits[s], c=conf[s], budget=budget[s])
         if ev is not None:
             ev[0].record(main)
@@ -238,6 +246,8 @@ def run(args):
             main.wait_stream(side)
         if trim:
             eng.trim_evict_compact(-1, budget[s], lbetas[s])
+        elif arkv:
+            eng.arkv_ema_evict_compact(-1, budget[s], n_orig)
         else:
             eng.ema_evict_compact(-1, budget[s])
 
@@ -287,8 +297,8 @@ def run(args):
         "metric": METRIC, "value": round(sps, 3), "unit": "steps/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms / args.steps, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": (f"int8+{wl.dtype16}" if wl.policy == "confkv" else wl.dtype16)
-                 + " operands, f32 accumulate",
+        "dtype": ({"confkv": f"int8+{wl.dtype16}", "arkv": f"fp8(e4m3)+{wl.dtype16}"}
+                  .get(wl.policy, wl.dtype16) + " operands, f32 accumulate"),
         "data": "synthetic",
         "config": {"workload": wl.name, "policy": wl.policy, "headwise": wl.headwise,
                    "layers": L, "batch": B,
@@ -416,9 +426,10 @@ def main():
     ap.add_argument("--workload", default="qwen32b_gqa_b8_32k")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--policy", choices=("confkv", "full", "window", "trim"), default="confkv",
+    ap.add_argument("--policy", choices=("confkv", "full", "window", "trim", "arkv"),
+                    default="confkv",
                     help="cache policy: CONF-KV, or the full-KV / sliding-window / retention-"
-                         "eviction baseline on the same kernels")
+                         "eviction / ARKV baseline on the same kernels")
     ap.add_argument("--headwise", action="store_true",
                     help="head-wise keep sets: each KV head keeps its own tokens, the layer's "
                          "Hkv * N pairs shared by the heads")

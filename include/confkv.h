@@ -20,6 +20,8 @@
  *                 eviction (a related method in the same bundle)
  *   [heads]       Significance and claims (the method composes with head-wise
  *                 allocation)
+ *   [arkv]        the ARKV page, Methodology: three-state assignment;
+ *                 decoding-phase token ranking (a related method in the bundle)
  *
  * Conventions shared by every call
  *   - Every pointer argument is a DEVICE pointer owned by the caller, except
@@ -88,11 +90,23 @@ enum { CONF_F16 = 1, CONF_BF16 = 2 };
  *                       ema arrays hold ln(beta).  A step is conf_attend, then
  *                       conf_trim_evict_compact; the prefill's ln(beta) is set
  *                       by conf_cache_set_retention after conf_cache_ingest.
+ *   CONF_POLICY_ARKV    ARKV's three-state cache [arkv]: Original tokens in 16
+ *                       bits (the window arrays), Quantized ones as e4m3 codes
+ *                       (the 8-bit arrays: sign, 4 exponent bits with bias 7, 3
+ *                       mantissa bits, largest 448; scale = absmax / 448 per (KV
+ *                       head, channel), round to nearest even, requantised on a
+ *                       new maximum), Evicted ones gone.  The ema arrays hold the
+ *                       EMA of the heavy-hitter score mean_k m_k + var_k m_k over
+ *                       the KV heads k (m_k: the token's attention averaged over
+ *                       head k's query heads; population variance).  A step is
+ *                       conf_attend, then conf_arkv_ema_evict_compact; W only sizes
+ *                       the 16-bit arrays (at least the largest N_O), and the
+ *                       prefill's positions < prefill_len - W are Quantized.
  * The baselines and TRIM need no per-token attention mass: their attention is a
  * single online pass whatever the cache length, and they keep no EMA (it stays
  * 0 for FULL and WINDOW). */
 enum { CONF_POLICY_CONFKV = 0, CONF_POLICY_FULL = 1, CONF_POLICY_WINDOW = 2,
-       CONF_POLICY_TRIM = 3 };
+       CONF_POLICY_TRIM = 3, CONF_POLICY_ARKV = 4 };
 
 /* Device status word bits (conf_cache.status), set by kernels, never cleared
  * except by conf_cache_reset(). */
@@ -228,9 +242,14 @@ int conf_confidence(const conf_params* p, const float* logits, float* c, int32_t
  * cached tokens of KV head h / (Hq/Hkv), INT8 tokens dequantised as code*amax/127
  * inside the block reads.  out: fp32 [L][B][Hq][d].  Then every token's EMA
  * becomes decay*e + (1-decay)*mass_j, mass_j = mean over the Hq heads of its
- * softmax probability; the new token starts from e = 0.  CONF_E_INVALID under
- * CONF_POLICY_TRIM (whose step is conf_attend + conf_trim_evict_compact);
- * conf_ema_evict_compact and conf_step likewise.
+ * softmax probability; the new token starts from e = 0.  Under CONF_POLICY_ARKV
+ * the EMA is that of ARKV's heavy-hitter score (see the policy).
+ * CONF_E_INVALID under CONF_POLICY_TRIM, whose step is conf_attend followed by
+ * conf_trim_evict_compact.  Policy limits of the calls below: conf_step and
+ * conf_ema_evict_compact return CONF_E_INVALID under CONF_POLICY_TRIM and
+ * CONF_POLICY_ARKV; conf_evict_compact and conf_compact_demote under
+ * CONF_POLICY_ARKV, which demotes by rank, not by position (its calls are
+ * conf_arkv_*).
  */
 int conf_decode_attn(const conf_params* p, conf_cache* c, int32_t layer, const void* q,
                      const void* k_new, const void* v_new, float* out, void* ws,
@@ -299,6 +318,28 @@ int conf_ema_evict_compact(const conf_params* p, conf_cache* c, int32_t layer,
 int conf_trim_evict_compact(const conf_params* p, conf_cache* c, int32_t layer,
                             const int32_t* budget, const float* log_beta, void* ws,
                             conf_stream_t stream);
+
+/*
+ * ARKV's eviction and quantisation (CONF_POLICY_ARKV only) [arkv], after
+ * conf_decode_attn (which applied the heavy-hitter score EMA, the new token's
+ * from 0): each (layer, sequence) keeps its newest P positions and its
+ * budget[b][l] - |P| best other tokens by (EMA desc, position desc); then, while
+ * more than n_orig[b][l] kept tokens are Original, the lowest-ranked unprotected
+ * Original token is quantised to e4m3 (lowest first; one per step in the steady
+ * state).  budget, n_orig: int32 [B][L].  CONF_E_INVALID under any other policy.
+ */
+int conf_arkv_evict_compact(const conf_params* p, conf_cache* c, int32_t layer,
+                            const int32_t* budget, const int32_t* n_orig, void* ws,
+                            conf_stream_t stream);
+
+/*
+ * The same after conf_attend: the pending score EMA first (n16 and t advance),
+ * in the same launch.  conf_attend + conf_arkv_ema_evict_compact give exactly
+ * the results of conf_decode_attn + conf_arkv_evict_compact.
+ */
+int conf_arkv_ema_evict_compact(const conf_params* p, conf_cache* c, int32_t layer,
+                                const int32_t* budget, const int32_t* n_orig, void* ws,
+                                conf_stream_t stream);
 
 /*
  * The prefill's retention (CONF_POLICY_TRIM only), right after

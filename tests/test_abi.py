@@ -176,8 +176,31 @@ def test_policy_gated_entries(lib):
                                         null) == E_INVALID
     assert lib.conf_cache_set_retention(ctypes.byref(trim), ctypes.byref(cache), 0, fake, 0,
                                         null) == 0          # nothing to set: no launch
-    rc, _ = _layout(lib, _p(policy=4))
+    rc, _ = _layout(lib, _p(policy=5))
     assert rc == E_INVALID
+
+
+def test_arkv_gated_entries(lib):
+    """ARKV's calls need CONF_POLICY_ARKV and both budgets; the CONF-KV eviction
+    calls, which demote by position, refuse an ARKV cache."""
+    fake = ctypes.c_void_p(0x1000)           # never dereferenced: validation fails first
+    null = ctypes.c_void_p(0)
+    cache = binding.ConfCache(*([0x1000] * 14))
+    conf, arkv = _p(), _p(policy=binding.POLICY["arkv"])
+    for fn in (lib.conf_arkv_evict_compact, lib.conf_arkv_ema_evict_compact):
+        assert fn(ctypes.byref(conf), ctypes.byref(cache), -1, fake, fake, fake, null) == E_INVALID
+        assert fn(ctypes.byref(arkv), ctypes.byref(cache), -1, fake, null, fake, null) == E_INVALID
+        assert fn(ctypes.byref(arkv), ctypes.byref(cache), -1, null, fake, fake, null) == E_INVALID
+        assert fn(ctypes.byref(arkv), ctypes.byref(cache), 64, fake, fake, fake, null) == E_INVALID
+    assert lib.conf_ema_evict_compact(ctypes.byref(arkv), ctypes.byref(cache), -1, fake, fake,
+                                      null) == E_INVALID
+    assert lib.conf_evict_compact(ctypes.byref(arkv), ctypes.byref(cache), -1, fake, fake,
+                                  null) == E_INVALID
+    assert lib.conf_compact_demote(ctypes.byref(arkv), ctypes.byref(cache), -1, fake, fake,
+                                   null) == E_INVALID
+    assert lib.conf_step(ctypes.byref(arkv), ctypes.byref(cache), *([fake] * 8), null) == E_INVALID
+    assert _layout(lib, _p(policy=binding.POLICY["arkv"], headwise=1))[0] in (E_INVALID,
+                                                                              E_CAPACITY)
 
 
 @pytest.mark.skipif(torch.cuda.is_available(),

@@ -542,3 +542,133 @@ def test_headwise_entry_points_agree(case):
                         assert np.array_equal(np.asarray(ea[key]), np.asarray(ec[key])), \
                             ("evict_compact", step, l, s_, key)
     assert a.status() == 0 and b.status() == 0 and c.status() == 0
+
+
+def _arkv_cases():
+    return {"mha_f16_d64": (TINY["mha_f16_d64"], 190), "gqa5_bf16_d128": (TINY["gqa5_bf16_d128"], 24),
+            "gqa8_bf16_d64": (TINY["gqa8_bf16_d64"], 24), "mha16_f16_d128": (TINY["mha16_f16_d128"], 12),
+            "gqa16_bf16_d64_long": (TINY["gqa16_bf16_d64_long"], 8)}
+
+
+def _arkv_wl(base, steps):
+    # the full prefill, so that ingest quantises its older part to e4m3 and the first
+    # step after a long one takes the two-pass attention over FP8 tokens
+    return base.baseline("arkv", steps).scaled(prefill=base.prefill)
+
+
+def _fp8_state(st):
+    f = O.Fp8State(st.k16.shape[1], st.k16.shape[2], st.dtype16)
+    for k in ("pos", "is8", "k16", "v16", "k8", "v8", "ema", "amax_k", "amax_v", "t"):
+        setattr(f, k, getattr(st, k))
+    return f
+
+
+def _arkv_budgets(wl, step, n_orig0):
+    """N kept tokens per (sequence, layer), with every seventh step cutting 9 to 40;
+    N_O from the layer's OQ ratio, lowered by up to 12 on some steps so that a step
+    has several tokens to quantise."""
+    B, L = wl.batch, wl.n_layers
+    N = torch.full((B, L), wl.n_high, dtype=torch.int32)
+    NO = n_orig0[None, :].repeat(B, 1).clone()
+    if step % 7 == 3:
+        for b in range(B):
+            for l in range(L):
+                N[b, l] = wl.n_high - (9 + 11 * b + 5 * l) % 32
+    if step % 5 == 2:
+        for b in range(B):
+            NO[b] = torch.clamp(NO[b] - (3 + 4 * b) % 13, min=wl.protect)
+    NO = torch.minimum(NO, N)
+    return N, NO
+
+
+@pytest.mark.parametrize("case", list(_arkv_cases()))
+def test_arkv_teacher_forced(case):
+    """ARKV through the C ABI (decode_attn with the heavy-hitter score EMA, then
+    arkv_evict_compact), teacher-forced against the oracle's arkv_step on every
+    (layer, sequence): attention within tolerance, the score EMA within 1e-5,
+    kept positions, which tokens are Original or FP8, e4m3 codes, absmax and
+    window bits bit-exact."""
+    base, steps = _arkv_cases()[case]
+    wl = _arkv_wl(base, steps)
+    prm = oracle_params(wl)
+    # Original budgets a little above P, so that the short runs after a prefill
+    # (whose kept tokens are mostly FP8 at first) reach them and quantise
+    n_orig0 = torch.minimum(synth.arkv_n_orig(wl, SEED),
+                            wl.protect + 6 + 3 * torch.arange(wl.n_layers, dtype=torch.int32))
+    _say("arkv", case, "N", wl.n_high, "W", wl.window, "N_O", n_orig0.tolist())
+    eng = Engine(wl)
+    if wl.prefill:
+        pre = _ingest(eng, wl, SEED)
+        for l in range(wl.n_layers):
+            for b in range(wl.batch):
+                ref = O.ingest_fp8(pre[l][0][b], pre[l][1][b], wl.window, wl.dtype16)
+                assert_same_state(to_oracle_state(eng.export(l, b), wl.dtype16), ref, ema_rtol=0,
+                                  what=("ingest", l, b))
+    worst = 0.0
+    demoted = 0
+    for step in range(steps):
+        S0 = _snap(eng, wl)
+        q = synth.q_new(wl, step, SEED)
+        k, v = synth.kv_new(wl, step, SEED)
+        N, NO = _arkv_budgets(wl, step, n_orig0)
+        out = eng.decode_attn(-1, q.cuda(), k.cuda(), v.cuda())
+        S1 = _snap(eng, wl)
+        eng.arkv_evict_compact(-1, N.cuda(), NO.cuda())
+        S2 = _snap(eng, wl)
+        out = out.cpu().numpy()
+        qb, kb, vb = bits16(q), bits16(k), bits16(v)
+        for l in range(wl.n_layers):
+            for b in range(wl.batch):
+                what = (case, step, l, b)
+                st = _fp8_state(to_oracle_state(S0[l][b], wl.dtype16))
+                e_gpu = ema_by_pos(S1[l][b])
+                override = np.array([e_gpu[p] for p in np.append(st.pos, st.t + 1).tolist()],
+                                    np.float32)
+                r = O.arkv_step(st, qb[l, b], kb[l, b], vb[l, b], int(N[b, l]), int(NO[b, l]),
+                                prm, ema32_override=override)
+                err = attn_rel_err(out[l, b], r["o"])
+                worst = max(worst, err)
+                assert err <= ATTN_TOL, (what, err)
+                np.testing.assert_allclose(override, r["ema"], rtol=EMA_RTOL, atol=1e-12,
+                                           err_msg=str(what))
+                assert_same_state(to_oracle_state(S2[l][b], wl.dtype16), st, ema_rtol=0, what=what)
+                demoted += len(r["demoted"])
+    assert eng.status() == 0
+    assert demoted > 0
+    _say("  worst attention rel err", worst, "tokens quantised", demoted)
+
+
+@pytest.mark.parametrize("case", ["mha_f16_d64", "gqa5_bf16_d128", "gqa16_bf16_d64_long"])
+def test_arkv_fused_equals_split(case):
+    """attend + arkv_ema_evict_compact (the score EMA in the eviction launch) leaves
+    exactly the cache and output of decode_attn + arkv_evict_compact, for all
+    layers at once and layer by layer."""
+    base, steps = _arkv_cases()[case]
+    wl = _arkv_wl(base, steps)
+    n_orig0 = torch.minimum(synth.arkv_n_orig(wl, SEED),
+                            wl.protect + 6 + 3 * torch.arange(wl.n_layers, dtype=torch.int32))
+    _say("arkv fused", case)
+    a, b = Engine(wl), Engine(wl)
+    if wl.prefill:
+        _ingest(a, wl, SEED)
+        _ingest(b, wl, SEED)
+    for step in range(min(steps, 60)):
+        q = synth.q_new(wl, step, SEED).cuda()
+        k, v = (x.cuda() for x in synth.kv_new(wl, step, SEED))
+        N, NO = (x.cuda() for x in _arkv_budgets(wl, step, n_orig0))
+        layers = [-1] if step % 2 == 0 else list(range(wl.n_layers))
+        for l in layers:
+            ql, kl, vl = (x if l < 0 else x[l].contiguous() for x in (q, k, v))
+            oa = a.attend(l, ql, kl, vl)
+            a.arkv_ema_evict_compact(l, N, NO)
+            ob = b.decode_attn(l, ql, kl, vl)
+            b.arkv_evict_compact(l, N, NO)
+            assert torch.equal(oa, ob), (step, l)
+        if step % 5 == 4:
+            for l in range(wl.n_layers):
+                for s_ in range(wl.batch):
+                    ea, eb = a.export(l, s_), b.export(l, s_)
+                    for key in ea:
+                        assert np.array_equal(np.asarray(ea[key]), np.asarray(eb[key])), \
+                            (step, l, s_, key)
+    assert a.status() == 0 and b.status() == 0
