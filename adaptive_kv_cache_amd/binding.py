@@ -170,6 +170,37 @@ class Engine:
         self.ws = torch.zeros(max(ws.value, 256), dtype=torch.uint8, device=dev)
         self.reset()
 
+    def layer_view(self, l0: int, nl: int) -> "Engine":
+        """Layers l0 .. l0+nl-1 of this cache as a cache of its own (the arrays are
+        layer-major, so the view is pointer offsets into the same memory), with a
+        workspace of its own, so that calls on two views may run concurrently on
+        two streams.  The view's `layer` arguments count from l0, and its
+        per-layer inputs (q, k, v, out, budget columns) cover its nl layers."""
+        wl = self.wl
+        if not (0 <= l0 and nl >= 1 and l0 + nl <= wl.n_layers):
+            raise ValueError(f"layers {l0}..{l0 + nl - 1} outside 0..{wl.n_layers - 1}")
+        v = Engine.__new__(Engine)
+        v.lib, v.device, v.dtype16 = self.lib, self.device, self.dtype16
+        v.wl = wl.scaled(n_layers=nl, name=f"{wl.name}_layers{l0}-{l0 + nl - 1}")
+        v.p = ConfParams.from_buffer_copy(self.p)
+        v.p.n_layers = nl
+        v.cap8, v.cap16, v.n_sub = self.cap8, self.cap16, self.n_sub
+        per_layer = lambda t: t.numel() // wl.n_layers  # noqa: E731
+        for f in _CACHE_FIELDS:
+            t = getattr(self, "t_" + f)
+            if f == "status":
+                setattr(v, "t_" + f, t)
+            elif t.dim() == 1:
+                n = per_layer(t)
+                setattr(v, "t_" + f, t[l0 * n:(l0 + nl) * n])
+            else:
+                setattr(v, "t_" + f, t[l0:l0 + nl])
+        v.cache = ConfCache(*[_ptr(getattr(v, "t_" + f)) for f in _CACHE_FIELDS])
+        ws = c_size_t()
+        _check(v.lib.conf_workspace_bytes(ctypes.byref(v.p), ctypes.byref(ws)), "workspace")
+        v.ws = torch.zeros(max(ws.value, 256), dtype=torch.uint8, device=v.device)
+        return v
+
     # -- helpers ------------------------------------------------------------
     def _stream(self):
         return c_void_p(torch.cuda.current_stream(self.device).cuda_stream)

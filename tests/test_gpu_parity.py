@@ -672,3 +672,48 @@ def test_arkv_fused_equals_split(case):
                         assert np.array_equal(np.asarray(ea[key]), np.asarray(eb[key])), \
                             (step, l, s_, key)
     assert a.status() == 0 and b.status() == 0
+
+
+@pytest.mark.parametrize("name", ["mha_f16_d64", "gqa5_bf16_d128"])
+def test_layer_views_on_two_streams_equal_the_whole_cache(name):
+    """Two layer-range views of one cache, each with its own workspace, driven on
+    two concurrent streams (the bench's layer split) leave exactly the cache and
+    outputs of the whole cache driven on one stream."""
+    wl = TINY[name].scaled(name=name + "_4l", n_layers=4)
+    L = wl.n_layers
+    _say("layer views", wl.name)
+    a, b = Engine(wl), Engine(wl)
+    if wl.prefill:
+        _ingest(a, wl, SEED)
+        _ingest(b, wl, SEED)
+    halves = [(0, 2), (2, 4)]
+    views = [b.layer_view(l0, l1 - l0) for l0, l1 in halves]
+    main = torch.cuda.current_stream()
+    streams = [main, torch.cuda.Stream()]
+    out_b = torch.empty(L, wl.batch, wl.n_q_heads, wl.head_dim, dtype=torch.float32, device="cuda")
+    for step in range(min(wl.steps, 60) if wl.prefill else 200):
+        z = synth.logits(wl, step, SEED).cuda()
+        q = synth.q_new(wl, step, SEED).cuda()
+        k, v = (x.cuda() for x in synth.kv_new(wl, step, SEED))
+        out_a = a.attend(-1, q, k, v)
+        _, bud = a.confidence(z)
+        a.ema_evict_compact(-1, bud)
+        _, bud_b = b.confidence(z)
+        cols = [bud_b[:, l0:l1].contiguous() for l0, l1 in halves]
+        for st in streams[1:]:
+            st.wait_stream(main)
+        for (l0, l1), view, st, col in zip(halves, views, streams, cols):
+            with torch.cuda.stream(st):
+                view.attend(-1, q[l0:l1], k[l0:l1], v[l0:l1], out=out_b[l0:l1])
+                view.ema_evict_compact(-1, col)
+        for st in streams[1:]:
+            main.wait_stream(st)
+        assert torch.equal(out_a, out_b), step
+        if step % 20 == 19:
+            for l in range(L):
+                for s_ in range(wl.batch):
+                    ea, eb = a.export(l, s_), b.export(l, s_)
+                    for key in ea:
+                        assert np.array_equal(np.asarray(ea[key]), np.asarray(eb[key])), \
+                            (step, l, s_, key)
+    assert a.status() == 0 and b.status() == 0
