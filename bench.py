@@ -29,7 +29,8 @@ runs beside the other half's attention rather than after all of it (measured on 
 Qwen-32B batch-8 cache: 0.494 against 0.540 ms per step; four or eight parts were
 slower).  The attention time of a step is then the union of its two launches, from
 the first start to the last end, and the roofline's bytes are those of all layers.
---split 1|2 overrides the choice.
+Only caches whose attention launch has at least 2048 workgroups are split (the
+Qwen-32B batch-1 cache, 512, fell to 0.55x).  --split 1|2 overrides the choice.
 
 --policy full | window runs the same step under the full-KV or the sliding-window
 baseline (the pages' comparison policies) on the same kernels and shape: full KV
@@ -46,6 +47,7 @@ Prints one JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import contextlib
 import json
 import os
 import sys
@@ -232,7 +234,11 @@ def run(args):
     side = main if streams == "1" else torch.cuda.Stream(device=dev)
     split = args.split
     if split == "auto":
-        split = "2" if big else "1"
+        # halves of at least 1024 workgroups each (four per compute unit); smaller
+        # launches lose more to the extra launches and waits than the overlap gains
+        # (measured: the Qwen-32B batch-1 cache, 512 units, fell from 8476 to 4684 steps/s)
+        units = L * B * wl.n_kv_heads
+        split = "2" if big and units >= 2048 else "1"
     split = int(split)
     if split > 1 and side is main:
         side = torch.cuda.Stream(device=dev)  # the halves must not wait on each other
@@ -250,6 +256,15 @@ def run(args):
     # per-view budget columns (copied after the confidence), ln(beta) rows, N_O columns
     bsl = [budget[:, :, a:b].clone() for a, b in ranges] if split > 1 else [budget]
     norig_v = [n_orig[:, a:b].contiguous() for a, b in ranges] if arkv else None
+    # every step's per-view arguments, sliced once here: on the launch-bound caches the
+    # Python between a launch's start event and the launch is part of what is timed
+    if split == 1:
+        vargs = [[(qs[s], ks[s], vs[s], out, budget[s], lbetas[s] if trim else None)]
+                 for s in range(total)]
+    else:
+        vargs = [[(qs[s][a:b], ks[s][a:b], vs[s][a:b], out[a:b], bsl[k][s],
+                   lbetas[s][a:b] if trim else None) for k, (a, b) in enumerate(ranges)]
+                 for s in range(total)]
     torch.cuda.synchronize()
     log(f"inputs resident; warm-up (streams {streams}, layer split {split})")
 
@@ -269,21 +284,21 @@ def run(args):
                 if split > 1:
                     for (a, b), t in zip(ranges, bsl):
                         t[s].copy_(budget[s][:, a:b])
-        for k, ((a, b), v, st) in enumerate(zip(ranges, views, vstreams)):
-            with torch.cuda.stream(st):
+        for k, (v, st, (q_, k_, v_, o_, b_, lb_)) in enumerate(zip(views, vstreams, vargs[s])):
+            with (torch.cuda.stream(st) if st is not main else contextlib.nullcontext()):
                 if ev is not None:
                     ev[2 * k].record(st)
-                v.attend(-1, qs[s][a:b], ks[s][a:b], vs[s][a:b], out=out[a:b])
+                v.attend(-1, q_, k_, v_, out=o_)
                 if ev is not None:
                     ev[2 * k + 1].record(st)
                 if side is not st:
                     st.wait_stream(side)
                 if trim:
-                    v.trim_evict_compact(-1, bsl[k][s], lbetas[s][a:b])
+                    v.trim_evict_compact(-1, b_, lb_)
                 elif arkv:
-                    v.arkv_ema_evict_compact(-1, bsl[k][s], norig_v[k])
+                    v.arkv_ema_evict_compact(-1, b_, norig_v[k])
                 else:
-                    v.ema_evict_compact(-1, bsl[k][s])
+                    v.ema_evict_compact(-1, b_)
 
     for s in range(args.warmup):
         one_step(s)
