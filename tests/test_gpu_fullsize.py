@@ -15,7 +15,9 @@ The caches that start empty are checked at their first demotion into INT8, at
 the first eviction and deep into their sawtooth.  Tolerances are those of the
 small-shape parity tests.  Confidence and budgets are checked for every sequence
 at every checked step.  The steps between checked ones run the benchmark's
-launches (conf_attend, then the EMA fused into the selection + compaction).  A
+launches (conf_attend, then the EMA fused into the selection + compaction; on
+the caches whose attention launch has at least 2048 workgroups, on two layer
+halves as views of the cache on two concurrent streams, as the benchmark does).  A
 checked step runs conf_decode_attn, so that the EMA can be read before the
 selection, and then on even steps the fused selection + compaction, on odd steps
 the two separate ones; on a fused step the kept set is read off the cache after
@@ -85,11 +87,35 @@ def test_full_size_sampled_pairs(name):
                                   ema_rtol=0, what=("ingest", l, b))
         del k, v
     worst = 0.0
+    # the bench's schedule on the large caches: layer halves as two views of the
+    # cache on two concurrent streams, the confidence on a third
+    split = wl.n_layers * wl.batch * wl.n_kv_heads >= 2048 and wl.n_layers >= 2
+    if split:
+        L, h = wl.n_layers, wl.n_layers // 2
+        halves = [(0, h), (h, L)]
+        views = [eng.layer_view(a, b - a) for a, b in halves]
+        main = torch.cuda.current_stream(dev)
+        streams = [main, torch.cuda.Stream(dev)]
+        side = torch.cuda.Stream(dev)
     for step in range(max(CHECKED) + 1):
         check = step in CHECKED
         z = synth.logits(wl, step, SEED, device=dev)
         q = synth.q_new(wl, step, SEED, device=dev)
         k, v = synth.kv_new(wl, step, SEED, device=dev)
+        if not check and split:
+            for st in streams:
+                side.wait_stream(st)
+            with torch.cuda.stream(side):
+                _, budget = eng.confidence(z)
+                cols = [budget[:, a:b].contiguous() for a, b in halves]
+            for (a, b), view, st, col in zip(halves, views, streams, cols):
+                with torch.cuda.stream(st):
+                    view.attend(-1, q[a:b], k[a:b], v[a:b])
+                    st.wait_stream(side)
+                    view.ema_evict_compact(-1, col)
+            for st in (streams[1], side):
+                main.wait_stream(st)
+            continue
         if not check:
             eng.attend(-1, q, k, v)
             _, budget = eng.confidence(z)
