@@ -42,6 +42,12 @@ ranked Original tokens beyond the layer's N_O), with no confidence.
 stores the new token's ln(beta), ranks by (t - pos) * ln(beta) and compacts, with a
 16-bit cache of M = N_high tokens (the prefill cut to M) and no confidence.
 
+Besides the steady-state figures, the JSON line reports step0_ms, the one-off first
+step after the prefill (the cut of the prefilled cache to its budget), timed on its
+own during warm-up, and copy_ceiling_GBs, the best rate of a plain 2 GiB device copy
+on the same box (bytes read + written), as a measured ceiling next to the nominal
+8 TB/s.
+
 Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -300,8 +306,20 @@ def run(args):
                 else:
                     v.ema_evict_compact(-1, b_)
 
+    step0 = None
     for s in range(args.warmup):
+        if s == 0:  # the one-off step after the prefill, timed on its own
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
         one_step(s)
+        if s == 0:
+            for st in vstreams[1:]:
+                main.wait_stream(st)
+            main.wait_stream(side)
+            e1.record()
+            torch.cuda.synchronize()
+            step0 = e0.elapsed_time(e1)
         if s % 32 == 0:
             torch.cuda.synchronize()
             log(f"  warm-up step {s}")
@@ -389,6 +407,8 @@ def run(args):
         "step_roofline": {"achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(step_gbs / HBM_PEAK_GBS, 4),
                           "alg_bytes_per_step": int(sum(s_bytes) / len(s_bytes))},
+        "step0_ms": None if step0 is None else round(step0, 3),
+        "copy_ceiling_GBs": round(copy_ceiling(dev), 1),
     }
     return res, wl
 
@@ -474,6 +494,27 @@ def stored_traffic(workload):
     if vals.get("workload") != workload or vals.get("source") != attn_source_hash():
         return None
     return int(vals["bytes_per_launch"])
+
+
+def copy_ceiling(dev, mib=2048, reps=8):
+    """Measured HBM ceiling on this machine: a plain device copy (torch.neg, one read
+    and one write of `mib` MiB per launch), best of `reps` launches, in GB/s of
+    bytes read + written."""
+    n = mib * (1 << 20) // 4
+    src = torch.empty(n, device=dev).uniform_()
+    dst = torch.empty_like(src)
+    best = None
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.neg(src, out=dst)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        best = ms if best is None else min(best, ms)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n * 4 / (best * 1e-3) / 1e9
 
 
 def copy_calibration(mib, reps):
