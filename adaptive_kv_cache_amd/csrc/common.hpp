@@ -102,6 +102,16 @@ __device__ inline int8_t quant_code(float x, float s) {
   return (int8_t)(int)r;
 }
 
+// The device a host call runs on, for per-device one-time set-up (function
+// attributes are set per device); devices beyond kMaxDevices share slot 0's answer
+// and set their attributes on every call.
+constexpr int kMaxDevices = 64;
+inline int current_device_slot() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+  return dev;
+}
+
 // e4m3 code (OCP "fn" form: sign, four exponent bits with bias 7, three mantissa
 // bits, largest finite 448) of y, |y| <= 448, by round-to-nearest-even; the sign
 // bit follows y.  ARKV's Quantized state [the ARKV page, Methodology: three-state

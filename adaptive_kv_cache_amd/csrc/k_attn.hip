@@ -39,6 +39,8 @@
 // mass is formed once the softmax normaliser is final.  Otherwise (the first step
 // after a long prefill) the kernel makes two passes over the keys: the first
 // finds each head's log-sum-exp, the second forms probabilities, mass and values.
+#include <atomic>
+
 #include "ema.hpp"
 
 namespace confkv {
@@ -806,11 +808,13 @@ template <int D, bool BF16, bool FP8>
 static void launch_t(const Dims& dm, const conf_cache& c, int layer0, int nl, const void* q,
                      const void* k_new, const void* v_new, float* out, float* massp,
                      int32_t* snap, bool with_ema, hipStream_t st) {
-  static bool attr_set = false;
-  if (!attr_set) {
+  // the dynamic-LDS limit is a per-device attribute of the function: set it once per device
+  static std::atomic<bool> attr_set[kMaxDevices];
+  const int slot = current_device_slot();
+  if (slot < 0 || !attr_set[slot].load(std::memory_order_acquire)) {
     (void)hipFuncSetAttribute((const void*)attn_kernel<D, BF16, FP8>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, kLdsDynBytes);
-    attr_set = true;
+    if (slot >= 0) attr_set[slot].store(true, std::memory_order_release);
   }
   hipLaunchKernelGGL((attn_kernel<D, BF16, FP8>), dim3(nl * dm.B * dm.Hkv), dim3(kAttnThreads),
                      attn_dyn_lds(dm), st, c, dm, layer0, (const uint16_t*)q,

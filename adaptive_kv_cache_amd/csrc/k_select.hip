@@ -4,6 +4,8 @@
 // select_core (select.hpp), shared with the fused selection + compaction kernel.
 //
 // CONF-KV explainer, Methodology, token ranking and eviction.
+#include <atomic>
+
 #include "select.hpp"
 
 namespace confkv {
@@ -179,22 +181,26 @@ __global__ __launch_bounds__(kSelThreads) void joint_select_kernel(
 }
 
 // Dynamic LDS of the head-wise selection: as much of the workgroup's LDS as the
-// device allows, less the static part and a margin.
+// device allows, less the static part and a margin.  Read and set once per device.
 static int joint_dyn_bytes() {
-  static int bytes = -1;
-  if (bytes < 0) {
-    int dev = 0, max_lds = 65536;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
-            hipSuccess)
-      max_lds = 65536;
-    const int want = max_lds - 2048;  // the static part (about 500 bytes) and a margin
-    bytes = want < 32768 ? 32768 : want;
-    (void)hipFuncSetAttribute((const void*)joint_select_kernel<true>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    (void)hipFuncSetAttribute((const void*)joint_select_kernel<false>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  static std::atomic<int> bytes_of[kMaxDevices];  // 0: not yet set on that device
+  const int slot = current_device_slot();
+  if (slot >= 0) {
+    const int b = bytes_of[slot].load(std::memory_order_acquire);
+    if (b > 0) return b;
   }
+  int dev = 0, max_lds = 65536;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+          hipSuccess)
+    max_lds = 65536;
+  const int want = max_lds - 2048;  // the static part (about 500 bytes) and a margin
+  const int bytes = want < 32768 ? 32768 : want;
+  (void)hipFuncSetAttribute((const void*)joint_select_kernel<true>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  (void)hipFuncSetAttribute((const void*)joint_select_kernel<false>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (slot >= 0) bytes_of[slot].store(bytes, std::memory_order_release);
   return bytes;
 }
 
