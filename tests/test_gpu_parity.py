@@ -717,3 +717,33 @@ def test_layer_views_on_two_streams_equal_the_whole_cache(name):
                         assert np.array_equal(np.asarray(ea[key]), np.asarray(eb[key])), \
                             (step, l, s_, key)
     assert a.status() == 0 and b.status() == 0
+
+
+def test_full_window_sets_the_status_bit_and_keeps_the_cache():
+    """Full KV with a window of 64 slots and a 60-token prefill: four appends fit;
+    from the fifth step on each new token is dropped, CONF_ST_WINDOW_FULL is set, and
+    the cache keeps exactly the 64 tokens it holds (positions 0..63, bits unchanged),
+    while the attention still runs over them."""
+    from adaptive_kv_cache_amd.binding import ST_WINDOW_FULL
+    wl = TINY["gqa8_bf16_d64"].scaled(name="full_window_64", prefill=60)
+    wl = wl.baseline("full", 1).scaled(window=63, n_high=64, n_low=64)
+    _say("window full", wl.name, "W", wl.window)
+    eng = Engine(wl)
+    _ingest(eng, wl, SEED)
+    assert eng.cap16 == 64
+    for step in range(8):
+        z = synth.logits(wl, step, SEED).cuda()
+        q = synth.q_new(wl, step, SEED).cuda()
+        k, v = (x.cuda() for x in synth.kv_new(wl, step, SEED))
+        before = [eng.export(l, b) for l in range(wl.n_layers) for b in range(wl.batch)]
+        out, _, _ = eng.step(z, q, k, v)
+        assert torch.isfinite(out).all()
+        after = [eng.export(l, b) for l in range(wl.n_layers) for b in range(wl.batch)]
+        full = step >= 4
+        assert bool(eng.status() & ST_WINDOW_FULL) == full, step
+        for x0, x1 in zip(before, after):
+            assert x1["n16"] == min(60 + step + 1, 64)
+            if full:   # nothing changes once the window is full
+                for key in ("pos16", "k16", "v16"):
+                    assert np.array_equal(x0[key], x1[key]), (step, key)
+    assert sorted(after[0]["pos16"].tolist()) == list(range(64))
