@@ -149,21 +149,41 @@ constexpr int kLdsFlags8 = 4096;  // INT8 keep flags cached in LDS (beyond: glob
 constexpr int kLdsFlags16 = 2048; // window keep flags cached in LDS (beyond: workspace)
 constexpr int kLdsMoves = 2048;   // move-list pairs per region kept in LDS (beyond: workspace)
 
-struct CompFlags {  // keep flags cached in LDS
-  uint8_t k8[kLdsFlags8];
-  uint8_t k16[kLdsFlags16];
+// A compaction configuration: threads per workgroup and the LDS capacities of the
+// flag caches, move lists and grown-channel list (what does not fit goes to
+// global memory).  A workgroup spreads the 2*Hkv*d (K|V, KV head, channel)
+// triples of a demotion over its threads, at most eight each.
+template <int NT_, int F8_, int F16_, int MV_, int MG_>
+struct CompCfg {
+  static constexpr int NT = NT_, W = NT_ / 64, F8 = F8_, F16 = F16_, MV = MV_, MG = MG_;
 };
-struct CompScratch {  // move lists and the grown-channel list
-  int mv8[2 * kLdsMoves];   // (source, destination) pairs
-  int mv16[2 * kLdsMoves];
-  int grown[kMaxGrown];
-  float gold[kMaxGrown], gnew[kMaxGrown];
+// one (layer, sequence) with all its KV heads
+using CompBig = CompCfg<kCompThreads, kLdsFlags8, kLdsFlags16, kLdsMoves, kMaxGrown>;
+// one (sequence, KV head) of a head-wise cache: 2*d <= 256 triples, and little LDS,
+// so that many workgroups share a compute unit
+using CompSmall = CompCfg<128, 2048, 1024, 256, 256>;
+
+template <class C>
+struct CompFlagsT {  // keep flags cached in LDS
+  uint8_t k8[C::F8];
+  uint8_t k16[C::F16];
 };
-struct CompMisc {
-  int wcnt[2][kCompWaves];
-  int c8[kCompWaves], c16[kCompWaves];
+template <class C>
+struct CompScratchT {  // move lists and the grown-channel list
+  int mv8[2 * C::MV];   // (source, destination) pairs
+  int mv16[2 * C::MV];
+  int grown[C::MG];
+  float gold[C::MG], gnew[C::MG];
+};
+template <class C>
+struct CompMiscT {
+  int wcnt[2][C::W];
+  int c8[C::W], c16[C::W];
   int jd, ngrown, first_hole;
 };
+using CompFlags = CompFlagsT<CompBig>;
+using CompScratch = CompScratchT<CompBig>;
+using CompMisc = CompMiscT<CompBig>;
 
 // Ordered ranks of the slots of [0, max(n, nnew)) that are holes (slot < nnew,
 // not kept; slots >= n count as not kept) or survivors (slot >= nnew, kept).  The
@@ -171,13 +191,13 @@ struct CompMisc {
 // hole skip + k receives survivor k: pair k = (survivor k, hole skip + k).
 // `flag(i)` reads slot i's keep flag (i < n).  Returns the number of pairs.
 // Every thread must call it.
-template <typename Flag>
+template <class C, typename Flag>
 __device__ int build_moves(int n, int nnew, int skip, Flag flag, int* lds_mv, int32_t* gl_mv,
-                           int (*wcnt)[kCompWaves], int* first_hole) {
+                           int (*wcnt)[C::W], int* first_hole) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int end = n > nnew ? n : nnew;
   int hb = 0, sb = 0;
-  for (int c0 = 0; c0 < end; c0 += kCompThreads) {
+  for (int c0 = 0; c0 < end; c0 += C::NT) {
     const int i = c0 + tid;
     const bool k = i < n && flag(i);
     const bool hole = i < nnew && !k, surv = i >= nnew && k;
@@ -189,7 +209,7 @@ __device__ int build_moves(int n, int nnew, int skip, Flag flag, int* lds_mv, in
     }
     __syncthreads();
     int oh = 0, os = 0, th = 0, ts = 0;
-    for (int w = 0; w < kCompWaves; ++w) {
+    for (int w = 0; w < C::W; ++w) {
       const int ch = wcnt[0][w], cs = wcnt[1][w];
       oh += w < wave ? ch : 0;
       os += w < wave ? cs : 0;
@@ -200,7 +220,7 @@ __device__ int build_moves(int n, int nnew, int skip, Flag flag, int* lds_mv, in
       const int r = hb + oh + __popcll(bh & below) - skip;
       if (r < 0) {
         if (r == -skip) *first_hole = i;
-      } else if (r < kLdsMoves) {
+      } else if (r < C::MV) {
         lds_mv[2 * r + 1] = i;
       } else {
         gl_mv[2 * r + 1] = i;
@@ -208,7 +228,7 @@ __device__ int build_moves(int n, int nnew, int skip, Flag flag, int* lds_mv, in
     }
     if (surv) {
       const int r = sb + os + __popcll(bs & below);
-      if (r < kLdsMoves) lds_mv[2 * r] = i; else gl_mv[2 * r] = i;
+      if (r < C::MV) lds_mv[2 * r] = i; else gl_mv[2 * r] = i;
     }
     hb += th;
     sb += ts;
@@ -217,8 +237,9 @@ __device__ int build_moves(int n, int nnew, int skip, Flag flag, int* lds_mv, in
   return hb - skip;  // holes below the new end, less those set aside = survivors above it
 }
 
+template <class C>
 __device__ inline int mv_at(const int* lds_mv, const int32_t* gl_mv, int e) {
-  return e < 2 * kLdsMoves ? lds_mv[e] : gl_mv[e];
+  return e < 2 * C::MV ? lds_mv[e] : gl_mv[e];
 }
 
 // Steps 2-4 of the compaction for one (layer, sequence), once the keep flags are
@@ -226,9 +247,10 @@ __device__ inline int mv_at(const int* lds_mv, const int32_t* gl_mv, int e) {
 // global memory) the others; the window flag of the demotee (window slot jd, or
 // -1) is already cleared, and n8n / n16n count the kept INT8 / window tokens.
 // M.ngrown must be 0.  All kCompThreads threads call it.
+template <class C>
 __device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8, int n16, int t,
                              int n8n, int n16n, int jd, const uint8_t* keep8, const uint8_t* wkeep,
-                             CompFlags& F, CompScratch& X, CompMisc& M, int32_t* plan_all,
+                             CompFlagsT<C>& F, CompScratchT<C>& X, CompMiscT<C>& M, int32_t* plan_all,
                              int32_t* mv8_all, int32_t* mv16_all) {
 #pragma clang fp contract(off)
   const int tid = threadIdx.x;
@@ -246,12 +268,12 @@ __device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8
   // INT8 token, so nothing moves); without one it ends at n8'.
   const bool demote = jd >= 0 && n8n < dm.cap8;
   const int n8end = n8n + (demote ? 1 : 0);
-  const int nm8 = build_moves(
+  const int nm8 = build_moves<C>(
       n8, n8end, demote ? 1 : 0,
-      [&](int i) { return i < kLdsFlags8 ? F.k8[i] != 0 : keep8[i] != 0; }, X.mv8, mv8, M.wcnt,
+      [&](int i) { return i < C::F8 ? F.k8[i] != 0 : keep8[i] != 0; }, X.mv8, mv8, M.wcnt,
       &M.first_hole);
-  const int nm16 = build_moves(
-      n16, n16n, 0, [&](int w) { return w < kLdsFlags16 ? F.k16[w] != 0 : wkeep[w] != 0; },
+  const int nm16 = build_moves<C>(
+      n16, n16n, 0, [&](int w) { return w < C::F16 ? F.k16[w] != 0 : wkeep[w] != 0; },
       X.mv16, mv16, M.wcnt, &M.first_hole);
   const int dest = demote ? M.first_hole : -1;  // written by build_moves before its last barrier
   // ---- 3. INT8 moves; the demotion's reads and arithmetic; window-move reads.
@@ -260,8 +282,8 @@ __device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8
   const int per = dm.Hkv * D;
   constexpr int kMv = 2;       // move elements per thread in the register path
   constexpr int kDemPer = 8;   // (K|V, KV head, channel) triples per thread: 2*Hkv*d <= 4096 (host-checked)
-  const bool fast = nm8 * per <= kMv * kCompThreads && nm16 * per <= kMv * kCompThreads &&
-                    nm8 <= kCompThreads && nm16 <= kCompThreads;
+  const bool fast = nm8 * per <= kMv * C::NT && nm16 * per <= kMv * C::NT &&
+                    nm8 <= C::NT && nm16 <= C::NT;
   // loaded values are held widened to 32 bits: packing 8- or 16-bit values into
   // shared registers would make each load wait before the next one issues
   int32_t mk[kMv], mvv[kMv];
@@ -271,52 +293,52 @@ __device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8
   if (fast) {
 #pragma unroll
     for (int e = 0; e < kMv; ++e) {
-      const int i = tid + e * kCompThreads;
+      const int i = tid + e * C::NT;
       if (i < nm8 * per) {
         const int k = i / per, r = i % per, hk = r / D, ch = r % D;
         const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap8 * D;
-        const int src = mv_at(X.mv8, mv8, 2 * k);
+        const int src = mv_at<C>(X.mv8, mv8, 2 * k);
         mk[e] = c.k8[ub + k8_off(src, ch, D)];
         mvv[e] = c.v8[ub + v8_off(src, ch, D)];
       }
       if (i < nm16 * per) {
         const int k = i / per, r = i % per, hk = r / D, ch = r % D;
         const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap16 * D;
-        const int src = mv_at(X.mv16, mv16, 2 * k);
+        const int src = mv_at<C>(X.mv16, mv16, 2 * k);
         wk[e] = ((const uint16_t*)c.k16)[ub + k16_off(src, ch, D)];
         wv[e] = ((const uint16_t*)c.v16)[ub + v16_off(src, ch, D)];
       }
     }
     if (tid < nm8) {
-      const int src = mv_at(X.mv8, mv8, 2 * tid);
+      const int src = mv_at<C>(X.mv8, mv8, 2 * tid);
       mp8 = pos8[src];
       me8 = ema8[src];
     }
     if (tid < nm16) {
-      const int src = mv_at(X.mv16, mv16, 2 * tid);
+      const int src = mv_at<C>(X.mv16, mv16, 2 * tid);
       mp16 = pos16[src];
       me16 = ema16[src];
     }
   } else {
-    for (int k = tid; k < nm8; k += kCompThreads) {
-      const int src = mv_at(X.mv8, mv8, 2 * k), dst = mv_at(X.mv8, mv8, 2 * k + 1);
+    for (int k = tid; k < nm8; k += C::NT) {
+      const int src = mv_at<C>(X.mv8, mv8, 2 * k), dst = mv_at<C>(X.mv8, mv8, 2 * k + 1);
       pos8[dst] = pos8[src];
       ema8[dst] = ema8[src];
     }
     // Bulk moves: keys as 16-byte chunks (16 channels are contiguous in a key
     // tile), values byte by byte; the move index varies fastest, so neighbouring
     // threads read neighbouring slots of one channel (coalesced sources).
-    for (int i = tid; i < nm8 * dm.Hkv * (D / 16); i += kCompThreads) {
+    for (int i = tid; i < nm8 * dm.Hkv * (D / 16); i += C::NT) {
       const int k = i % nm8, r = i / nm8, hk = r / (D / 16), cg = r % (D / 16);
       const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap8 * D;
-      const int src = mv_at(X.mv8, mv8, 2 * k), dst = mv_at(X.mv8, mv8, 2 * k + 1);
+      const int src = mv_at<C>(X.mv8, mv8, 2 * k), dst = mv_at<C>(X.mv8, mv8, 2 * k + 1);
       *(cu4*)(c.k8 + ub + k8_off(dst, 16 * cg, D)) =
           *(const cu4*)(c.k8 + ub + k8_off(src, 16 * cg, D));
     }
-    for (int i = tid; i < nm8 * per; i += kCompThreads) {
+    for (int i = tid; i < nm8 * per; i += C::NT) {
       const int k = i % nm8, r = i / nm8, hk = r / D, ch = r % D;
       const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap8 * D;
-      const int src = mv_at(X.mv8, mv8, 2 * k), dst = mv_at(X.mv8, mv8, 2 * k + 1);
+      const int src = mv_at<C>(X.mv8, mv8, 2 * k), dst = mv_at<C>(X.mv8, mv8, 2 * k + 1);
       c.v8[ub + v8_off(dst, ch, D)] = c.v8[ub + v8_off(src, ch, D)];
     }
   }
@@ -336,8 +358,8 @@ __device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8
     float oldr[kDemPer];
 #pragma unroll
     for (int e = 0; e < kDemPer; ++e) {
-      if (e * kCompThreads >= 2 * per) break;  // uniform
-      const int pi = min(tid + e * kCompThreads, 2 * per - 1);
+      if (e * C::NT >= 2 * per) break;  // uniform
+      const int pi = min(tid + e * C::NT, 2 * per - 1);
       const int kind = pi / per, hc = pi % per, hk = hc / D, ch = hc % D;
       const size_t u = (size_t)lb * dm.Hkv + hk;
       xr[e] = kind == 0 ? ((const uint16_t*)c.k16)[u * (size_t)dm.cap16 * D + k16_off(jd, ch, D)]
@@ -346,7 +368,7 @@ __device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8
     }
 #pragma unroll
     for (int e = 0; e < kDemPer; ++e) {
-      const int pi = tid + e * kCompThreads;
+      const int pi = tid + e * C::NT;
       grew[e] = false;
       listed[e] = false;
       if (pi < 2 * per) {
@@ -360,7 +382,7 @@ __device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8
         if (a > old) {
           grew[e] = true;
           const int slot = atomicAdd(&M.ngrown, 1);
-          if (slot < kMaxGrown) {
+          if (slot < C::MG) {
             listed[e] = true;
             X.grown[slot] = pi;
             X.gold[slot] = s_old[e];
@@ -374,17 +396,17 @@ __device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8
     // INT8 stores go to holes below n8', which no load of this phase reads
 #pragma unroll
     for (int e = 0; e < kMv; ++e) {
-      const int i = tid + e * kCompThreads;
+      const int i = tid + e * C::NT;
       if (i < nm8 * per) {
         const int k = i / per, r = i % per, hk = r / D, ch = r % D;
         const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap8 * D;
-        const int dst = mv_at(X.mv8, mv8, 2 * k + 1);
+        const int dst = mv_at<C>(X.mv8, mv8, 2 * k + 1);
         c.k8[ub + k8_off(dst, ch, D)] = (int8_t)mk[e];
         c.v8[ub + v8_off(dst, ch, D)] = (int8_t)mvv[e];
       }
     }
     if (tid < nm8) {
-      const int dst = mv_at(X.mv8, mv8, 2 * tid + 1);
+      const int dst = mv_at<C>(X.mv8, mv8, 2 * tid + 1);
       pos8[dst] = mp8;
       ema8[dst] = me8;
     }
@@ -398,7 +420,7 @@ __device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8
     }
 #pragma unroll
     for (int e = 0; e < kDemPer; ++e) {
-      const int pi = tid + e * kCompThreads;
+      const int pi = tid + e * C::NT;
       if (pi < 2 * per) {
         const int kind = pi / per, hc = pi % per, hk = hc / D, ch = hc % D;
         const size_t u = (size_t)lb * dm.Hkv + hk;
@@ -411,39 +433,39 @@ __device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8
   if (fast) {
 #pragma unroll
     for (int e = 0; e < kMv; ++e) {
-      const int i = tid + e * kCompThreads;
+      const int i = tid + e * C::NT;
       if (i < nm16 * per) {
         const int k = i / per, r = i % per, hk = r / D, ch = r % D;
         const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap16 * D;
-        const int dst = mv_at(X.mv16, mv16, 2 * k + 1);
+        const int dst = mv_at<C>(X.mv16, mv16, 2 * k + 1);
         ((uint16_t*)c.k16)[ub + k16_off(dst, ch, D)] = (uint16_t)wk[e];
         ((uint16_t*)c.v16)[ub + v16_off(dst, ch, D)] = (uint16_t)wv[e];
       }
     }
     if (tid < nm16) {
-      const int dst = mv_at(X.mv16, mv16, 2 * tid + 1);
+      const int dst = mv_at<C>(X.mv16, mv16, 2 * tid + 1);
       pos16[dst] = mp16;
       ema16[dst] = me16;
     }
   } else {
-    for (int k = tid; k < nm16; k += kCompThreads) {
-      const int src = mv_at(X.mv16, mv16, 2 * k), dst = mv_at(X.mv16, mv16, 2 * k + 1);
+    for (int k = tid; k < nm16; k += C::NT) {
+      const int src = mv_at<C>(X.mv16, mv16, 2 * k), dst = mv_at<C>(X.mv16, mv16, 2 * k + 1);
       pos16[dst] = pos16[src];
       ema16[dst] = ema16[src];
     }
     // bulk window moves: keys as 16-byte chunks (8 channels), values element by
     // element, the move index fastest
-    for (int i = tid; i < nm16 * dm.Hkv * (D / 8); i += kCompThreads) {
+    for (int i = tid; i < nm16 * dm.Hkv * (D / 8); i += C::NT) {
       const int k = i % nm16, r = i / nm16, hk = r / (D / 8), cg = r % (D / 8);
       const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap16 * D;
-      const int src = mv_at(X.mv16, mv16, 2 * k), dst = mv_at(X.mv16, mv16, 2 * k + 1);
+      const int src = mv_at<C>(X.mv16, mv16, 2 * k), dst = mv_at<C>(X.mv16, mv16, 2 * k + 1);
       uint16_t* k16 = (uint16_t*)c.k16 + ub;
       *(cu4*)(k16 + k16_off(dst, 8 * cg, D)) = *(const cu4*)(k16 + k16_off(src, 8 * cg, D));
     }
-    for (int i = tid; i < nm16 * per; i += kCompThreads) {
+    for (int i = tid; i < nm16 * per; i += C::NT) {
       const int k = i % nm16, r = i / nm16, hk = r / D, ch = r % D;
       const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap16 * D;
-      const int src = mv_at(X.mv16, mv16, 2 * k), dst = mv_at(X.mv16, mv16, 2 * k + 1);
+      const int src = mv_at<C>(X.mv16, mv16, 2 * k), dst = mv_at<C>(X.mv16, mv16, 2 * k + 1);
       uint16_t* v16 = (uint16_t*)c.v16 + ub;
       v16[v16_off(dst, ch, D)] = v16[v16_off(src, ch, D)];
     }
@@ -451,8 +473,8 @@ __device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8
   if (dest >= 0) {
     // codes of every other INT8 slot of each grown channel: c = clamp(rne((c * s_old) / s_new))
     const int ng = M.ngrown;
-    const int ngl = ng < kMaxGrown ? ng : kMaxGrown;
-    for (int i = tid; i < ngl * n8end; i += kCompThreads) {
+    const int ngl = ng < C::MG ? ng : C::MG;
+    for (int i = tid; i < ngl * n8end; i += C::NT) {
       const int e = i % ngl, tok = i / ngl;
       if (tok == dest) continue;
       const int pi = X.grown[e], kind = pi / per, hc = pi % per, hk = hc / D, ch = hc % D;
@@ -465,7 +487,7 @@ __device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8
 #pragma unroll
     for (int e = 0; e < kDemPer; ++e) {
       if (!grew[e] || listed[e]) continue;
-      const int pi = tid + e * kCompThreads;
+      const int pi = tid + e * C::NT;
       const int kind = pi / per, hc = pi % per, hk = hc / D, ch = hc % D;
       int8_t* base = (kind == 0 ? c.k8 : c.v8) + ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap8 * D;
       const float s_new = amax_new[e] / cmax;
@@ -491,7 +513,8 @@ __device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8
 }
 
 // Sums per-thread counts of kept INT8 and window tokens over the workgroup.
-__device__ inline void count_kept(int c8, int c16, CompMisc& M, int& n8n, int& n16n) {
+template <class C>
+__device__ inline void count_kept(int c8, int c16, CompMiscT<C>& M, int& n8n, int& n16n) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int off = 32; off > 0; off >>= 1) {
     c8 += __shfl_xor(c8, off);
@@ -504,21 +527,22 @@ __device__ inline void count_kept(int c8, int c16, CompMisc& M, int& n8n, int& n
   __syncthreads();
   n8n = 0;
   n16n = 0;
-  for (int w = 0; w < kCompWaves; ++w) {
+  for (int w = 0; w < C::W; ++w) {
     n8n += M.c8[w];
     n16n += M.c16[w];
   }
 }
 
-__global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dims dm, int layer0,
+template <class C>
+__global__ __launch_bounds__(C::NT) void compact_kernel(conf_cache c, Dims dm, int layer0,
                                                                const uint8_t* __restrict__ keep_all,
                                                                int32_t* __restrict__ plan_all,
                                                                int32_t* __restrict__ mv8_all,
                                                                int32_t* __restrict__ mv16_all,
                                                                uint8_t* __restrict__ wkeep_all) {
-  __shared__ CompFlags F;
-  __shared__ CompScratch X;
-  __shared__ CompMisc M;
+  __shared__ CompFlagsT<C> F;
+  __shared__ CompScratchT<C> X;
+  __shared__ CompMiscT<C> M;
   const int lb = layer0 * dm.B + blockIdx.x;
   const int tid = threadIdx.x;
   const int n8 = c.n8[lb], n16 = c.n16[lb], t = c.t[lb];
@@ -536,18 +560,18 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(conf_cache c, Dim
   const int target =
       dm.policy == CONF_POLICY_FULL || dm.policy == CONF_POLICY_TRIM ? -1 : t - dm.W;
   int c8 = 0, c16 = 0;
-  for (int i = tid; i < n8; i += kCompThreads) {
+  for (int i = tid; i < n8; i += C::NT) {
     const uint8_t k = keep8[i] ? 1 : 0;
-    if (i < kLdsFlags8) F.k8[i] = k;
+    if (i < C::F8) F.k8[i] = k;
     c8 += k;
   }
-  for (int w = tid; w < n16; w += kCompThreads) {
+  for (int w = tid; w < n16; w += C::NT) {
     uint8_t k = keep16[w] ? 1 : 0;
     if (k && target >= 0 && pos16[w] == target) {
       M.jd = w;  // at most one slot holds this position
       k = 0;
     }
-    if (w < kLdsFlags16) F.k16[w] = k; else wkeep[w] = k;
+    if (w < C::F16) F.k16[w] = k; else wkeep[w] = k;
     c16 += k;
   }
   int n8n, n16n;
@@ -954,8 +978,14 @@ void launch_arkv(const Dims& dm, const conf_cache& c, int layer0, int nl, const 
 
 void launch_compact(const Dims& dm, const conf_cache& c, int layer0, int nl, const uint8_t* keep,
                     int32_t* plan, int32_t* mv8, int32_t* mv16, uint8_t* wkeep, hipStream_t st) {
-  hipLaunchKernelGGL(compact_kernel, dim3(nl * dm.B), dim3(kCompThreads), 0, st, c, dm, layer0,
-                     keep, plan, mv8, mv16, wkeep);
+  // a head-wise cache compacts one KV head per workgroup: small workgroups with
+  // little LDS, many of them resident per compute unit
+  if (dm.headwise && 2 * dm.Hkv * dm.D <= 8 * CompSmall::NT)
+    hipLaunchKernelGGL(compact_kernel<CompSmall>, dim3(nl * dm.B), dim3(CompSmall::NT), 0, st, c,
+                       dm, layer0, keep, plan, mv8, mv16, wkeep);
+  else
+    hipLaunchKernelGGL(compact_kernel<CompBig>, dim3(nl * dm.B), dim3(CompBig::NT), 0, st, c, dm,
+                       layer0, keep, plan, mv8, mv16, wkeep);
 }
 
 void launch_evict(const Dims& dm, const conf_cache& c, int layer0, int nl, const int32_t* budget,
