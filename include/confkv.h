@@ -275,7 +275,12 @@ int conf_attend(const conf_params* p, conf_cache* c, int32_t layer, const void* 
  * keep the positions (t-P, t] and the N - |protected| best other tokens in the
  * order (score desc, position desc), score = s_ema*(e/e_max) + s_rec*(pos/t),
  * evaluated in fp32 one rounding per operation (e/e_max = 0 if e_max = 0;
- * pos/t = 1 if t = 0).
+ * pos/t = 1 if t = 0).  Under the other policies the policy's own rule decides
+ * (see the policies above): full KV keeps every token, the sliding window the
+ * positions (t-W, t], retention eviction ranks by (t - pos) * ln(beta), ARKV by
+ * its score EMA.
+ * Head-wise, the keep flags are those of the joint selection over the heads of
+ * each (layer, sequence), keep [L][B*Hkv][cap8 + cap16].
  */
 int conf_rank_evict(const conf_params* p, conf_cache* c, int32_t layer, const int32_t* budget,
                     uint8_t* keep, void* ws, conf_stream_t stream);
@@ -287,7 +292,8 @@ int conf_rank_evict(const conf_params* p, conf_cache* c, int32_t layer, const in
  * t - W, if it survived, from the window to INT8: per (KV head, channel)
  * a = |x|; if a > absmax the channel's stored codes become
  * clamp(rne((code*s_old)/s_new)) and absmax = a; then code = clamp(rne(x/s)),
- * s = absmax/127 (s = 0 gives code 0).
+ * s = absmax/127 (s = 0 gives code 0).  Full KV and retention eviction demote
+ * nothing; under ARKV (which demotes by rank) the call returns CONF_E_INVALID.
  */
 int conf_compact_demote(const conf_params* p, conf_cache* c, int32_t layer, const uint8_t* keep,
                         void* ws, conf_stream_t stream);
