@@ -236,7 +236,9 @@ def test_conf_step_equals_the_four_calls(name):
 @pytest.mark.parametrize("name", ["gqa5_bf16_d128", "mha_f16_d64"])
 def test_rank_evict_budget_sweep(name):
     """Selection alone against the oracle, bit-exact, for budgets that evict 1 .. 40
-    tokens (a few evictions take minimum rounds, more take the radix select)."""
+    tokens (a few evictions take minimum rounds, more take the radix select), for a
+    budget of exactly the protected window and one more, and for budgets the cache
+    is already within."""
     wl = TINY[name]
     prm = oracle_params(wl)
     eng = Engine(wl)
@@ -249,8 +251,13 @@ def test_rank_evict_budget_sweep(name):
     S = _snap(eng, wl)
     ntok = (eng.t_n8 + eng.t_n16).cpu().numpy()
     cap8 = eng.cap8
-    for e in (1, 2, 3, 5, 8, 9, 17, 40):
-        budget = np.ascontiguousarray((ntok - e).T).astype(np.int32)
+    P = wl.protect
+    cases = [ntok - e for e in (1, 2, 3, 5, 8, 9, 17, 40)]
+    # the degenerate budgets: only the protected window (K = 0), one more, and
+    # budgets the cache is within (a no-op)
+    cases += [np.full_like(ntok, P), np.full_like(ntok, P + 1), ntok, ntok + 5]
+    for bud in cases:
+        budget = np.ascontiguousarray(bud.T).astype(np.int32)
         keep = eng.rank_evict(-1, torch.from_numpy(budget).cuda()).cpu().numpy()
         for l in range(wl.n_layers):
             for b in range(wl.batch):
@@ -259,8 +266,8 @@ def test_rank_evict_budget_sweep(name):
                                             prm.s_ema, prm.s_rec)
                 kr = O.select_keep(scores, st.pos, st.t, prm.protect, int(budget[b, l]))
                 got = kept_positions(S[l][b], keep[l, b], cap8)
-                assert got == set(st.pos[kr].tolist()), (e, l, b)
-                assert len(got) == int(budget[b, l])
+                assert got == set(st.pos[kr].tolist()), (int(budget[b, l]), l, b)
+                assert len(got) == min(int(budget[b, l]), st.n)
 
 
 @pytest.mark.parametrize("policy", ["full", "window"])
