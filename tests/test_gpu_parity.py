@@ -154,12 +154,13 @@ def _teacher_forced(wl, steps, seed=SEED):
     return worst
 
 
+@pytest.mark.parametrize("seed", [SEED, 99])
 @pytest.mark.parametrize("name", list(TINY))
-def test_teacher_forced_steps(name):
+def test_teacher_forced_steps(name, seed):
     wl = TINY[name]
     steps = 150 if wl.prefill == 0 else 12
-    _say("teacher-forced", name, steps)
-    worst = _teacher_forced(wl, steps)
+    _say("teacher-forced", name, steps, "seed", seed)
+    worst = _teacher_forced(wl, steps, seed)
     _say("  worst attention rel err", worst)
 
 
