@@ -755,3 +755,34 @@ def test_full_window_sets_the_status_bit_and_keeps_the_cache():
                 for key in ("pos16", "k16", "v16"):
                     assert np.array_equal(x0[key], x1[key]), (step, key)
     assert sorted(after[0]["pos16"].tolist()) == list(range(64))
+
+
+@pytest.mark.parametrize("name,policy", [("gqa5_bf16_d128", "confkv"), ("gqa8_bf16_d64", "trim"),
+                                         ("mha16_f16_d128", "window")])
+def test_ingest_all_layers_at_once(name, policy):
+    """conf_cache_ingest (and conf_cache_set_retention) with layer = -1, every
+    layer in one launch from [L][B][Hkv][L0][d], leaves exactly the cache of the
+    per-layer calls."""
+    base = TINY[name].scaled(name=name + "_3l", n_layers=3)
+    wl = base if policy == "confkv" else base.baseline(policy, 4)
+    _say("ingest all layers", wl.name)
+    a, b = Engine(wl), Engine(wl)
+    ks, vs, lbs = [], [], []
+    for l in range(wl.n_layers):
+        k, v = synth.prefill_kv(wl, l, SEED, device="cuda")
+        a.ingest(l, k, v)
+        ks.append(k)
+        vs.append(v)
+        if policy == "trim":
+            lb = synth.log_beta_prefill(wl, l, SEED, device="cuda")
+            a.set_retention(l, lb)
+            lbs.append(lb)
+    b.ingest(-1, torch.stack(ks).contiguous(), torch.stack(vs).contiguous())
+    if policy == "trim":
+        b.set_retention(-1, torch.stack(lbs).contiguous())
+    for l in range(wl.n_layers):
+        for s_ in range(wl.batch):
+            ea, eb = a.export(l, s_), b.export(l, s_)
+            for key in ea:
+                assert np.array_equal(np.asarray(ea[key]), np.asarray(eb[key])), (l, s_, key)
+    assert a.status() == 0 and b.status() == 0
