@@ -151,8 +151,9 @@ class Engine:
         self.n_sub = S
         self.t_k8 = torch.zeros(U * self.cap8 * D, dtype=torch.int8, device=dev)
         self.t_v8 = torch.zeros_like(self.t_k8)
-        self.t_k16 = torch.zeros(U * self.cap16 * D, dtype=torch.int16, device=dev)
-        self.t_v16 = torch.zeros_like(self.t_k16)
+        # the reset below zeroes the window arrays itself
+        self.t_k16 = torch.empty(U * self.cap16 * D, dtype=torch.int16, device=dev)
+        self.t_v16 = torch.empty_like(self.t_k16)
         self.t_k_amax = torch.zeros(L, B, Hkv, D, dtype=torch.float32, device=dev)
         self.t_v_amax = torch.zeros_like(self.t_k_amax)
         self.t_pos8 = torch.zeros(L, S, self.cap8, dtype=torch.int32, device=dev)

@@ -13,7 +13,8 @@ int conf_vchunks(int V);
 void launch_confidence(const Dims&, const float*, float*, float*, int32_t*, hipStream_t);
 void launch_reset(const Dims&, const conf_cache&, hipStream_t);
 void launch_attn(const Dims&, const conf_cache&, int, int, const void*, const void*, const void*,
-                 float*, float*, int32_t*, bool, hipStream_t);
+                 float*, float*, int32_t*, float*, bool, hipStream_t);
+size_t attn_spill_bytes(const Dims&);
 void launch_ingest(const Dims&, const conf_cache&, int, int, int, const void*, const void*,
                    hipStream_t);
 void launch_select(const Dims&, const conf_cache&, int, int, const int32_t*, uint8_t*, hipStream_t);
@@ -122,8 +123,6 @@ WsMap make_ws(const Dims& d) {
   off = align256(off + (size_t)d.B * w.n_vchunks * 8 * sizeof(float));
   w.massp = off;
   off = align256(off + LB * d.Hkv * d.capt * sizeof(float));
-  w.lse = off;
-  off = align256(off + LB * d.Hq * sizeof(float));
   w.keep = off;
   off = align256(off + LB * d.capt);
   w.plan = off;
@@ -136,6 +135,9 @@ WsMap make_ws(const Dims& d) {
   off = align256(off + LB * d.cap16);
   w.snap = off;
   off = align256(off + LB * 3 * sizeof(int32_t));
+  const size_t spill = attn_spill_bytes(d);
+  w.spill = spill ? off : 0;
+  off = align256(off + spill);
   w.total = off;
   return w;
 }
@@ -144,6 +146,9 @@ template <typename T>
 T* at(void* ws, size_t off) {
   return (T*)((char*)ws + off);
 }
+
+// The attention's score rows beyond LDS, or null where no cache can need them.
+float* spill_rows(void* ws, const WsMap& w) { return w.spill ? at<float>(ws, w.spill) : nullptr; }
 
 // The per-sequence dimensions (logits, confidence and budgets are per sequence
 // also when the cache is kept per KV head).
@@ -274,7 +279,7 @@ static int decode_attn(const conf_params* p, conf_cache* c, int32_t layer, const
     return CONF_E_INVALID;
   const WsMap w = make_ws(d);
   launch_attn(d, *c, l0, nl, q, k_new, v_new, out, at<float>(ws, w.massp), at<int32_t>(ws, w.snap),
-              with_ema, (hipStream_t)stream);
+              spill_rows(ws, w), with_ema, (hipStream_t)stream);
   return check_launch(name);
 }
 
@@ -417,13 +422,13 @@ int conf_step(const conf_params* p, conf_cache* c, const float* logits, const vo
   hipStream_t st = (hipStream_t)stream;
   if (d.headwise) {
     launch_attn(d, *c, 0, d.L, q, k_new, v_new, out, at<float>(ws, w.massp),
-                at<int32_t>(ws, w.snap), true, st);
+                at<int32_t>(ws, w.snap), spill_rows(ws, w), true, st);
     launch_confidence(seq_dims(d), logits, at<float>(ws, w.conf_part), conf, budget, st);
     headwise_evict(d, *c, 0, d.L, budget, ws, w, false, st);
     return check_launch("conf_step");
   }
   launch_attn(d, *c, 0, d.L, q, k_new, v_new, out, at<float>(ws, w.massp), at<int32_t>(ws, w.snap),
-              false, st);
+              spill_rows(ws, w), false, st);
   launch_confidence(d, logits, at<float>(ws, w.conf_part), conf, budget, st);
   launch_evict(d, *c, 0, d.L, budget, at<uint8_t>(ws, w.keep), at<int32_t>(ws, w.plan),
                at<int32_t>(ws, w.mv8), at<int32_t>(ws, w.mv16), at<uint8_t>(ws, w.wkeep),

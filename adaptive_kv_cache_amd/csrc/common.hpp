@@ -31,13 +31,13 @@ struct Dims {
 struct WsMap {
   size_t conf_part;   // float [B][n_vchunks][8]
   size_t massp;       // float [L][B][Hkv][capt]  per-KV-head attention mass
-  size_t lse;         // float [L][B][Hq]         log-sum-exp per query head
   size_t keep;        // uint8 [L][B][capt]       keep flags of conf_step
   size_t plan;        // int32 [L][B][16]         compaction plan
   size_t mv8;         // int32 [L][B][cap8]       (src, dst) pairs, INT8 region
   size_t mv16;        // int32 [L][B][cap16]      (src, dst) pairs, window
   size_t wkeep;       // uint8 [L][B][cap16]      window keep flags minus the demotee
   size_t snap;        // int32 [L][B][3]          (n8, n16, t) before the step's append
+  size_t spill;       // float [L][B][Hkv][G][capt] scores beyond the attention's LDS rows
   size_t total;
   int n_vchunks;      // vocab chunks per sequence in the confidence reduction
 };

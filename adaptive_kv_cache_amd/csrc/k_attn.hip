@@ -35,10 +35,13 @@
 // windows.  Accumulation is fp32 throughout.  The INT8 value scale multiplies the
 // accumulator once, between a wavefront's INT8 items and its window items.
 //
-// Scores of the whole unit stay in LDS (fp32) when they fit, and the per-token
-// mass is formed once the softmax normaliser is final.  Otherwise (the first step
-// after a long prefill) the kernel makes two passes over the keys: the first
-// finds each head's log-sum-exp, the second forms probabilities, mass and values.
+// One pass over the keys and values in every case.  The raw scores of the unit
+// (fp32) are kept for the per-token mass, which is formed once the softmax
+// normaliser is final: in LDS while they fit, and from the first item that does
+// not fit on (a cache longer than the LDS rows, such as the first steps after a
+// long prefill) in per-unit rows of the workspace.  That costs 4*g bytes per
+// token written and read back, against the 2*d (INT8) or 4*d (16-bit) bytes of
+// keys and values the unit streams for it.
 #include <atomic>
 
 #include "ema.hpp"
@@ -55,9 +58,10 @@ constexpr int kWaves = 4;
 constexpr int kAttnThreads = kWaves * 64;
 constexpr int kLdsDynBytes = 76 * 1024;  // dynamic LDS of one workgroup (two fit a CU)
 
-// ONLINE: one pass, scores kept in LDS for the mass; LSE + FINAL: two passes when
-// they do not fit; PLAIN: one pass for a policy that needs no mass.
-enum { MODE_ONLINE = 0, MODE_LSE = 1, MODE_FINAL = 2, MODE_PLAIN = 3 };
+// ONLINE: scores kept in LDS for the mass; SPILL: the same, with the items from
+// the first one that does not fit in LDS writing their scores to the workspace;
+// PLAIN: no scores kept, for a policy that needs no mass.
+enum { MODE_ONLINE = 0, MODE_SPILL = 1, MODE_PLAIN = 2 };
 
 __device__ inline f4 mma_f16(h8 a, h8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -267,6 +271,10 @@ __device__ inline void pv_i8(const Buf<D>& R, const float p[4][4], f4* o) {
   }
 }
 
+// O += P . V over a window half.  Slots past the item's end meet p = 0; their
+// values are read too, so they must be finite (0 * NaN is NaN in the matrix
+// core): conf_cache_reset zeroes the window, and every later write stores a
+// caller-supplied or moved value.  (8-bit codes always convert to finite values.)
 template <int D, bool BF16>
 __device__ inline void pv_16(const Buf<D>& R, const float p[2][4], f4* o) {
   if constexpr (BF16) {
@@ -319,14 +327,24 @@ __device__ inline float wave_max(float x) {
   return x;
 }
 
-// Softmax bookkeeping of one item with R row blocks (R = 4 INT8, 2 window).
-// MODE_ONLINE: update the running (max, sum), store the scores, rescale O, fill p.
-// MODE_LSE:    update the running (max, sum) only.
-// MODE_FINAL:  p = exp(score - lse); write the group mass of each token.
+// Where a unit's raw scores go: LDS rows [G][stride] indexed by the unit's token
+// index for the items before token `jsp`, and from there on the workspace rows
+// [G][capt] fp32, indexed by slot like the mass rows (INT8 slot i at i, window
+// slot w at cap8 + w), so that every stored row block is 16-byte aligned.
+struct ScoreSink {
+  float* lds;
+  int stride;
+  rsrc_t spill;
+  int capt;
+  int jsp;
+};
+
+// Softmax bookkeeping of one item with R row blocks (R = 4 INT8, 2 window):
+// update the running (max, sum), keep the scores (MODE_ONLINE, MODE_SPILL),
+// rescale O and fill p.
 template <int R, int MODE, int D>
 __device__ inline void softmax_item(const f4* acc, float scale, bool head_ok, const Item& I,
-                                    WaveAcc<D>& wa, float* sc, int stride, float lse, float* massp,
-                                    float p[R][4]) {
+                                    WaveAcc<D>& wa, const ScoreSink& sk, float p[R][4]) {
   const int lane = threadIdx.x & 63, g = lane >> 4, h = lane & 15;
   float sig[R][4];
   float mloc = -INFINITY;
@@ -338,54 +356,58 @@ __device__ inline void softmax_item(const f4* acc, float scale, bool head_ok, co
       sig[r][i] = (head_ok && tk < I.n_valid) ? acc[r][i] * scale : -INFINITY;
       mloc = fmaxf(mloc, sig[r][i]);
     }
-  if constexpr (MODE == MODE_FINAL) {
+  const float mnew = fmaxf(wa.m, head_max(mloc));
+  const float corr = wa.m > -INFINITY ? __expf(wa.m - mnew) : 0.f;
+  float lsum = 0.f;
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+  for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[r][i] = sig[r][i] > -INFINITY ? __expf(sig[r][i] - lse) : 0.f;
-        const float s = group_sum(p[r][i]);
-        const int tk = 16 * r + 4 * g + i;
-        if (h == 0 && tk < I.n_valid) massp[I.mass0 + tk] = s;
-      }
-  } else {
-    const float mnew = fmaxf(wa.m, head_max(mloc));
-    const float corr = wa.m > -INFINITY ? __expf(wa.m - mnew) : 0.f;
-    float lsum = 0.f;
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[r][i] = sig[r][i] > -INFINITY ? __expf(sig[r][i] - mnew) : 0.f;
-        lsum += p[r][i];
-      }
-    wa.l = wa.l * corr + head_sum(lsum);
-    wa.m = mnew;
-    if constexpr (MODE == MODE_ONLINE || MODE == MODE_PLAIN) {
-      if (MODE == MODE_ONLINE && head_ok) {
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int tk = 16 * r + 4 * g + i;
-            if (tk < I.n_valid) sc[h * stride + I.tok0 + tk] = sig[r][i];
-          }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float ci = __shfl(corr, 4 * g + i);
-#pragma unroll
-        for (int cb = 0; cb < D / 16; ++cb) wa.o[cb][i] *= ci;
-      }
+    for (int i = 0; i < 4; ++i) {
+      p[r][i] = sig[r][i] > -INFINITY ? __expf(sig[r][i] - mnew) : 0.f;
+      lsum += p[r][i];
     }
+  wa.l = wa.l * corr + head_sum(lsum);
+  wa.m = mnew;
+  if constexpr (MODE != MODE_PLAIN) {
+    const bool to_lds = MODE == MODE_ONLINE || I.tok0 < sk.jsp;  // wave-uniform
+    if (to_lds && head_ok) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tk = 16 * r + 4 * g + i;
+          if (tk < I.n_valid) sk.lds[h * sk.stride + I.tok0 + tk] = sig[r][i];
+        }
+    }
+    if constexpr (MODE == MODE_SPILL) {
+      // one 16-byte store per row block: this lane's four tokens of its head.
+      // Every item issues them; those of an item kept in LDS and of padding heads
+      // go to an offset past the rows' range and are dropped, so no branch
+      // surrounds a store and the wait counts of the loads in flight stay exact.
+      // Tokens past the item's end store -inf into their own (unused) slots.
+      const uint32_t base =
+          (!to_lds && head_ok) ? 4u * (uint32_t)(h * sk.capt + I.mass0 + 4 * g) : kNoItem;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            (u4){__float_as_uint(sig[r][0]), __float_as_uint(sig[r][1]),
+                 __float_as_uint(sig[r][2]), __float_as_uint(sig[r][3])},
+            sk.spill, (int)(base + 64u * r), 0, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float ci = __shfl(corr, 4 * g + i);
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb) wa.o[cb][i] *= ci;
   }
 }
 
 template <int D, bool BF16, int MODE, bool FP8>
 __device__ inline void compute_item(const Item& I, Buf<D>& K, const Buf<D>& V,
                                     const QOps<D, BF16>& q, float scale8, float scale16,
-                                    bool head_ok, WaveAcc<D>& wa, float* sc, int stride, float lse,
-                                    float* massp, rsrc_t kr, uint32_t koff, int klane) {
+                                    bool head_ok, WaveAcc<D>& wa, const ScoreSink& sk, rsrc_t kr,
+                                    uint32_t koff, int klane) {
   // Re-read the query operands from LDS for every item instead of letting the
   // compiler hoist 48 registers' worth of them out of the item loop.
   QOps<D, BF16> ql = q;
@@ -395,17 +417,17 @@ __device__ inline void compute_item(const Item& I, Buf<D>& K, const Buf<D>& V,
     scores_i8<D, BF16, FP8>(K, ql, acc);
     load_run_rs<D>(kr, koff, klane, K);  // the keys are used: the next item's start loading
     float p[4][4];
-    softmax_item<4, MODE, D>(acc, scale8, head_ok, I, wa, sc, stride, lse, massp, p);
+    softmax_item<4, MODE, D>(acc, scale8, head_ok, I, wa, sk, p);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (MODE != MODE_LSE) pv_i8<D, FP8>(V, p, wa.o);
+    pv_i8<D, FP8>(V, p, wa.o);
   } else {
     f4 acc[2];
     scores_16<D, BF16>(K, ql, acc);
     load_run_rs<D>(kr, koff, klane, K);
     float p[2][4];
-    softmax_item<2, MODE, D>(acc, scale16, head_ok, I, wa, sc, stride, lse, massp, p);
+    softmax_item<2, MODE, D>(acc, scale16, head_ok, I, wa, sk, p);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (MODE != MODE_LSE) pv_16<D, BF16>(V, p, wa.o);
+    pv_16<D, BF16>(V, p, wa.o);
   }
 }
 
@@ -447,37 +469,42 @@ struct UnitRs {
 template <int D, bool BF16, int MODE, bool FP8>
 __device__ inline void wave_pass(int nitems, int nb8, int n8, int nw, int cap8, const UnitRs& rs,
                                  const QOps<D, BF16>& q, float scale8, float scale16, bool head_ok,
-                                 WaveAcc<D>& wa, bool& vscaled, const float* sv, float* sc,
-                                 int stride, float lse, float* massp, Buf<D>& kb, bool preloaded) {
+                                 WaveAcc<D>& wa, bool& vscaled, const float* sv,
+                                 const ScoreSink& sk, Buf<D>& kb) {
   // wave-uniform, so that the descriptor choice per item is a scalar select
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   if (wave >= nitems) return;
   const int klane = 16 * lane, vlane = 16 * D * (lane >> 4) + 16 * (lane & 15);
   const uint32_t ib = (uint32_t)kTile * D;  // bytes per item in every region
-  if (!preloaded)
-    load_run_rs<D>(wave < nb8 ? rs.k8 : rs.k16, (uint32_t)(wave < nb8 ? wave : wave - nb8) * ib,
-                   klane, kb);
   Buf<D> V;
   int it = wave;
   for (;;) {
-    if constexpr (MODE != MODE_LSE)
-      load_run_rs<D, 256>(it < nb8 ? rs.v8 : rs.v16, (uint32_t)(it < nb8 ? it : it - nb8) * ib,
-                          vlane, V);
+    load_run_rs<D, 256>(it < nb8 ? rs.v8 : rs.v16, (uint32_t)(it < nb8 ? it : it - nb8) * ib,
+                        vlane, V);
     const int nx = it + kWaves;
-    if constexpr (MODE != MODE_LSE) {
-      if (it >= nb8 && !vscaled) {
-        apply_vscale<D>(wa, sv);
-        vscaled = true;
-      }
+    if (it >= nb8 && !vscaled) {
+      apply_vscale<D>(wa, sv);
+      vscaled = true;
     }
     compute_item<D, BF16, MODE, FP8>(item_of(it, nb8, n8, nw, cap8), kb, V, q, scale8, scale16,
-                                head_ok, wa, sc, stride, lse, massp, nx < nb8 ? rs.k8 : rs.k16,
-                                nx < nitems ? (uint32_t)(nx < nb8 ? nx : nx - nb8) * ib : kNoItem,
-                                klane);
+                                     head_ok, wa, sk, nx < nb8 ? rs.k8 : rs.k16,
+                                     nx < nitems ? (uint32_t)(nx < nb8 ? nx : nx - nb8) * ib
+                                                 : kNoItem,
+                                     klane);
     it = nx;
     if (it >= nitems) break;
   }
+}
+
+// First unit token whose item keeps its scores in the workspace rather than in
+// LDS rows of `cap` tokens: INT8 block i ends at 64(i+1) and window half j at
+// n8 + 32(j+1), and an item stays in LDS when it ends at or before `cap`.  Every
+// item from that one on spills, so the LDS holds tokens [0, jsp) and the
+// workspace rows the rest.
+__host__ __device__ inline int spill_start(int n8, int cap) {
+  const int c64 = cap & ~63;
+  return n8 > c64 ? c64 : n8 + ((cap - n8) & ~31);
 }
 
 // One workgroup per unit.  The unit of KV head 0 also records the (layer,
@@ -488,9 +515,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     conf_cache c, Dims dm, int layer0, const uint16_t* __restrict__ q_all,
     const uint16_t* __restrict__ knew_all, const uint16_t* __restrict__ vnew_all,
     float* __restrict__ out_all, float* __restrict__ massp_all, int32_t* __restrict__ snap,
-    int score_cap) {
+    float* __restrict__ spill_all, int score_cap) {
   // Dynamic LDS: the query operands, the O merge buffer [4][G][D], and the
   // scores [G][stride] (apart, so that the O merge runs beside the mass pass).
+  // Scores beyond the LDS rows go to spill_all [L][B][Hkv][G][capt].
   extern __shared__ float dyn_lds[];
   u4* s_qops = (u4*)dyn_lds;
   float* ob = dyn_lds + 4 * qops_u4<D>(dm.G);
@@ -557,8 +585,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
   const int nitems = nb8 + (nw + 31) / 32;
   // CONF-KV and ARKV rank on each token's attention mass; the baselines do not
   const bool mass = dm.policy == CONF_POLICY_CONFKV || dm.policy == CONF_POLICY_ARKV;
-  const bool in_lds = mass && n <= score_cap;
-  const bool one_pass = in_lds || !mass;
+  const int nc = n8 + nw;  // cached tokens (this step's token is handled apart)
+  const int jsp = min(spill_start(n8, score_cap), nc);
+  const ScoreSink sink{smem, stride,
+                       make_rsrc(spill_all + u * (size_t)G * dm.capt,
+                                 mass && spill_all ? (uint32_t)(G * dm.capt * 4) : 0u),
+                       dm.capt, jsp};
   // the speculative keys are this wavefront's first item unless the INT8 part is short
   if (wave < nitems && wave >= nb8)
     load_run_rs<D>(urs.k16, (uint32_t)(wave - nb8) * ib, 16 * lane, cur);
@@ -645,32 +677,25 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
   for (int cb = 0; cb < D / 16; ++cb) wa.o[cb] = (f4){0.f, 0.f, 0.f, 0.f};
   bool vscaled = false;
 
-  if (in_lds) {
-    wave_pass<D, BF16, MODE_ONLINE, FP8>(nitems, nb8, n8, nw, dm.cap8, urs, q, scale8,
-                                     scale16, head_ok, wa, vscaled, s_sv, smem, stride, 0.f, nullptr,
-                                     cur, true);
-    if (appended && tid < G) smem[tid * stride + n - 1] = s_snew[tid];
-  } else if (!mass) {
-    wave_pass<D, BF16, MODE_PLAIN, FP8>(nitems, nb8, n8, nw, dm.cap8, urs, q, scale8,
-                                    scale16, head_ok, wa, vscaled, s_sv, nullptr, 0, 0.f, nullptr,
-                                    cur, true);
-  } else {
-    wave_pass<D, BF16, MODE_LSE, FP8>(nitems, nb8, n8, nw, dm.cap8, urs, q, scale8,
-                                  scale16, head_ok, wa, vscaled, s_sv, nullptr, 0, 0.f, nullptr,
-                                  cur, true);
-  }
-  // ---- merge the waves' running (max, sum) and add this step's token.  On the
-  // single-pass path each wavefront's O (value scale applied, not yet normalised)
-  // goes to LDS before the barrier, and the O merge shares a phase with the mass.
+  if (!mass)
+    wave_pass<D, BF16, MODE_PLAIN, FP8>(nitems, nb8, n8, nw, dm.cap8, urs, q, scale8, scale16,
+                                        head_ok, wa, vscaled, s_sv, sink, cur);
+  else if (jsp >= nc)
+    wave_pass<D, BF16, MODE_ONLINE, FP8>(nitems, nb8, n8, nw, dm.cap8, urs, q, scale8, scale16,
+                                         head_ok, wa, vscaled, s_sv, sink, cur);
+  else
+    wave_pass<D, BF16, MODE_SPILL, FP8>(nitems, nb8, n8, nw, dm.cap8, urs, q, scale8, scale16,
+                                        head_ok, wa, vscaled, s_sv, sink, cur);
+  // ---- merge the waves' running (max, sum) and add this step's token.  Each
+  // wavefront's O (value scale applied, not yet normalised) goes to LDS before
+  // the barrier, and the O merge shares a phase with the mass.
   if (lane < 16) {
     s_m[wave][lane] = wa.m;
     s_l[wave][lane] = wa.l;
   }
-  if (one_pass) {
-    if (!vscaled) apply_vscale<D>(wa, s_sv);
-    store_o<D>(wa, ob, G);
-  }
-  __syncthreads();
+  if (!vscaled) apply_vscale<D>(wa, s_sv);
+  store_o<D>(wa, ob, G);
+  __syncthreads();  // also orders the spilled scores before their reads below
   if (tid < G) {
     float M = -INFINITY;
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][tid]);
@@ -688,15 +713,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
   __syncthreads();
 
   float* out = out_all + ((size_t)lbl * dm.Hq + (size_t)hk * G) * D;
-  if (one_pass) {
-    // per-token mass of this query group from the stored scores: four tokens per
-    // thread, the scores of four heads read from LDS together (an index past the
-    // end reads the last token and is not stored)
-    for (int j0 = tid; in_lds && j0 < n; j0 += 4 * kAttnThreads) {
+  if (mass) {
+    // Per-token mass of this query group from the stored scores, summed over the
+    // heads in order: four tokens per thread, the scores of four heads read
+    // together (an index past the end reads the last token and is not stored).
+    // Tokens [0, jsp) from the LDS rows, the rest from the workspace rows.
+    const int nl = jsp;
+    for (int j0 = tid; j0 < nl; j0 += 4 * kAttnThreads) {
       float s[4] = {0.f, 0.f, 0.f, 0.f};
       int jj[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) jj[k] = min(j0 + k * kAttnThreads, n - 1);
+      for (int k = 0; k < 4; ++k) jj[k] = min(j0 + k * kAttnThreads, nl - 1);
       int h = 0;
       for (; h + 4 <= G; h += 4) {
         float x[4][4];
@@ -720,36 +747,55 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int j = j0 + k * kAttnThreads;
-        if (j < n) massp[j < n8 ? j : dm.cap8 + (j - n8)] = s[k];
+        if (j < nl) massp[j < n8 ? j : dm.cap8 + (j - n8)] = s[k];
       }
     }
-    // O = sum over wavefronts of O_w * exp(m_w - lse), plus this step's token
-    for (int i = tid; i < G * D; i += kAttnThreads) {
-      const int hh = i / D, ch = i % D;
-      float s = 0.f;
-      for (int w = 0; w < kWaves; ++w) s += ob[(w * G + hh) * D + ch] * s_f[w][hh];
-      out[i] = fmaf(s_pnew[hh], s_vn[ch], s);
+    const float* sp = spill_all + u * (size_t)G * dm.capt;
+    for (int j0 = nl + tid; j0 < nc; j0 += 4 * kAttnThreads) {
+      float s[4] = {0.f, 0.f, 0.f, 0.f};
+      int sl[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int j = min(j0 + k * kAttnThreads, nc - 1);
+        sl[k] = j < n8 ? j : dm.cap8 + (j - n8);
+      }
+      int h = 0;
+      for (; h + 4 <= G; h += 4) {
+        float x[4][4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) x[e][k] = sp[(size_t)(h + e) * dm.capt + sl[k]];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float l = s_lse[h + e];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) s[k] += __expf(x[e][k] - l);
+        }
+      }
+      for (; h < G; ++h) {
+        const float l = s_lse[h];
+        const float* row = sp + (size_t)h * dm.capt;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) s[k] += __expf(row[sl[k]] - l);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (j0 + k * kAttnThreads < nc) massp[sl[k]] = s[k];
     }
-  } else {
-    // second pass: probabilities with the final normaliser, mass and values
-    const float lse = head_ok ? s_lse[hl] : 0.f;
-    wave_pass<D, BF16, MODE_FINAL, FP8>(nitems, nb8, n8, nw, dm.cap8, urs, q, scale8,
-                                    scale16, head_ok, wa, vscaled, s_sv, nullptr, 0, lse, massp,
-                                    cur, false);
-    if (appended && tid == 0) {
+    // this step's token, from its score in registers (same sums, same order)
+    if (appended && tid == kAttnThreads - 1) {
       float s = 0.f;
-      for (int h = 0; h < G; ++h) s += s_pnew[h];
+      for (int h = 0; h < G; ++h) s += __expf(s_snew[h] - s_lse[h]);
       massp[dm.cap8 + nw] = s;
     }
-    if (!vscaled) apply_vscale<D>(wa, s_sv);
-    store_o<D>(wa, ob, G);
-    __syncthreads();
-    for (int i = tid; i < G * D; i += kAttnThreads) {
-      const int hh = i / D, ch = i % D;
-      float s = 0.f;
-      for (int w = 0; w < kWaves; ++w) s += ob[(w * G + hh) * D + ch];
-      out[i] = fmaf(s_pnew[hh], s_vn[ch], s);
-    }
+  }
+  // O = sum over wavefronts of O_w * exp(m_w - lse), plus this step's token
+  for (int i = tid; i < G * D; i += kAttnThreads) {
+    const int hh = i / D, ch = i % D;
+    float s = 0.f;
+    for (int w = 0; w < kWaves; ++w) s += ob[(w * G + hh) * D + ch] * s_f[w][hh];
+    out[i] = fmaf(s_pnew[hh], s_vn[ch], s);
   }
 }
 
@@ -798,6 +844,15 @@ int attn_score_cap(const Dims& dm) {
   return cap < dm.capt + 2 ? cap : dm.capt + 2;
 }
 
+// Workspace rows for the scores a unit cannot keep in LDS: [U][G][capt] fp32, needed
+// by the policies that rank on attention mass once a cache may outgrow the LDS rows
+// (a cache of at most score_cap tokens never spills).
+size_t attn_spill_bytes(const Dims& dm) {
+  const bool mass = dm.policy == CONF_POLICY_CONFKV || dm.policy == CONF_POLICY_ARKV;
+  if (!mass || attn_score_cap(dm) >= dm.capt) return 0;
+  return (size_t)dm.L * dm.B * dm.Hkv * dm.G * dm.capt * sizeof(float);
+}
+
 size_t attn_dyn_lds(const Dims& dm) {
   const size_t sc = (size_t)dm.G * (attn_score_cap(dm) | 1);
   const size_t ob = (size_t)kWaves * dm.G * dm.D;
@@ -807,7 +862,7 @@ size_t attn_dyn_lds(const Dims& dm) {
 template <int D, bool BF16, bool FP8>
 static void launch_t(const Dims& dm, const conf_cache& c, int layer0, int nl, const void* q,
                      const void* k_new, const void* v_new, float* out, float* massp,
-                     int32_t* snap, bool with_ema, hipStream_t st) {
+                     int32_t* snap, float* spill, bool with_ema, hipStream_t st) {
   // the dynamic-LDS limit is a per-device attribute of the function: set it once per device
   static std::atomic<bool> attr_set[kMaxDevices];
   const int slot = current_device_slot();
@@ -818,7 +873,7 @@ static void launch_t(const Dims& dm, const conf_cache& c, int layer0, int nl, co
   }
   hipLaunchKernelGGL((attn_kernel<D, BF16, FP8>), dim3(nl * dm.B * dm.Hkv), dim3(kAttnThreads),
                      attn_dyn_lds(dm), st, c, dm, layer0, (const uint16_t*)q,
-                     (const uint16_t*)k_new, (const uint16_t*)v_new, out, massp, snap,
+                     (const uint16_t*)k_new, (const uint16_t*)v_new, out, massp, snap, spill,
                      attn_score_cap(dm));
   if (with_ema) launch_ema(dm, c, layer0, nl, massp, snap, st);
   // otherwise a launch that applies the EMA itself follows
@@ -833,12 +888,13 @@ struct Variant {
 
 void launch_attn(const Dims& dm, const conf_cache& c, int layer0, int nl, const void* q,
                  const void* k_new, const void* v_new, float* out, float* massp, int32_t* snap,
-                 bool with_ema, hipStream_t st) {
+                 float* spill, bool with_ema, hipStream_t st) {
   auto go = [&](auto kernel_tag) {
     constexpr int D = decltype(kernel_tag)::D;
     constexpr bool BF16 = decltype(kernel_tag)::BF16;
     constexpr bool FP8 = decltype(kernel_tag)::FP8;
-    launch_t<D, BF16, FP8>(dm, c, layer0, nl, q, k_new, v_new, out, massp, snap, with_ema, st);
+    launch_t<D, BF16, FP8>(dm, c, layer0, nl, q, k_new, v_new, out, massp, snap, spill, with_ema,
+                           st);
   };
   // the 8-bit region holds e4m3 codes under ARKV, INT8 codes otherwise
   const bool fp8 = dm.policy == CONF_POLICY_ARKV;

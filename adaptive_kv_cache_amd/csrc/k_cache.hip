@@ -30,10 +30,26 @@ __global__ void reset_kernel(conf_cache c, Dims dm) {
   if (i == 0) c.status[0] = 0;
 }
 
+// The 16-bit window arrays to zero.  The attention reads whole window halves and
+// gives the slots past a unit's count probability 0, which only cancels a finite
+// value; every later write into the window stores a caller-supplied or moved value.
+__global__ void zero16_kernel(uint4* __restrict__ a, uint4* __restrict__ b, size_t n) {
+  const uint4 z = {0u, 0u, 0u, 0u};
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    a[i] = z;
+    b[i] = z;
+  }
+}
+
 void launch_reset(const Dims& dm, const conf_cache& c, hipStream_t st) {
   const size_t n = (size_t)dm.L * dm.B * dm.Hkv * dm.D;
   const size_t blocks = (n + 255) / 256;
   hipLaunchKernelGGL(reset_kernel, dim3((unsigned)blocks), dim3(256), 0, st, c, dm);
+  const size_t n16 = (size_t)dm.L * dm.B * dm.Hkv * dm.cap16 * dm.D * 2 / 16;
+  const size_t zb = (n16 + 255) / 256;
+  hipLaunchKernelGGL(zero16_kernel, dim3((unsigned)(zb < 4096 ? zb : 4096)), dim3(256), 0, st,
+                     (uint4*)c.k16, (uint4*)c.v16, n16);
 }
 
 // ---------------------------------------------------------------- ingest
@@ -556,9 +572,12 @@ __global__ __launch_bounds__(C::NT) void compact_kernel(conf_cache c, Dims dm, i
   }
   __syncthreads();
   // ---- 1. keep flags (one read), counts, the demotee
-  // the token that leaves the window (full KV and retention eviction demote nothing)
-  const int target =
-      dm.policy == CONF_POLICY_FULL || dm.policy == CONF_POLICY_TRIM ? -1 : t - dm.W;
+  // the token that leaves the window (the baselines and retention eviction demote
+  // nothing: their tokens stay 16-bit)
+  const int target = dm.policy == CONF_POLICY_FULL || dm.policy == CONF_POLICY_TRIM ||
+                             dm.policy == CONF_POLICY_WINDOW
+                         ? -1
+                         : t - dm.W;
   int c8 = 0, c16 = 0;
   for (int i = tid; i < n8; i += C::NT) {
     const uint8_t k = keep8[i] ? 1 : 0;
@@ -704,9 +723,12 @@ __global__ __launch_bounds__(kCompThreads, 6) void evict_kernel(conf_cache c, Di
     M.ngrown = 0;
   }
   __syncthreads();
-  // the token that leaves the window (full KV and retention eviction demote nothing)
-  const int target =
-      dm.policy == CONF_POLICY_FULL || dm.policy == CONF_POLICY_TRIM ? -1 : t - dm.W;
+  // the token that leaves the window (the baselines and retention eviction demote
+  // nothing: their tokens stay 16-bit)
+  const int target = dm.policy == CONF_POLICY_FULL || dm.policy == CONF_POLICY_TRIM ||
+                             dm.policy == CONF_POLICY_WINDOW
+                         ? -1
+                         : t - dm.W;
   int c8 = 0, c16 = 0;
   select_core<kCompThreads, EMA>(c, dm, lb, n8, n16, t, N, U.sel, SM, [&](int j, int k, uint64_t key) {
     if (j < n8) {

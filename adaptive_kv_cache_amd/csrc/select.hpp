@@ -248,18 +248,19 @@ __device__ void select_core(const conf_cache& c, const Dims& dm, int lb, int n8,
                             int N, SelScratch& X, SelMisc& M, Sink sink) {
   const int n = n8 + n16;
   const int tid = threadIdx.x;
-  // full KV keeps everything, as CONF-KV does under its budget
-  if (n <= N || dm.policy == CONF_POLICY_FULL) {
-    for (int j = tid; j < n; j += NT) sink(j, 1, kAllKept);
-    return;
-  }
   const int32_t* pos8 = c.pos8 + (size_t)lb * dm.cap8;
   const float* ema8 = c.ema8 + (size_t)lb * dm.cap8;
   const int32_t* pos16 = c.pos16 + (size_t)lb * dm.cap16;
   const float* ema16 = c.ema16 + (size_t)lb * dm.cap16;
-  if (dm.policy == CONF_POLICY_WINDOW) {  // the newest W positions, (t-W, t]
+  // the sliding window keeps the newest W positions, (t-W, t], whatever the budget
+  if (dm.policy == CONF_POLICY_WINDOW) {
     for (int j = tid; j < n; j += NT)
       sink(j, (j < n8 ? pos8[j] : pos16[j - n8]) > t - dm.W, kAllKept);
+    return;
+  }
+  // full KV keeps everything, as CONF-KV does under its budget
+  if (n <= N || dm.policy == CONF_POLICY_FULL) {
+    for (int j = tid; j < n; j += NT) sink(j, 1, kAllKept);
     return;
   }
   auto tok = [&](int j, float& e, uint32_t& tag) {

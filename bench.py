@@ -422,7 +422,6 @@ def _plan_offset(eng):
     nch = -(-wl.vocab // (256 * 16))
     off = a(wl.n_sub * nch * 8 * 4)
     off = a(off + LB * _heads(wl) * (eng.cap8 + eng.cap16) * 4)
-    off = a(off + LB * _qheads(wl) * 4)
     off = a(off + LB * (eng.cap8 + eng.cap16))
     return off
 

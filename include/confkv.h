@@ -27,8 +27,11 @@
  *   - Every pointer argument is a DEVICE pointer owned by the caller, except
  *     the `const conf_params*` / `conf_cache*` structs themselves, which are
  *     host memory read during the call only.  The library allocates no device
- *     memory and keeps no mutable global state; scratch lives in the caller's
- *     workspace `ws` of conf_workspace_bytes() bytes (256-byte aligned).
+ *     memory; scratch lives in the caller's workspace `ws` of
+ *     conf_workspace_bytes() bytes (256-byte aligned).  Its only process-wide
+ *     state is one flag per (device, attention kernel variant) recording that
+ *     the kernel's dynamic-LDS limit has been raised (an idempotent, thread-
+ *     safe one-time set-up; nothing that holds data).
  *   - A call validates its arguments on the host, enqueues kernels on `stream`
  *     (a hipStream_t; NULL is the null stream) and returns without waiting for
  *     the device.  Results are valid once the stream has been synchronised.
@@ -207,8 +210,13 @@ int conf_cache_layout(const conf_params* p, conf_cache_bytes_t* out);
 /* Workspace bytes every call below may use for `p`. */
 int conf_workspace_bytes(const conf_params* p, size_t* bytes);
 
-/* Empty every (layer, sequence): n8 = n16 = 0, t = -1, absmax = 0, status = 0.
- * Fills with kernels (no memset nodes), so it may be graph-captured. */
+/* Empty every (layer, sequence): n8 = n16 = 0, t = -1, absmax = 0, status = 0,
+ * and every element of k16 and v16 = 0.  The attention reads whole 32-token
+ * window halves and gives the free slots past n16 probability 0, which cancels
+ * only a finite value (0 * NaN is NaN), so the window's free slots must hold
+ * finite bits: the reset establishes that, and the library keeps it as long as
+ * k_new, v_new, k_pre and v_pre are finite.  Fills with kernels (no memset
+ * nodes), so it may be graph-captured. */
 int conf_cache_reset(const conf_params* p, conf_cache* c, conf_stream_t stream);
 
 /*
@@ -242,7 +250,10 @@ int conf_confidence(const conf_params* p, const float* logits, float* c, int32_t
  * cached tokens of KV head h / (Hq/Hkv), INT8 tokens dequantised as code*amax/127
  * inside the block reads.  out: fp32 [L][B][Hq][d].  Then every token's EMA
  * becomes decay*e + (1-decay)*mass_j, mass_j = mean over the Hq heads of its
- * softmax probability; the new token starts from e = 0.  Under CONF_POLICY_ARKV
+ * softmax probability; the new token starts from e = 0.  K and V are read once
+ * whatever the cache length: the raw scores wait for the final softmax
+ * normaliser in LDS, and those of a cache longer than the LDS rows in ws.
+ * Under CONF_POLICY_ARKV
  * the EMA is that of ARKV's heavy-hitter score (see the policy).
  * CONF_E_INVALID under CONF_POLICY_TRIM, whose step is conf_attend followed by
  * conf_trim_evict_compact.  Policy limits of the calls below: conf_step and

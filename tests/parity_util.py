@@ -111,7 +111,8 @@ def tiny_workloads() -> dict:
         name="mha_bf16_d128_empty", n_layers=1, batch=2, n_q_heads=8, n_kv_heads=8, head_dim=128,
         vocab=500, dtype16="bf16", window=24, protect=6, n_high=40, n_low=70, prefill=0,
         steps=150)
-    # more scores than the LDS holds at the first step: exercises the two-pass path
+    # more scores than the LDS holds at the first step: the items past the LDS rows
+    # keep theirs in the workspace
     w["gqa16_bf16_d64_long"] = Workload(
         name="gqa16_bf16_d64_long", n_layers=1, batch=2, n_q_heads=16, n_kv_heads=1, head_dim=64,
         vocab=500, dtype16="bf16", window=64, protect=8, n_high=100, n_low=300, prefill=2500,
@@ -122,10 +123,17 @@ def tiny_workloads() -> dict:
         name="mha16_f16_d128", n_layers=1, batch=2, n_q_heads=16, n_kv_heads=16, head_dim=128,
         vocab=600, dtype16="f16", window=40, protect=8, n_high=60, n_low=100, prefill=150,
         steps=12)
-    # every budget above what the LDS score rows hold, so that each step after the
-    # first also takes the two-pass path with the window's free slot masked
+    # every budget above what the LDS score rows hold, so that every step also keeps
+    # scores in the workspace
     w["gqa16_bf16_d64_wide"] = Workload(
         name="gqa16_bf16_d64_wide", n_layers=1, batch=2, n_q_heads=16, n_kv_heads=1,
         head_dim=64, vocab=500, dtype16="bf16", window=64, protect=8, n_high=1300, n_low=1400,
         prefill=2500, steps=6)
+    # d = 128 with 16 query heads: the LDS keeps the scores of about 500 tokens, and
+    # the window of 600 is longer than that, so the items that keep their scores in
+    # the workspace start inside the window (the INT8 part fits)
+    w["gqa16_f16_d128_winspill"] = Workload(
+        name="gqa16_f16_d128_winspill", n_layers=1, batch=2, n_q_heads=16, n_kv_heads=1,
+        head_dim=128, vocab=700, dtype16="f16", window=600, protect=50, n_high=700, n_low=900,
+        prefill=1000, steps=8)
     return w

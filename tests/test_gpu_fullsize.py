@@ -7,8 +7,8 @@ their device state (teacher forcing) at chosen steps.  The steps of the
 Qwen-32B-shaped batch-8 cache (the benchmark's) are the three kinds a decode
 step can be:
   * step 0: the one-off cut of the prefilled 32769 tokens to the budget (the
-    scores exceed the LDS, so the kernel takes its two-pass path);
-  * step 1: a loose-budget step with 4097 tokens (also two-pass);
+    scores exceed the LDS rows, so most items keep theirs in the workspace);
+  * step 1: a loose-budget step with 4097 tokens (also beyond the LDS rows);
   * step 66: after the first confident phase, about 2050 tokens (single pass,
     scores in LDS), the steady state the benchmark times.
 The caches that start empty are checked at their first demotion into INT8, at

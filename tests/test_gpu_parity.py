@@ -110,9 +110,16 @@ def test_ingest_bit_exact(name):
     assert eng.status() == 0
 
 
-def _teacher_forced(wl, steps, seed=SEED):
+def _teacher_forced(wl, steps, seed=SEED, poison=False):
     prm = oracle_params(wl)
     eng = Engine(wl)
+    if poison:
+        # NaN bit patterns in every window slot, then a reset: the attention reads
+        # whole window halves, so it relies on the reset having zeroed the free slots
+        nan = 0x7FC0 if wl.dtype16 == "bf16" else 0x7E00
+        eng.t_k16.fill_(nan)
+        eng.t_v16.fill_(nan)
+        eng.reset()
     if wl.prefill:
         _ingest(eng, wl, seed)
     cap8 = eng.cap8
@@ -161,6 +168,18 @@ def test_teacher_forced_steps(name, seed):
     steps = 150 if wl.prefill == 0 else 12
     _say("teacher-forced", name, steps, "seed", seed)
     worst = _teacher_forced(wl, steps, seed)
+    _say("  worst attention rel err", worst)
+
+
+@pytest.mark.parametrize("name", ["mha_bf16_d128_empty", "mha_f16_d64", "gqa16_bf16_d64_long"])
+def test_reset_zeroes_the_window(name):
+    """Window arrays full of NaN bit patterns before conf_cache_reset: every output,
+    EMA and cache state still matches the oracle (the free slots of partial window
+    halves meet probability 0, which cancels only the finite values the reset left)."""
+    wl = TINY[name]
+    steps = 60 if wl.prefill == 0 else 6
+    _say("poisoned window before reset", name, steps)
+    worst = _teacher_forced(wl, steps, poison=True)
     _say("  worst attention rel err", worst)
 
 
@@ -320,6 +339,44 @@ def test_baseline_policies(policy, name):
                     assert st.pos.tolist() == list(range(max(0, st.t - wl.window + 1), st.t + 1))
     assert eng.status() == 0
     _say("  worst attention rel err", worst)
+
+
+@pytest.mark.parametrize("name", ["gqa5_bf16_d128", "mha_f16_d64"])
+def test_window_policy_ignores_the_budget(name):
+    """The sliding window keeps exactly (t-W, t] in 16 bits even when the budgets
+    exceed W: the oracle runs the window's own parameters (N = P = W), the library
+    budgets of W + 37 and W + 90 that the window rule must override."""
+    import dataclasses
+    base = TINY[name]
+    steps = 16 if base.prefill else 100
+    wl_ref = base.baseline("window", steps)
+    W = wl_ref.window
+    wl = dataclasses.replace(wl_ref, n_high=W + 37, n_low=W + 90, protect=max(1, W // 4))
+    prm = oracle_params(wl_ref)
+    _say("window with budgets above W", name)
+    eng = Engine(wl)
+    if wl.prefill:
+        _ingest(eng, wl, SEED)
+    for step in range(steps):
+        S0 = _snap(eng, wl)
+        z = synth.logits(wl, step, SEED)
+        q = synth.q_new(wl, step, SEED)
+        k, v = synth.kv_new(wl, step, SEED)
+        out, _, budget = eng.step(z.cuda(), q.cuda(), k.cuda(), v.cuda())
+        assert int(budget.min()) > W
+        out = out.cpu().numpy()
+        S2 = _snap(eng, wl)
+        qb, kb, vb = bits16(q), bits16(k), bits16(v)
+        for l in range(wl.n_layers):
+            for b in range(wl.batch):
+                st = to_oracle_state(S0[l][b], wl.dtype16)
+                r = O.step_layer(st, qb[l, b], kb[l, b], vb[l, b], W, prm)
+                assert attn_rel_err(out[l, b], r["o"]) <= ATTN_TOL, (name, step, l, b)
+                got = to_oracle_state(S2[l][b], wl.dtype16)
+                assert_same_state(got, st, what=("window", step, l, b))
+                assert not got.is8.any()
+                assert got.pos.tolist() == list(range(max(0, got.t - W + 1), got.t + 1))
+    assert eng.status() == 0
 
 
 def test_sawtooth_and_no_op_from_empty():
