@@ -133,10 +133,12 @@ def step_bytes(wl, n8, nw, plan):
 
 
 # ---------------------------------------------------------------- CPU baseline
-def cpu_baseline(wl, seed, budget_s=20.0):
-    """The oracle as it stands, on a bounded sample: every layer of one sequence
-    stepped from a steady-state-sized cache (N_high + 64 tokens, the top of the
-    confident-phase sawtooth) for as many steps as fit in about `budget_s`."""
+def cpu_baseline(wl, seed, n_tokens, first_step, budget_s=20.0):
+    """The oracle as it stands, on a bounded sample of the timed regime: every
+    layer of one sequence, stepped from a cache of the size the timed GPU steps
+    attended (n_tokens - 1 cached tokens plus the appended one) with the logits of
+    the timed steps from `first_step` on, for as many steps as fit in about
+    `budget_s`."""
     import numpy as np
 
     import oracle as O
@@ -150,7 +152,7 @@ def cpu_baseline(wl, seed, budget_s=20.0):
                          head_dim=wl.head_dim, dtype16=wl.dtype16, window=wl.window,
                          protect=wl.protect, n_high=wl.n_high, n_low=wl.n_low,
                          pyramid=wl.pyramid, tau=wl.tau)
-    n0 = wl.n_high + 64
+    n0 = max(1, int(round(n_tokens)) - 1)
     rng = np.random.default_rng(seed)
     states = []
     for l in range(wl.n_layers):
@@ -160,7 +162,7 @@ def cpu_baseline(wl, seed, budget_s=20.0):
     steps = 0
     t0 = time.perf_counter()
     while True:
-        z = synth.logits(wl.scaled(batch=1), 64 + steps, seed).numpy().astype(np.float64)
+        z = synth.logits(wl.scaled(batch=1), first_step + steps, seed).numpy().astype(np.float64)
         q = O.encode16(rng.standard_normal((wl.n_layers, 1, wl.n_q_heads, wl.head_dim)),
                        wl.dtype16)
         kk = O.encode16(rng.standard_normal((wl.n_layers, 1, wl.n_kv_heads, wl.head_dim)),
@@ -176,8 +178,10 @@ def cpu_baseline(wl, seed, budget_s=20.0):
     return {
         "value": 1.0 / (per_seq_step * wl.batch), "unit": "steps/s", "cores": cores,
         "blas_threads": blas, "kind": "oracle",
-        "sample": (f"{steps} steps x {wl.n_layers} layers x 1 sequence from a {n0}-token cache; "
-                   f"{per_seq_step:.3f} s per sequence-step, extrapolated to batch {wl.batch}"),
+        "sample": (f"{steps} steps x {wl.n_layers} layers x 1 sequence from a {n0 + 1}-token "
+                   f"cache (the timed steps' mean), logits of steps {first_step}.."
+                   f"{first_step + steps - 1}; {per_seq_step:.3f} s per sequence-step, "
+                   f"extrapolated to batch {wl.batch}"),
     }
 
 
@@ -401,7 +405,8 @@ def run(args):
                                 "launch intervals)"),
                      "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": stored_traffic(wl.name),
+                     "traffic": stored_traffic(wl.name, args.steps, args.warmup,
+                                                round(n_mean, 1)),
                      "avg_launch_us": round(attn_avg_ms * 1e3, 2),
                      "alg_bytes_per_launch": int(sum(a_bytes) / len(a_bytes))},
         "step_roofline": {"achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -477,22 +482,25 @@ def attn_source_hash():
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload):
-    """HBM bytes per attention launch from the committed counter summary, or
-    None when it is missing, for another workload, or taken on other kernel source."""
+def stored_traffic(workload, steps, warmup, tokens):
+    """HBM bytes per attention launch (one step's attention) from the committed
+    counter summary, for exactly this regime: the same workload, timed steps,
+    warm-up steps and mean tokens attended (the 4097-token phase after the prefill
+    and the 2065-token steady state stream different bytes), on the same attention
+    sources.  None when no such line exists."""
     try:
         text = open(TRAFFIC_FILE).read()
     except OSError:
         return None
-    vals = {}
+    want = {"workload": workload, "steps": str(steps), "warmup": str(warmup),
+            "tokens": f"{tokens:.1f}", "source": attn_source_hash()}
     for line in text.splitlines():
-        if line.startswith("traffic:"):
-            for kv in line[len("traffic:"):].split():
-                k, _, v = kv.partition("=")
-                vals[k] = v
-    if vals.get("workload") != workload or vals.get("source") != attn_source_hash():
-        return None
-    return int(vals["bytes_per_launch"])
+        if not line.startswith("traffic:"):
+            continue
+        vals = dict(kv.partition("=")[::2] for kv in line[len("traffic:"):].split())
+        if all(vals.get(k) == v for k, v in want.items()):
+            return int(vals["bytes_per_launch"])
+    return None
 
 
 def copy_ceiling(dev, mib=2048, reps=8):
@@ -593,7 +601,9 @@ def main():
     res, wl = run(args)
     if not args.no_cpu_baseline and args.policy == "confkv" and not args.headwise:
         log("cpu baseline (oracle)")
-        res["cpu_baseline"] = cpu_baseline(wl, args.seed, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(wl, args.seed,
+                                           res["config"]["mean_tokens_attended"], args.warmup,
+                                           args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 
