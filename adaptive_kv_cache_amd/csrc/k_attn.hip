@@ -160,25 +160,6 @@ struct Item {
   int mass0;      // mass-row index of the first slot
 };
 
-__device__ inline Item item_of(int it, int nb8, int n8, int nw, int cap8) {
-  Item I;
-  if (it < nb8) {
-    I.i8 = true;
-    I.blk = it;
-    I.n_valid = min(kTile, n8 - it * kTile);
-    I.tok0 = it * kTile;
-    I.mass0 = it * kTile;
-  } else {
-    const int j = it - nb8;
-    I.i8 = false;
-    I.blk = j;
-    I.n_valid = min(32, nw - 32 * j);
-    I.tok0 = n8 + 32 * j;
-    I.mass0 = cap8 + 32 * j;
-  }
-  return I;
-}
-
 // Every item's keys and values are read as D/16 loads of 16 bytes per lane.
 // Keys: load i reads the 1 KB run at 1 KB * i, a lane at 16 * lane inside it.
 // Values: load i reads 16 channels (16i .. 16i+15) of the four token groups g,
@@ -458,10 +439,11 @@ __device__ inline void apply_vscale(WaveAcc<D>& wa, const float* sv) {
 // pipelined on one key and one value buffer: an item's values load from the
 // start of its stage, and the next item's keys as soon as this item's scores
 // are formed.  The key load is issued for every stage (an item past the end
-// reads at kNoItem), so no branch surrounds a load.  With non-temporal loads the
-// kernel runs as fast as a copy of it with the arithmetic removed, and a second
-// key buffer (a stage more of key prefetch) measured no faster.
-// `kb` holds (or is receiving) the keys of item `wave` if `preloaded`.
+// reads at kNoItem), so no branch surrounds a load.  The INT8 items and the
+// window items run as two loops: each loop body is straight-line code, so the
+// compiler's wait counts stay exact (with both item kinds in one loop body it
+// merged the two paths' counts and waited for the values before the scores).
+// `kb` holds (or is receiving) the keys of item `wave`.
 struct UnitRs {
   rsrc_t k8, v8, k16, v16;  // the unit's four regions
 };
@@ -469,31 +451,43 @@ struct UnitRs {
 template <int D, bool BF16, int MODE, bool FP8>
 __device__ inline void wave_pass(int nitems, int nb8, int n8, int nw, int cap8, const UnitRs& rs,
                                  const QOps<D, BF16>& q, float scale8, float scale16, bool head_ok,
-                                 WaveAcc<D>& wa, bool& vscaled, const float* sv,
-                                 const ScoreSink& sk, Buf<D>& kb) {
+                                 WaveAcc<D>& wa, const float* sv, const ScoreSink& sk,
+                                 Buf<D>& kb) {
   // wave-uniform, so that the descriptor choice per item is a scalar select
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
-  if (wave >= nitems) return;
   const int klane = 16 * lane, vlane = 16 * D * (lane >> 4) + 16 * (lane & 15);
   const uint32_t ib = (uint32_t)kTile * D;  // bytes per item in every region
   Buf<D> V;
   int it = wave;
-  for (;;) {
-    load_run_rs<D, 256>(it < nb8 ? rs.v8 : rs.v16, (uint32_t)(it < nb8 ? it : it - nb8) * ib,
-                        vlane, V);
+  for (; it < nb8; it += kWaves) {  // INT8 blocks
+    load_run_rs<D, 256>(rs.v8, (uint32_t)it * ib, vlane, V);
     const int nx = it + kWaves;
-    if (it >= nb8 && !vscaled) {
-      apply_vscale<D>(wa, sv);
-      vscaled = true;
-    }
-    compute_item<D, BF16, MODE, FP8>(item_of(it, nb8, n8, nw, cap8), kb, V, q, scale8, scale16,
-                                     head_ok, wa, sk, nx < nb8 ? rs.k8 : rs.k16,
-                                     nx < nitems ? (uint32_t)(nx < nb8 ? nx : nx - nb8) * ib
-                                                 : kNoItem,
-                                     klane);
-    it = nx;
-    if (it >= nitems) break;
+    Item I;
+    I.i8 = true;
+    I.blk = it;
+    I.n_valid = min(kTile, n8 - it * kTile);
+    I.tok0 = it * kTile;
+    I.mass0 = it * kTile;
+    compute_item<D, BF16, MODE, FP8>(
+        I, kb, V, q, scale8, scale16, head_ok, wa, sk, nx < nb8 ? rs.k8 : rs.k16,
+        nx < nitems ? (uint32_t)(nx < nb8 ? nx : nx - nb8) * ib : kNoItem, klane);
+  }
+  // the INT8 value scale, once, between the INT8 and the window items (O is still 0
+  // for a wavefront without INT8 items)
+  apply_vscale<D>(wa, sv);
+  for (; it < nitems; it += kWaves) {  // window halves
+    const int j = it - nb8;
+    load_run_rs<D, 256>(rs.v16, (uint32_t)j * ib, vlane, V);
+    const int nx = it + kWaves;
+    Item I;
+    I.i8 = false;
+    I.blk = j;
+    I.n_valid = min(32, nw - 32 * j);
+    I.tok0 = n8 + 32 * j;
+    I.mass0 = cap8 + 32 * j;
+    compute_item<D, BF16, MODE, FP8>(I, kb, V, q, scale8, scale16, head_ok, wa, sk, rs.k16,
+                                     nx < nitems ? (uint32_t)(nx - nb8) * ib : kNoItem, klane);
   }
 }
 
@@ -675,17 +669,16 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
   wa.l = 0.f;
 #pragma unroll
   for (int cb = 0; cb < D / 16; ++cb) wa.o[cb] = (f4){0.f, 0.f, 0.f, 0.f};
-  bool vscaled = false;
 
   if (!mass)
     wave_pass<D, BF16, MODE_PLAIN, FP8>(nitems, nb8, n8, nw, dm.cap8, urs, q, scale8, scale16,
-                                        head_ok, wa, vscaled, s_sv, sink, cur);
+                                        head_ok, wa, s_sv, sink, cur);
   else if (jsp >= nc)
     wave_pass<D, BF16, MODE_ONLINE, FP8>(nitems, nb8, n8, nw, dm.cap8, urs, q, scale8, scale16,
-                                         head_ok, wa, vscaled, s_sv, sink, cur);
+                                         head_ok, wa, s_sv, sink, cur);
   else
     wave_pass<D, BF16, MODE_SPILL, FP8>(nitems, nb8, n8, nw, dm.cap8, urs, q, scale8, scale16,
-                                        head_ok, wa, vscaled, s_sv, sink, cur);
+                                        head_ok, wa, s_sv, sink, cur);
   // ---- merge the waves' running (max, sum) and add this step's token.  Each
   // wavefront's O (value scale applied, not yet normalised) goes to LDS before
   // the barrier, and the O merge shares a phase with the mass.
@@ -693,7 +686,6 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     s_m[wave][lane] = wa.m;
     s_l[wave][lane] = wa.l;
   }
-  if (!vscaled) apply_vscale<D>(wa, s_sv);
   store_o<D>(wa, ob, G);
   __syncthreads();  // also orders the spilled scores before their reads below
   if (tid < G) {

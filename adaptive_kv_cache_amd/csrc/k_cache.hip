@@ -53,79 +53,213 @@ void launch_reset(const Dims& dm, const conf_cache& c, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------- ingest
-// Prefill of L0 tokens for one unit: positions < L0 - W become INT8 with the
-// absmax over exactly those tokens (a sliding window drops them); the rest go to
-// the window.
-__global__ __launch_bounds__(256) void ingest_kernel(conf_cache c, Dims dm, int layer0, int L0,
-                                                     const uint16_t* __restrict__ kp,
-                                                     const uint16_t* __restrict__ vp) {
-#pragma clang fp contract(off)
+// Prefill of L0 tokens per unit: positions < L0 - W become INT8 (e4m3 under ARKV)
+// with the absmax over exactly those tokens (a sliding window drops them); the
+// rest go to the window.  Three launches, spread over the whole GPU rather than one
+// workgroup per unit: the units' absmax rows are cleared; every chunk of
+// kIngChunk tokens folds its per-channel |x| maxima into them with atomic maxima on
+// the float bits (exact: for x >= 0 the bits order like the values); then every
+// 64-token tile is quantised (or, for the window, copied) through LDS, so that
+// each load and store is a 16-byte access.
+constexpr int kIngThreads = 256;
+constexpr int kIngChunk = 1024;  // tokens per absmax workgroup
+
+struct IngGeom {
+  int old, n8, nw;  // positions older than the window; INT8 tokens; window tokens
+};
+__host__ __device__ inline IngGeom ing_geom(const Dims& dm, int L0) {
+  IngGeom g;
+  g.old = L0 > dm.W ? L0 - dm.W : 0;
+  g.n8 = dm.policy == CONF_POLICY_WINDOW ? 0 : g.old;
+  g.nw = L0 - g.old;
+  return g;
+}
+
+__global__ __launch_bounds__(kIngThreads) void ingest_clear_kernel(conf_cache c, Dims dm,
+                                                                    int layer0, int nunits) {
+  const size_t u0 = (size_t)layer0 * dm.B * dm.Hkv;
+  const size_t n = (size_t)nunits * dm.D;
+  for (size_t i = (size_t)blockIdx.x * kIngThreads + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * kIngThreads) {
+    c.k_amax[u0 * dm.D + i] = 0.f;
+    c.v_amax[u0 * dm.D + i] = 0.f;
+  }
+}
+
+// grid (units, chunks): per-channel max |x| of tokens [kIngChunk*y, ...) below n8
+__global__ __launch_bounds__(kIngThreads) void ingest_amax_kernel(conf_cache c, Dims dm,
+                                                                   int layer0, int L0,
+                                                                   const uint16_t* __restrict__ kp,
+                                                                   const uint16_t* __restrict__ vp) {
   const int unit_local = blockIdx.x;
-  const int hk = unit_local % dm.Hkv;
-  const int lbl = unit_local / dm.Hkv;
-  const int lb = layer0 * dm.B + lbl;
-  const size_t u = unit_of(dm, lb, hk);
-  const int D = dm.D;
-  const int old = L0 > dm.W ? L0 - dm.W : 0;  // positions older than the window
-  const int n8 = dm.policy == CONF_POLICY_WINDOW ? 0 : old;
-  const bool fp8 = dm.policy == CONF_POLICY_ARKV;  // ARKV quantises to e4m3
-  const int nw = L0 - old;
-  const uint16_t* ksrc = kp + (size_t)unit_local * L0 * D;
-  const uint16_t* vsrc = vp + (size_t)unit_local * L0 * D;
-  __shared__ float amk[256], amv[256];
-  __shared__ float sk[128], sv[128];
-  // absmax per channel: thread (ch, part) with 256/D parts striding over tokens
-  const int parts = blockDim.x / D;
-  const int ch = threadIdx.x % D, part = threadIdx.x / D;
-  float mk = 0.f, mv = 0.f;
-  if (part < parts) {
-    for (int i = part; i < n8; i += parts) {
-      mk = fmaxf(mk, fabsf(h16_to_f32(ksrc[(size_t)i * D + ch], dm.bf16)));
-      mv = fmaxf(mv, fabsf(h16_to_f32(vsrc[(size_t)i * D + ch], dm.bf16)));
+  const size_t u = (size_t)layer0 * dm.B * dm.Hkv + unit_local;
+  const int D = dm.D, G8 = D / 8;  // 8-channel groups per token
+  const IngGeom gm = ing_geom(dm, L0);
+  const int t0 = blockIdx.y * kIngChunk, t1 = min(gm.n8, t0 + kIngChunk);
+  const uint16_t* ks = kp + (size_t)unit_local * L0 * D;
+  const uint16_t* vs = vp + (size_t)unit_local * L0 * D;
+  const int cg = threadIdx.x % G8, rows = kIngThreads / G8;
+  float mk[8], mv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) mk[e] = mv[e] = 0.f;
+  for (int tok = t0 + threadIdx.x / G8; tok < t1; tok += rows) {
+    const uint4 a = *(const uint4*)(ks + (size_t)tok * D + 8 * cg);
+    const uint4 b = *(const uint4*)(vs + (size_t)tok * D + 8 * cg);
+    const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      mk[e] = fmaxf(mk[e], fabsf(h16_to_f32((uint16_t)(wa[e >> 1] >> (16 * (e & 1))), dm.bf16)));
+      mv[e] = fmaxf(mv[e], fabsf(h16_to_f32((uint16_t)(wb[e >> 1] >> (16 * (e & 1))), dm.bf16)));
     }
   }
-  amk[threadIdx.x] = mk;
-  amv[threadIdx.x] = mv;
+  // fold the rows that share a channel group: [row][D] in LDS, then one thread per channel
+  __shared__ float sk[kIngThreads * 8], sv[kIngThreads * 8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    sk[(threadIdx.x / G8) * D + 8 * cg + e] = mk[e];
+    sv[(threadIdx.x / G8) * D + 8 * cg + e] = mv[e];
+  }
   __syncthreads();
   if (threadIdx.x < D) {
     float a = 0.f, b = 0.f;
-    for (int p = 0; p < parts; ++p) {
-      a = fmaxf(a, amk[p * D + threadIdx.x]);
-      b = fmaxf(b, amv[p * D + threadIdx.x]);
+    for (int r = 0; r < rows; ++r) {
+      a = fmaxf(a, sk[r * D + threadIdx.x]);
+      b = fmaxf(b, sv[r * D + threadIdx.x]);
     }
-    c.k_amax[u * D + threadIdx.x] = a;
-    c.v_amax[u * D + threadIdx.x] = b;
-    sk[threadIdx.x] = a / code_max(fp8);
-    sv[threadIdx.x] = b / code_max(fp8);
+    atomicMax((unsigned int*)&c.k_amax[u * D + threadIdx.x], __float_as_uint(a));
+    atomicMax((unsigned int*)&c.v_amax[u * D + threadIdx.x], __float_as_uint(b));
+  }
+}
+
+// grid (units, INT8 tiles + window tiles): one 64-token tile of one unit.  The
+// tile's K and V rows are staged in LDS with 16-byte loads; a key tile is then
+// written as 16-channel runs of one token, a value tile as 16-token runs of one
+// channel (8 for the window), each one 16-byte store.
+__global__ __launch_bounds__(kIngThreads) void ingest_tile_kernel(conf_cache c, Dims dm, int layer0,
+                                                                   int L0,
+                                                                   const uint16_t* __restrict__ kp,
+                                                                   const uint16_t* __restrict__ vp) {
+#pragma clang fp contract(off)
+  const int unit_local = blockIdx.x;
+  const int hk = unit_local % dm.Hkv;
+  const int lb = layer0 * dm.B + unit_local / dm.Hkv;
+  const size_t u = (size_t)lb * dm.Hkv + hk;
+  const int D = dm.D;
+  const IngGeom gm = ing_geom(dm, L0);
+  const bool fp8 = dm.policy == CONF_POLICY_ARKV;  // ARKV quantises to e4m3
+  const int nt8 = (gm.n8 + kTile - 1) / kTile;
+  const bool i8 = (int)blockIdx.y < nt8;
+  const int tile = i8 ? blockIdx.y : blockIdx.y - nt8;
+  const int base = kTile * tile;                            // first slot of the tile
+  const int cnt = min(kTile, (i8 ? gm.n8 : gm.nw) - base);  // slots of the tile in use
+  const int src0 = (i8 ? 0 : gm.old) + base;                 // its first prefill position
+  const uint16_t* ks = kp + ((size_t)unit_local * L0 + src0) * D;
+  const uint16_t* vs = vp + ((size_t)unit_local * L0 + src0) * D;
+  __shared__ uint4 tk[kTile * 128 / 8], tv[kTile * 128 / 8];  // [64][D] 16-bit, 16-byte chunks
+  __shared__ float sk[128], sv[128];
+  const int G8 = D / 8;
+  for (int i = threadIdx.x; i < kTile * G8; i += kIngThreads) {
+    const int r = i / G8;
+    const uint4 z = {0u, 0u, 0u, 0u};
+    tk[i] = r < cnt ? *(const uint4*)(ks + (size_t)i * 8) : z;
+    tv[i] = r < cnt ? *(const uint4*)(vs + (size_t)i * 8) : z;
+  }
+  if (i8 && threadIdx.x < D) {
+    sk[threadIdx.x] = c.k_amax[u * D + threadIdx.x] / code_max(fp8);
+    sv[threadIdx.x] = c.v_amax[u * D + threadIdx.x] / code_max(fp8);
   }
   __syncthreads();
-  int8_t* k8 = c.k8 + u * (size_t)dm.cap8 * D;
-  int8_t* v8 = c.v8 + u * (size_t)dm.cap8 * D;
-  for (size_t i = threadIdx.x; i < (size_t)n8 * D; i += blockDim.x) {
-    const int tok = (int)(i / D), cc = (int)(i % D);
-    k8[k8_off(tok, cc, D)] = quant8(h16_to_f32(ksrc[i], dm.bf16), sk[cc], fp8);
-    v8[v8_off(tok, cc, D)] = quant8(h16_to_f32(vsrc[i], dm.bf16), sv[cc], fp8);
+  const uint16_t* hk16 = (const uint16_t*)tk;
+  const uint16_t* hv16 = (const uint16_t*)tv;
+  if (i8) {
+    int8_t* k8 = c.k8 + u * (size_t)dm.cap8 * D;
+    int8_t* v8 = c.v8 + u * (size_t)dm.cap8 * D;
+    // keys: (token, 16-channel group), token fastest
+    for (int i = threadIdx.x; i < kTile * (D / 16); i += kIngThreads) {
+      const int r = i % kTile, cg = i / kTile;
+      if (r >= cnt) continue;
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t x = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ch = 16 * cg + 4 * q + e;
+          const int8_t code = quant8(h16_to_f32(hk16[r * D + ch], dm.bf16), sk[ch], fp8);
+          x |= (uint32_t)(uint8_t)code << (8 * e);
+        }
+        w[q] = x;
+      }
+      *(uint4*)(k8 + k8_off(base + r, 16 * cg, D)) = (uint4){w[0], w[1], w[2], w[3]};
+    }
+    // values: (token group g, channel), channel fastest; the 16 bytes hold tokens
+    // 32u + 16a + 4g + b at byte 8u + 4a + b (slots past cnt get code 0)
+    for (int i = threadIdx.x; i < 4 * D; i += kIngThreads) {
+      const int ch = i % D, g = i / D;
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t x = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int byte = 4 * q + e, uu = byte >> 3, a = (byte >> 2) & 1, b = byte & 3;
+          const int r = 32 * uu + 16 * a + 4 * g + b;
+          const int8_t code =
+              r < cnt ? quant8(h16_to_f32(hv16[r * D + ch], dm.bf16), sv[ch], fp8) : (int8_t)0;
+          x |= (uint32_t)(uint8_t)code << (8 * e);
+        }
+        w[q] = x;
+      }
+      // byte 0 of the run is slot 4g (u = a = b = 0)
+      *(uint4*)(v8 + v8_off(base + 4 * g, ch, D)) = (uint4){w[0], w[1], w[2], w[3]};
+    }
+  } else {
+    uint16_t* k16 = (uint16_t*)c.k16 + u * (size_t)dm.cap16 * D;
+    uint16_t* v16 = (uint16_t*)c.v16 + u * (size_t)dm.cap16 * D;
+    // keys: (token, 8-channel group) -> 16 contiguous bytes of the key tile
+    for (int i = threadIdx.x; i < kTile * G8; i += kIngThreads) {
+      const int r = i % kTile, cg = i / kTile;
+      if (r >= cnt) continue;
+      *(uint4*)(k16 + k16_off(base + r, 8 * cg, D)) = tk[r * G8 + cg];
+    }
+    // values: per 32-token half u, (token group g, channel) -> tokens 16a + 4g + b
+    // at element 4a + b; only whole halves in use are written, a partial one
+    // element by element (the slots past nw keep the zeros of the reset)
+    for (int i = threadIdx.x; i < 2 * 4 * D; i += kIngThreads) {
+      const int ch = i % D, g = (i / D) % 4, uu = i / (4 * D);
+      uint16_t e16[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 32 * uu + 16 * (e >> 2) + 4 * g + (e & 3);
+        e16[e] = r < cnt ? hv16[r * D + ch] : (uint16_t)0;
+      }
+      uint16_t* dst = v16 + v16_off(base + 32 * uu + 4 * g, ch, D);  // element 0 of the run
+      if (32 * uu + 32 <= cnt) {
+        *(uint4*)dst = (uint4){e16[0] | (uint32_t)e16[1] << 16, e16[2] | (uint32_t)e16[3] << 16,
+                               e16[4] | (uint32_t)e16[5] << 16, e16[6] | (uint32_t)e16[7] << 16};
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 32 * uu + 16 * (e >> 2) + 4 * g + (e & 3);
+          if (r < cnt) dst[e] = e16[e];
+        }
+      }
+    }
   }
-  uint16_t* k16 = (uint16_t*)c.k16 + u * (size_t)dm.cap16 * D;
-  uint16_t* v16 = (uint16_t*)c.v16 + u * (size_t)dm.cap16 * D;
-  for (size_t i = threadIdx.x; i < (size_t)nw * D; i += blockDim.x) {
-    const int w = (int)(i / D), cc = (int)(i % D);
-    const size_t s = (size_t)(old + w) * D + cc;
-    k16[k16_off(w, cc, D)] = ksrc[s];
-    v16[v16_off(w, cc, D)] = vsrc[s];
-  }
+  // positions and EMA of the (layer, sequence), written by its KV head 0
   if (hk == 0) {
-    for (int i = threadIdx.x; i < n8; i += blockDim.x) {
-      c.pos8[(size_t)lb * dm.cap8 + i] = i;
-      c.ema8[(size_t)lb * dm.cap8 + i] = 0.f;
+    for (int r = threadIdx.x; r < cnt; r += kIngThreads) {
+      if (i8) {
+        c.pos8[(size_t)lb * dm.cap8 + base + r] = base + r;
+        c.ema8[(size_t)lb * dm.cap8 + base + r] = 0.f;
+      } else {
+        c.pos16[(size_t)lb * dm.cap16 + base + r] = gm.old + base + r;
+        c.ema16[(size_t)lb * dm.cap16 + base + r] = 0.f;
+      }
     }
-    for (int w = threadIdx.x; w < nw; w += blockDim.x) {
-      c.pos16[(size_t)lb * dm.cap16 + w] = old + w;
-      c.ema16[(size_t)lb * dm.cap16 + w] = 0.f;
-    }
-    if (threadIdx.x == 0) {
-      c.n8[lb] = n8;
-      c.n16[lb] = nw;
+    if (blockIdx.y == 0 && threadIdx.x == 0) {
+      c.n8[lb] = gm.n8;
+      c.n16[lb] = gm.nw;
       c.t[lb] = L0 - 1;
     }
   }
@@ -133,8 +267,20 @@ __global__ __launch_bounds__(256) void ingest_kernel(conf_cache c, Dims dm, int 
 
 void launch_ingest(const Dims& dm, const conf_cache& c, int layer0, int nl, int L0, const void* k,
                    const void* v, hipStream_t st) {
-  hipLaunchKernelGGL(ingest_kernel, dim3(nl * dm.B * dm.Hkv), dim3(256), 0, st, c, dm, layer0, L0,
-                     (const uint16_t*)k, (const uint16_t*)v);
+  const int units = nl * dm.B * dm.Hkv;
+  const IngGeom gm = ing_geom(dm, L0);
+  const size_t na = (size_t)units * dm.D;
+  const size_t cb = (na + kIngThreads - 1) / kIngThreads;
+  hipLaunchKernelGGL(ingest_clear_kernel, dim3((unsigned)(cb < 1024 ? cb : 1024)),
+                     dim3(kIngThreads), 0, st, c, dm, layer0, units);
+  if (gm.n8 > 0)
+    hipLaunchKernelGGL(ingest_amax_kernel, dim3(units, (gm.n8 + kIngChunk - 1) / kIngChunk),
+                       dim3(kIngThreads), 0, st, c, dm, layer0, L0, (const uint16_t*)k,
+                       (const uint16_t*)v);
+  const int tiles = (gm.n8 + kTile - 1) / kTile + (gm.nw + kTile - 1) / kTile;
+  if (tiles > 0)
+    hipLaunchKernelGGL(ingest_tile_kernel, dim3(units, tiles), dim3(kIngThreads), 0, st, c, dm,
+                       layer0, L0, (const uint16_t*)k, (const uint16_t*)v);
 }
 
 // ---------------------------------------------------------------- compaction + demotion
@@ -258,6 +404,29 @@ __device__ inline int mv_at(const int* lds_mv, const int32_t* gl_mv, int e) {
   return e < 2 * C::MV ? lds_mv[e] : gl_mv[e];
 }
 
+// Bulk copy of `total` elements, element i from src(i) to dst(i), spread over the
+// workgroup: each thread loads a batch of NB elements into registers and only
+// then stores them.  Sources are survivors above the new end and destinations
+// holes below it, so no store of a batch can feed a load of a later one; batching
+// keeps the loads of a batch in flight together (a plain loop waits on every load,
+// since the compiler cannot prove the store does not alias the next load).
+template <int NT, int NB, typename T, typename Src, typename Dst>
+__device__ inline void bulk_copy(int total, Src src, Dst dst) {
+  for (int i0 = threadIdx.x; i0 < total; i0 += NT * NB) {
+    T v[NB];
+#pragma unroll
+    for (int e = 0; e < NB; ++e) {
+      const int i = i0 + e * NT;
+      if (i < total) v[e] = *src(i);
+    }
+#pragma unroll
+    for (int e = 0; e < NB; ++e) {
+      const int i = i0 + e * NT;
+      if (i < total) *dst(i) = v[e];
+    }
+  }
+}
+
 // Steps 2-4 of the compaction for one (layer, sequence), once the keep flags are
 // known: F holds those of slots below kLdsFlags8 / kLdsFlags16, keep8 / wkeep (in
 // global memory) the others; the window flag of the demotee (window slot jd, or
@@ -344,19 +513,31 @@ __device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8
     // Bulk moves: keys as 16-byte chunks (16 channels are contiguous in a key
     // tile), values byte by byte; the move index varies fastest, so neighbouring
     // threads read neighbouring slots of one channel (coalesced sources).
-    for (int i = tid; i < nm8 * dm.Hkv * (D / 16); i += C::NT) {
-      const int k = i % nm8, r = i / nm8, hk = r / (D / 16), cg = r % (D / 16);
-      const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap8 * D;
-      const int src = mv_at<C>(X.mv8, mv8, 2 * k), dst = mv_at<C>(X.mv8, mv8, 2 * k + 1);
-      *(cu4*)(c.k8 + ub + k8_off(dst, 16 * cg, D)) =
-          *(const cu4*)(c.k8 + ub + k8_off(src, 16 * cg, D));
-    }
-    for (int i = tid; i < nm8 * per; i += C::NT) {
-      const int k = i % nm8, r = i / nm8, hk = r / D, ch = r % D;
-      const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap8 * D;
-      const int src = mv_at<C>(X.mv8, mv8, 2 * k), dst = mv_at<C>(X.mv8, mv8, 2 * k + 1);
-      c.v8[ub + v8_off(dst, ch, D)] = c.v8[ub + v8_off(src, ch, D)];
-    }
+    const int kg = D / 16;
+    bulk_copy<C::NT, 2, cu4>(
+        nm8 * dm.Hkv * kg,
+        [&](int i) {
+          const int k = i % nm8, r = i / nm8;
+          const size_t ub = ((size_t)lb * dm.Hkv + r / kg) * (size_t)dm.cap8 * D;
+          return (const cu4*)(c.k8 + ub + k8_off(mv_at<C>(X.mv8, mv8, 2 * k), 16 * (r % kg), D));
+        },
+        [&](int i) {
+          const int k = i % nm8, r = i / nm8;
+          const size_t ub = ((size_t)lb * dm.Hkv + r / kg) * (size_t)dm.cap8 * D;
+          return (cu4*)(c.k8 + ub + k8_off(mv_at<C>(X.mv8, mv8, 2 * k + 1), 16 * (r % kg), D));
+        });
+    bulk_copy<C::NT, 8, int8_t>(
+        nm8 * per,
+        [&](int i) {
+          const int k = i % nm8, r = i / nm8;
+          const size_t ub = ((size_t)lb * dm.Hkv + r / D) * (size_t)dm.cap8 * D;
+          return (const int8_t*)(c.v8 + ub + v8_off(mv_at<C>(X.mv8, mv8, 2 * k), r % D, D));
+        },
+        [&](int i) {
+          const int k = i % nm8, r = i / nm8;
+          const size_t ub = ((size_t)lb * dm.Hkv + r / D) * (size_t)dm.cap8 * D;
+          return c.v8 + ub + v8_off(mv_at<C>(X.mv8, mv8, 2 * k + 1), r % D, D);
+        });
   }
   int8_t code[kDemPer];
   float amax_new[kDemPer], s_old[kDemPer];
@@ -471,20 +652,33 @@ __device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8
     }
     // bulk window moves: keys as 16-byte chunks (8 channels), values element by
     // element, the move index fastest
-    for (int i = tid; i < nm16 * dm.Hkv * (D / 8); i += C::NT) {
-      const int k = i % nm16, r = i / nm16, hk = r / (D / 8), cg = r % (D / 8);
-      const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap16 * D;
-      const int src = mv_at<C>(X.mv16, mv16, 2 * k), dst = mv_at<C>(X.mv16, mv16, 2 * k + 1);
-      uint16_t* k16 = (uint16_t*)c.k16 + ub;
-      *(cu4*)(k16 + k16_off(dst, 8 * cg, D)) = *(const cu4*)(k16 + k16_off(src, 8 * cg, D));
-    }
-    for (int i = tid; i < nm16 * per; i += C::NT) {
-      const int k = i % nm16, r = i / nm16, hk = r / D, ch = r % D;
-      const size_t ub = ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap16 * D;
-      const int src = mv_at<C>(X.mv16, mv16, 2 * k), dst = mv_at<C>(X.mv16, mv16, 2 * k + 1);
-      uint16_t* v16 = (uint16_t*)c.v16 + ub;
-      v16[v16_off(dst, ch, D)] = v16[v16_off(src, ch, D)];
-    }
+    const int wg = D / 8;
+    uint16_t* k16a = (uint16_t*)c.k16;
+    uint16_t* v16a = (uint16_t*)c.v16;
+    bulk_copy<C::NT, 2, cu4>(
+        nm16 * dm.Hkv * wg,
+        [&](int i) {
+          const int k = i % nm16, r = i / nm16;
+          const size_t ub = ((size_t)lb * dm.Hkv + r / wg) * (size_t)dm.cap16 * D;
+          return (const cu4*)(k16a + ub + k16_off(mv_at<C>(X.mv16, mv16, 2 * k), 8 * (r % wg), D));
+        },
+        [&](int i) {
+          const int k = i % nm16, r = i / nm16;
+          const size_t ub = ((size_t)lb * dm.Hkv + r / wg) * (size_t)dm.cap16 * D;
+          return (cu4*)(k16a + ub + k16_off(mv_at<C>(X.mv16, mv16, 2 * k + 1), 8 * (r % wg), D));
+        });
+    bulk_copy<C::NT, 8, uint16_t>(
+        nm16 * per,
+        [&](int i) {
+          const int k = i % nm16, r = i / nm16;
+          const size_t ub = ((size_t)lb * dm.Hkv + r / D) * (size_t)dm.cap16 * D;
+          return (const uint16_t*)(v16a + ub + v16_off(mv_at<C>(X.mv16, mv16, 2 * k), r % D, D));
+        },
+        [&](int i) {
+          const int k = i % nm16, r = i / nm16;
+          const size_t ub = ((size_t)lb * dm.Hkv + r / D) * (size_t)dm.cap16 * D;
+          return v16a + ub + v16_off(mv_at<C>(X.mv16, mv16, 2 * k + 1), r % D, D);
+        });
   }
   if (dest >= 0) {
     // codes of every other INT8 slot of each grown channel: c = clamp(rne((c * s_old) / s_new))

@@ -22,7 +22,18 @@ WORKLOAD_NAMES = (
     "qwen32b_gqa_b8_32k",
     "qwen32b_gqa_b1_32k",
     "gptoss20b_gqa_b32_16k",
+    "gptoss20b_gqa_b32_16k_stress",
 )
+
+# Confidence threshold of the gpt-oss-20b-shaped stress variant: the median of the
+# confidence c over every step and sequence of that workload's own seeded logits
+# (seed 0, 512 steps x 32 sequences, T ~ U[1.5, 3], drawn on the GPU as the bench
+# draws them), as the CPU checker computes it, rounded to float32.  It is the c of
+# one row (step 318, sequence 31), so one step sits at the threshold.  With it
+# about half the steps are confident and a sequence's budget changes on about half
+# of consecutive steps.  Written by tests/golden/make_tau_stress.py into
+# tests/golden/gptoss20b_tau_stress.json.
+TAU_STRESS_GPTOSS = 0.2645609676837921
 
 
 @dataclass(frozen=True)
@@ -141,6 +152,10 @@ def _mk() -> dict:
         name="gptoss20b_gqa_b32_16k", n_layers=24, batch=32, n_q_heads=64, n_kv_heads=8,
         head_dim=64, vocab=201088, dtype16="bf16", window=256, protect=64, n_high=1024,
         n_low=2048, prefill=16384, steps=512, pyramid=True, temp_schedule="uniform")
+    # the same shape with c near tau, so that budgets flip often (the high-temperature
+    # regime the pages single out, where the confidence signal is least informative)
+    w["gptoss20b_gqa_b32_16k_stress"] = replace(
+        w["gptoss20b_gqa_b32_16k"], name="gptoss20b_gqa_b32_16k_stress", tau=TAU_STRESS_GPTOSS)
     return w
 
 

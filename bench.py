@@ -201,15 +201,21 @@ def run(args):
     arkv = wl.policy == "arkv"
     no_conf = trim or arkv  # these policies take no confidence-chosen budget
     t0 = time.perf_counter()
+    ingest_ms = 0.0
     if wl.prefill:
         for l in range(wl.n_layers):
             k, v = synth.prefill_kv(wl, l, args.seed, device=dev)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
             eng.ingest(l, k, v)
+            b.record()
             if trim:
                 eng.set_retention(l, synth.log_beta_prefill(wl, l, args.seed, device=dev))
+            b.synchronize()
+            ingest_ms += a.elapsed_time(b)
             del k, v
     torch.cuda.synchronize()
-    log(f"ingest done in {time.perf_counter() - t0:.1f} s")
+    log(f"ingest done in {time.perf_counter() - t0:.1f} s (conf_cache_ingest {ingest_ms:.1f} ms)")
     L, B = wl.n_layers, wl.batch
     logits = torch.empty(total, B, wl.vocab, dtype=torch.float32, device=dev)
     qs = torch.empty(total, L, B, wl.n_q_heads, wl.head_dim, dtype=eng.dtype16, device=dev)
@@ -413,9 +419,33 @@ def run(args):
                           "frac": round(step_gbs / HBM_PEAK_GBS, 4),
                           "alg_bytes_per_step": int(sum(s_bytes) / len(s_bytes))},
         "step0_ms": None if step0 is None else round(step0, 3),
+        "budgets": None if no_conf else budget_stats(budget[args.warmup:total, :, 0].cpu(), wl),
         "copy_ceiling_GBs": round(copy_ceiling(dev), 1),
+        "ingest": ingest_stats(wl, ingest_ms) if wl.prefill else None,
     }
     return res, wl
+
+
+def ingest_stats(wl, ms):
+    """conf_cache_ingest over every layer: time and algorithmic bytes (the 16-bit
+    prefill read once, the 8-bit codes and the window written).  The kernels read
+    the INT8 part of the prefill twice, once for the absmax and once for the codes."""
+    units = wl.n_layers * wl.batch * wl.n_kv_heads
+    old = max(0, wl.prefill - wl.window)
+    n8 = 0 if wl.policy == "window" else old
+    nw = wl.prefill - old
+    byts = units * wl.head_dim * (2 * 2 * (n8 + nw) + 2 * n8 + 2 * 2 * nw)
+    return {"ms": round(ms, 2), "bytes": byts, "GBs": round(byts / (ms * 1e-3) / 1e9, 1)}
+
+
+def budget_stats(b0, wl):
+    """Budgets the confidence chose in the timed steps (layer 0's column [steps][B]):
+    the fraction of (step, sequence) pairs on the tight budget N_high, and the
+    fraction of sequences whose budget changed from one timed step to the next."""
+    b0 = b0.long()
+    flips = float((b0[1:] != b0[:-1]).float().mean()) if b0.shape[0] > 1 else 0.0
+    return {"confident_fraction": round(float((b0 == wl.n_high).float().mean()), 4),
+            "flip_rate": round(flips, 4)}
 
 
 def _plan_offset(eng):

@@ -23,6 +23,9 @@ selection, and then on even steps the fused selection + compaction, on odd steps
 the two separate ones; on a fused step the kept set is read off the cache after
 compaction.
 """
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -46,6 +49,10 @@ CASES = {
     "qwen32b_gqa_b1_32k": ([(0, 0), (63, 0)], (0, 66)),
     "qwen14b_gqa_b8_8k": ([(0, 3), (47, 6)], (0, 1, 66)),
     "gptoss20b_gqa_b32_16k": ([(0, 0), (23, 31), (11, 17)], (0, 1, 40)),
+    # c near tau: sequence 31's confidence at step 318 is the threshold itself (the
+    # median row); checked steps come in consecutive pairs, so budget flips show
+    "gptoss20b_gqa_b32_16k_stress": ([(0, 31), (23, 31), (11, 17)],
+                                     (0, 1, 317, 318)),
     "gpt2_1layer_b1": ([(0, 0)], (129, 600, 2047)),
     "gpt2_12layer_b8_pyramid": ([(0, 0), (11, 7), (5, 3)], (129, 700, 1500)),
 }
@@ -97,6 +104,7 @@ def test_full_size_sampled_pairs(name):
         main = torch.cuda.current_stream(dev)
         streams = [main, torch.cuda.Stream(dev)]
         side = torch.cuda.Stream(dev)
+    budgets, confs = {}, {}
     for step in range(max(CHECKED) + 1):
         check = step in CHECKED
         z = synth.logits(wl, step, SEED, device=dev)
@@ -134,7 +142,8 @@ def test_full_size_sampled_pairs(name):
         _say("  checking step", step)
         S2 = {s: eng.export(*s) for s in SAMPLES}
         budget_h = budget.cpu().numpy()
-        _check_conf(c.cpu().numpy(), budget_h, z.cpu().numpy().astype(np.float64), wl)
+        budgets[step], confs[step] = budget_h, c.cpu().numpy()
+        _check_conf(confs[step], budget_h, z.cpu().numpy().astype(np.float64), wl)
         keep_h = None if fused else keep.cpu().numpy()
         out_h = out.cpu().numpy()
         qb, kb, vb = bits16(q), bits16(k), bits16(v)
@@ -160,5 +169,18 @@ def test_full_size_sampled_pairs(name):
             _say(f"    {what}: n={len(new_pos)} attention rel err {err:.2e}")
     assert eng.status() == 0
     _say("  worst attention rel err", worst)
+    if name.endswith("_stress"):
+        gold = json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                                           "gptoss20b_tau_stress.json")))
+        s_, b_ = gold["median_step"], gold["median_seq"]
+        # the threshold's own row: c within the tolerance of tau, so both budgets were
+        # accepted there and the GPU's choice drove the oracle (teacher forcing)
+        assert abs(float(confs[s_][b_]) - wl.tau) <= C_TOL
+        z_row = synth.logits(wl, s_, SEED, device=dev)[b_].cpu().numpy().astype(np.float64)
+        assert O.confidence(z_row, wl.w_H, wl.w_m, wl.w_p)["c"] == gold["tau"]
+        flips = [int((budgets[a][:, 0] != budgets[a + 1][:, 0]).sum())
+                 for a in CHECKED if a + 1 in CHECKED]
+        _say("  budget flips between consecutive checked steps:", flips)
+        assert min(flips) >= 1
     del eng, out, q, k, v, z
     torch.cuda.empty_cache()
