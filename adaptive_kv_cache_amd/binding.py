@@ -21,13 +21,14 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libc
 CONF_F16, CONF_BF16 = 1, 2
 DTYPE16 = {"f16": (CONF_F16, torch.float16), "bf16": (CONF_BF16, torch.bfloat16)}
 ST_WINDOW_FULL, ST_INT8_FULL = 1, 2
+STATIC_SCRATCH_BYTES = 32 << 20   # CONF_STATIC_SCRATCH_BYTES: conf_step_static's workspace
 POLICY = {"confkv": 0, "full": 1, "window": 2, "trim": 3, "arkv": 4}
 
 EXPORTED = ("conf_cache_layout", "conf_workspace_bytes", "conf_cache_reset", "conf_cache_ingest",
             "conf_confidence", "conf_decode_attn", "conf_rank_evict", "conf_compact_demote",
             "conf_evict_compact", "conf_attend", "conf_ema_evict_compact",
             "conf_trim_evict_compact", "conf_cache_set_retention", "conf_arkv_evict_compact",
-            "conf_arkv_ema_evict_compact", "conf_step",
+            "conf_arkv_ema_evict_compact", "conf_step", "conf_step_static",
             "conf_cache_export", "conf_last_error", "conf_status_string")
 
 
@@ -82,6 +83,7 @@ def load() -> ctypes.CDLL:
         "conf_arkv_evict_compact": [P, C, c_int32, vp, vp, vp, vp],
         "conf_arkv_ema_evict_compact": [P, C, c_int32, vp, vp, vp, vp],
         "conf_step": [P, C, vp, vp, vp, vp, vp, vp, vp, vp, vp],
+        "conf_step_static": [P, C, vp, vp, vp, vp, vp, vp, vp, vp],
         "conf_cache_export": [P, C, c_int32, c_int32, vp, vp, vp, vp, vp],
     }
     for name, args in sig.items():
@@ -338,7 +340,9 @@ class Engine:
                                            _ptr(budget), _ptr(self.ws), self._stream()),
                "conf_evict_compact")
 
-    def step(self, logits, q, k_new, v_new, out=None, c=None, budget=None):
+    def step(self, logits, q, k_new, v_new, out=None, c=None, budget=None, static=False):
+        """conf_step (static=False, this engine's workspace) or conf_step_static (the
+        library's own static scratch; shapes beyond it raise ConfKVError)."""
         wl = self.wl
         self._expect(logits, (wl.batch, wl.vocab), torch.float32, "logits")
         self._expect(q, (wl.n_layers, wl.batch, wl.n_q_heads, wl.head_dim), self.dtype16, "q")
@@ -354,9 +358,16 @@ class Engine:
         self._expect(out, q.shape, torch.float32, "out")
         self._expect(c, (wl.batch,), torch.float32, "c")
         self._expect(budget, (wl.batch, wl.n_layers), torch.int32, "budget")
-        _check(self.lib.conf_step(ctypes.byref(self.p), ctypes.byref(self.cache), _ptr(logits),
-                                  _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(c),
-                                  _ptr(budget), _ptr(self.ws), self._stream()), "conf_step")
+        if static:
+            _check(self.lib.conf_step_static(ctypes.byref(self.p), ctypes.byref(self.cache),
+                                             _ptr(logits), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                             _ptr(out), _ptr(c), _ptr(budget), self._stream()),
+                   "conf_step_static")
+        else:
+            _check(self.lib.conf_step(ctypes.byref(self.p), ctypes.byref(self.cache),
+                                      _ptr(logits), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out),
+                                      _ptr(c), _ptr(budget), _ptr(self.ws), self._stream()),
+                   "conf_step")
         return out, c, budget
 
     def export(self, layer: int, seq: int) -> dict:

@@ -5,6 +5,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "common.hpp"
 
 namespace confkv {
@@ -407,6 +410,71 @@ int conf_cache_set_retention(const conf_params* p, conf_cache* c, int32_t layer,
   if (prefill_len == 0) return CONF_OK;
   launch_set_retention(d, *c, l0, nl, log_beta, prefill_len, (hipStream_t)stream);
   return check_launch("conf_cache_set_retention");
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- conf_step_static
+// The workspace of conf_step_static: a device array of the library's own, one copy
+// per GPU, held until the process ends.  Host code never passes `scratch` itself to
+// a kernel (on the host it is only a stand-in for the symbol); it uses the device
+// address that hipGetSymbolAddress returns, looked up once per device.
+constexpr size_t kStaticScratchBytes = CONF_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch` (set up on the first call per device).
+int static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "conf_step_static: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) {
+    snprintf(g_err, sizeof g_err, "conf_step_static: device %d beyond the %d supported", dev,
+             kMaxDevices);
+    return CONF_E_UNSUPPORTED;
+  }
+  void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      e = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return fail_hip(e, "conf_step_static: hipGetSymbolAddress");
+      if (!ptr) {
+        snprintf(g_err, sizeof g_err, "conf_step_static: no device address for the scratch array");
+        return CONF_E_HIP;
+      }
+      g_scratch[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return CONF_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int conf_step_static(const conf_params* p, conf_cache* c, const float* logits, const void* q,
+                     const void* k_new, const void* v_new, float* out, float* conf,
+                     int32_t* budget, conf_stream_t stream) {
+  Dims d;
+  int rc = make_dims(p, &d);
+  if (rc) return rc;
+  const size_t need = make_ws(d).total;
+  if (need > kStaticScratchBytes) {  // before any device call
+    snprintf(g_err, sizeof g_err,
+             "conf_step_static: this shape needs %zu bytes of workspace; the static scratch holds "
+             "%zu (use conf_step with a workspace of conf_workspace_bytes())",
+             need, kStaticScratchBytes);
+    return CONF_E_CAPACITY;
+  }
+  void* ws = nullptr;
+  rc = static_scratch(&ws);
+  if (rc) return rc;
+  return conf_step(p, c, logits, q, k_new, v_new, out, conf, budget, ws, stream);
 }
 
 int conf_step(const conf_params* p, conf_cache* c, const float* logits, const void* q,

@@ -379,6 +379,25 @@ int conf_step(const conf_params* p, conf_cache* c, const float* logits, const vo
               void* ws, conf_stream_t stream);
 
 /*
+ * conf_step without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The step's scratch (conf_workspace_bytes() of it) is a
+ * static device array inside the library, CONF_STATIC_SCRATCH_BYTES (32 MiB) per
+ * GPU, which each GPU holds from the library's first use on it until the process
+ * ends; the call allocates nothing.  Shapes whose workspace exceeds that return
+ * CONF_E_CAPACITY before any device work (conf_last_error() says how much they
+ * need).  Every call on one GPU shares that GPU's array and leaves its contents
+ * behind (nothing in it needs to start at zero): calls that overlap on one GPU
+ * race, so a process must order them (one stream, or events).  The first call
+ * on a device looks up the array's device address (hipGetSymbolAddress) and
+ * keeps it; CONF_E_HIP if that fails.  Results are identical to conf_step's.
+ */
+#define CONF_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+int conf_step_static(const conf_params* p, conf_cache* c, const float* logits, const void* q,
+                     const void* k_new, const void* v_new, float* out, float* conf,
+                     int32_t* budget, conf_stream_t stream);
+
+/*
  * Copy one (layer, sequence) into plain row-major arrays in slot order, for
  * inspection: k8, v8: int8 [cap8][Hkv][d]; k16, v16: 16-bit [cap16][Hkv][d].
  * Slots beyond n8 / n16 hold whatever the cache held.
@@ -386,7 +405,8 @@ int conf_step(const conf_params* p, conf_cache* c, const float* logits, const vo
 int conf_cache_export(const conf_params* p, const conf_cache* c, int32_t layer, int32_t seq,
                       int8_t* k8, int8_t* v8, void* k16, void* v16, conf_stream_t stream);
 
-/* Text of the last CONF_E_HIP error on this thread, or of a status code. */
+/* Text of the last CONF_E_HIP error on this thread (and of conf_step_static's
+ * CONF_E_CAPACITY), or of a status code. */
 const char* conf_last_error(void);
 const char* conf_status_string(int status);
 
