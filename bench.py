@@ -256,6 +256,10 @@ def run(args):
         units = L * B * wl.n_kv_heads
         split = "2" if big and units >= 2048 else "1"
     split = int(split)
+    if args.graph:
+        if split != 1 or streams != "1":
+            raise SystemExit("--graph captures one stream: use --split 1 --streams 1 (or auto on a "
+                             "small cache)")
     if split > 1 and side is main:
         side = torch.cuda.Stream(device=dev)  # the halves must not wait on each other
     # Layer halves: two views of the one cache, each with its own workspace, each
@@ -342,14 +346,37 @@ def run(args):
     n8_first.copy_(eng.t_n8)
     n16_first.copy_(eng.t_n16)
     torch.cuda.synchronize()
-    start.record()
-    for st in vstreams[1:]:
-        st.wait_event(start)
-    for i in range(args.steps):
-        one_step(args.warmup + i, evs[i], i)
-    for st in vstreams[1:]:
-        main.wait_stream(st)
-    end.record()
+    if args.graph:
+        # every timed step captured in one HIP graph (kernel nodes, and the plan
+        # copies of the byte model as copy nodes), replayed once in the timed region
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                s = args.warmup + i
+                q_, k_, v_, o_, b_, lb_ = vargs[s][0]
+                if i:
+                    hplan[i - 1].copy_(ws_plans[0])
+                eng.attend(-1, q_, k_, v_, out=o_)
+                if trim:
+                    eng.trim_evict_compact(-1, b_, lb_)
+                elif arkv:
+                    eng.arkv_ema_evict_compact(-1, b_, norig_v[0])
+                else:
+                    eng.confidence(logits[s], c=conf[s], budget=budget[s])
+                    eng.ema_evict_compact(-1, b_)
+        torch.cuda.synchronize()
+        start.record()
+        graph.replay()
+        end.record()
+    else:
+        start.record()
+        for st in vstreams[1:]:
+            st.wait_event(start)
+        for i in range(args.steps):
+            one_step(args.warmup + i, evs[i], i)
+        for st in vstreams[1:]:
+            main.wait_stream(st)
+        end.record()
     for (a, b), wp in zip(ranges, ws_plans):
         hplan[args.steps - 1, a:b].copy_(wp)
     torch.cuda.synchronize()
@@ -357,17 +384,22 @@ def run(args):
     # attention-busy time: the union of every attention launch's [start, end] over the
     # timed region (one launch per step: the sum of their durations; with layer parts
     # on concurrent streams the launches of a step, and of successive steps, overlap)
-    spans = sorted((start.elapsed_time(e[2 * k]), start.elapsed_time(e[2 * k + 1]))
-                   for e in evs for k in range(split))
-    busy, cur0, cur1 = 0.0, None, None
-    for a0, a1 in spans:
-        if cur1 is None or a0 > cur1:
-            busy += 0.0 if cur1 is None else cur1 - cur0
-            cur0, cur1 = a0, a1
-        else:
-            cur1 = max(cur1, a1)
-    busy += cur1 - cur0
-    attn_ms = [busy / args.steps]
+    if args.graph:
+        # no per-launch events inside a graph: the whole step time bounds the
+        # attention's (its rate below is then a lower bound)
+        attn_ms = [ms / args.steps]
+    else:
+        spans = sorted((start.elapsed_time(e[2 * k]), start.elapsed_time(e[2 * k + 1]))
+                       for e in evs for k in range(split))
+        busy, cur0, cur1 = 0.0, None, None
+        for a0, a1 in spans:
+            if cur1 is None or a0 > cur1:
+                busy += 0.0 if cur1 is None else cur1 - cur0
+                cur0, cur1 = a0, a1
+            else:
+                cur1 = max(cur1, a1)
+        busy += cur1 - cur0
+        attn_ms = [busy / args.steps]
     st = eng.status()
     if st:
         raise RuntimeError(f"cache status word {st}: a capacity was exceeded")
@@ -402,10 +434,13 @@ def run(args):
                    "prefill": wl.prefill, "n_high": wl.n_high, "n_low": wl.n_low,
                    "protect": wl.protect, "window": wl.window, "pyramid": wl.pyramid,
                    "vocab": wl.vocab, "mean_tokens_attended": round(n_mean, 1),
-                   "streams": 1 + (split - 1) + (side is not main), "layer_split": split},
+                   "streams": 1 + (split - 1) + (side is not main), "layer_split": split,
+                   "graph": bool(args.graph)},
         "roofline": {"bound": "hbm",
                      "kernel": "attn_kernel (conf_attend; " +
-                               ("one launch per step)" if split == 1 else
+                               ("graph replay of every timed step: duration = the whole step, so "
+                                "the rate is a lower bound)" if args.graph else
+                                "one launch per step)" if split == 1 else
                                 f"{split} concurrent launches per step over layer ranges; "
                                 "duration = attention-busy time per step, the union of all "
                                 "launch intervals)"),
@@ -606,6 +641,9 @@ def main():
     ap.add_argument("--streams", choices=("auto", "1", "2"), default="auto",
                     help="2: confidence on a second stream beside the attention; auto: 2 when "
                          "the attention streams at least 256 MB per launch")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture every timed step in one HIP graph and replay it (one stream, "
+                         "no layer split: for the launch-bound small caches)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--rocpd-summary", metavar="DB",
                     help="print per-kernel durations of a rocprofv3 database and exit")
