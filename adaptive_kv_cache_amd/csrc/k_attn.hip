@@ -56,7 +56,11 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kAttnThreads = kWaves * 64;
-constexpr int kLdsDynBytes = 76 * 1024;  // dynamic LDS of one workgroup (two fit a CU)
+// Dynamic LDS of one workgroup.  At d = 128 as much as lets two workgroups share
+// a compute unit (160 KB) beside their static arrays (2 KB each), so that the
+// 4097-token caches after a long prefill keep more of their scores on chip; at
+// d = 64, whose caches fit either way, 76 KB measured 2% faster than that.
+__host__ __device__ constexpr int lds_dyn_bytes(int D) { return D == 64 ? 76 * 1024 : 79360; }
 
 // ONLINE: scores kept in LDS for the mass; SPILL: the same, with the items from
 // the first one that does not fit in LDS writing their scores to the workspace;
@@ -510,13 +514,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
     const uint16_t* __restrict__ knew_all, const uint16_t* __restrict__ vnew_all,
     float* __restrict__ out_all, float* __restrict__ massp_all, int32_t* __restrict__ snap,
     float* __restrict__ spill_all, int score_cap) {
-  // Dynamic LDS: the query operands, the O merge buffer [4][G][D], and the
-  // scores [G][stride] (apart, so that the O merge runs beside the mass pass).
+  // Dynamic LDS: the query operands, then a region of score_cap | 1 rows for the
+  // scores [G][stride], stride = the unit's LDS-held tokens | 1.  The O merge
+  // buffer [4][G][D] follows the unit's rows when the region has room for both;
+  // otherwise it takes the rows' space once the mass phase has read them.
   // Scores beyond the LDS rows go to spill_all [L][B][Hkv][G][capt].
   extern __shared__ float dyn_lds[];
   u4* s_qops = (u4*)dyn_lds;
-  float* ob = dyn_lds + 4 * qops_u4<D>(dm.G);
-  float* smem = ob + kWaves * dm.G * D;
+  float* smem = dyn_lds + 4 * qops_u4<D>(dm.G);
   __shared__ float s_qscale[kMaxGroup];    // power-of-two scale of the INT8 query
   __shared__ float s_snew[kMaxGroup];      // score of this step's token
   __shared__ float s_m[kWaves][kMaxGroup], s_l[kWaves][kMaxGroup];
@@ -531,7 +536,6 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
   const int lb = layer0 * dm.B + lbl;
   const size_t u = (size_t)lb * dm.Hkv + hk;
   const int G = dm.G;
-  const int stride = score_cap | 1;
   const int8_t* k8 = c.k8 + u * (size_t)dm.cap8 * D;
   const int8_t* v8 = c.v8 + u * (size_t)dm.cap8 * D;
   uint16_t* k16 = (uint16_t*)c.k16 + u * (size_t)dm.cap16 * D;
@@ -581,6 +585,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
   const bool mass = dm.policy == CONF_POLICY_CONFKV || dm.policy == CONF_POLICY_ARKV;
   const int nc = n8 + nw;  // cached tokens (this step's token is handled apart)
   const int jsp = min(spill_start(n8, score_cap), nc);
+  const int stride = jsp | 1;  // odd, so that the 16 heads of a store spread over banks
+  const int region = max(G * (score_cap | 1), kWaves * G * D);
+  const bool ob_apart = G * stride + kWaves * G * D <= region;  // uniform over the workgroup
+  float* ob = ob_apart ? smem + G * stride : smem;
   const ScoreSink sink{smem, stride,
                        make_rsrc(spill_all + u * (size_t)G * dm.capt,
                                  mass && spill_all ? (uint32_t)(G * dm.capt * 4) : 0u),
@@ -681,12 +689,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
                                         head_ok, wa, s_sv, sink, cur);
   // ---- merge the waves' running (max, sum) and add this step's token.  Each
   // wavefront's O (value scale applied, not yet normalised) goes to LDS before
-  // the barrier, and the O merge shares a phase with the mass.
+  // the barrier, and the O merge shares a phase with the mass; when its buffer
+  // reuses the scores' space, O waits in registers until the mass phase is done.
   if (lane < 16) {
     s_m[wave][lane] = wa.m;
     s_l[wave][lane] = wa.l;
   }
-  store_o<D>(wa, ob, G);
+  if (ob_apart) store_o<D>(wa, ob, G);
   __syncthreads();  // also orders the spilled scores before their reads below
   if (tid < G) {
     float M = -INFINITY;
@@ -782,6 +791,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
       massp[dm.cap8 + nw] = s;
     }
   }
+  if (!ob_apart) {
+    __syncthreads();  // every score read: their space takes the O merge buffer
+    store_o<D>(wa, ob, G);
+    __syncthreads();
+  }
   // O = sum over wavefronts of O_w * exp(m_w - lse), plus this step's token
   for (int i = tid; i < G * D; i += kAttnThreads) {
     const int hh = i / D, ch = i % D;
@@ -824,14 +838,14 @@ void launch_ema(const Dims& dm, const conf_cache& c, int layer0, int nl, const f
 }
 
 // Scores one workgroup keeps in LDS (G rows of stride cap | 1, odd so that the
-// 16 heads of a store spread over banks), after the query operands and the O
-// merge buffer.
+// 16 heads of a store spread over banks), after the query operands; the O merge
+// buffer reuses their space after the mass phase.
 static int qops_bytes(const Dims& dm) {
   return 16 * (dm.D == 64 ? qops_u4<64>(dm.G) : qops_u4<128>(dm.G));
 }
 
 int attn_score_cap(const Dims& dm) {
-  int cap = (kLdsDynBytes - qops_bytes(dm) - 4 * kWaves * dm.G * dm.D) / (4 * dm.G) - 1;
+  int cap = (lds_dyn_bytes(dm.D) - qops_bytes(dm)) / (4 * dm.G) - 1;
   cap &= ~1;
   return cap < dm.capt + 2 ? cap : dm.capt + 2;
 }
@@ -847,8 +861,8 @@ size_t attn_spill_bytes(const Dims& dm) {
 
 size_t attn_dyn_lds(const Dims& dm) {
   const size_t sc = (size_t)dm.G * (attn_score_cap(dm) | 1);
-  const size_t ob = (size_t)kWaves * dm.G * dm.D;
-  return (size_t)qops_bytes(dm) + 4 * (ob + sc);
+  const size_t ob = (size_t)kWaves * dm.G * dm.D;  // shares the scores' space
+  return (size_t)qops_bytes(dm) + 4 * (sc > ob ? sc : ob);
 }
 
 template <int D, bool BF16, bool FP8>
@@ -860,7 +874,7 @@ static void launch_t(const Dims& dm, const conf_cache& c, int layer0, int nl, co
   const int slot = current_device_slot();
   if (slot < 0 || !attr_set[slot].load(std::memory_order_acquire)) {
     (void)hipFuncSetAttribute((const void*)attn_kernel<D, BF16, FP8>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kLdsDynBytes);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds_dyn_bytes(D));
     if (slot >= 0) attr_set[slot].store(true, std::memory_order_release);
   }
   hipLaunchKernelGGL((attn_kernel<D, BF16, FP8>), dim3(nl * dm.B * dm.Hkv), dim3(kAttnThreads),

@@ -511,8 +511,10 @@ __device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8
       ema8[dst] = ema8[src];
     }
     // Bulk moves: keys as 16-byte chunks (16 channels are contiguous in a key
-    // tile), values byte by byte; the move index varies fastest, so neighbouring
-    // threads read neighbouring slots of one channel (coalesced sources).
+    // tile), the move index fastest; values byte by byte with the channel fastest:
+    // one token's bytes lie 16 bytes apart in its tile, so a wavefront's 64 channels
+    // of one token fall in eight 128-byte lines (with the move index fastest each
+    // lane touched a line of its own, one request per byte).
     const int kg = D / 16;
     bulk_copy<C::NT, 2, cu4>(
         nm8 * dm.Hkv * kg,
@@ -529,12 +531,12 @@ __device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8
     bulk_copy<C::NT, 8, int8_t>(
         nm8 * per,
         [&](int i) {
-          const int k = i % nm8, r = i / nm8;
+          const int k = i / per, r = i % per;
           const size_t ub = ((size_t)lb * dm.Hkv + r / D) * (size_t)dm.cap8 * D;
           return (const int8_t*)(c.v8 + ub + v8_off(mv_at<C>(X.mv8, mv8, 2 * k), r % D, D));
         },
         [&](int i) {
-          const int k = i % nm8, r = i / nm8;
+          const int k = i / per, r = i % per;
           const size_t ub = ((size_t)lb * dm.Hkv + r / D) * (size_t)dm.cap8 * D;
           return c.v8 + ub + v8_off(mv_at<C>(X.mv8, mv8, 2 * k + 1), r % D, D);
         });
@@ -650,8 +652,8 @@ __device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8
       pos16[dst] = pos16[src];
       ema16[dst] = ema16[src];
     }
-    // bulk window moves: keys as 16-byte chunks (8 channels), values element by
-    // element, the move index fastest
+    // bulk window moves: keys as 16-byte chunks (8 channels), the move index
+    // fastest; values element by element, the channel fastest (as above)
     const int wg = D / 8;
     uint16_t* k16a = (uint16_t*)c.k16;
     uint16_t* v16a = (uint16_t*)c.v16;
@@ -670,12 +672,12 @@ __device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8
     bulk_copy<C::NT, 8, uint16_t>(
         nm16 * per,
         [&](int i) {
-          const int k = i % nm16, r = i / nm16;
+          const int k = i / per, r = i % per;
           const size_t ub = ((size_t)lb * dm.Hkv + r / D) * (size_t)dm.cap16 * D;
           return (const uint16_t*)(v16a + ub + v16_off(mv_at<C>(X.mv16, mv16, 2 * k), r % D, D));
         },
         [&](int i) {
-          const int k = i % nm16, r = i / nm16;
+          const int k = i / per, r = i % per;
           const size_t ub = ((size_t)lb * dm.Hkv + r / D) * (size_t)dm.cap16 * D;
           return v16a + ub + v16_off(mv_at<C>(X.mv16, mv16, 2 * k + 1), r % D, D);
         });

@@ -129,11 +129,11 @@ def tiny_workloads() -> dict:
         name="gqa16_bf16_d64_wide", n_layers=1, batch=2, n_q_heads=16, n_kv_heads=1,
         head_dim=64, vocab=500, dtype16="bf16", window=64, protect=8, n_high=1300, n_low=1400,
         prefill=2500, steps=6)
-    # d = 128 with 16 query heads: the LDS keeps the scores of about 500 tokens, and
-    # the window of 600 is longer than that, so the items that keep their scores in
+    # d = 128 with 16 query heads: the LDS keeps the scores of about 1040 tokens, and
+    # the window of 1200 is longer than that, so the items that keep their scores in
     # the workspace start inside the window (the INT8 part fits)
     w["gqa16_f16_d128_winspill"] = Workload(
         name="gqa16_f16_d128_winspill", n_layers=1, batch=2, n_q_heads=16, n_kv_heads=1,
-        head_dim=128, vocab=700, dtype16="f16", window=600, protect=50, n_high=700, n_low=900,
-        prefill=1000, steps=8)
+        head_dim=128, vocab=700, dtype16="f16", window=1200, protect=50, n_high=1400,
+        n_low=1700, prefill=1600, steps=8)
     return w
