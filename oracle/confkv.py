@@ -51,6 +51,14 @@ function):
   * pyramid: N_l = floor(N * (2(L-1) - l) / (2(L-1))), i.e. 1.0x at layer 0 and
     0.5x at the last layer; applies to both budgets.
   * attention scale 1/sqrt(d); the new token attends to itself; no mask.
+  * ARKV's prefill phase: each layer's statistics are those of the softmax
+    attention of the first query that attends to the whole prefill (the first
+    decode step's query) over the 16-bit prefill keys; entropy, variance and
+    kurtosis of the weights are each normalised to [0, 1], their mean (with the
+    entropy as 1 - H^) is the layer's concentration, averaged over its query
+    heads; more concentrated counts as more sensitive to precision loss, and the
+    OQ ratio runs linearly from 0.75 (least concentrated layer of the sequence)
+    to 0.95 (most concentrated).
 
 Baseline policies the pages compare CONF-KV with ([Problem] sliding windows,
 [Results] full KV) are the same step under other parameters:
@@ -119,6 +127,8 @@ __all__ = [
     "retention_scores", "trim_step", "joint_keep", "headwise_step",
     "FP8_MAX", "fp8_decode", "fp8_encode", "quant_codes_fp8", "requant_codes_fp8",
     "arkv_stat", "Fp8State", "ingest_fp8", "arkv_step",
+    "ARKV_R_LO", "ARKV_R_HI", "attention_weights_stats", "arkv_prefill_concentration",
+    "arkv_orig_budgets",
 ]
 
 
@@ -807,6 +817,89 @@ def arkv_step(st: Fp8State, q_bits, k_bits, v_bits, N: int, N_O: int, prm: Oracl
         demoted.append(int(st.pos[j]))
         st.quantise(int(j))
     return dict(o=o, p=p, ema=ema64, keep=keep, pos_before=pos_before, demoted=demoted)
+
+
+# --------------------------------------------------------------------------
+# ARKV prefill phase: layer-wise Original budgets from attention statistics
+# [ARKV: Methodology, 1. prefill phase (layer-wise budget assignment)]
+# --------------------------------------------------------------------------
+ARKV_R_LO, ARKV_R_HI = 0.75, 0.95   # the OQ ratios of the least and most concentrated layer
+
+
+def attention_weights_stats(p) -> dict:
+    """Entropy, variance and kurtosis of one attention distribution p over L0
+    tokens (float64), each normalised to [0, 1] so that higher means more
+    concentrated.  [ARKV: prefill statistics: entropy (spatial spread), variance
+    (difference in token weights), kurtosis (shape of the distribution)]
+
+      H^ = -sum p ln p / ln L0                (1: uniform, 0: one token)
+      d  = p - 1/L0                           (deviations from the uniform weight)
+      v^ = L0 * sum d^2 / (L0 - 1)            (the weights' variance over its
+                                               one-token maximum: 0 uniform, 1 one token)
+      k  = L0 * sum d^4 / (sum d^2)^2         (fourth standardised moment of the weights)
+      k^ = ln(max(k, 1)) / ln L0              (0 for uniform weights, where k is undefined)
+      concentration = ((1 - H^) + v^ + k^) / 3
+    Two passes: the deviations are formed from the normalised weights, not from
+    power sums, so near-uniform weights keep their precision.
+    """
+    p = np.asarray(p, F64).ravel()
+    L0 = p.size
+    if L0 < 2:
+        raise ValueError("at least two tokens")
+    pos = p[p > 0]
+    H_hat = float(-np.sum(pos * np.log(pos)) / math.log(L0))
+    d = p - 1.0 / L0
+    s2 = float(np.sum(d * d))
+    s4 = float(np.sum(d ** 4))
+    v_hat = L0 * s2 / (L0 - 1)
+    if s2 > 0.0:
+        kurt = L0 * s4 / (s2 * s2)
+        k_hat = math.log(max(kurt, 1.0)) / math.log(L0)
+    else:
+        kurt, k_hat = float("nan"), 0.0
+    conc = ((1.0 - H_hat) + v_hat + k_hat) / 3.0
+    return dict(H_hat=H_hat, v_hat=v_hat, kurtosis=kurt, k_hat=k_hat, conc=conc)
+
+
+def arkv_prefill_concentration(q, K, group: int) -> np.ndarray:
+    """Per query head of one (layer, sequence): the concentration of the softmax
+    attention of its probe query q [Hq, d] over the prefill keys K [Hkv, L0, d]
+    (float64, scale 1/sqrt(d), KV head h // group), and their mean over the
+    heads as the (layer, sequence)'s value.  Returns [Hq + 1]: the heads' values,
+    then the mean.  [ARKV: prefill phase]"""
+    q = np.asarray(q, F64)
+    K = np.asarray(K, F64)
+    Hq, d = q.shape
+    out = np.zeros(Hq + 1, F64)
+    for h in range(Hq):
+        z = K[h // group] @ q[h] / math.sqrt(d)
+        p = np.exp(z - z.max())
+        p /= p.sum()
+        out[h] = attention_weights_stats(p)["conc"]
+    out[Hq] = out[:Hq].mean()
+    return out
+
+
+def arkv_orig_budgets(conc32, N: int, P: int) -> np.ndarray:
+    """Original budget N_O of each layer of one sequence from its layers'
+    concentrations (float32, one per layer): the most concentrated layer keeps
+    ARKV_R_HI of its N tokens Original, the least ARKV_R_LO, linearly between by
+    concentration; all layers alike give the midpoint.  N_O = max(P, ceil(r N)).
+    Evaluated in float32 one rounding at a time (it decides an integer).
+    [ARKV: prefill phase: layers more sensitive to precision loss get a larger
+    full-precision budget]"""
+    c = np.asarray(conc32, F32)
+    lo, hi = F32(c.min()), F32(c.max())
+    span = F32(hi - lo)
+    r_lo, r_hi = F32(ARKV_R_LO), F32(ARKV_R_HI)
+    width = F32(r_hi - r_lo)
+    if span > F32(0):
+        t = ((c - lo).astype(F32) / span).astype(F32)
+        r = (r_lo + (width * t).astype(F32)).astype(F32)
+    else:
+        r = np.full(c.shape, F32(F32(r_lo + r_hi) / F32(2)), F32)
+    n = np.ceil((r * F32(N)).astype(F32)).astype(np.int64)
+    return np.maximum(n, P).astype(np.int32)
 
 
 def decode_step(states, logits, q_bits, k_bits, v_bits, prm: OracleParams,

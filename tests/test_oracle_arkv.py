@@ -7,10 +7,17 @@ float8_e4m3fn rounding; the quantiser and its requantisation in closed form;
 the score in closed form; and on random runs the invariants that fix the three
 states (exactly min(n, N) tokens kept, at most N_O Original unless protected,
 protected tokens Original, quantised tokens the lowest-ranked Original ones).
+The prefill phase's attention statistics (entropy, variance, kurtosis of the
+weights) are pinned to closed forms and to scipy's own routines, and the layer
+budgets to their endpoints and monotonicity.
 """
+import math
+
 import numpy as np
+import pytest
 import torch
 
+import oracle as O
 from oracle import (FP8_MAX, OracleParams, arkv_stat, arkv_step, encode16, fp8_decode,
                     fp8_encode, ingest_fp8, quant_codes_fp8, requant_codes_fp8)
 
@@ -128,3 +135,98 @@ def test_ingest_quantises_the_old_prefill_to_fp8():
     rel = np.abs(K[old] - x[old])[big] / np.abs(x[old])[big]
     assert rel.max() <= 2.0 ** -4
     assert np.array_equal(K[~old], x[~old])
+
+
+# ---------------------------------------------------------------- prefill statistics
+def test_weight_stats_uniform_and_one_hot_closed_forms():
+    for L0 in (2, 7, 1946):
+        u = O.attention_weights_stats(np.full(L0, 1.0 / L0))
+        assert u["H_hat"] == pytest.approx(1.0, abs=1e-12)
+        assert u["v_hat"] == pytest.approx(0.0, abs=1e-15) and u["k_hat"] == 0.0
+        assert u["conc"] == pytest.approx(0.0, abs=1e-12)
+        e = np.zeros(L0)
+        e[L0 // 3] = 1.0
+        o = O.attention_weights_stats(e)
+        s2 = (L0 - 1) / L0
+        s4 = ((L0 - 1) / L0) ** 4 + (L0 - 1) / L0 ** 4
+        kurt = L0 * s4 / s2 ** 2
+        assert o["H_hat"] == 0.0
+        assert o["v_hat"] == pytest.approx(1.0, rel=1e-12)
+        assert o["kurtosis"] == pytest.approx(kurt, rel=1e-12)
+        assert o["k_hat"] == pytest.approx(math.log(kurt) / math.log(L0), rel=1e-12)
+
+
+def test_weight_stats_two_level_closed_form():
+    L0, k, a = 500, 7, 0.1
+    b = (1.0 - k * a) / (L0 - k)
+    p = np.full(L0, b)
+    p[:k] = a
+    H = -(k * a * math.log(a) + (L0 - k) * b * math.log(b))
+    da, db = a - 1 / L0, b - 1 / L0
+    s2 = k * da ** 2 + (L0 - k) * db ** 2
+    s4 = k * da ** 4 + (L0 - k) * db ** 4
+    r = O.attention_weights_stats(p)
+    assert r["H_hat"] == pytest.approx(H / math.log(L0), rel=1e-12)
+    assert r["v_hat"] == pytest.approx(L0 * s2 / (L0 - 1), rel=1e-12)
+    assert r["kurtosis"] == pytest.approx(L0 * s4 / s2 ** 2, rel=1e-10)
+
+
+def test_weight_stats_agree_with_scipy():
+    """scipy's own entropy and (Pearson, population) kurtosis of the same weights."""
+    import scipy.stats as ss
+    rng = np.random.default_rng(3)
+    for L0 in (64, 1000, 4096):
+        z = rng.standard_normal(L0) * rng.uniform(0.5, 4.0)
+        p = np.exp(z - z.max())
+        p /= p.sum()
+        r = O.attention_weights_stats(p)
+        assert r["H_hat"] == pytest.approx(ss.entropy(p) / math.log(L0), rel=1e-12)
+        assert r["kurtosis"] == pytest.approx(ss.kurtosis(p, fisher=False, bias=True), rel=1e-9)
+        assert r["v_hat"] == pytest.approx(np.var(p) * L0 ** 2 / (L0 - 1), rel=1e-9)
+
+
+def test_sharper_attention_is_more_concentrated():
+    rng = np.random.default_rng(5)
+    z = rng.standard_normal(800)
+    prev = -1.0
+    for beta in (0.0, 0.5, 1.0, 2.0, 4.0, 8.0, 16.0):
+        p = np.exp(beta * z - (beta * z).max())
+        p /= p.sum()
+        c = O.attention_weights_stats(p)["conc"]
+        assert c > prev - 1e-12
+        prev = c
+    assert prev > 0.5
+
+
+def test_prefill_concentration_heads_and_group_mapping():
+    """q = 0 gives uniform attention (0); a query aligned with one key of large norm
+    gives nearly one-hot attention; each query head reads KV head h // group."""
+    rng = np.random.default_rng(9)
+    Hkv, group, L0, d = 2, 3, 300, 64
+    K = rng.standard_normal((Hkv, L0, d))
+    K[1, 17] = 40.0 * np.ones(d) / math.sqrt(d)          # a sharp key in KV head 1 only
+    q = np.zeros((Hkv * group, d))
+    q[3:] = np.ones(d) / math.sqrt(d) * 10.0              # heads 3..5 read KV head 1
+    r = O.arkv_prefill_concentration(q, K, group)
+    assert np.allclose(r[:3], 0.0, atol=1e-12)            # heads 0..2: q = 0, uniform
+    assert np.all(r[3:6] > 0.9)
+    assert r[6] == pytest.approx(r[:6].mean())
+    # the same sharp key in KV head 0 instead: heads 3..5 see no sharp key
+    K2 = K.copy()
+    K2[0, 17], K2[1, 17] = K[1, 17], K[0, 17]
+    r2 = O.arkv_prefill_concentration(q, K2, group)
+    assert np.all(r2[3:6] < 0.2)
+
+
+def test_orig_budgets_endpoints_monotone_and_floor():
+    N, P = 2048, 32
+    c = np.array([0.02, 0.30, 0.11, 0.30, 0.05, 0.21], np.float32)
+    n = O.arkv_orig_budgets(c, N, P)
+    assert n[0] == math.ceil(np.float32(0.75) * N)                   # least concentrated
+    assert n[1] == n[3] == math.ceil(np.float32(0.95) * np.float32(N))  # most concentrated
+    order = np.argsort(c, kind="stable")
+    assert np.all(np.diff(n[order]) >= 0)                            # monotone in c
+    same = O.arkv_orig_budgets(np.full(4, 0.4, np.float32), N, P)
+    assert np.all(same == math.ceil(np.float32(0.85) * N))
+    tiny = O.arkv_orig_budgets(c, 20, 32)                            # never below P
+    assert np.all(tiny == 32)
