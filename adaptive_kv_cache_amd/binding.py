@@ -28,7 +28,8 @@ EXPORTED = ("conf_cache_layout", "conf_workspace_bytes", "conf_cache_reset", "co
             "conf_confidence", "conf_decode_attn", "conf_rank_evict", "conf_compact_demote",
             "conf_evict_compact", "conf_attend", "conf_ema_evict_compact",
             "conf_trim_evict_compact", "conf_cache_set_retention", "conf_arkv_evict_compact",
-            "conf_arkv_ema_evict_compact", "conf_step", "conf_step_static",
+            "conf_arkv_ema_evict_compact", "conf_arkv_prefill_stats", "conf_arkv_orig_budgets",
+            "conf_step", "conf_step_static",
             "conf_cache_export", "conf_last_error", "conf_status_string")
 
 
@@ -82,6 +83,8 @@ def load() -> ctypes.CDLL:
         "conf_cache_set_retention": [P, C, c_int32, vp, c_int32, vp],
         "conf_arkv_evict_compact": [P, C, c_int32, vp, vp, vp, vp],
         "conf_arkv_ema_evict_compact": [P, C, c_int32, vp, vp, vp, vp],
+        "conf_arkv_prefill_stats": [P, c_int32, vp, vp, c_int32, vp, vp, vp],
+        "conf_arkv_orig_budgets": [P, vp, vp, vp],
         "conf_step": [P, C, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         "conf_step_static": [P, C, vp, vp, vp, vp, vp, vp, vp, vp],
         "conf_cache_export": [P, C, c_int32, c_int32, vp, vp, vp, vp, vp],
@@ -303,6 +306,35 @@ class Engine:
         """conf_arkv_ema_evict_compact (after attend): the score EMA, then the same."""
         self._arkv(self.lib.conf_arkv_ema_evict_compact, "conf_arkv_ema_evict_compact", layer,
                    budget, n_orig)
+
+    def arkv_prefill_stats(self, layer: int, q_probe, k_pre, conc=None):
+        """conf_arkv_prefill_stats: the concentration of each (layer, sequence)'s prefill
+        attention (q_probe 16-bit [L][B][Hq][d] or [B][Hq][d], k_pre as for ingest);
+        conc fp32 [L][B], the selected layers' rows written."""
+        wl = self.wl
+        L0 = k_pre.shape[-2]
+        self._expect(q_probe, self._layer_shape(layer, wl.batch, wl.n_q_heads, wl.head_dim),
+                     self.dtype16, "q_probe")
+        self._expect(k_pre, self._layer_shape(layer, wl.batch, wl.n_kv_heads, L0, wl.head_dim),
+                     self.dtype16, "k_pre")
+        if conc is None:
+            conc = torch.zeros(wl.n_layers, wl.batch, dtype=torch.float32, device=self.device)
+        self._expect(conc, (wl.n_layers, wl.batch), torch.float32, "conc")
+        _check(self.lib.conf_arkv_prefill_stats(ctypes.byref(self.p), layer, _ptr(q_probe),
+                                                _ptr(k_pre), L0, _ptr(conc), _ptr(self.ws),
+                                                self._stream()), "conf_arkv_prefill_stats")
+        return conc
+
+    def arkv_orig_budgets(self, conc, n_orig=None):
+        """conf_arkv_orig_budgets: n_orig int32 [B][L] from conc fp32 [L][B]."""
+        wl = self.wl
+        self._expect(conc, (wl.n_layers, wl.batch), torch.float32, "conc")
+        if n_orig is None:
+            n_orig = torch.empty(wl.batch, wl.n_layers, dtype=torch.int32, device=self.device)
+        self._expect(n_orig, (wl.batch, wl.n_layers), torch.int32, "n_orig")
+        _check(self.lib.conf_arkv_orig_budgets(ctypes.byref(self.p), _ptr(conc), _ptr(n_orig),
+                                               self._stream()), "conf_arkv_orig_budgets")
+        return n_orig
 
     def set_retention(self, layer: int, log_beta):
         """conf_cache_set_retention: ln(beta) of the prefill, fp32 [L][B][L0] or

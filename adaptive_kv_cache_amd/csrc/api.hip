@@ -33,6 +33,9 @@ void launch_arkv(const Dims&, const conf_cache&, int, int, const int32_t*, const
                  bool, hipStream_t);
 void launch_set_retention(const Dims&, const conf_cache&, int, int, const float*, int, hipStream_t);
 void launch_export(const Dims&, const conf_cache&, int, int8_t*, int8_t*, void*, void*, hipStream_t);
+void launch_arkv_stats(const Dims&, int, int, int, const void*, const void*, float*, float*,
+                       hipStream_t);
+void launch_arkv_budgets(const Dims&, const float*, int32_t*, hipStream_t);
 }  // namespace confkv
 
 using namespace confkv;
@@ -141,6 +144,8 @@ WsMap make_ws(const Dims& d) {
   const size_t spill = attn_spill_bytes(d);
   w.spill = spill ? off : 0;
   off = align256(off + spill);
+  w.arkv_part = off;
+  off = align256(off + (d.policy == CONF_POLICY_ARKV ? LB * d.Hkv * sizeof(float) : 0));
   w.total = off;
   return w;
 }
@@ -502,6 +507,32 @@ int conf_step(const conf_params* p, conf_cache* c, const float* logits, const vo
                at<int32_t>(ws, w.mv8), at<int32_t>(ws, w.mv16), at<uint8_t>(ws, w.wkeep),
                at<float>(ws, w.massp), at<int32_t>(ws, w.snap), nullptr, true, st);
   return check_launch("conf_step");
+}
+
+int conf_arkv_prefill_stats(const conf_params* p, int32_t layer, const void* q,
+                            const void* k_pre, int32_t prefill_len, float* conc, void* ws,
+                            conf_stream_t stream) {
+  Dims d;
+  int rc = make_dims(p, &d);
+  if (rc) return rc;
+  int l0, nl;
+  if (d.policy != CONF_POLICY_ARKV || !a16(q) || !a16(k_pre) || !conc || !ws ||
+      prefill_len < 2 || !layer_range(d, layer, &l0, &nl))
+    return CONF_E_INVALID;
+  const WsMap w = make_ws(d);
+  launch_arkv_stats(d, l0, nl, prefill_len, q, k_pre, at<float>(ws, w.arkv_part), conc,
+                    (hipStream_t)stream);
+  return check_launch("conf_arkv_prefill_stats");
+}
+
+int conf_arkv_orig_budgets(const conf_params* p, const float* conc, int32_t* n_orig,
+                           conf_stream_t stream) {
+  Dims d;
+  int rc = make_dims(p, &d);
+  if (rc) return rc;
+  if (d.policy != CONF_POLICY_ARKV || !conc || !n_orig) return CONF_E_INVALID;
+  launch_arkv_budgets(d, conc, n_orig, (hipStream_t)stream);
+  return check_launch("conf_arkv_orig_budgets");
 }
 
 int conf_cache_export(const conf_params* p, const conf_cache* c, int32_t layer, int32_t seq,

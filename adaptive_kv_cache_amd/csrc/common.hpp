@@ -38,6 +38,7 @@ struct WsMap {
   size_t wkeep;       // uint8 [L][B][cap16]      window keep flags minus the demotee
   size_t snap;        // int32 [L][B][3]          (n8, n16, t) before the step's append
   size_t spill;       // float [L][B][Hkv][G][capt] scores beyond the attention's LDS rows
+  size_t arkv_part;   // float [L][B][Hkv]        ARKV prefill statistics per KV head
   size_t total;
   int n_vchunks;      // vocab chunks per sequence in the confidence reduction
 };

@@ -130,9 +130,10 @@ def log_beta_prefill(wl: Workload, layer: int, seed: int, device="cpu", length=N
 
 
 def arkv_n_orig(wl: Workload, seed: int) -> torch.Tensor:
-    """Original-token budget of each layer, int32 [L]: ceil(r_l * N_high) with the
-    layer's OQ ratio r_l ~ U[0.75, 0.95], at least P.  Stands in for the ratios
-    that ARKV derives from prefill attention statistics."""
+    """Original-token budget of each layer, int32 [L]: ceil(r_l * N_high) with a
+    random OQ ratio r_l ~ U[0.75, 0.95], at least P.  For tests of the three-state
+    step that choose their own budgets; ARKV's own budgets follow from the prefill
+    attention statistics (conf_arkv_prefill_stats, conf_arkv_orig_budgets)."""
     g = _gen(seed, _TAG_OQ, 0, "cpu")
     r = 0.75 + 0.2 * torch.rand(wl.n_layers, generator=g, dtype=torch.float64)
     n = torch.ceil(r * wl.n_high).to(torch.int32)

@@ -202,6 +202,11 @@ def run(args):
     no_conf = trim or arkv  # these policies take no confidence-chosen budget
     t0 = time.perf_counter()
     ingest_ms = 0.0
+    if wl.policy == "arkv":
+        # ARKV's prefill phase: the first decode step's queries over each layer's prefill
+        # keys give the layers' concentrations, from which their Original budgets follow
+        q0 = synth.q_new(wl, 0, args.seed, device=dev)
+        conc = torch.zeros(wl.n_layers, wl.batch, dtype=torch.float32, device=dev)
     if wl.prefill:
         for l in range(wl.n_layers):
             k, v = synth.prefill_kv(wl, l, args.seed, device=dev)
@@ -209,6 +214,8 @@ def run(args):
             a.record()
             eng.ingest(l, k, v)
             b.record()
+            if wl.policy == "arkv":
+                eng.arkv_prefill_stats(l, q0[l], k, conc)
             if trim:
                 eng.set_retention(l, synth.log_beta_prefill(wl, l, args.seed, device=dev))
             b.synchronize()
@@ -236,7 +243,8 @@ def run(args):
         budget.fill_(wl.n_high)
     if arkv:
         # ARKV: N = N_high kept tokens, N_O of them Original per the layer's OQ ratio
-        n_orig = synth.arkv_n_orig(wl, args.seed).to(dev)[None, :].repeat(B, 1).contiguous()
+        # from its prefill attention statistics
+        n_orig = eng.arkv_orig_budgets(conc)
     S = wl.n_sub
     n8_first = torch.empty(L, S, dtype=torch.int32, device=dev)
     n16_first = torch.empty_like(n8_first)
@@ -455,6 +463,9 @@ def run(args):
                           "alg_bytes_per_step": int(sum(s_bytes) / len(s_bytes))},
         "step0_ms": None if step0 is None else round(step0, 3),
         "budgets": None if no_conf else budget_stats(budget[args.warmup:total, :, 0].cpu(), wl),
+        "arkv_n_orig": None if not arkv else {
+            "min": int(n_orig.min()), "max": int(n_orig.max()),
+            "mean": round(float(n_orig.float().mean()), 1), "of_N": wl.n_high},
         "copy_ceiling_GBs": round(copy_ceiling(dev), 1),
         "ingest": ingest_stats(wl, ingest_ms) if wl.prefill else None,
     }

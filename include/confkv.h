@@ -22,6 +22,8 @@
  *                 allocation)
  *   [arkv]        the ARKV page, Methodology: three-state assignment;
  *                 decoding-phase token ranking (a related method in the bundle)
+ *   [arkv-prefill] the ARKV page, Methodology: 1. prefill phase (layer-wise
+ *                 budget assignment from entropy, variance and kurtosis)
  *
  * Conventions shared by every call
  *   - Every pointer argument is a DEVICE pointer owned by the caller, except
@@ -357,6 +359,40 @@ int conf_arkv_evict_compact(const conf_params* p, conf_cache* c, int32_t layer,
 int conf_arkv_ema_evict_compact(const conf_params* p, conf_cache* c, int32_t layer,
                                 const int32_t* budget, const int32_t* n_orig, void* ws,
                                 conf_stream_t stream);
+
+/*
+ * ARKV's prefill phase [arkv-prefill] (CONF_POLICY_ARKV only): the statistics
+ * from which each layer's Original budget follows.  For every (layer, sequence)
+ * of the layer selector and each query head h: the softmax, scale 1/sqrt(d), of
+ * the probe query q_h over the prefill keys of KV head h / (Hq/Hkv) gives
+ * weights p over prefill_len = L0 tokens; with d_j = p_j - 1/L0,
+ *   H^ = -sum p ln p / ln L0,   v^ = L0 sum d^2 / (L0 - 1),
+ *   k^ = ln(max(L0 sum d^4 / (sum d^2)^2, 1)) / ln L0  (0 when every d is 0),
+ *   concentration = ((1 - H^) + v^ + k^) / 3,
+ * and conc[l][b] is its mean over the Hq heads (float32; two passes over the
+ * keys, the heads of a KV head summed in order, then the KV heads in order).
+ * q: 16-bit [L][B][Hq][d] (layer = -1) or [B][Hq][d] (layer = l): the first query
+ * that attends to the whole prefill (the first decode step's); k_pre: 16-bit
+ * [L][B][Hkv][L0][d] or [B][Hkv][L0][d], as given to conf_cache_ingest.  conc:
+ * fp32 [L][B]; only the selected layers' rows are written.  CONF_E_INVALID
+ * under any other policy, for L0 < 2, or on a null or misaligned pointer.
+ */
+int conf_arkv_prefill_stats(const conf_params* p, int32_t layer, const void* q,
+                            const void* k_pre, int32_t prefill_len, float* conc, void* ws,
+                            conf_stream_t stream);
+
+/*
+ * ARKV's layer-wise Original budgets [arkv-prefill] (CONF_POLICY_ARKV only) from
+ * conc (fp32 [L][B], conf_arkv_prefill_stats): per sequence b, with lo and hi
+ * the least and largest concentration over its layers, the OQ ratio of layer l
+ * is r = 0.75 + (0.95 - 0.75) (conc - lo) / (hi - lo) (r = (0.75 + 0.95) / 2
+ * when hi = lo): the more concentrated a layer's prefill attention, the more of
+ * its budget stays Original.  n_orig[b][l] = max(P, ceil(r * n_high)), int32
+ * [B][L], computed in float32 one rounding at a time.  n_orig is the n_orig of
+ * conf_arkv_evict_compact / conf_arkv_ema_evict_compact.
+ */
+int conf_arkv_orig_budgets(const conf_params* p, const float* conc, int32_t* n_orig,
+                           conf_stream_t stream);
 
 /*
  * The prefill's retention (CONF_POLICY_TRIM only), right after

@@ -99,10 +99,31 @@ def test_full_size_arkv():
     dev = torch.device("cuda", 0)
     _say("full size arkv: ingest", wl.name, "W", wl.window, "prefill", wl.prefill)
     eng = Engine(wl, dev)
-    _ingest(eng, wl, dev)
+    # ARKV's prefill phase: each layer's Original budget from its prefill attention
+    q0 = synth.q_new(wl, 0, SEED, device=dev)
+    conc = torch.zeros(wl.n_layers, wl.batch, dtype=torch.float32, device=dev)
+    pre = {}
+
+    def stats(l, k, v):
+        eng.arkv_prefill_stats(l, q0[l], k, conc)
+        for (sl, b) in SAMPLES:
+            if sl == l:
+                pre[(l, b)] = bits16(k[b])
+
+    _ingest(eng, wl, dev, check=stats)
     budget = torch.full((wl.batch, wl.n_layers), wl.n_high, dtype=torch.int32, device=dev)
-    n_orig = synth.arkv_n_orig(wl, SEED).to(dev)[None, :].repeat(wl.batch, 1).contiguous()
+    n_orig = eng.arkv_orig_budgets(conc)
     no_h = n_orig.cpu().numpy()
+    conc_h = conc.cpu().numpy()
+    qb0 = bits16(q0)
+    for (l, b) in SAMPLES:
+        ref = O.arkv_prefill_concentration(O.decode16(qb0[l, b], wl.dtype16),
+                                           O.decode16(pre[(l, b)], wl.dtype16), wl.group)
+        assert abs(float(conc_h[l, b]) - ref[-1]) <= 2e-5, ("prefill concentration", l, b)
+    for b in range(wl.batch):
+        assert no_h[b].tolist() == O.arkv_orig_budgets(conc_h[:, b], wl.n_high,
+                                                       wl.protect).tolist(), ("N_O", b)
+    _say("  N_O of sequence 0 over the layers:", sorted(set(no_h[0].tolist())))
     worst = 0.0
     quantised = 0
     for step in range(151):

@@ -9,6 +9,8 @@ oracle is run from a snapshot of the device state copied back before each step
   * keep sets, INT8 codes, absmax, window bits, positions: bit-exact (the oracle's
     selection is fed the device's fp32 EMA, so both rank identical score arrays)
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -843,3 +845,69 @@ def test_ingest_all_layers_at_once(name, policy):
             for key in ea:
                 assert np.array_equal(np.asarray(ea[key]), np.asarray(eb[key])), (l, s_, key)
     assert a.status() == 0 and b.status() == 0
+
+
+@pytest.mark.parametrize("case", ["gqa5_bf16_d128", "gqa8_bf16_d64", "mha16_f16_d128",
+                                  "gqa16_bf16_d64_long"])
+def test_arkv_prefill_budgets(case):
+    """ARKV's prefill phase through the C ABI: each (layer, sequence)'s concentration
+    of the probe queries' attention over the prefill keys within 2e-5 of the
+    oracle's float64 value, and the Original budgets bit-exact against the oracle's
+    float32 mapping of the same (device) concentrations.  Six layers, so the
+    per-sequence spread between the least and most concentrated layer is real;
+    the one-layer shape takes the midpoint."""
+    base = TINY[case]
+    wl = _arkv_wl(base, 4)
+    if case == "gqa5_bf16_d128":
+        wl = wl.scaled(n_layers=6)
+    eng = Engine(wl)
+    q0 = synth.q_new(wl, 0, SEED)
+    conc = torch.zeros(wl.n_layers, wl.batch, dtype=torch.float32, device="cuda")
+    pre = []
+    for l in range(wl.n_layers):
+        k, v = synth.prefill_kv(wl, l, SEED)
+        eng.arkv_prefill_stats(l, q0[l].cuda(), k.cuda(), conc)
+        pre.append(bits16(k))
+    n_orig = eng.arkv_orig_budgets(conc).cpu().numpy()
+    conc_h = conc.cpu().numpy()
+    qb = bits16(q0)
+    worst = 0.0
+    for l in range(wl.n_layers):
+        for b in range(wl.batch):
+            ref = O.arkv_prefill_concentration(O.decode16(qb[l, b], wl.dtype16),
+                                               O.decode16(pre[l][b], wl.dtype16), wl.group)
+            err = abs(float(conc_h[l, b]) - ref[-1])
+            worst = max(worst, err)
+            assert err <= 2e-5, (case, l, b, float(conc_h[l, b]), ref[-1])
+    for b in range(wl.batch):
+        want = O.arkv_orig_budgets(conc_h[:, b], wl.n_high, wl.protect)
+        assert n_orig[b].tolist() == want.tolist(), (case, b)
+    _say("arkv prefill", case, "worst concentration error", worst, "N_O", n_orig[0].tolist())
+
+
+def test_arkv_prefill_special_inputs():
+    """q = 0 gives uniform attention, concentration 0 exactly; a query aligned with
+    one key of large norm gives almost one-hot attention; all layers alike give the
+    midpoint ratio."""
+    wl = _arkv_wl(TINY["gqa5_bf16_d128"], 4).scaled(n_layers=3)
+    eng = Engine(wl)
+    L0, d = 400, wl.head_dim
+    g = torch.Generator().manual_seed(3)
+    k = torch.randn(wl.n_layers, wl.batch, wl.n_kv_heads, L0, d, generator=g)
+    q = torch.zeros(wl.n_layers, wl.batch, wl.n_q_heads, d)
+    # layer 2: every head's query points at key 123 of its KV head, scaled far up
+    for b in range(wl.batch):
+        for h in range(wl.n_q_heads):
+            kv = h // wl.group
+            k[2, b, kv, 123] = 6.0 * torch.ones(d)
+            q[2, b, h] = 6.0 * torch.ones(d)
+    dt = eng.dtype16
+    conc = eng.arkv_prefill_stats(-1, q.to(dt).cuda(), k.to(dt).cuda())
+    c = conc.cpu()
+    assert torch.all(c[0] == 0.0) and torch.all(c[1] == 0.0)
+    assert torch.all(c[2] > 0.9)
+    n = eng.arkv_orig_budgets(conc).cpu()
+    assert torch.all(n[:, 2] == math.ceil(np.float32(0.95) * np.float32(wl.n_high)))
+    assert torch.all(n[:, 0] == max(wl.protect, math.ceil(np.float32(0.75) * wl.n_high)))
+    flat = eng.arkv_orig_budgets(torch.zeros_like(conc)).cpu()
+    assert torch.all(flat == max(wl.protect, math.ceil(np.float32(0.85) * wl.n_high)))
