@@ -79,6 +79,18 @@ __host__ __device__ inline size_t v16_off(int slot, int c, int D) {
   return (size_t)(slot >> 5) * (size_t)(D * 32) + (size_t)(g * D + c) * 8 + (size_t)((a << 2) | b);
 }
 
+// Buffer descriptors over one region.  A load whose offset lies past the range
+// returns zeros without touching memory (and a store there is dropped), so a
+// lane with nothing to access uses kNoItem instead of a branch around the access:
+// a branch around a load makes the compiler's wait counts wait for every load in
+// flight.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kNoItem = 0x7fff0000u;  // beyond every region (all are < 2 GiB)
+
+__device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
 __device__ inline float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 __device__ inline float f16_to_f32(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);

@@ -172,17 +172,9 @@ struct Item {
 // one straight-line load sequence serves both.
 //
 // The item loads go through buffer descriptors (one per region of the
-// unit: INT8 keys, INT8 values, window keys, window values).  A load whose offset
-// lies past a descriptor's range returns zeros without touching memory; an item
-// that does not exist is loaded at kNoItem, so every stage issues the same load
-// instructions with no branch around them, and the compiler's wait counts stay
-// exact (a branch around a load makes them wait for every load in flight).
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-constexpr uint32_t kNoItem = 0x7fff0000u;  // beyond every region (all are < 2 GiB)
-
-__device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
-}
+// unit: INT8 keys, INT8 values, window keys, window values); an item that does
+// not exist is loaded at kNoItem (a zero-returning offset past the range), so
+// every stage issues the same load instructions with no branch around them.
 
 // Keys and values are read once per step: the loads carry the non-temporal cache
 // policy (cache-policy bit 1), which keeps 2.7 GB of single-use data per step

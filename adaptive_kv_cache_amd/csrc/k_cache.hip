@@ -352,10 +352,12 @@ using CompMisc = CompMiscT<CompBig>;
 // first `skip` holes are set aside (the first one's slot goes to *first_hole);
 // hole skip + k receives survivor k: pair k = (survivor k, hole skip + k).
 // `flag(i)` reads slot i's keep flag (i < n).  Returns the number of pairs.
-// Every thread must call it.
+// With ntb > 0, tile_base[T] (T < ntb) receives the number of holes in slots
+// [0, 64T), set-aside ones included.  Every thread must call it.
 template <class C, typename Flag>
 __device__ int build_moves(int n, int nnew, int skip, Flag flag, int* lds_mv, int32_t* gl_mv,
-                           int (*wcnt)[C::W], int* first_hole) {
+                           int (*wcnt)[C::W], int* first_hole, int32_t* tile_base = nullptr,
+                           int ntb = 0) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int end = n > nnew ? n : nnew;
   int hb = 0, sb = 0;
@@ -378,6 +380,8 @@ __device__ int build_moves(int n, int nnew, int skip, Flag flag, int* lds_mv, in
       th += ch;
       ts += cs;
     }
+    // a wavefront's 64 slots are one tile (c0 and the wavefront's offset are multiples of 64)
+    if (lane == 0 && ((c0 >> 6) + wave) < ntb) tile_base[(c0 >> 6) + wave] = hb + oh;
     if (hole) {
       const int r = hb + oh + __popcll(bh & below) - skip;
       if (r < 0) {
@@ -427,6 +431,64 @@ __device__ inline void bulk_copy(int total, Src src, Dst dst) {
   }
 }
 
+// Bulk INT8 value moves by destination run.  A value tile keeps the 16 tokens of
+// each group g in one 16-byte run per channel, so a moved token's bytes lie one per
+// run, 16 bytes apart: moved token by token, every byte is a store of its own into
+// a line it shares with 15 other tokens.  Here each wavefront takes one (KV head,
+// destination tile) at a time and rebuilds the tile's runs whole: it reads a run,
+// puts each hole's byte from the survivor that fills it (byte loads, every one of
+// a run issued before the first wait, those of slots that receive nothing at
+// kNoItem) and writes the run back, so that the stores are 16 bytes per lane and
+// contiguous over the lanes.  Hole r (over all holes in slot order, less the
+// `skip` set aside) takes survivor r: its rank is tile_base[T] plus the tile's holes
+// below it.  Each run belongs to one item; the bytes of slots that receive nothing
+// are written back as read (survivors in the last tile, which are sources, keep
+// their values).  All threads call it; no barrier.
+template <class C, typename Flag>
+__device__ void v8_moves_by_run(const conf_cache& c, const Dims& dm, int lb, int n8, int n8end,
+                                int skip, Flag flag, const int* lds_mv, const int32_t* gl_mv,
+                                const int32_t* tile_base) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int D = dm.D;
+  const int ntiles = (n8end + 63) >> 6;
+  const uint32_t tile_bytes = (uint32_t)(kTile * D);
+  for (int item = wave; item < ntiles * dm.Hkv; item += C::W) {
+    const int T = item / dm.Hkv, hk = item % dm.Hkv;
+    const int s = 64 * T + lane;
+    const bool hole = s < n8end && !(s < n8 && flag(s));
+    const unsigned long long bh = __ballot(hole);
+    const int rank = tile_base[T] + __popcll(bh & ((1ull << lane) - 1ull)) - skip;
+    const int src = hole && rank >= 0 ? mv_at<C>(lds_mv, gl_mv, 2 * rank) : -1;
+    if (__ballot(src >= 0) == 0ull) continue;  // nothing lands in this tile
+    const rsrc_t rv = make_rsrc(c.v8 + ((size_t)lb * dm.Hkv + hk) * (size_t)dm.cap8 * D,
+                                (uint32_t)dm.cap8 * D);
+    // lane `lane` takes the runs (g, ch) = divmod(lane + 64 i, D), i = 0 .. 4D/64 - 1
+    for (int i = 0; i < 4 * D / 64; ++i) {
+      const int g = (64 * i) / D, ch = (64 * i) % D + lane;  // g is uniform
+      const uint32_t ro = (uint32_t)T * tile_bytes + (uint32_t)(g * D + ch) * 16u;
+      cu4 run = __builtin_bit_cast(cu4, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)ro, 0, 0));
+      uint32_t by[16];
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        // byte x of a run is slot 32u + 16a + 4g + b of the tile, x = 8u + 4a + b
+        const int j = 32 * (x >> 3) + 16 * ((x >> 2) & 1) + 4 * g + (x & 3);
+        const int sx = __builtin_amdgcn_readlane(src, j);
+        const uint32_t off = sx >= 0 ? (uint32_t)v8_off(sx, ch, D) : kNoItem;
+        by[x] = __builtin_amdgcn_raw_buffer_load_b8(rv, (int)off, 0, 0);
+      }
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int j = 32 * (x >> 3) + 16 * ((x >> 2) & 1) + 4 * g + (x & 3);
+        if (__builtin_amdgcn_readlane(src, j) >= 0) {
+          const int sh = 8 * (x & 3);
+          run[x >> 2] = (run[x >> 2] & ~(0xffu << sh)) | ((by[x] & 0xffu) << sh);
+        }
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(run, rv, (int)ro, 0, 0);
+    }
+  }
+}
+
 // Steps 2-4 of the compaction for one (layer, sequence), once the keep flags are
 // known: F holds those of slots below kLdsFlags8 / kLdsFlags16, keep8 / wkeep (in
 // global memory) the others; the window flag of the demotee (window slot jd, or
@@ -453,10 +515,13 @@ __device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8
   // INT8 token, so nothing moves); without one it ends at n8'.
   const bool demote = jd >= 0 && n8n < dm.cap8;
   const int n8end = n8n + (demote ? 1 : 0);
-  const int nm8 = build_moves<C>(
-      n8, n8end, demote ? 1 : 0,
-      [&](int i) { return i < C::F8 ? F.k8[i] != 0 : keep8[i] != 0; }, X.mv8, mv8, M.wcnt,
-      &M.first_hole);
+  auto flag8 = [&](int i) { return i < C::F8 ? F.k8[i] != 0 : keep8[i] != 0; };
+  // per-tile hole counts for the run-based value moves, in the part of the
+  // workspace move list that the LDS list stands for (entries below 2 * C::MV)
+  const int ntiles8 = (n8end + 63) >> 6;
+  const int ntb = ntiles8 <= 2 * C::MV ? ntiles8 : 0;
+  const int nm8 = build_moves<C>(n8, n8end, demote ? 1 : 0, flag8, X.mv8, mv8, M.wcnt,
+                                 &M.first_hole, mv8, ntb);
   const int nm16 = build_moves<C>(
       n16, n16n, 0, [&](int w) { return w < C::F16 ? F.k16[w] != 0 : wkeep[w] != 0; },
       X.mv16, mv16, M.wcnt, &M.first_hole);
@@ -528,18 +593,23 @@ __device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8
           const size_t ub = ((size_t)lb * dm.Hkv + r / kg) * (size_t)dm.cap8 * D;
           return (cu4*)(c.k8 + ub + k8_off(mv_at<C>(X.mv8, mv8, 2 * k + 1), 16 * (r % kg), D));
         });
-    bulk_copy<C::NT, 8, int8_t>(
-        nm8 * per,
-        [&](int i) {
-          const int k = i / per, r = i % per;
-          const size_t ub = ((size_t)lb * dm.Hkv + r / D) * (size_t)dm.cap8 * D;
-          return (const int8_t*)(c.v8 + ub + v8_off(mv_at<C>(X.mv8, mv8, 2 * k), r % D, D));
-        },
-        [&](int i) {
-          const int k = i / per, r = i % per;
-          const size_t ub = ((size_t)lb * dm.Hkv + r / D) * (size_t)dm.cap8 * D;
-          return c.v8 + ub + v8_off(mv_at<C>(X.mv8, mv8, 2 * k + 1), r % D, D);
-        });
+    // Values: by destination run once the moves average four or more per tile
+    // (whole runs then cost less than single-byte stores), else byte by byte.
+    if (ntb > 0 && 16 * nm8 >= n8end)
+      v8_moves_by_run<C>(c, dm, lb, n8, n8end, demote ? 1 : 0, flag8, X.mv8, mv8, mv8);
+    else
+      bulk_copy<C::NT, 8, int8_t>(
+          nm8 * per,
+          [&](int i) {
+            const int k = i / per, r = i % per;
+            const size_t ub = ((size_t)lb * dm.Hkv + r / D) * (size_t)dm.cap8 * D;
+            return (const int8_t*)(c.v8 + ub + v8_off(mv_at<C>(X.mv8, mv8, 2 * k), r % D, D));
+          },
+          [&](int i) {
+            const int k = i / per, r = i % per;
+            const size_t ub = ((size_t)lb * dm.Hkv + r / D) * (size_t)dm.cap8 * D;
+            return c.v8 + ub + v8_off(mv_at<C>(X.mv8, mv8, 2 * k + 1), r % D, D);
+          });
   }
   int8_t code[kDemPer];
   float amax_new[kDemPer], s_old[kDemPer];

@@ -122,9 +122,9 @@ class Workload:
                            n_high=m, n_low=m, pyramid=False, prefill=min(self.prefill, m),
                            needle=False)
         if policy == "arkv":
-            # N = N_high kept tokens, at most 95% of them Original (the OQ ratios are
-            # drawn per layer in [0.75, 0.95]); the window arrays hold the Original
-            # ones; the page's example protects the newest 32
+            # N = N_high kept tokens, at most 95% of them Original (the layers' OQ
+            # ratios lie in [0.75, 0.95]); the window arrays hold the Original ones;
+            # the page's example protects the newest 32
             n = self.n_high
             w = -(-95 * n // 100)
             return replace(self, name=f"{self.name}_arkv", policy="arkv", window=w,

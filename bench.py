@@ -44,7 +44,9 @@ stores the new token's ln(beta), ranks by (t - pos) * ln(beta) and compacts, wit
 
 Besides the steady-state figures, the JSON line reports step0_ms, the one-off first
 step after the prefill (the cut of the prefilled cache to its budget), timed on its
-own during warm-up, and copy_ceiling_GBs, the best rate of a plain 2 GiB device copy
+own during warm-up (after one step of a one-layer copy of the workload and a first
+use of every stream, so that it holds the step's work and not the process's first
+kernel launches or queue set-up), and copy_ceiling_GBs, the best rate of a plain 2 GiB device copy
 on the same box (bytes read + written), as a measured ceiling next to the nominal
 8 TB/s.
 
@@ -186,6 +188,40 @@ def cpu_baseline(wl, seed, n_tokens, first_step, budget_s=20.0):
 
 
 # ---------------------------------------------------------------- GPU run
+def prime_kernels(wl, dev, seed):
+    """One decode step of a one-layer, one-sequence copy of the workload (same head
+    shape, precision and policy, a shorter prefill), so that every kernel the step
+    launches has been launched once in this process before step 0 is timed: a
+    kernel's first launch loads its code and sets its attributes, a one-off cost of
+    the process rather than of the step."""
+    small = wl.scaled(n_layers=1, batch=1,
+                      prefill=min(wl.prefill, 2 * (wl.n_low + wl.window)) if wl.prefill else 0)
+    e = Engine(small, dev)
+    if small.prefill:
+        k, v = synth.prefill_kv(small, 0, seed, device=dev)
+        e.ingest(0, k, v)
+        if small.policy == "arkv":
+            conc = e.arkv_prefill_stats(0, synth.q_new(small, 0, seed, device=dev)[0], k)
+        if small.policy == "trim":
+            e.set_retention(0, synth.log_beta_prefill(small, 0, seed, device=dev))
+    q = synth.q_new(small, 0, seed, device=dev)
+    k, v = synth.kv_new(small, 0, seed, device=dev)
+    e.attend(-1, q, k, v)
+    if small.policy == "trim":
+        e.trim_evict_compact(-1, torch.full((1, 1), small.n_high, dtype=torch.int32, device=dev),
+                             synth.log_beta_new(small, 0, seed, device=dev))
+    elif small.policy == "arkv":
+        budget = torch.full((1, 1), small.n_high, dtype=torch.int32, device=dev)
+        n_orig = e.arkv_orig_budgets(conc) if small.prefill else budget.clone()
+        e.arkv_ema_evict_compact(-1, budget, n_orig)
+    else:
+        _, budget = e.confidence(synth.logits(small, 0, seed, device=dev))
+        e.ema_evict_compact(-1, budget)
+    torch.cuda.synchronize()
+    del e
+    torch.cuda.empty_cache()
+
+
 def run(args):
     wl = WORKLOADS[args.workload].baseline(args.policy, args.warmup + args.steps)
     if args.headwise:
@@ -196,6 +232,7 @@ def run(args):
     if total > wl.steps:
         log(f"note: {total} steps exceed the workload's {wl.steps}; inputs are generated anyway")
     log(f"set-up {wl.name}: cap8={wl.cap8} prefill={wl.prefill}")
+    prime_kernels(wl, dev, args.seed)
     eng = Engine(wl, dev)
     trim = wl.policy == "trim"
     arkv = wl.policy == "arkv"
@@ -293,6 +330,10 @@ def run(args):
         vargs = [[(qs[s][a:b], ks[s][a:b], vs[s][a:b], out[a:b], bsl[k][s],
                    lbetas[s][a:b] if trim else None) for k, (a, b) in enumerate(ranges)]
                  for s in range(total)]
+    # a stream's first use sets up its hardware queue: done here, not inside step 0
+    for st in {id(x): x for x in vstreams + [side]}.values():
+        with torch.cuda.stream(st):
+            torch.zeros(1, device=dev)
     torch.cuda.synchronize()
     log(f"inputs resident; warm-up (streams {streams}, layer split {split})")
 
