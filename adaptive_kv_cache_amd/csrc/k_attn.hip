@@ -58,9 +58,15 @@ constexpr int kWaves = 4;
 constexpr int kAttnThreads = kWaves * 64;
 // Dynamic LDS of one workgroup.  At d = 128 as much as lets two workgroups share
 // a compute unit (160 KB) beside their static arrays (2 KB each), so that the
-// 4097-token caches after a long prefill keep more of their scores on chip; at
-// d = 64, whose caches fit either way, 76 KB measured 2% faster than that.
-__host__ __device__ constexpr int lds_dyn_bytes(int D) { return D == 64 ? 76 * 1024 : 79360; }
+// 4097-token caches after a long prefill keep more of their scores on chip.  At
+// d = 64 the kernel needs 128 registers, so four workgroups can share a compute
+// unit when each takes 38 KB: the units of a d = 64 cache are small (about 1000
+// tokens of 128 bytes), their fixed phases (set-up, merge, mass) weigh more, and
+// more resident workgroups hide them (measured: attention 0.51 -> 0.55 of 8 TB/s
+// on the gpt-oss-20b-shaped cache, against two 76 KB workgroups).
+__host__ __device__ constexpr int lds_dyn_bytes(int D) { return D == 64 ? 38 * 1024 : 79360; }
+// resident workgroups per compute unit the register budget is set for
+__host__ __device__ constexpr int attn_min_blocks(int D) { return D == 64 ? 4 : 2; }
 
 // ONLINE: scores kept in LDS for the mass; SPILL: the same, with the items from
 // the first one that does not fit in LDS writing their scores to the workspace;
@@ -501,7 +507,7 @@ __host__ __device__ inline int spill_start(int n8, int cap) {
 // sequence)'s sizes before this step in `snap` [L][B][3] = (n8, n16, t) for the
 // EMA kernel, which must not read the counters it advances.
 template <int D, bool BF16, bool FP8>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(
+__global__ __launch_bounds__(kAttnThreads, attn_min_blocks(D)) void attn_kernel(
     conf_cache c, Dims dm, int layer0, const uint16_t* __restrict__ q_all,
     const uint16_t* __restrict__ knew_all, const uint16_t* __restrict__ vnew_all,
     float* __restrict__ out_all, float* __restrict__ massp_all, int32_t* __restrict__ snap,
