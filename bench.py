@@ -586,7 +586,7 @@ def rocpd_summary(db_path, timed_steps, split=1):
 
 
 # ---------------------------------------------------------------- counters
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_qwen32b_b8_32k.md")
+PROFILES = os.path.join(ROOT, "profiles")  # counter summaries: attn_traffic_*.md
 ATTN_SOURCES = ("adaptive_kv_cache_amd/csrc/k_attn.hip", "adaptive_kv_cache_amd/csrc/common.hpp")
 
 
@@ -606,17 +606,21 @@ def stored_traffic(workload, steps, warmup, tokens):
     and the 2065-token steady state stream different bytes), on the same attention
     sources.  None when no such line exists."""
     try:
-        text = open(TRAFFIC_FILE).read()
+        names = sorted(f for f in os.listdir(PROFILES)
+                       if f.startswith("attn_traffic_") and f.endswith(".md"))
     except OSError:
         return None
     want = {"workload": workload, "steps": str(steps), "warmup": str(warmup),
             "tokens": f"{tokens:.1f}", "source": attn_source_hash()}
-    for line in text.splitlines():
-        if not line.startswith("traffic:"):
-            continue
-        vals = dict(kv.partition("=")[::2] for kv in line[len("traffic:"):].split())
-        if all(vals.get(k) == v for k, v in want.items()):
-            return int(vals["bytes_per_launch"])
+    for name in names:
+        with open(os.path.join(PROFILES, name)) as fh:
+            text = fh.read()
+        for line in text.splitlines():
+            if not line.startswith("traffic:"):
+                continue
+            vals = dict(kv.partition("=")[::2] for kv in line[len("traffic:"):].split())
+            if all(vals.get(k) == v for k, v in want.items()):
+                return int(vals["bytes_per_launch"])
     return None
 
 

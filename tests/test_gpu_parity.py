@@ -619,7 +619,7 @@ def _arkv_cases():
 
 def _arkv_wl(base, steps):
     # the full prefill, so that ingest quantises its older part to e4m3 and the first
-    # step after a long one takes the two-pass attention over FP8 tokens
+    # step after a long one attends past the LDS score rows over FP8 tokens
     return base.baseline("arkv", steps).scaled(prefill=base.prefill)
 
 
