@@ -354,53 +354,89 @@ using CompMisc = CompMiscT<CompBig>;
 // `flag(i)` reads slot i's keep flag (i < n).  Returns the number of pairs.
 // With ntb > 0, tile_base[T] (T < ntb) receives the number of holes in slots
 // [0, 64T), set-aside ones included.  Every thread must call it.
+//
+// Each wavefront takes a contiguous range of 64-slot tiles.  It counts its holes
+// and survivors with ballots, one barrier exchanges the counts, and a second walk
+// over its tiles writes the pairs from its offsets: two barriers in all, where a
+// workgroup-wide pass per 512 slots took two per pass (the steady state's caches
+// have a hole or two in thousands of slots).  The flags of four tiles are read
+// together.
 template <class C, typename Flag>
 __device__ int build_moves(int n, int nnew, int skip, Flag flag, int* lds_mv, int32_t* gl_mv,
                            int (*wcnt)[C::W], int* first_hole, int32_t* tile_base = nullptr,
                            int ntb = 0) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int end = n > nnew ? n : nnew;
-  int hb = 0, sb = 0;
-  for (int c0 = 0; c0 < end; c0 += C::NT) {
-    const int i = c0 + tid;
-    const bool k = i < n && flag(i);
-    const bool hole = i < nnew && !k, surv = i >= nnew && k;
-    const unsigned long long bh = __ballot(hole), bs = __ballot(surv);
-    const unsigned long long below = (1ull << lane) - 1ull;
-    if (lane == 0) {
-      wcnt[0][wave] = __popcll(bh);
-      wcnt[1][wave] = __popcll(bs);
+  const int ntiles = (end + 63) >> 6;
+  const int t0 = (int)((long long)ntiles * wave / C::W);
+  const int t1 = (int)((long long)ntiles * (wave + 1) / C::W);
+  const unsigned long long below = (1ull << lane) - 1ull;
+  constexpr int kU = 4;
+  auto tile_masks = [&](int T0, unsigned long long (&bh)[kU], unsigned long long (&bs)[kU]) {
+    bool kk[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = 64 * (T0 + u) + lane;
+      kk[u] = T0 + u < t1 && i < n && flag(i);
     }
-    __syncthreads();
-    int oh = 0, os = 0, th = 0, ts = 0;
-    for (int w = 0; w < C::W; ++w) {
-      const int ch = wcnt[0][w], cs = wcnt[1][w];
-      oh += w < wave ? ch : 0;
-      os += w < wave ? cs : 0;
-      th += ch;
-      ts += cs;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = 64 * (T0 + u) + lane;
+      const bool in = T0 + u < t1;
+      bh[u] = __ballot(in && i < nnew && !kk[u]);
+      bs[u] = __ballot(in && i >= nnew && kk[u]);
     }
-    // a wavefront's 64 slots are one tile (c0 and the wavefront's offset are multiples of 64)
-    if (lane == 0 && ((c0 >> 6) + wave) < ntb) tile_base[(c0 >> 6) + wave] = hb + oh;
-    if (hole) {
-      const int r = hb + oh + __popcll(bh & below) - skip;
-      if (r < 0) {
-        if (r == -skip) *first_hole = i;
-      } else if (r < C::MV) {
-        lds_mv[2 * r + 1] = i;
-      } else {
-        gl_mv[2 * r + 1] = i;
-      }
+  };
+  int ch = 0, cs = 0;
+  for (int T0 = t0; T0 < t1; T0 += kU) {
+    unsigned long long bh[kU], bs[kU];
+    tile_masks(T0, bh, bs);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      ch += __popcll(bh[u]);
+      cs += __popcll(bs[u]);
     }
-    if (surv) {
-      const int r = sb + os + __popcll(bs & below);
-      if (r < C::MV) lds_mv[2 * r] = i; else gl_mv[2 * r] = i;
-    }
-    hb += th;
-    sb += ts;
-    __syncthreads();
   }
-  return hb - skip;  // holes below the new end, less those set aside = survivors above it
+  if (lane == 0) {
+    wcnt[0][wave] = ch;
+    wcnt[1][wave] = cs;
+  }
+  __syncthreads();
+  int hb = 0, sb = 0, th = 0;
+  for (int w = 0; w < C::W; ++w) {
+    const int a = wcnt[0][w], b = wcnt[1][w];
+    hb += w < wave ? a : 0;
+    sb += w < wave ? b : 0;
+    th += a;
+  }
+  for (int T0 = t0; T0 < t1; T0 += kU) {
+    unsigned long long bh[kU], bs[kU];
+    tile_masks(T0, bh, bs);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (T0 + u >= t1) break;  // uniform
+      const int i = 64 * (T0 + u) + lane;
+      if (lane == 0 && T0 + u < ntb) tile_base[T0 + u] = hb;
+      if ((bh[u] >> lane) & 1ull) {
+        const int r = hb + __popcll(bh[u] & below) - skip;
+        if (r < 0) {
+          if (r == -skip) *first_hole = i;
+        } else if (r < C::MV) {
+          lds_mv[2 * r + 1] = i;
+        } else {
+          gl_mv[2 * r + 1] = i;
+        }
+      }
+      if ((bs[u] >> lane) & 1ull) {
+        const int r = sb + __popcll(bs[u] & below);
+        if (r < C::MV) lds_mv[2 * r] = i; else gl_mv[2 * r] = i;
+      }
+      hb += __popcll(bh[u]);
+      sb += __popcll(bs[u]);
+    }
+  }
+  __syncthreads();  // the lists, the first hole and the tile counts are complete
+  return th - skip;  // holes below the new end, less those set aside = survivors above it
 }
 
 template <class C>
@@ -892,7 +928,12 @@ __device__ inline void ema_pairs(const conf_cache& c, const Dims& dm, int lb,
   const int32_t* pos8 = c.pos8 + (size_t)lb * dm.cap8;
   int32_t* pos16 = c.pos16 + (size_t)lb * dm.cap16;
   const float hq = (float)dm.Hq;
-  constexpr int kT = 5;  // one round up to 2560 tokens, within 80 VGPRs (6 waves/SIMD)
+  // Four tokens per thread and round; the mass rows of up to eight KV heads are
+  // loaded together with the EMA and positions, and only then summed (in head
+  // order): one memory round trip per round and eight heads, within 80 VGPRs
+  // (6 waves/SIMD).  (A loop over the heads that summed as it loaded waited once
+  // per unrolled pair of heads.)
+  constexpr int kT = 4, kHC = 8;
   for (int jb = threadIdx.x; jb < end; jb += kT * kCompThreads) {
     int idx[kT], po[kT];
     float a[kT], eo[kT];
@@ -905,10 +946,22 @@ __device__ inline void ema_pairs(const conf_cache& c, const Dims& dm, int lb,
       po[k] = j < n8 ? pos8[idx[k]] : pos16[w];
       a[k] = 0.f;
     }
-#pragma unroll 2
-    for (int hk = 0; hk < dm.Hkv; ++hk)
+    for (int h0 = 0; h0 < dm.Hkv; h0 += kHC) {
+      float r[kHC][kT];
 #pragma unroll
-      for (int k = 0; k < kT; ++k) a[k] += rows[(size_t)hk * dm.capt + idx[k]];
+      for (int i = 0; i < kHC; ++i) {
+        // heads past the last read the last one's row again and are not added
+        const int hk = min(h0 + i, dm.Hkv - 1);
+#pragma unroll
+        for (int k = 0; k < kT; ++k) r[i][k] = rows[(size_t)hk * dm.capt + idx[k]];
+      }
+#pragma unroll
+      for (int i = 0; i < kHC; ++i)
+        if (h0 + i < dm.Hkv) {
+#pragma unroll
+          for (int k = 0; k < kT; ++k) a[k] += r[i][k];
+        }
+    }
 #pragma unroll
     for (int k = 0; k < kT; ++k) {
       const int j = jb + k * kCompThreads;
@@ -1053,13 +1106,27 @@ __device__ inline void arkv_pairs(const conf_cache& c, const Dims& dm, int lb,
       a[k] = 0.f;
       a2[k] = 0.f;
     }
-    for (int hk = 0; hk < dm.Hkv; ++hk)
+    // up to eight KV heads' rows loaded together, then summed in head order (as in
+    // ema_pairs)
+    constexpr int kHC = 8;
+    for (int h0 = 0; h0 < dm.Hkv; h0 += kHC) {
+      float r[kHC][kT];
 #pragma unroll
-      for (int k = 0; k < kT; ++k) {
-        const float r = rows[(size_t)hk * dm.capt + idx[k]];
-        a[k] += r;
-        a2[k] += r * r;
+      for (int i = 0; i < kHC; ++i) {
+        const int hk = min(h0 + i, dm.Hkv - 1);
+#pragma unroll
+        for (int k = 0; k < kT; ++k) r[i][k] = rows[(size_t)hk * dm.capt + idx[k]];
       }
+#pragma unroll
+      for (int i = 0; i < kHC; ++i)
+        if (h0 + i < dm.Hkv) {
+#pragma unroll
+          for (int k = 0; k < kT; ++k) {
+            a[k] += r[i][k];
+            a2[k] += r[i][k] * r[i][k];
+          }
+        }
+    }
 #pragma unroll
     for (int k = 0; k < kT; ++k) {
       const int j = jb + k * kCompThreads;
