@@ -1257,7 +1257,10 @@ __global__ __launch_bounds__(kCompThreads) void arkv_kernel(
 // token, each the lowest-ranked unprotected Original of the cache as it stands,
 // moved by compact_core with every other token kept.  A workgroup whose cache is
 // within N_O returns at once, so in the steady state this launch does nothing.
-__global__ __launch_bounds__(kCompThreads) void arkv_rounds_kernel(
+// Registers are bounded to 128 (the loop spills): a workgroup that needs the
+// whole register file waits for a compute unit with no attention workgroup on
+// it, even to return at once.
+__global__ __launch_bounds__(kCompThreads, 4) void arkv_rounds_kernel(
     conf_cache c, Dims dm, int layer0, const int32_t* __restrict__ n_orig,
     uint8_t* __restrict__ keep_all, int32_t* __restrict__ plan_all, int32_t* __restrict__ mv8_all,
     int32_t* __restrict__ mv16_all, uint8_t* __restrict__ wkeep_all) {
