@@ -41,7 +41,11 @@
 // not fit on (a cache longer than the LDS rows, such as the first steps after a
 // long prefill) in per-unit rows of the workspace.  That costs 4*g bytes per
 // token written and read back, against the 2*d (INT8) or 4*d (16-bit) bytes of
-// keys and values the unit streams for it.
+// keys and values the unit streams for it.  At d = 128, a cache whose scores do
+// not all fit the LDS rows keeps those of its window halves in the wavefronts'
+// registers (up to four halves each, a 512-token window), so that the rows hold
+// the INT8 tokens only: the 4097-token caches after a long prefill then spill
+// nothing.
 #include <atomic>
 
 #include "ema.hpp"
@@ -168,7 +172,28 @@ struct Item {
   int n_valid;    // valid tokens in the item
   int tok0;       // unit token index of the first slot (scores in LDS)
   int mass0;      // mass-row index of the first slot
+  bool held;      // window half whose raw scores stay in the wavefront's registers
 };
+
+// Window halves whose raw scores a wavefront keeps in registers until the
+// normaliser is final, when every window half of the unit fits (nw <= 128 * NK):
+// s[m] holds the wavefront's m-th newest window half, in the score layout of
+// softmax_item (row block r, token 16r + 4*(lane/16) + i, head lane%16).
+template <int NK>
+struct Held {
+  float s[NK > 0 ? NK : 1][2][4];
+  int n;  // window halves held (wave-uniform)
+};
+// At d = 128 the four halves of a 512-token window (32 registers); at d = 64 the
+// two of a 256-token window (16 registers).
+__host__ __device__ constexpr int held_halves(int D) { return D == 128 ? 4 : 0; }
+
+// lane H of this lane's 16-lane row (DPP row broadcast, a VALU operand)
+template <int H>
+__device__ inline float row_lane(float x) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + H, 0xF, 0xF, false));
+}
 
 // Every item's keys and values are read as D/16 loads of 16 bytes per lane.
 // Keys: load i reads the 1 KB run at 1 KB * i, a lane at 16 * lane inside it.
@@ -327,9 +352,9 @@ struct ScoreSink {
 // rescale O and fill p.
 template <int R, int MODE, int D>
 __device__ inline void softmax_item(const f4* acc, float scale, bool head_ok, const Item& I,
-                                    WaveAcc<D>& wa, const ScoreSink& sk, float p[R][4]) {
+                                    WaveAcc<D>& wa, const ScoreSink& sk, float p[R][4],
+                                    float sig[R][4]) {
   const int lane = threadIdx.x & 63, g = lane >> 4, h = lane & 15;
-  float sig[R][4];
   float mloc = -INFINITY;
 #pragma unroll
   for (int r = 0; r < R; ++r)
@@ -352,7 +377,8 @@ __device__ inline void softmax_item(const f4* acc, float scale, bool head_ok, co
   wa.l = wa.l * corr + head_sum(lsum);
   wa.m = mnew;
   if constexpr (MODE != MODE_PLAIN) {
-    const bool to_lds = MODE == MODE_ONLINE || I.tok0 < sk.jsp;  // wave-uniform
+    // wave-uniform; a held window half goes neither to LDS nor to the workspace
+    const bool to_lds = !I.held && (MODE == MODE_ONLINE || I.tok0 < sk.jsp);
     if (to_lds && head_ok) {
 #pragma unroll
       for (int r = 0; r < R; ++r)
@@ -368,8 +394,9 @@ __device__ inline void softmax_item(const f4* acc, float scale, bool head_ok, co
       // go to an offset past the rows' range and are dropped, so no branch
       // surrounds a store and the wait counts of the loads in flight stay exact.
       // Tokens past the item's end store -inf into their own (unused) slots.
-      const uint32_t base =
-          (!to_lds && head_ok) ? 4u * (uint32_t)(h * sk.capt + I.mass0 + 4 * g) : kNoItem;
+      const uint32_t base = (!to_lds && !I.held && head_ok)
+                                ? 4u * (uint32_t)(h * sk.capt + I.mass0 + 4 * g)
+                                : kNoItem;
 #pragma unroll
       for (int r = 0; r < R; ++r)
         __builtin_amdgcn_raw_buffer_store_b128(
@@ -390,7 +417,7 @@ template <int D, bool BF16, int MODE, bool FP8>
 __device__ inline void compute_item(const Item& I, Buf<D>& K, const Buf<D>& V,
                                     const QOps<D, BF16>& q, float scale8, float scale16,
                                     bool head_ok, WaveAcc<D>& wa, const ScoreSink& sk, rsrc_t kr,
-                                    uint32_t koff, int klane) {
+                                    uint32_t koff, int klane, float hs[2][4]) {
   // Re-read the query operands from LDS for every item instead of letting the
   // compiler hoist 48 registers' worth of them out of the item loop.
   QOps<D, BF16> ql = q;
@@ -399,8 +426,8 @@ __device__ inline void compute_item(const Item& I, Buf<D>& K, const Buf<D>& V,
     f4 acc[4];
     scores_i8<D, BF16, FP8>(K, ql, acc);
     load_run_rs<D>(kr, koff, klane, K);  // the keys are used: the next item's start loading
-    float p[4][4];
-    softmax_item<4, MODE, D>(acc, scale8, head_ok, I, wa, sk, p);
+    float p[4][4], sig[4][4];
+    softmax_item<4, MODE, D>(acc, scale8, head_ok, I, wa, sk, p, sig);
     __builtin_amdgcn_sched_barrier(0);
     pv_i8<D, FP8>(V, p, wa.o);
   } else {
@@ -408,7 +435,7 @@ __device__ inline void compute_item(const Item& I, Buf<D>& K, const Buf<D>& V,
     scores_16<D, BF16>(K, ql, acc);
     load_run_rs<D>(kr, koff, klane, K);
     float p[2][4];
-    softmax_item<2, MODE, D>(acc, scale16, head_ok, I, wa, sk, p);
+    softmax_item<2, MODE, D>(acc, scale16, head_ok, I, wa, sk, p, hs);
     __builtin_amdgcn_sched_barrier(0);
     pv_16<D, BF16>(V, p, wa.o);
   }
@@ -437,6 +464,21 @@ __device__ inline void apply_vscale(WaveAcc<D>& wa, const float* sv) {
   for (int cb = 0; cb < D / 16; ++cb) wa.o[cb] *= sv[16 * cb + hl];
 }
 
+// sum[r][i] += e[r][i] of heads 0, 1, ..., G-1 in that order: every lane of a
+// 16-lane row (one token group, head = lane % 16) ends with its row's sum
+template <int H = 0>
+__device__ inline void add_heads_in_order(const float (&e)[2][4], float (&sum)[2][4], int G) {
+  if constexpr (H < kMaxGroup) {
+    if (H < G) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sum[r][i] += row_lane<H>(e[r][i]);
+      add_heads_in_order<H + 1>(e, sum, G);
+    }
+  }
+}
+
 // One pass of a wavefront over its items (it = wave, wave + 4, ...), software
 // pipelined on one key and one value buffer: an item's values load from the
 // start of its stage, and the next item's keys as soon as this item's scores
@@ -445,16 +487,17 @@ __device__ inline void apply_vscale(WaveAcc<D>& wa, const float* sv) {
 // window items run as two loops: each loop body is straight-line code, so the
 // compiler's wait counts stay exact (with both item kinds in one loop body it
 // merged the two paths' counts and waited for the values before the scores).
-// `kb` holds (or is receiving) the keys of item `wave`.
+// `kb` holds (or is receiving) the keys of item `wave`.  With `hold` every window
+// half of the wavefront (at most NK) keeps its raw scores in `held`.
 struct UnitRs {
   rsrc_t k8, v8, k16, v16;  // the unit's four regions
 };
 
-template <int D, bool BF16, int MODE, bool FP8>
+template <int D, bool BF16, int MODE, bool FP8, int NK>
 __device__ inline void wave_pass(int nitems, int nb8, int n8, int nw, int cap8, const UnitRs& rs,
                                  const QOps<D, BF16>& q, float scale8, float scale16, bool head_ok,
                                  WaveAcc<D>& wa, const float* sv, const ScoreSink& sk,
-                                 Buf<D>& kb) {
+                                 Buf<D>& kb, bool hold, Held<NK>& held) {
   // wave-uniform, so that the descriptor choice per item is a scalar select
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
@@ -471,9 +514,11 @@ __device__ inline void wave_pass(int nitems, int nb8, int n8, int nw, int cap8, 
     I.n_valid = min(kTile, n8 - it * kTile);
     I.tok0 = it * kTile;
     I.mass0 = it * kTile;
+    I.held = false;
+    float unused[2][4];
     compute_item<D, BF16, MODE, FP8>(
         I, kb, V, q, scale8, scale16, head_ok, wa, sk, nx < nb8 ? rs.k8 : rs.k16,
-        nx < nitems ? (uint32_t)(nx < nb8 ? nx : nx - nb8) * ib : kNoItem, klane);
+        nx < nitems ? (uint32_t)(nx < nb8 ? nx : nx - nb8) * ib : kNoItem, klane, unused);
   }
   // the INT8 value scale, once, between the INT8 and the window items (O is still 0
   // for a wavefront without INT8 items)
@@ -488,8 +533,24 @@ __device__ inline void wave_pass(int nitems, int nb8, int n8, int nw, int cap8, 
     I.n_valid = min(32, nw - 32 * j);
     I.tok0 = n8 + 32 * j;
     I.mass0 = cap8 + 32 * j;
+    I.held = NK > 0 && hold;
+    float hs[2][4];
     compute_item<D, BF16, MODE, FP8>(I, kb, V, q, scale8, scale16, head_ok, wa, sk, rs.k16,
-                                     nx < nitems ? (uint32_t)(nx - nb8) * ib : kNoItem, klane);
+                                     nx < nitems ? (uint32_t)(nx - nb8) * ib : kNoItem, klane,
+                                     hs);
+    if (NK > 0 && hold) {  // newest first
+#pragma unroll
+      for (int m = (NK > 0 ? NK : 1) - 1; m > 0; --m)
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) held.s[m][r][i] = held.s[m - 1][r][i];
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) held.s[0][r][i] = hs[r][i];
+      ++held.n;
+    }
   }
 }
 
@@ -582,7 +643,13 @@ __global__ __launch_bounds__(kAttnThreads, attn_min_blocks(D)) void attn_kernel(
   // CONF-KV and ARKV rank on each token's attention mass; the baselines do not
   const bool mass = dm.policy == CONF_POLICY_CONFKV || dm.policy == CONF_POLICY_ARKV;
   const int nc = n8 + nw;  // cached tokens (this step's token is handled apart)
-  const int jsp = min(spill_start(n8, score_cap), nc);
+  // When the cache's scores would not all fit the LDS rows and its window halves
+  // fit the wavefronts' registers, the LDS rows and the workspace keep the INT8
+  // tokens' scores only: ns tokens are kept there.
+  constexpr int NK = held_halves(D);
+  const bool hold = mass && nw <= kWaves * NK * 32 && spill_start(n8, score_cap) < nc;
+  const int ns = hold ? n8 : nc;
+  const int jsp = min(spill_start(n8, score_cap), ns);
   const int stride = jsp | 1;  // odd, so that the 16 heads of a store spread over banks
   const int region = max(G * (score_cap | 1), kWaves * G * D);
   const bool ob_apart = G * stride + kWaves * G * D <= region;  // uniform over the workgroup
@@ -676,15 +743,17 @@ __global__ __launch_bounds__(kAttnThreads, attn_min_blocks(D)) void attn_kernel(
 #pragma unroll
   for (int cb = 0; cb < D / 16; ++cb) wa.o[cb] = (f4){0.f, 0.f, 0.f, 0.f};
 
+  Held<NK> held;
+  held.n = 0;
   if (!mass)
-    wave_pass<D, BF16, MODE_PLAIN, FP8>(nitems, nb8, n8, nw, dm.cap8, urs, q, scale8, scale16,
-                                        head_ok, wa, s_sv, sink, cur);
-  else if (jsp >= nc)
-    wave_pass<D, BF16, MODE_ONLINE, FP8>(nitems, nb8, n8, nw, dm.cap8, urs, q, scale8, scale16,
-                                         head_ok, wa, s_sv, sink, cur);
+    wave_pass<D, BF16, MODE_PLAIN, FP8, NK>(nitems, nb8, n8, nw, dm.cap8, urs, q, scale8,
+                                            scale16, head_ok, wa, s_sv, sink, cur, false, held);
+  else if (jsp >= ns)
+    wave_pass<D, BF16, MODE_ONLINE, FP8, NK>(nitems, nb8, n8, nw, dm.cap8, urs, q, scale8,
+                                             scale16, head_ok, wa, s_sv, sink, cur, hold, held);
   else
-    wave_pass<D, BF16, MODE_SPILL, FP8>(nitems, nb8, n8, nw, dm.cap8, urs, q, scale8, scale16,
-                                        head_ok, wa, s_sv, sink, cur);
+    wave_pass<D, BF16, MODE_SPILL, FP8, NK>(nitems, nb8, n8, nw, dm.cap8, urs, q, scale8,
+                                            scale16, head_ok, wa, s_sv, sink, cur, hold, held);
   // ---- merge the waves' running (max, sum) and add this step's token.  Each
   // wavefront's O (value scale applied, not yet normalised) goes to LDS before
   // the barrier, and the O merge shares a phase with the mass; when its buffer
@@ -716,7 +785,38 @@ __global__ __launch_bounds__(kAttnThreads, attn_min_blocks(D)) void attn_kernel(
     // Per-token mass of this query group from the stored scores, summed over the
     // heads in order: four tokens per thread, the scores of four heads read
     // together (an index past the end reads the last token and is not stored).
-    // Tokens [0, jsp) from the LDS rows, the rest from the workspace rows.
+    // Tokens [0, jsp) from the LDS rows, the rest of the first ns from the
+    // workspace rows, and the window halves held in registers by their wavefronts
+    // (the heads' terms gathered lane by lane, added in the same order).
+    if (hold) {
+      // this wavefront's first window half; held.s[m] is its (held.n-1-m)-th
+      const int jf = (wave >= nb8 ? wave : wave + kWaves * ((nb8 - wave + kWaves - 1) / kWaves)) -
+                     nb8;
+      const float l = head_ok ? s_lse[hl] : 0.f;
+#pragma unroll
+      for (int m = 0; m < NK; ++m) {
+        if (m < held.n) {
+          const int j = jf + kWaves * (held.n - 1 - m);
+          const int nv = min(32, nw - 32 * j);
+          float e[2][4], sum[2][4];
+#pragma unroll
+          for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              e[r][i] = head_ok ? __expf(held.s[m][r][i] - l) : 0.f;
+              sum[r][i] = 0.f;
+            }
+          add_heads_in_order(e, sum, G);
+#pragma unroll
+          for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int tk = 16 * r + 4 * g + i;
+              if (hl == i && tk < nv) massp[dm.cap8 + 32 * j + tk] = sum[r][i];
+            }
+        }
+      }
+    }
     const int nl = jsp;
     for (int j0 = tid; j0 < nl; j0 += 4 * kAttnThreads) {
       float s[4] = {0.f, 0.f, 0.f, 0.f};
@@ -750,12 +850,12 @@ __global__ __launch_bounds__(kAttnThreads, attn_min_blocks(D)) void attn_kernel(
       }
     }
     const float* sp = spill_all + u * (size_t)G * dm.capt;
-    for (int j0 = nl + tid; j0 < nc; j0 += 4 * kAttnThreads) {
+    for (int j0 = nl + tid; j0 < ns; j0 += 4 * kAttnThreads) {
       float s[4] = {0.f, 0.f, 0.f, 0.f};
       int sl[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int j = min(j0 + k * kAttnThreads, nc - 1);
+        const int j = min(j0 + k * kAttnThreads, ns - 1);
         sl[k] = j < n8 ? j : dm.cap8 + (j - n8);
       }
       int h = 0;
@@ -780,7 +880,7 @@ __global__ __launch_bounds__(kAttnThreads, attn_min_blocks(D)) void attn_kernel(
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        if (j0 + k * kAttnThreads < nc) massp[sl[k]] = s[k];
+        if (j0 + k * kAttnThreads < ns) massp[sl[k]] = s[k];
     }
     // this step's token, from its score in registers (same sums, same order)
     if (appended && tid == kAttnThreads - 1) {

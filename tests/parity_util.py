@@ -136,4 +136,13 @@ def tiny_workloads() -> dict:
         name="gqa16_f16_d128_winspill", n_layers=1, batch=2, n_q_heads=16, n_kv_heads=1,
         head_dim=128, vocab=700, dtype16="f16", window=1200, protect=50, n_high=1400,
         n_low=1700, prefill=1600, steps=8)
+    # d = 128 with 16 query heads and a window of 250 (eight halves, the last one
+    # ragged): every cache holds more tokens than the LDS score rows, so the
+    # wavefronts keep their window halves' scores in registers; the first step's
+    # INT8 part is longer than the rows as well (its tail goes to the workspace),
+    # the later steps' INT8 part fits them
+    w["gqa16_bf16_d128_held"] = Workload(
+        name="gqa16_bf16_d128_held", n_layers=1, batch=2, n_q_heads=16, n_kv_heads=1,
+        head_dim=128, vocab=600, dtype16="bf16", window=250, protect=30, n_high=1100,
+        n_low=1250, prefill=2000, steps=8)
     return w
