@@ -254,7 +254,9 @@ int conf_confidence(const conf_params* p, const float* logits, float* c, int32_t
  * becomes decay*e + (1-decay)*mass_j, mass_j = mean over the Hq heads of its
  * softmax probability; the new token starts from e = 0.  K and V are read once
  * whatever the cache length: the raw scores wait for the final softmax
- * normaliser in LDS, and those of a cache longer than the LDS rows in ws.
+ * normaliser in LDS, and those of a cache longer than the LDS rows in ws (at
+ * d = 128 with a window of at most 512 tokens, its window's in registers, so
+ * that only INT8 tokens past the rows go to ws).
  * Under CONF_POLICY_ARKV
  * the EMA is that of ARKV's heavy-hitter score (see the policy).
  * CONF_E_INVALID under CONF_POLICY_TRIM, whose step is conf_attend followed by
