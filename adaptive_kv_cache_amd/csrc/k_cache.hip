@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kIngThreads) void ingest_amax_kernel(conf_cache c, 
     sv[(threadIdx.x / G8) * D + 8 * cg + e] = mv[e];
   }
   __syncthreads();
-  if (threadIdx.x < D) {
+  if ((int)threadIdx.x < D) {
     float a = 0.f, b = 0.f;
     for (int r = 0; r < rows; ++r) {
       a = fmaxf(a, sk[r * D + threadIdx.x]);
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kIngThreads) void ingest_tile_kernel(conf_cache c, 
     tk[i] = r < cnt ? *(const uint4*)(ks + (size_t)i * 8) : z;
     tv[i] = r < cnt ? *(const uint4*)(vs + (size_t)i * 8) : z;
   }
-  if (i8 && threadIdx.x < D) {
+  if (i8 && (int)threadIdx.x < D) {
     sk[threadIdx.x] = c.k_amax[u * D + threadIdx.x] / code_max(fp8);
     sv[threadIdx.x] = c.v_amax[u * D + threadIdx.x] / code_max(fp8);
   }
@@ -531,7 +531,7 @@ __device__ void v8_moves_by_run(const conf_cache& c, const Dims& dm, int lb, int
 // -1) is already cleared, and n8n / n16n count the kept INT8 / window tokens.
 // M.ngrown must be 0.  All kCompThreads threads call it.
 template <class C>
-__device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8, int n16, int t,
+__device__ void compact_core(const conf_cache& c, const Dims& dm, int lb, int n8, int n16,
                              int n8n, int n16n, int jd, const uint8_t* keep8, const uint8_t* wkeep,
                              CompFlagsT<C>& F, CompScratchT<C>& X, CompMiscT<C>& M, int32_t* plan_all,
                              int32_t* mv8_all, int32_t* mv16_all) {
@@ -897,7 +897,7 @@ __global__ __launch_bounds__(C::NT) void compact_kernel(conf_cache c, Dims dm, i
   }
   int n8n, n16n;
   count_kept(c8, c16, M, n8n, n16n);
-  compact_core(c, dm, lb, n8, n16, t, n8n, n16n, M.jd, keep8, wkeep, F, X, M, plan_all, mv8_all,
+  compact_core(c, dm, lb, n8, n16, n8n, n16n, M.jd, keep8, wkeep, F, X, M, plan_all, mv8_all,
                mv16_all);
 }
 
@@ -1069,7 +1069,7 @@ __global__ __launch_bounds__(kCompThreads, 6) void evict_kernel(conf_cache c, Di
   });
   int n8n, n16n;
   count_kept(c8, c16, M, n8n, n16n);  // its barrier also ends the key cache's use
-  compact_core(c, dm, lb, n8, n16, t, n8n, n16n, M.jd, keep8, wkeep, F, U.comp, M, plan_all,
+  compact_core(c, dm, lb, n8, n16, n8n, n16n, M.jd, keep8, wkeep, F, U.comp, M, plan_all,
                mv8_all, mv16_all);
 }
 
@@ -1248,7 +1248,7 @@ __global__ __launch_bounds__(kCompThreads) void arkv_kernel(
     jd = M.jd;
     if (jd >= 0) --n16n;
   }
-  compact_core(c, dm, lb, n8, n16, t, n8n, n16n, jd, keep8, wkeep, F, U.comp, M, plan_all,
+  compact_core(c, dm, lb, n8, n16, n8n, n16n, jd, keep8, wkeep, F, U.comp, M, plan_all,
                mv8_all, mv16_all);
 }
 
@@ -1311,7 +1311,7 @@ __global__ __launch_bounds__(kCompThreads, 4) void arkv_rounds_kernel(
     __syncthreads();
     const int jd = M.jd;
     if (jd < 0) break;  // every Original token is protected
-    compact_core(c, dm, lb, n8, n16, t, n8, n16 - 1, jd, keep8, wkeep, F, X, M, plan_all,
+    compact_core(c, dm, lb, n8, n16, n8, n16 - 1, jd, keep8, wkeep, F, X, M, plan_all,
                  mv8_all, mv16_all);
     // the demotee took the INT8 region's first free slot (or was dropped when it was full)
     n8 += n8 < dm.cap8 ? 1 : 0;
