@@ -30,10 +30,12 @@
  *     the `const conf_params*` / `conf_cache*` structs themselves, which are
  *     host memory read during the call only.  The library allocates no device
  *     memory; scratch lives in the caller's workspace `ws` of
- *     conf_workspace_bytes() bytes (256-byte aligned).  Its only process-wide
- *     state is one flag per (device, attention kernel variant) recording that
+ *     conf_workspace_bytes() bytes (256-byte aligned).  Its process-wide
+ *     state: one flag per (device, attention kernel variant) recording that
  *     the kernel's dynamic-LDS limit has been raised (an idempotent, thread-
- *     safe one-time set-up; nothing that holds data).
+ *     safe one-time set-up; nothing that holds data), and, for
+ *     conf_step_static only, that call's fixed scratch array on each GPU and
+ *     its looked-up device address (see conf_step_static).
  *   - A call validates its arguments on the host, enqueues kernels on `stream`
  *     (a hipStream_t; NULL is the null stream) and returns without waiting for
  *     the device.  Results are valid once the stream has been synchronised.
