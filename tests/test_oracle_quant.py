@@ -103,3 +103,51 @@ def test_state_demotes_position_t_minus_w():
     assert abs(K[0, 0, 0] - 1) <= 6 / 127 / 2 + 1e-6
     assert abs(K[1, 0, 0] - 2) <= 5 / 127 / 2 + 1e-6
     assert K[2, 0, 0] == pytest.approx(3.0 / 127 * 127, abs=1e-6)     # the absmax itself
+
+
+
+def _fl32_quotient(x, s):
+    """fl32(x / s) with one rounding: the binary64 quotient of two binary32 values
+    rounded to binary32 (53 >= 2*24 + 2, so the double rounding is innocuous)."""
+    return (np.asarray(x, F32).astype(np.float64) / np.asarray(s, F32).astype(np.float64)).astype(F32)
+
+
+def _near_halves(rng, n):
+    """fp32 pairs (x, s) whose quotient lies within a few ulps of k + 1/2 (k = 0..126):
+    the inputs on which the rounding of the quotient decides the code."""
+    s = rng.uniform(0.005, 0.05, n).astype(F32)
+    k = rng.integers(0, 127, n)
+    x = ((k + 0.5) * s.astype(np.float64)).astype(F32)
+    step = rng.integers(-3, 4, n)
+    for _ in range(3):  # move x by up to three ulps either way
+        x = np.where(step > 0, np.nextafter(x, F32(np.inf)), np.where(step < 0, np.nextafter(x, F32(-np.inf)), x))
+        step = step - np.sign(step)
+    sign = np.where(rng.random(n) < 0.5, F32(-1), F32(1))
+    return (x * sign).astype(F32), s
+
+
+def test_code_is_one_rounded_division_not_a_reciprocal_product():
+    """R19 reads the quotient x / s as one fp32 division.  On inputs where that and
+    x * fl32(1 / s) round to different codes, the oracle follows the division, both
+    for a fresh code and for a requantised one."""
+    rng = np.random.default_rng(7)
+    x, s = _near_halves(rng, 200_000)
+    div = np.clip(np.rint(_fl32_quotient(x, s)), -127, 127)
+    recip = np.clip(np.rint((x * (F32(1) / s).astype(F32)).astype(F32)), -127, 127)
+    differ = div != recip
+    assert differ.sum() >= 100, "the sample must hold cases that tell the two forms apart"
+    q = quant_codes(x, s)
+    assert np.array_equal(q.astype(np.float64), div)
+    # requantisation: clamp(rne(fl32(code * s_old) / s_new)), on products near k + 1/2
+    codes = rng.integers(-127, 128, 200_000).astype(np.int8)
+    s_old = rng.uniform(0.005, 0.05, codes.shape).astype(F32)
+    prod = (codes.astype(F32) * s_old).astype(F32)
+    k = np.floor(np.abs(codes.astype(np.float64)) * rng.uniform(0.3, 0.99, codes.shape))
+    s_new = (np.abs(prod).astype(np.float64) / (k + 0.5)).astype(F32)
+    ok = (codes != 0) & (s_new > s_old)
+    codes, s_old, s_new, prod = codes[ok], s_old[ok], s_new[ok], prod[ok]
+    div2 = np.clip(np.rint(_fl32_quotient(prod, s_new)), -127, 127)
+    recip2 = np.clip(np.rint((prod * (F32(1) / s_new).astype(F32)).astype(F32)), -127, 127)
+    assert (div2 != recip2).sum() >= 100
+    q2 = requant_codes(codes, s_old, s_new)
+    assert np.array_equal(q2.astype(np.float64), div2)
