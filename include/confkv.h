@@ -116,7 +116,10 @@ enum { CONF_POLICY_CONFKV = 0, CONF_POLICY_FULL = 1, CONF_POLICY_WINDOW = 2,
        CONF_POLICY_TRIM = 3, CONF_POLICY_ARKV = 4 };
 
 /* Device status word bits (conf_cache.status), set by kernels, never cleared
- * except by conf_cache_reset(). */
+ * except by conf_cache_reset().  CONF_ST_INT8_FULL cannot arise with parameters
+ * the library accepts (cap8 > n_low >= n_high bounds the INT8 part, and eviction
+ * runs before demotion); it guards a cache whose counters were changed outside
+ * the library. */
 enum {
   CONF_ST_WINDOW_FULL = 1, /* append found the 16-bit window full: token dropped */
   CONF_ST_INT8_FULL = 2    /* a demotion found the INT8 region full: token dropped */
