@@ -301,7 +301,8 @@ def run(args):
     big = L * B * wl.n_kv_heads * wl.head_dim * (wl.n_high + wl.window) * 2 >= 1 << 28
     streams = args.streams
     if streams == "auto":
-        streams = "2" if big and not no_conf else "1"  # nothing to overlap otherwise
+        # nothing to overlap otherwise; in a graph the confidence branch costs no launch
+        streams = "2" if (big or args.graph) and not no_conf else "1"
     side = main if streams == "1" else torch.cuda.Stream(device=dev)
     split = args.split
     if split == "auto":
@@ -311,10 +312,8 @@ def run(args):
         units = L * B * wl.n_kv_heads
         split = "2" if big and units >= 2048 else "1"
     split = int(split)
-    if args.graph:
-        if split != 1 or streams != "1":
-            raise SystemExit("--graph captures one stream: use --split 1 --streams 1 (or auto on a "
-                             "small cache)")
+    if args.graph and split != 1:
+        raise SystemExit("--graph captures one layer range: use --split 1 (or auto on a small cache)")
     if split > 1 and side is main:
         side = torch.cuda.Stream(device=dev)  # the halves must not wait on each other
     # Layer halves: two views of the one cache, each with its own workspace, each
@@ -412,21 +411,32 @@ def run(args):
     torch.cuda.synchronize()
     if args.graph:
         # every timed step captured in one HIP graph (kernel nodes, and the plan
-        # copies of the byte model as copy nodes), replayed once in the timed region
+        # copies of the byte model as copy nodes), replayed once in the timed region;
+        # with a second stream each step's confidence is a branch beside its
+        # attention, joined before its eviction
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream()
             for i in range(args.steps):
                 s = args.warmup + i
                 q_, k_, v_, o_, b_, lb_ = vargs[s][0]
                 if i:
                     hplan[i - 1].copy_(ws_plans[0])
+                fork = not no_conf and side is not main
+                if fork:
+                    side.wait_stream(cap)
+                    with torch.cuda.stream(side):
+                        eng.confidence(logits[s], c=conf[s], budget=budget[s])
                 eng.attend(-1, q_, k_, v_, out=o_)
                 if trim:
                     eng.trim_evict_compact(-1, b_, lb_)
                 elif arkv:
                     eng.arkv_ema_evict_compact(-1, b_, norig_v[0])
                 else:
-                    eng.confidence(logits[s], c=conf[s], budget=budget[s])
+                    if fork:
+                        cap.wait_stream(side)
+                    else:
+                        eng.confidence(logits[s], c=conf[s], budget=budget[s])
                     eng.ema_evict_compact(-1, b_)
         torch.cuda.synchronize()
         start.record()
@@ -718,8 +728,9 @@ def main():
                     help="2: confidence on a second stream beside the attention; auto: 2 when "
                          "the attention streams at least 256 MB per launch")
     ap.add_argument("--graph", action="store_true",
-                    help="capture every timed step in one HIP graph and replay it (one stream, "
-                         "no layer split: for the launch-bound small caches)")
+                    help="capture every timed step in one HIP graph and replay it (no layer "
+                         "split; the confidence a branch beside the attention unless --streams 1: "
+                         "for the launch-bound small caches)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--rocpd-summary", metavar="DB",
                     help="print per-kernel durations of a rocprofv3 database and exit")

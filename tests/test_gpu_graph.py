@@ -7,7 +7,9 @@ step (conf_attend, conf_confidence, conf_ema_evict_compact) capture as kernel
 nodes.  Two caches take identical inputs: one runs eagerly, the other replays a
 graph of ten steps five times, with eager work and synchronisations in between.
 After every replay both caches, outputs, confidences and budgets must be
-bit-identical (the same kernels on the same data)."""
+bit-identical (the same kernels on the same data).  The graph is captured from
+one stream, and again with each step's confidence a branch on a second stream
+beside its attention, joined before its eviction."""
 import pytest
 import torch
 
@@ -27,15 +29,26 @@ def _inputs(wl, steps0, n):
              *synth.kv_new(wl, s, SEED, device="cuda")) for s in range(steps0, steps0 + n)]
 
 
-def _step(eng, wl, inp, out, c, budget):
+def _step(eng, wl, inp, out, c, budget, side=None):
+    """One step; with `side` the confidence is a branch on that stream, forked
+    before the attention and joined before the eviction."""
     z, q, k, v = inp
+    if side is not None:
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            eng.confidence(z, c=c, budget=budget)
     eng.attend(-1, q, k, v, out=out)
-    eng.confidence(z, c=c, budget=budget)
+    if side is not None:
+        main.wait_stream(side)
+    else:
+        eng.confidence(z, c=c, budget=budget)
     eng.ema_evict_compact(-1, budget)
 
 
+@pytest.mark.parametrize("fork", [False, True], ids=["one-stream", "forked-confidence"])
 @pytest.mark.parametrize("name", ["gpt2_12layer_b8_pyramid", "gpt2_1layer_b1"])
-def test_graph_replays_equal_eager_steps(name):
+def test_graph_replays_equal_eager_steps(name, fork):
     wl = WORKLOADS[name]
     eager, graph = Engine(wl), Engine(wl)
     L, B = wl.n_layers, wl.batch
@@ -54,10 +67,11 @@ def test_graph_replays_equal_eager_steps(name):
     gout = [bufs() for _ in range(K)]
     eout = [bufs() for _ in range(K)]
     torch.cuda.synchronize()
+    side = torch.cuda.Stream() if fork else None
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for inp, b in zip(steps, gout):
-            _step(graph, wl, inp, *b)
+            _step(graph, wl, inp, *b, side=side)
     for r in range(REPLAYS):
         g.replay()
         for inp, b in zip(steps, eout):
