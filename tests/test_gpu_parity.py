@@ -81,8 +81,9 @@ def test_confidence(V, B, T):
     _check_conf(c.cpu().numpy(), budget.cpu().numpy(), z.numpy().astype(np.float64), wl)
 
 
-def test_confidence_special_cases():
-    V, B = 50257, 5
+@pytest.mark.parametrize("V", [50257, 152064], ids=["scalar-loads", "16-byte-loads"])
+def test_confidence_special_cases(V):
+    B = 5
     wl = _conf_wl(V, B, L=1, pyramid=False)
     eng = Engine(wl)
     z = torch.zeros(B, V)
