@@ -1049,10 +1049,13 @@ __global__ __launch_bounds__(kCompThreads, 6) void evict_kernel(conf_cache c, Di
                          ? -1
                          : t - dm.W;
   int c8 = 0, c16 = 0;
+  // (both counts advance on every token: with the increment inside each branch the
+  // compiler kept the two counts in private memory and added through a selected
+  // address, one scratch round trip per token)
   select_core<kCompThreads, EMA>(c, dm, lb, n8, n16, t, N, U.sel, SM, [&](int j, int k, uint64_t key) {
-    if (j < n8) {
+    const bool is8 = j < n8;
+    if (is8) {
       if (j < kLdsFlags8) F.k8[j] = (uint8_t)k; else keep8[j] = (uint8_t)k;
-      c8 += k;
     } else {
       const int w = j - n8;
       if (k && target >= 0) {
@@ -1064,8 +1067,9 @@ __global__ __launch_bounds__(kCompThreads, 6) void evict_kernel(conf_cache c, Di
         }
       }
       if (w < kLdsFlags16) F.k16[w] = (uint8_t)k; else wkeep[w] = (uint8_t)k;
-      c16 += k;
     }
+    c8 += is8 ? k : 0;
+    c16 += is8 ? 0 : k;
   });
   int n8n, n16n;
   count_kept(c8, c16, M, n8n, n16n);  // its barrier also ends the key cache's use
@@ -1214,9 +1218,9 @@ __global__ __launch_bounds__(kCompThreads) void arkv_kernel(
   int ms = -1;
   int c8 = 0, c16 = 0;
   select_core<kCompThreads, EMA>(c, dm, lb, n8, n16, t, N, U.sel, SM, [&](int j, int k, uint64_t key) {
-    if (j < n8) {
+    const bool is8 = j < n8;  // both counts advance on every token (no private-memory counts)
+    if (is8) {
       if (j < kLdsFlags8) F.k8[j] = (uint8_t)k; else keep8[j] = (uint8_t)k;
-      c8 += k;
     } else {
       const int w = j - n8;
       if (k) {
@@ -1227,8 +1231,9 @@ __global__ __launch_bounds__(kCompThreads) void arkv_kernel(
         }
       }
       if (w < kLdsFlags16) F.k16[w] = (uint8_t)k; else wkeep[w] = (uint8_t)k;
-      c16 += k;
     }
+    c8 += is8 ? k : 0;
+    c16 += is8 ? 0 : k;
   });
   int n8n, n16n;
   count_kept(c8, c16, M, n8n, n16n);  // its barrier also ends the key cache's use

@@ -17,13 +17,12 @@ namespace confkv {
 constexpr int kConfThreads = 256;
 constexpr int kConfPer = 16;  // logits per thread per chunk
 
+// (a, b) = the two largest values seen, duplicates counted; z is never NaN.  Written
+// with min/max: as a branch the compiler kept (a, b) in private memory and stored
+// through a selected address.
 __device__ inline void top2_push(float z, float& a, float& b) {
-  if (z > a) {
-    b = a;
-    a = z;
-  } else if (z > b) {
-    b = z;
-  }
+  b = fmaxf(b, fminf(a, z));
+  a = fmaxf(a, z);
 }
 __device__ inline void top2_merge(float& a, float& b, float a2, float b2) {
   const float hi = fmaxf(a, a2), lo = fminf(a, a2);
@@ -41,41 +40,38 @@ __global__ __launch_bounds__(kConfThreads) void conf_partial_kernel(const float*
   const int chunk = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const float* row = logits + (size_t)b * V;
   const int base = chunk * kConfThreads * kConfPer;
+  // Every load is issued before the first use, unconditionally (an index past the
+  // row reads the row's last element and is then discarded), so that the chunk
+  // costs one memory round trip: with a branch around each load the compiler
+  // waits for every load before issuing the next.
   float z[kConfPer];
-  float m = -INFINITY, a = -INFINITY, a2 = -INFINITY;
-  int bad = 0;
   if constexpr (VEC) {
-    // thread tid reads elements base + 4*(i*256 + tid) .. +3
+    // thread tid reads elements base + 4*(i*256 + tid) .. +3 (V is a multiple of 4)
 #pragma unroll
     for (int i = 0; i < kConfPer / 4; ++i) {
       const int idx = base + 4 * (i * kConfThreads + tid);
-      float4 v4 = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-      if (idx < V) v4 = *(const float4*)(row + idx);
-      const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float v = vv[e];
-        if (idx < V) {
-          if (!isfinite(v)) { bad = 1; v = -INFINITY; }
-          top2_push(v, a, a2);
-        }
-        z[4 * i + e] = v;
-        m = fmaxf(m, v);
-      }
+      const float4 v4 = *(const float4*)(row + (idx < V ? idx : V - 4));
+      z[4 * i] = v4.x;
+      z[4 * i + 1] = v4.y;
+      z[4 * i + 2] = v4.z;
+      z[4 * i + 3] = v4.w;
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < kConfPer; ++i) {
-      const int idx = base + i * kConfThreads + tid;
-      float v = -INFINITY;
-      if (idx < V) {
-        v = row[idx];
-        if (!isfinite(v)) { bad = 1; v = -INFINITY; }
-        top2_push(v, a, a2);
-      }
-      z[i] = v;
-      m = fmaxf(m, v);
-    }
+    for (int i = 0; i < kConfPer; ++i) z[i] = row[min(base + i * kConfThreads + tid, V - 1)];
+  }
+  float m = -INFINITY, a = -INFINITY, a2 = -INFINITY;
+  int bad = 0;
+#pragma unroll
+  for (int i = 0; i < kConfPer; ++i) {
+    const int idx = VEC ? base + 4 * ((i / 4) * kConfThreads + tid) + (i % 4)
+                        : base + i * kConfThreads + tid;
+    const bool ok = idx < V, fin = isfinite(z[i]);
+    bad |= (ok && !fin) ? 1 : 0;
+    const float v = (ok && fin) ? z[i] : -INFINITY;  // non-finite logits count as -inf
+    top2_push(v, a, a2);
+    z[i] = v;
+    m = fmaxf(m, v);
   }
   __shared__ float red[kConfThreads / 64][6];
   __shared__ float bm;
