@@ -29,8 +29,11 @@ runs beside the other half's attention rather than after all of it (measured on 
 Qwen-32B batch-8 cache: 0.494 against 0.540 ms per step; four or eight parts were
 slower).  The attention time of a step is then the union of its two launches, from
 the first start to the last end, and the roofline's bytes are those of all layers.
-Only caches whose attention launch has at least 2048 workgroups are split (the
-Qwen-32B batch-1 cache, 512, fell to 0.55x).  --split 1|2 overrides the choice.
+Only caches whose attention launch has at least 2048 workgroups and whose K/V at the
+tight budget, counted at one byte per channel, reach 512 MiB per step are split (the
+Qwen-32B batch-1 cache, 512 workgroups, fell to 0.55x; the 256-token sliding-window
+baselines of the Qwen-14B and gpt-oss-20b shapes, 384 MiB, to 0.55-0.69x).  --split
+1|2 overrides the choice.
 
 A half's attention of step s+1 waits for that half's eviction of step s and for
 nothing of the other half, so successive steps overlap across the halves: every
@@ -297,8 +300,11 @@ def run(args):
     n16_first = torch.empty_like(n8_first)
     hplan = torch.empty(args.steps, L, S, 16, dtype=torch.int32, device=dev)
     main = torch.cuda.current_stream(dev)
-    # K/V bytes one attention launch streams at the tight budget
-    big = L * B * wl.n_kv_heads * wl.head_dim * (wl.n_high + wl.window) * 2 >= 1 << 28
+    # K/V bytes of one step's attention at the tight budget, counted at one byte per
+    # channel: the split and the second stream pay from 512 MiB (measured: the CONF-KV
+    # Qwen-14B and gpt-oss-20b caches, 960 MiB by this count, gain from the halves;
+    # their 256-token sliding-window baselines, 384 MiB, ran 0.55-0.69x with them)
+    big = L * B * wl.n_kv_heads * wl.head_dim * (wl.n_high + wl.window) * 2 >= 1 << 29
     streams = args.streams
     if streams == "auto":
         # nothing to overlap otherwise; in a graph the confidence branch costs no launch
