@@ -69,7 +69,10 @@ def _check_conf(c_gpu, budget_gpu, z, wl):
         assert list(budget_gpu[b]) == want
 
 
-@pytest.mark.parametrize("V,B", [(1000, 3), (4097, 1), (50257, 2), (152064, 8), (201088, 4)])
+# V = 2, 3, 4 and 5: rows shorter than one thread's loads (the loads past the row
+# are clamped into it and discarded), with 16-byte loads at V = 4
+@pytest.mark.parametrize("V,B", [(2, 2), (3, 1), (4, 2), (5, 3), (1000, 3), (4097, 1), (50257, 2),
+                                 (152064, 8), (201088, 4)])
 @pytest.mark.parametrize("T", [0.5, 2.0, 8.0])
 def test_confidence(V, B, T):
     _say("confidence", V, B, T)
